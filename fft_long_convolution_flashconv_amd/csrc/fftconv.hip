@@ -1,0 +1,204 @@
+// fftconv.hip -- fused FFT long convolution kernels (fp32 VALU engine) for
+// h3conv_fft_conv and h3conv_h3_mix.
+//
+// One workgroup owns one channel.  It first transforms the channel's filter
+// (with the residual weight D folded into tap 0, since D*u is the convolution
+// of u with D*delta) and keeps the spectrum in registers; it then walks over
+// the batch two rows at a time, packing row 2s into the real part and row
+// 2s+1 into the imaginary part of one complex signal.  Because the filter is
+// real, the inverse transform of (spectrum of the pair) x (filter spectrum)
+// returns the two convolutions in the real and imaginary parts, so one
+// complex transform pair serves two rows.
+//
+// Method: paperlayer.ai summary of "Hungry Hungry Hippos", section 2
+// "Convolutional view" (FFT, pointwise product, inverse FFT), section 4
+// ("fuses FFT, pointwise multiplication, and inverse FFT"), Appendix C.1
+// (zero-pad to 2L, keep the first N).
+#include "h3conv_device.h"
+#include "h3conv_internal.h"
+
+namespace h3c {
+
+int fused_log2m(int64_t N) {
+    int l = 5;  // Np >= 32
+    while ((int64_t(1) << l) < N) ++l;
+    return l + 1;
+}
+
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(Plan<LOG2M>::NT) void k_fft_conv(
+    const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f,
+    const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
+    using T = typename io_elem<IO>::T;
+    __shared__ cf lds[Plan<LOG2M>::LDS_ELEMS];
+    const int tid = threadIdx.x;
+    const int h = blockIdx.x;
+    const float *fh = f + (size_t)h * N;
+    const float dh = D[h];
+
+    FiltReg<LOG2M> F;
+    auto ldf = [&](int pos) -> cf {
+        float v = (pos < N) ? fh[pos] : 0.f;
+        if (pos == 0) v += dh;
+        return mk(v, 0.f);
+    };
+    filter_spectrum<LOG2M>(lds, tid, ldf, F);
+
+    const int nsig = (B + 1) / 2;
+    for (int s = 0; s < nsig; ++s) {
+        const int b0 = 2 * s;
+        const bool has1 = (b0 + 1) < B;
+        const T *u0 = u + ((size_t)b0 * H + h) * N;
+        const T *u1 = u0 + (size_t)H * N;
+        T *y0 = y + ((size_t)b0 * H + h) * N;
+        T *y1 = y0 + (size_t)H * N;
+        auto ld = [&](int pos) -> cf {
+            if (pos >= N) return mk(0.f, 0.f);
+            return mk(ld_io<IO>(u0 + pos), has1 ? ld_io<IO>(u1 + pos) : 0.f);
+        };
+        auto st = [&](int pos, cf v) {
+            if (pos < N) {
+                st_io<IO>(y0 + pos, v.x);
+                if (has1) st_io<IO>(y1 + pos, v.y);
+            }
+        };
+        conv_signal<LOG2M>(lds, tid, F, ld, st);
+    }
+}
+
+// H3 mix (head dimension 1), channel-last [B,N,Dm]: the loader forms
+// m_t = (sum_{i<L} w_i k_{t-i}) * v_t, the store applies out_t = q_t * z_t.
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(Plan<LOG2M>::NT) void k_h3_mix(
+    const typename io_elem<IO>::T *__restrict__ q, const typename io_elem<IO>::T *__restrict__ k,
+    const typename io_elem<IO>::T *__restrict__ v, const float *__restrict__ w,
+    const float *__restrict__ f, const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ out,
+    int B, int N, int Dm, int L) {
+    using T = typename io_elem<IO>::T;
+    __shared__ cf lds[Plan<LOG2M>::LDS_ELEMS];
+    const int tid = threadIdx.x;
+    const int d = blockIdx.x;
+    const float *fd = f + (size_t)d * N;
+    const float dd = D[d];
+    float wd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wd[i] = (i < L) ? w[(size_t)d * L + i] : 0.f;
+
+    FiltReg<LOG2M> F;
+    auto ldf = [&](int pos) -> cf {
+        float x = (pos < N) ? fd[pos] : 0.f;
+        if (pos == 0) x += dd;
+        return mk(x, 0.f);
+    };
+    filter_spectrum<LOG2M>(lds, tid, ldf, F);
+
+    const size_t rowstride = (size_t)N * Dm;
+    const int nsig = (B + 1) / 2;
+    for (int s = 0; s < nsig; ++s) {
+        const int b0 = 2 * s;
+        const bool has1 = (b0 + 1) < B;
+        const size_t o0 = (size_t)b0 * rowstride + d;
+        const size_t o1 = o0 + rowstride;
+        auto mval = [&](size_t o, int t) -> float {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < L && i <= t) acc = fmaf(wd[i], ld_io<IO>(k + o + (size_t)(t - i) * Dm), acc);
+            return acc * ld_io<IO>(v + o + (size_t)t * Dm);
+        };
+        auto ld = [&](int t) -> cf {
+            if (t >= N) return mk(0.f, 0.f);
+            return mk(mval(o0, t), has1 ? mval(o1, t) : 0.f);
+        };
+        auto st = [&](int t, cf z) {
+            if (t < N) {
+                const size_t a0 = o0 + (size_t)t * Dm;
+                st_io<IO>(out + a0, ld_io<IO>(q + a0) * z.x);
+                if (has1) {
+                    const size_t a1 = o1 + (size_t)t * Dm;
+                    st_io<IO>(out + a1, ld_io<IO>(q + a1) * z.y);
+                }
+            }
+        };
+        conv_signal<LOG2M>(lds, tid, F, ld, st);
+    }
+}
+
+template <int LOG2M, int IO>
+static hipError_t launch_fc(const void *u, const float *f, const float *D, void *y, int B, int H,
+                            int N, hipStream_t s) {
+    using T = typename io_elem<IO>::T;
+    hipLaunchKernelGGL((k_fft_conv<LOG2M, IO>), dim3(H), dim3(Plan<LOG2M>::NT), 0, s,
+                       (const T *)u, f, D, (T *)y, B, H, N);
+    return hipGetLastError();
+}
+
+template <int IO>
+static hipError_t fc_dispatch(int log2m, const void *u, const float *f, const float *D, void *y,
+                              int B, int H, int N, hipStream_t s) {
+    switch (log2m) {
+        case 6: return launch_fc<6, IO>(u, f, D, y, B, H, N, s);
+        case 7: return launch_fc<7, IO>(u, f, D, y, B, H, N, s);
+        case 8: return launch_fc<8, IO>(u, f, D, y, B, H, N, s);
+        case 9: return launch_fc<9, IO>(u, f, D, y, B, H, N, s);
+        case 10: return launch_fc<10, IO>(u, f, D, y, B, H, N, s);
+        case 11: return launch_fc<11, IO>(u, f, D, y, B, H, N, s);
+        case 12: return launch_fc<12, IO>(u, f, D, y, B, H, N, s);
+        case 13: return launch_fc<13, IO>(u, f, D, y, B, H, N, s);
+        case 14: return launch_fc<14, IO>(u, f, D, y, B, H, N, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fft_conv(const void *u, const float *f, const float *D, void *y, int B, int H,
+                           int N, int io, hipStream_t s) {
+    const int l = fused_log2m(N);
+    switch (io) {
+        case IO_F32: return fc_dispatch<IO_F32>(l, u, f, D, y, B, H, N, s);
+        case IO_F16: return fc_dispatch<IO_F16>(l, u, f, D, y, B, H, N, s);
+        case IO_BF16: return fc_dispatch<IO_BF16>(l, u, f, D, y, B, H, N, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int LOG2M, int IO>
+static hipError_t launch_hm(const void *q, const void *k, const void *v, const float *w,
+                            const float *f, const float *D, void *out, int B, int N, int Dm, int L,
+                            hipStream_t s) {
+    using T = typename io_elem<IO>::T;
+    hipLaunchKernelGGL((k_h3_mix<LOG2M, IO>), dim3(Dm), dim3(Plan<LOG2M>::NT), 0, s, (const T *)q,
+                       (const T *)k, (const T *)v, w, f, D, (T *)out, B, N, Dm, L);
+    return hipGetLastError();
+}
+
+template <int IO>
+static hipError_t hm_dispatch(int log2m, const void *q, const void *k, const void *v,
+                              const float *w, const float *f, const float *D, void *out, int B,
+                              int N, int Dm, int L, hipStream_t s) {
+    switch (log2m) {
+        case 6: return launch_hm<6, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case 7: return launch_hm<7, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case 8: return launch_hm<8, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case 9: return launch_hm<9, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case 10: return launch_hm<10, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case 11: return launch_hm<11, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case 12: return launch_hm<12, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case 13: return launch_hm<13, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case 14: return launch_hm<14, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_h3_mix(const void *q, const void *k, const void *v, const float *w,
+                         const float *f, const float *D, void *out, int B, int N, int Dm, int L,
+                         int io, hipStream_t s) {
+    const int l = fused_log2m(N);
+    switch (io) {
+        case IO_F32: return hm_dispatch<IO_F32>(l, q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case IO_F16: return hm_dispatch<IO_F16>(l, q, k, v, w, f, D, out, B, N, Dm, L, s);
+        case IO_BF16: return hm_dispatch<IO_BF16>(l, q, k, v, w, f, D, out, B, N, Dm, L, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace h3c
