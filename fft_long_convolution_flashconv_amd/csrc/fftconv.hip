@@ -16,6 +16,7 @@
 // (zero-pad to 2L, keep the first N).
 #include "h3conv_device.h"
 #include "h3conv_internal.h"
+#include "mfma_engine.h"
 
 namespace h3c {
 
@@ -124,6 +125,108 @@ __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_h3_mix(
     }
 }
 
+
+// ---------------------------------------------------------------- MFMA block-FFT variants
+// fp16 / bf16 activations, 2N >= 256: same per-channel structure, transforms on
+// the matrix cores (see mfma_engine.h).
+
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_fft_conv_mfma(
+    const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f,
+    const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
+    using T = typename io_elem<IO>::T;
+    using SH = mf::Shape<LOG2M>;
+    constexpr int KIND = IO == IO_F16 ? mf::IN_F16 : mf::IN_BF16;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[SH::LDS_DWORDS];
+    mf::Engine<LOG2M, KIND> E(smem);
+    E.init();
+    const int h = blockIdx.x;
+    const float *fh = f + (size_t)h * N;
+    const float dh = D[h];
+    const size_t rs = (size_t)H * N;          // stride between batch rows
+    const T *uh = u + (size_t)h * N;
+    T *yh = y + (size_t)h * N;
+    const int hb = mf::half_bits(N);
+    auto ldf = [&](int pos) -> float {
+        float v = fh[pos];
+        if (pos == 0) v += dh;
+        return v;
+    };
+    // complex signal `sig` = batch rows 2 sig (real part), 2 sig + 1 (imaginary)
+    auto rows = [&](int sig) -> mf::RowPtrs {
+        const int b0 = 2 * sig;
+        const bool two = b0 + 1 < B;
+        const uint16_t *i0 = (const uint16_t *)(uh + (size_t)b0 * rs);
+        uint16_t *o0 = (uint16_t *)(yh + (size_t)b0 * rs);
+        return {i0, two ? i0 + rs : nullptr, o0, two ? o0 + rs : nullptr};
+    };
+    E.run_raw(ldf, N, rows, (B + 1) / 2, N, hb);
+}
+
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_h3_mix_mfma(
+    const typename io_elem<IO>::T *__restrict__ q, const typename io_elem<IO>::T *__restrict__ k,
+    const typename io_elem<IO>::T *__restrict__ v, const float *__restrict__ w,
+    const float *__restrict__ f, const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ out,
+    int B, int N, int Dm, int L) {
+    using SH = mf::Shape<LOG2M>;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[SH::LDS_DWORDS];
+    mf::Engine<LOG2M, mf::IN_FP32> E(smem);
+    E.init();
+    const int d = blockIdx.x;
+    const float *fd = f + (size_t)d * N;
+    const float dd = D[d];
+    float wd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wd[i] = (i < L) ? w[(size_t)d * L + i] : 0.f;
+    const int hb = mf::half_bits(N);
+    auto ldf = [&](int pos) -> float {
+        float x = fd[pos];
+        if (pos == 0) x += dd;
+        return x;
+    };
+    const size_t rowstride = (size_t)N * Dm;
+    auto mval = [&](size_t o, int t) -> float {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i < L && i <= t) acc = fmaf(wd[i], ld_io<IO>(k + o + (size_t)(t - i) * Dm), acc);
+        return acc * ld_io<IO>(v + o + (size_t)t * Dm);
+    };
+    auto ld = [&](int sig, int t) -> cf {
+        const int b0 = 2 * sig;
+        if (t >= N) return mk(0.f, 0.f);
+        const size_t o0 = (size_t)b0 * rowstride + d;
+        return mk(mval(o0, t), (b0 + 1 < B) ? mval(o0 + rowstride, t) : 0.f);
+    };
+    auto st = [&](int sig, int t, float re, float im) {
+        const int b0 = 2 * sig;
+        const size_t a0 = (size_t)b0 * rowstride + d + (size_t)t * Dm;
+        st_io<IO>(out + a0, ld_io<IO>(q + a0) * re);
+        if (b0 + 1 < B) st_io<IO>(out + a0 + rowstride, ld_io<IO>(q + a0 + rowstride) * im);
+    };
+    E.run_fp32(ldf, N, ld, st, (B + 1) / 2, N, hb);
+}
+
+template <int LOG2M, int IO>
+static hipError_t launch_fc_mfma(const void *u, const float *f, const float *D, void *y, int B,
+                                 int H, int N, hipStream_t s) {
+    using T = typename io_elem<IO>::T;
+    hipLaunchKernelGGL((k_fft_conv_mfma<LOG2M, IO>), dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
+                       (const T *)u, f, D, (T *)y, B, H, N);
+    return hipGetLastError();
+}
+
+template <int LOG2M, int IO>
+static hipError_t launch_hm_mfma(const void *q, const void *k, const void *v, const float *w,
+                                 const float *f, const float *D, void *out, int B, int N, int Dm,
+                                 int L, hipStream_t s) {
+    using T = typename io_elem<IO>::T;
+    hipLaunchKernelGGL((k_h3_mix_mfma<LOG2M, IO>), dim3(Dm), dim3(mf::Shape<LOG2M>::NT), 0, s,
+                       (const T *)q, (const T *)k, (const T *)v, w, f, D, (T *)out, B, N, Dm, L);
+    return hipGetLastError();
+}
+
 template <int LOG2M, int IO>
 static hipError_t launch_fc(const void *u, const float *f, const float *D, void *y, int B, int H,
                             int N, hipStream_t s) {
@@ -136,6 +239,17 @@ static hipError_t launch_fc(const void *u, const float *f, const float *D, void 
 template <int IO>
 static hipError_t fc_dispatch(int log2m, const void *u, const float *f, const float *D, void *y,
                               int B, int H, int N, hipStream_t s) {
+    if constexpr (IO != IO_F32) {
+        switch (log2m) {
+            case 9: return launch_fc_mfma<9, IO>(u, f, D, y, B, H, N, s);
+            case 10: return launch_fc_mfma<10, IO>(u, f, D, y, B, H, N, s);
+            case 11: return launch_fc_mfma<11, IO>(u, f, D, y, B, H, N, s);
+            case 12: return launch_fc_mfma<12, IO>(u, f, D, y, B, H, N, s);
+            case 13: return launch_fc_mfma<13, IO>(u, f, D, y, B, H, N, s);
+            case 14: return launch_fc_mfma<14, IO>(u, f, D, y, B, H, N, s);
+            default: break;
+        }
+    }
     switch (log2m) {
         case 6: return launch_fc<6, IO>(u, f, D, y, B, H, N, s);
         case 7: return launch_fc<7, IO>(u, f, D, y, B, H, N, s);
@@ -175,6 +289,17 @@ template <int IO>
 static hipError_t hm_dispatch(int log2m, const void *q, const void *k, const void *v,
                               const float *w, const float *f, const float *D, void *out, int B,
                               int N, int Dm, int L, hipStream_t s) {
+    if constexpr (IO != IO_F32) {
+        switch (log2m) {
+            case 9: return launch_hm_mfma<9, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+            case 10: return launch_hm_mfma<10, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+            case 11: return launch_hm_mfma<11, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+            case 12: return launch_hm_mfma<12, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+            case 13: return launch_hm_mfma<13, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+            case 14: return launch_hm_mfma<14, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
+            default: break;
+        }
+    }
     switch (log2m) {
         case 6: return launch_hm<6, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);
         case 7: return launch_hm<7, IO>(q, k, v, w, f, D, out, B, N, Dm, L, s);

@@ -17,6 +17,7 @@
 // the same factored power tables.
 #include "h3conv_device.h"
 #include "h3conv_internal.h"
+#include "mfma_engine.h"
 
 namespace h3c {
 
@@ -302,12 +303,47 @@ __global__ __launch_bounds__(256) void k_sp_correct(typename io_elem<IO>::T *__r
     }
 }
 
+// Same chunk convolution on the MFMA block-FFT engine (fp16 / bf16 I/O).
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_sp_chunk_conv_mfma(
+    const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ fT,
+    typename io_elem<IO>::T *__restrict__ y, int B, int H, int64_t N, int T) {
+    using SH = mf::Shape<LOG2M>;
+    constexpr int KIND = IO == IO_F16 ? mf::IN_F16 : mf::IN_BF16;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[SH::LDS_DWORDS];
+    mf::Engine<LOG2M, KIND> E(smem);
+    E.init();
+    const int h = blockIdx.x;
+    const int C = (int)(N / T);
+    const float *fh = fT + (size_t)h * T;
+    const int hb = mf::half_bits(T);
+    const int rows = B * C;
+    auto off = [&](int r) -> size_t {
+        const int b = r / C, c = r % C;
+        return ((size_t)b * H + h) * N + (size_t)c * T;
+    };
+    // complex signal `sig` = row chunks 2 sig (real part), 2 sig + 1 (imaginary)
+    auto rowp = [&](int sig) -> mf::RowPtrs {
+        const int r = 2 * sig;
+        const bool two = r + 1 < rows;
+        const uint16_t *ub = (const uint16_t *)u;
+        uint16_t *yb = (uint16_t *)y;
+        return {ub + off(r), two ? ub + off(r + 1) : nullptr, yb + off(r), two ? yb + off(r + 1) : nullptr};
+    };
+    E.run_raw([&](int pos) -> float { return fh[pos]; }, T, rowp, (rows + 1) / 2, T, hb);
+}
+
 template <int LOG2M, int IO>
 static hipError_t sp_conv(const void *u, const float *fT, void *y, int B, int H, int64_t N, int T,
                           hipStream_t s) {
     using T_ = typename io_elem<IO>::T;
-    hipLaunchKernelGGL((k_sp_chunk_conv<LOG2M, IO>), dim3(H), dim3(Plan<LOG2M>::NT), 0, s,
-                       (const T_ *)u, fT, (T_ *)y, B, H, N, T);
+    if constexpr (IO != IO_F32 && LOG2M >= 9) {
+        hipLaunchKernelGGL((k_sp_chunk_conv_mfma<LOG2M, IO>), dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
+                           (const T_ *)u, fT, (T_ *)y, B, H, N, T);
+    } else {
+        hipLaunchKernelGGL((k_sp_chunk_conv<LOG2M, IO>), dim3(H), dim3(Plan<LOG2M>::NT), 0, s,
+                           (const T_ *)u, fT, (T_ *)y, B, H, N, T);
+    }
     return hipGetLastError();
 }
 
