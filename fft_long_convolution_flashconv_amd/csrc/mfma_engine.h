@@ -1,36 +1,39 @@
 // mfma_engine.h -- fused block-FFT convolution engine for fp16/bf16 activations
-// on gfx950: radix-16 DFT blocks as dense matrix products on the matrix cores
-// (v_mfma_f32_16x16x32_f16, fp16 operands, fp32 accumulation), twiddles and
-// the pointwise product on the vector ALUs, the signal resident in LDS as
-// packed fp16 complex between passes.
+// on gfx950: the radix-16 (and radix-8) DFT blocks of the transform run as
+// dense matrix products on the matrix cores (fp16 operands, fp32
+// accumulation); twiddles, scaling and the pointwise product run on the
+// vector ALUs in packed fp16; between passes the signal lives in LDS as
+// packed fp16 complex.
 //
 // Method: the paperlayer.ai summary of "Hungry Hungry Hippos", section 4
-// (FlashConv: fused FFT, pointwise product and inverse FFT; the block FFT
-// rewrites the FFT as small matrix multiplications so it runs on matrix
-// units, possibly with more FLOPs), section 2 "Convolutional view" and
-// Appendix C.1 (zero-pad to 2L, keep the first N).
+// (FlashConv: FFT, pointwise product and inverse FFT fused in one kernel; the
+// FFT rewritten as small dense matrix products so that it runs on matrix
+// units, at the price of more FLOPs), section 2 "Convolutional view" and
+// Appendix C.1 (zero-pad to 2N, keep the first N outputs).
 //
-// Transform of size M = 2^LOG2M = V * 16^NM (V = 2..16):
-//   pass 0      VALU radix-V decimation-in-frequency on the zero-padded input
-//               (read from HBM, only the first V/2 points of each butterfly
-//               are non-zero), twiddle, to LDS;
-//   pass 1..NM  radix-16 DIF passes; the 16x16 complex DFT is a 32x32 real
-//               matrix [[Re W, -Im W], [Im W, Re W]] applied by two MFMAs to
-//               16 butterflies (columns) at a time;
-//   last pass   (L = 16) keeps the spectrum in registers, multiplies by the
-//               filter spectrum, and feeds the product straight into the
-//               inverse radix-16 MFMA (the accumulator layout is reused as the
-//               next operand layout, no LDS round trip);
-//   inverse     the same passes in reverse order (decimation in time), the
-//               last one on the VALU writes only the first N outputs.
-// Spectra stay in digit-reversed order; the filter spectrum is produced by
-// the same forward passes, so the pointwise product needs no reordering.
+// Transform of size M = 2^LOG2M = 16 * 16^K * R (R = 2, 4, 8 or 16):
+//   pass 0      radix-16 decimation-in-frequency pass on the zero-padded
+//               input straight from HBM (only the first 8 points of each
+//               16-point column are non-zero): one 32x32x16 MFMA per 32
+//               columns, twiddle, to LDS;
+//   pass 1..K   radix-16 DIF passes, two 16x16x32 MFMAs per 16 columns, each
+//               lane reading and writing back the same four LDS slots;
+//   last pass   radix-R DFT of contiguous groups, product with the filter
+//               spectrum (held in registers), and the inverse of the same
+//               radix straight from registers;
+//   inverse     passes K..1 and the inverse of pass 0 (decimation in time),
+//               which writes only the first N outputs.
+// Spectra stay in digit-reversed order; the filter spectrum goes through the
+// same passes, so the pointwise product needs no reordering.  Inverse DFTs use
+// the forward matrices: IDFT(x) = conj(DFT(conj(x))), with the conjugations
+// folded into the twiddle multiply and the fp32 -> fp16 conversion.
 //
-// Range: activations are scaled by a power of two chosen from max|u| per
-// round of signals so that no fp16 intermediate can overflow
-// (|U| <= N max|u| s < 2^15), and the spectrum product is rescaled the same
-// way from its own maximum before the inverse; all scales are powers of two
-// and are undone exactly at the output.
+// Range: the activations of each round of signals are scaled by a power of
+// two chosen from their maximum so that no fp16 intermediate can overflow
+// (|U| <= N max|u| s < 2^15); the filter is scaled from sum |f|, which bounds
+// every partial sum of its transform; the spectrum product is rescaled from
+// its own maximum before the inverse.  All scales are powers of two and are
+// undone exactly at the output.
 #pragma once
 
 #include "h3conv_device.h"
@@ -39,74 +42,198 @@ namespace h3c {
 namespace mf {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------- packed fp16 complex
-
-// Packed fp16 complex helpers, written as plain vector code: the compiler
-// emits v_cvt_pk_f16_f32 (round to nearest even) and v_pk_mul_f16 /
-// v_pk_fma_f16 with op_sel / neg modifiers, and it knows their hazards
-// against the matrix-core results they consume.
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// (re, im) -> one dword, round to nearest even.
+// ================================================================ constant tables
+// DFT matrices and per-thread twiddles are evaluated at compile time (cosine
+// and sine from their Taylor series on the first octant, extended by
+// symmetry) and stored as packed fp16 (round to nearest even) in read-only
+// device memory; a workgroup loads its share with a few coalesced 16-byte
+// loads instead of evaluating them.
+namespace tab {
+
+constexpr double kPi = 3.14159265358979323846;
+constexpr int kBaseLog = 14;
+constexpr int kBaseM = 1 << kBaseLog;  // finest root of unity: exp(-2 pi i / 16384)
+
+// cos x and sin x for 0 <= x <= pi/4 (Taylor terms up to x^29)
+constexpr void cos_sin_small(double x, double &c, double &s) {
+    const double x2 = x * x;
+    double tc = 1.0, ts = x;
+    c = 0.0;
+    s = 0.0;
+    for (int n = 0; n < 15; ++n) {
+        c += tc;
+        s += ts;
+        tc *= -x2 / (double)((2 * n + 1) * (2 * n + 2));
+        ts *= -x2 / (double)((2 * n + 2) * (2 * n + 3));
+    }
+}
+
+struct Octant {
+    double c[kBaseM / 8 + 1], s[kBaseM / 8 + 1];  // cos, sin of 2 pi r / kBaseM, r <= kBaseM / 8
+};
+constexpr Octant make_octant() {
+    Octant o{};
+    for (int r = 0; r <= kBaseM / 8; ++r) cos_sin_small(2.0 * kPi * (double)r / (double)kBaseM, o.c[r], o.s[r]);
+    return o;
+}
+constexpr Octant kOct = make_octant();
+
+constexpr uint32_t pk16(double re, double im) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)re) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)im) << 16);
+}
+
+// exp(-2 pi i r / kBaseM) for 0 <= r <= kBaseM / 4, packed fp16 (re low, im high)
+struct Quadrant {
+    uint32_t v[kBaseM / 4 + 1];
+};
+constexpr Quadrant make_quadrant() {
+    Quadrant t{};
+    for (int r = 0; r <= kBaseM / 4; ++r) {
+        // cos and sin of the angle from the first octant by symmetry
+        const bool lo = r <= kBaseM / 8;
+        const int o = lo ? r : kBaseM / 4 - r;
+        const double c = lo ? kOct.c[o] : kOct.s[o], s = lo ? kOct.s[o] : kOct.c[o];
+        t.v[r] = pk16(c, -s + 0.0);
+    }
+    return t;
+}
+constexpr Quadrant kQuad = make_quadrant();
+
+// packed fp16 complex times -i: (re, im) -> (im, -re), exact on the bits
+constexpr uint32_t times_neg_i(uint32_t x) {
+    uint32_t nre = (x & 0xffffu) ^ 0x8000u;
+    if ((nre & 0x7fffu) == 0) nre = 0;  // no negative zero
+    return (x >> 16) | (nre << 16);
+}
+
+// exp(-2 pi i t / m), packed fp16, for m a power of two dividing kBaseM
+constexpr uint32_t wpk(long t, long m) {
+    const long u = (t % m + m) % m * (kBaseM / m);  // in [0, kBaseM)
+    uint32_t x = kQuad.v[u % (kBaseM / 4)];
+    for (long q = u / (kBaseM / 4); q > 0; --q) x = times_neg_i(x);
+    return x;
+}
+// the same, unpacked (exact fp16 values, for the matrix entries)
+constexpr void root(long t, long m, double &re, double &im) {
+    const uint32_t x = wpk(t, m);
+    re = (double)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+    im = (double)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+}
+
+// Entry of the real 2R x 2R form of the forward R-point DFT, W = exp(-2 pi i/R):
+// output (k, part p) from input (m, part q); parts 0 = re, 1 = im.
+constexpr double dft_real(int r, int k, int p, int m, int q) {
+    double wr = 0.0, wi = 0.0;
+    root((long)k * m, r, wr, wi);
+    if (p == 0) return q == 0 ? wr : -wi;
+    return q == 0 ? wi : wr;
+}
+
+// Chained slot order of a 16-point column in the 16x16x32 layouts: lane
+// group g (= lane / 16) holds points 2g + {0, 1, 8, 9}, which is also where
+// that group's accumulator rows land, so a pass reads and writes the same
+// slots and results feed the next product without reordering.
+constexpr int kChain[4] = {0, 1, 8, 9};
+constexpr int chain(int g, int t) { return 2 * g + kChain[t]; }
+// output point of accumulator pair v (v even) in the 32x32x16 layout, lane half h
+constexpr int q32(int v, int h) { return 4 * (v >> 2) + 2 * h + ((v & 3) >> 1); }
+
+// Per-lane matrix operands, as quads [4][64 lanes][4 dwords]:
+//   0: 32x32x16 A, zero-padded forward DFT-16: row l%32 -> output (l%32 / 2,
+//      part l%2); K slot (l/32, e) -> input 4 (l/32) + e/2, part e%2
+//   1, 2: 16x16x32 A, forward DFT-16 outputs 0..7 / 8..15 (row l%16 ->
+//      output l%16/2 (+8), part l%2) in chained K order (slot (l/16, e) ->
+//      input chain(l/16, e/2), part e%2)
+//   3: 16x16x16 A, forward DFT-8 (row l%16 -> output l%16/2, part l%2; slot
+//      (l/16, e) -> input 2 (l/16) + e/2, part e%2), dwords 2, 3 zero
+struct MatTab {
+    uint32_t q[4][64][4];
+};
+constexpr MatTab make_mat() {
+    MatTab t{};
+    for (int l = 0; l < 64; ++l) {
+        const int i32 = l & 31, g32 = l >> 5, j = l & 15, g = l >> 4;
+        for (int e = 0; e < 8; e += 2) {
+            double a[2] = {0.0, 0.0}, c0[2] = {0.0, 0.0}, c1[2] = {0.0, 0.0};
+            for (int h = 0; h < 2; ++h) {
+                const int q = (e + h) & 1;
+                a[h] = dft_real(16, i32 >> 1, i32 & 1, 4 * g32 + ((e + h) >> 1), q);
+                const int mc = chain(g, (e + h) >> 1);
+                c0[h] = dft_real(16, j >> 1, j & 1, mc, q);
+                c1[h] = dft_real(16, 8 + (j >> 1), j & 1, mc, q);
+            }
+            t.q[0][l][e / 2] = pk16(a[0], a[1]);
+            t.q[1][l][e / 2] = pk16(c0[0], c0[1]);
+            t.q[2][l][e / 2] = pk16(c1[0], c1[1]);
+        }
+        for (int e = 0; e < 4; e += 2) {
+            const int m = 2 * g + (e >> 1);
+            t.q[3][l][e / 2] = pk16(dft_real(8, j >> 1, j & 1, m, 0), dft_real(8, j >> 1, j & 1, m, 1));
+        }
+    }
+    return t;
+}
+__device__ const MatTab kMat = make_mat();
+
+}  // namespace tab
+
+// ================================================================ packed fp16 complex
+// Written as plain vector code: the compiler emits v_cvt_pk_f16_f32 (round
+// to nearest even) and v_pk_mul_f16 / v_pk_fma_f16 with op_sel / neg
+// modifiers, and it knows their hazards against the matrix-core results they
+// consume.
+
 __device__ __forceinline__ uint32_t pk(float re, float im) {
     const f2 v = {re, im};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
 }
-__device__ __forceinline__ float h_lo(uint32_t v) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
-}
-__device__ __forceinline__ float h_hi(uint32_t v) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-__device__ __forceinline__ cf unpk(uint32_t v) { return mk(h_lo(v), h_hi(v)); }
-
-// x * w on packed fp16 complex.
+// x * w
 __device__ __forceinline__ uint32_t cmulh(uint32_t xx, uint32_t ww) {
     const h2 x = __builtin_bit_cast(h2, xx), w = __builtin_bit_cast(h2, ww);
     const h2 t = x.xx * w;
     const h2 nw = {-w.y, w.x};
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(x.yy, nw, t));
 }
-// x * conj(w) on packed fp16 complex.
-__device__ __forceinline__ uint32_t cmulh_conj(uint32_t xx, uint32_t ww) {
+// conj(x) * w
+__device__ __forceinline__ uint32_t cmulh_cx(uint32_t xx, uint32_t ww) {
     const h2 x = __builtin_bit_cast(h2, xx), w = __builtin_bit_cast(h2, ww);
-    const h2 cw = {w.x, -w.y};
-    const h2 t = x.xx * cw;
-    const h2 sw = {w.y, w.x};
+    const h2 t = x.xx * w;
+    const h2 sw = {w.y, -w.x};
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(x.yy, sw, t));
 }
-// both halves times the same packed factor
+// both halves times the matching halves of a packed factor
 __device__ __forceinline__ uint32_t pkmul(uint32_t xx, uint32_t ss) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, xx) * __builtin_bit_cast(h2, ss));
 }
-
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    u4 v = {a, b, c, d};
+    const u32x4 v = {a, b, c, d};
     return __builtin_bit_cast(half8, v);
 }
-
-// One real entry of the 32x32 real form of the complex 16-point DFT:
-// output (k, part p) from input (m, part q), W = exp(-+2 pi i k m / 16).
-// v_cos_f32 / v_sin_f32 take revolutions; their error (~1e-7) is far below
-// the fp16 rounding the entry gets anyway.
-__device__ __forceinline__ float dft_entry(int k, int p, int m, int q, bool inv) {
-    const float r = (float)((k * m) & 15) * 0.0625f;
-    const float wr = __builtin_amdgcn_cosf(r), s = __builtin_amdgcn_sinf(r);
-    const float wi = inv ? s : -s;
-    if (p == 0) return q == 0 ? wr : -wi;
-    return q == 0 ? wi : wr;
+__device__ __forceinline__ half4 as_half4(uint32_t a, uint32_t b) {
+    const u32x2 v = {a, b};
+    return __builtin_bit_cast(half4, v);
+}
+// max(|re|, |im|) of a packed fp16 complex, as fp32
+__device__ __forceinline__ float habs_max(uint32_t v) {
+    const h2 a = __builtin_elementwise_abs(__builtin_bit_cast(h2, v));
+    return (float)__builtin_elementwise_max(a.x, a.y);
 }
 
 // Shared-memory index swizzle for packed-complex dwords: bits 4-5 are XORed
-// with a fold of bits 6 and up, so 16-dword groups stay contiguous (b128
-// reads) while strided MFMA operand gathers spread over the 64 banks.  The
-// map is linear over XOR, so phys(a + b) = phys(a) ^ phys(b) whenever a and
-// b have disjoint bits; addresses are split that way into per-lane and
-// compile-time parts.
+// with a fold of bits 6 and up, so 16-dword groups stay contiguous while
+// strided operand gathers spread over the banks.  The map is linear over XOR,
+// so phys(a + b) = phys(a) ^ phys(b) whenever a and b have disjoint bits;
+// addresses are split that way into per-lane and compile-time parts.
 __host__ __device__ constexpr int phys(int i) {
     int x = i >> 6;
     x = (x ^ (x >> 2) ^ (x >> 4) ^ (x >> 6)) & 3;
@@ -119,22 +246,20 @@ template <> struct Cfg<9> { static constexpr int SIG = 8, NW = 2; };
 template <> struct Cfg<10> { static constexpr int SIG = 4, NW = 4; };
 template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8; };
 template <> struct Cfg<12> { static constexpr int SIG = 2, NW = 8; };
-template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 16; };
-template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 16; };
+template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 8; };
+template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8; };
 
-// M = 16 * 16^K * R (R = 2, 4, 8 or 16): pass 0 is a zero-padded radix-16
-// pass, then K radix-16 passes, then the last pass of radix R.
 template <int LOG2M>
 struct Shape {
     static constexpr int M = 1 << LOG2M;
     static constexpr int K = (LOG2M - 5) / 4;          // middle radix-16 passes
     static constexpr int LR = LOG2M - 4 - 4 * K;       // log2 of the last radix
     static constexpr int R = 1 << LR;
-    static constexpr int S0 = M / 16;                  // pass-0 stride (= butterflies)
+    static constexpr int S0 = M / 16;                  // pass-0 columns per signal
     static constexpr int SIG = Cfg<LOG2M>::SIG, NW = Cfg<LOG2M>::NW, NT = 64 * NW;
-    static constexpr int T0 = SIG * S0 / 32;           // pass-0 tiles (32 butterflies) per round
+    static constexpr int T0 = SIG * S0 / 32;           // pass-0 tiles (32 columns) per round
     static constexpr int T0W = T0 / NW;
-    static constexpr int TI = SIG * S0 / 16;           // inverse pass-0 tiles (16 butterflies)
+    static constexpr int TI = SIG * S0 / 16;           // inverse pass-0 tiles (16 columns)
     static constexpr int TIW = TI / NW;
     static constexpr int TM = M / 256;                 // middle-pass tiles per signal
     static constexpr int TPW = TM / NW;
@@ -146,13 +271,59 @@ struct Shape {
     static constexpr int DATA = SIG * M;
     static constexpr int LDS_DWORDS = SIG * M + 64;
     static constexpr int DELTA = 256 * NW;             // butterfly-base step between a wave's tiles
+    // distinct column offsets a thread meets in pass 0 (32-column tiles) and
+    // in its inverse (16-column tiles)
+    static constexpr int ND0 = S0 > 32 * NW ? S0 / (32 * NW) : 1;
+    static constexpr int NDI = S0 > 16 * NW ? S0 / (16 * NW) : 1;
+    // per-thread twiddle quads: pass 0 (2 per offset), inverse pass 0, middle passes
+    static constexpr int Q_TU = 2 * ND0, Q_MID = 2 * ND0 + NDI, NQ = 2 * ND0 + NDI + K;
+    static constexpr bool TWREG = 4 * NQ <= 24;        // twiddles held in registers
+    static_assert(S0 >= 32, "pass-0 tiles must lie within one signal");
     static_assert(T0 % NW == 0 && TI % NW == 0, "pass-0 tiles must split evenly over waves");
     static_assert(K == 0 || TM % NW == 0, "middle tiles must split evenly over waves");
     static_assert(R != 8 || TL8 % NW == 0, "radix-8 tiles must split evenly over waves");
     static_assert(R > 4 || NBL % NT == 0 || NT % NBL == 0, "radix-2/4 butterflies must tile the threads");
-    static_assert(M <= 256 * 16 * NW, "a lane must see one butterfly offset per middle pass");
+    static_assert(M <= 256 * 16 * NW, "a lane must see one column offset per middle pass");
     __host__ __device__ static constexpr int L(int p) { return M >> (4 * p); }  // p = 1..K
 };
+
+namespace tab {
+// Per-thread twiddles of one transform size, as quads [NQ][NT][4]:
+//   2d, 2d+1   pass 0, offset d: w_M^(n q) for this lane's 8 outputs q = q32(v, h)
+//   Q_TU + d   inverse pass 0, offset d: w_M^(n k), k = chain(g, 0..3)
+//   Q_MID + p  middle pass p+1 (length L, stride S = L/16): w_L^(n k), k = chain(g, 0..3)
+template <int LOG2M>
+struct TwTab {
+    uint32_t q[Shape<LOG2M>::NQ][Shape<LOG2M>::NT][4];
+};
+template <int LOG2M>
+constexpr TwTab<LOG2M> make_tw() {
+    using SH = Shape<LOG2M>;
+    TwTab<LOG2M> t{};
+    for (int tid = 0; tid < SH::NT; ++tid) {
+        const int w = tid >> 6, lane = tid & 63, j = lane & 15, g = lane >> 4;
+        for (int d = 0; d < SH::ND0; ++d) {
+            const long n = (32 * (w + d * SH::NW) + (lane & 31)) % SH::S0;
+            for (int v = 0; v < 16; v += 2)
+                t.q[2 * d + (v >> 3)][tid][(v >> 1) & 3] = wpk(n * q32(v, lane >> 5), SH::M);
+        }
+        for (int d = 0; d < SH::NDI; ++d) {
+            const long n = (16 * (w + d * SH::NW) + j) % SH::S0;
+            for (int c = 0; c < 4; ++c) t.q[SH::Q_TU + d][tid][c] = wpk(n * chain(g, c), SH::M);
+        }
+        for (int p = 1; p <= SH::K; ++p) {
+            const int L = SH::L(p), S = L / 16;
+            const long n = (16 * w + j) % S;
+            for (int c = 0; c < 4; ++c) t.q[SH::Q_MID + p - 1][tid][c] = wpk(n * chain(g, c), L);
+        }
+    }
+    return t;
+}
+template <int LOG2M>
+__device__ const TwTab<LOG2M> kTw = make_tw<LOG2M>();
+}  // namespace tab
+
+// ================================================================ helpers
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -173,12 +344,6 @@ __device__ __forceinline__ float pow2_scale(float amax, int hb) {
     return ldexpf(1.f, 8 - e - hb);
 }
 
-// max(|re|, |im|) of a packed fp16 complex, as fp32
-__device__ __forceinline__ float habs_max(uint32_t v) {
-    const h2 a = __builtin_elementwise_abs(__builtin_bit_cast(h2, v));
-    return (float)__builtin_elementwise_max(a.x, a.y);
-}
-
 // opaque copy: keeps lane-derived indices from being hoisted (and held in
 // registers) across the whole kernel
 __device__ __forceinline__ int opaque(int x) {
@@ -186,12 +351,26 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef float f16v __attribute__((ext_vector_type(16)));
+// Fresh copies of loop-invariant packed operands right before a pass: without
+// it the compiler hoists the half swaps that the complex multiply applies to
+// them out of every loop and keeps the swapped copies in extra registers; on
+// a fresh copy the swaps fold into op_sel / neg modifiers instead.
+template <int N>
+__device__ __forceinline__ void launder(uint32_t (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
 
-// How a round's inputs arrive: RAW_F16 / RAW_BF16 = two 16-bit activations
-// packed in a dword (row 2s low half, row 2s+1 high half); FP32 = a complex
-// value already in fp32 (used when the loader computes its input).
+// ceil(log2(n) / 2) for n >= 1
+__device__ __forceinline__ int half_bits(int n) {
+    int b = 0;
+    while ((1 << b) < n) ++b;
+    return (b + 1) / 2;
+}
+
+// How a round's inputs arrive: IN_F16 / IN_BF16 = two 16-bit activations
+// packed in a dword (real part low half, imaginary part high half); IN_FP32 =
+// a complex value in fp32 (used when the loader computes its input).
 enum InKind { IN_FP32 = 0, IN_F16 = 1, IN_BF16 = 2 };
 template <int KIND> struct InT { using T = cf; };
 template <> struct InT<IN_F16> { using T = uint32_t; };
@@ -213,12 +392,14 @@ __device__ __forceinline__ uint32_t in_scaled(const typename InT<KIND>::T &x, fl
 }
 
 // Row pointers of one complex signal (two activation rows) for the 16-bit
-// activation kinds: in0/out0 carry the real part, in1/out1 (may be null) the
-// imaginary part.
+// activation kinds: in0/out0 carry the real part, in1/out1 (null when the
+// signal has one row) the imaginary part.
 struct RowPtrs {
     const uint16_t *in0, *in1;
     uint16_t *out0, *out1;
 };
+
+// ================================================================ engine
 
 template <int LOG2M, int KIND>
 struct Engine {
@@ -226,25 +407,25 @@ struct Engine {
     using IT = typename InT<KIND>::T;
     static constexpr int M = SH::M, K = SH::K, R = SH::R, S0 = SH::S0, SIG = SH::SIG, NW = SH::NW,
                          NT = SH::NT, T0W = SH::T0W, TIW = SH::TIW, TPW = SH::TPW, T8W = SH::T8W,
-                         NBL = SH::NBL, NSL = SH::NSL, BPTL = SH::BPTL, DELTA = SH::DELTA;
-    static_assert(S0 >= 32, "pass-0 tiles must lie within one signal");
-    static constexpr int KM = K > 0 ? K : 1;          // array sizes
+                         NBL = SH::NBL, NSL = SH::NSL, BPTL = SH::BPTL, DELTA = SH::DELTA,
+                         ND0 = SH::ND0, NDI = SH::NDI;
+    static constexpr bool TWREG = SH::TWREG;
+    static constexpr int KM = K > 0 ? K : 1;
     static constexpr int FN = R == 16 ? TPW * 4 : (R == 8 ? T8W * 2 : NSL * R);  // filter values / lane
-    // distinct butterfly offsets a lane meets in pass 0 (32-column tiles) and
-    // in its inverse (16-column tiles)
-    static constexpr int ND0 = S0 > 32 * NW ? S0 / (32 * NW) : 1;
-    static constexpr int NDI = S0 > 16 * NW ? S0 / (16 * NW) : 1;
+    static constexpr int NV = R == 16 ? 4 : (R == 8 ? 2 : R);                     // values per last-pass slot
+    static constexpr int NLS = R == 16 ? TPW : (R == 8 ? T8W : BPTL);            // slots per round
+    static constexpr int NU = R >= 8 ? SIG * NLS : NLS;                           // (signal, slot) units
 
     uint32_t *data;  // [SIG][M] packed complex (swizzled)
     float *red;      // [2][NW] reduction slots
     int tid, w, lane, j, g;
-    half8 A0;                               // pass 0: 32x32x16, zero-padded DFT-16
-    half8 Af0, Af1, Ai0, Ai1, Ac0, Ac1;     // 16x16x32: forward, inverse, chained inverse
-    half4 A8f, A8i;                         // 16x16x16: radix-8 forward and inverse
+    const u32x4 *twt;                       // this thread's column of the twiddle table
+    half8 A0, C0, C1;                       // DFT-16: zero-padded 32x32x16; chained 16x16x32
+    half4 A8;                               // DFT-8: 16x16x16
+    uint32_t tw0[TWREG ? ND0 : 1][8];       // pass-0 twiddles (when held in registers)
+    uint32_t tu0[TWREG ? NDI : 1][4];       // inverse pass-0 twiddles
+    uint32_t twm[TWREG ? KM : 1][4];        // middle-pass twiddles
     uint32_t F[FN];                         // filter spectrum * cF (packed fp16)
-    uint32_t twf[KM][4], twi[KM][4];        // middle pass p: w_L^{n k} (write / read slots)
-    uint32_t tw0[ND0][8];                   // pass 0:  w_M^{n q}, q = this lane's 8 outputs
-    uint32_t tu0[NDI][4];                   // inverse pass 0: w_M^{n k}, k = 4g .. 4g+3
     float cF;
     IT pin[T0W][4], pnx[T0W][4];            // pass-0 operands: this round, next round
     int rbank = 0;
@@ -253,75 +434,73 @@ struct Engine {
         data = smem;
         red = (float *)(smem + SH::DATA);
         tid = threadIdx.x;
-        w = tid >> 6;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
         lane = tid & 63;
         j = lane & 15;
         g = lane >> 4;
     }
 
-    __device__ static uint32_t tw_m(int t) {  // w_M^t = exp(-2 pi i t / M), t in [0, M)
-        const float r = (float)(t & (M - 1)) * (1.0f / (float)M);
-        return pk(__builtin_amdgcn_cosf(r), -__builtin_amdgcn_sinf(r));
-    }
-    // output q of accumulator pair v (v even) in the 32x32 layout, lane half h
-    __device__ static __forceinline__ int q32(int v, int h) { return 4 * (v >> 2) + 2 * h + ((v & 3) >> 1); }
-
-    template <int P>
-    __device__ void init_mid() {
-        if constexpr (P <= K) {
-            constexpr int L = SH::L(P), S = L / 16, SHF = LOG2M - __builtin_ctz(L);
-            const int n = (16 * w + j) % S;
-            twf[P - 1][0] = tw_m((n * (2 * g)) << SHF);
-            twf[P - 1][1] = tw_m((n * (2 * g + 1)) << SHF);
-            twf[P - 1][2] = tw_m((n * (8 + 2 * g)) << SHF);
-            twf[P - 1][3] = tw_m((n * (9 + 2 * g)) << SHF);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) twi[P - 1][e] = tw_m((n * (4 * g + e)) << SHF);
-            init_mid<P + 1>();
-        }
-    }
+    __device__ __forceinline__ u32x4 tq(int c) const { return twt[c * NT]; }
 
     __device__ void init() {
-        const int p = j & 1, kk = j >> 1;
-        const int i32 = lane & 31, g32 = lane >> 5;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // 16x16x32 natural K order: slot (g, e) <-> input m = 4g + e/2, part e%2
-            const int m = 4 * g + (e >> 1), q = e & 1;
-            Af0[e] = (_Float16)dft_entry(kk, p, m, q, false);
-            Af1[e] = (_Float16)dft_entry(kk + 8, p, m, q, false);
-            Ai0[e] = (_Float16)dft_entry(kk, p, m, q, true);
-            Ai1[e] = (_Float16)dft_entry(kk + 8, p, m, q, true);
-            // chained K order: slot (g, e) <-> k = 8 (e/4) + 2g + (e%4)/2, part e%2
-            const int kc = 8 * (e >> 2) + 2 * g + ((e & 3) >> 1);
-            Ac0[e] = (_Float16)dft_entry(kk, p, kc, q, true);
-            Ac1[e] = (_Float16)dft_entry(kk + 8, p, kc, q, true);
-            // 32x32x16: row i32 -> output (i32/2, i32%2); slot (g32, e) -> input
-            // m = 4 g32 + e/2 (inputs 8..15 are the zero padding)
-            A0[e] = (_Float16)dft_entry(i32 >> 1, i32 & 1, 4 * g32 + (e >> 1), q, false);
+        const u32x4 *mt = (const u32x4 *)&tab::kMat.q[0][0][0];
+        A0 = __builtin_bit_cast(half8, mt[lane]);
+        C0 = __builtin_bit_cast(half8, mt[64 + lane]);
+        C1 = __builtin_bit_cast(half8, mt[128 + lane]);
+        if constexpr (R == 8) {
+            const u32x4 a = mt[192 + lane];
+            const uint32_t a0 = a.x, a1 = a.y;
+            A8 = as_half4(a0, a1);
         }
+        twt = (const u32x4 *)&tab::kTw<LOG2M>.q[0][0][0] + tid;
+        if constexpr (TWREG) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // 16x16x16 (radix 8): row j -> output (j/2, j%2); slot (g, e) -> m = 2g + e/2
-            const int m = 2 * g + (e >> 1), q = e & 1;
-            const float r = (float)((kk * m) & 7) * 0.125f;
-            const float wr = __builtin_amdgcn_cosf(r), ws = __builtin_amdgcn_sinf(r);
-            A8f[e] = (_Float16)(p == 0 ? (q == 0 ? wr : ws) : (q == 0 ? -ws : wr));
-            A8i[e] = (_Float16)(p == 0 ? (q == 0 ? wr : -ws) : (q == 0 ? ws : wr));
+            for (int d = 0; d < ND0; ++d) {
+                const u32x4 a = tq(2 * d), b = tq(2 * d + 1);
+                tw0[d][0] = a.x; tw0[d][1] = a.y; tw0[d][2] = a.z; tw0[d][3] = a.w;
+                tw0[d][4] = b.x; tw0[d][5] = b.y; tw0[d][6] = b.z; tw0[d][7] = b.w;
+            }
+#pragma unroll
+            for (int d = 0; d < NDI; ++d) {
+                const u32x4 a = tq(SH::Q_TU + d);
+                tu0[d][0] = a.x; tu0[d][1] = a.y; tu0[d][2] = a.z; tu0[d][3] = a.w;
+            }
+#pragma unroll
+            for (int p = 0; p < K; ++p) {
+                const u32x4 a = tq(SH::Q_MID + p);
+                twm[p][0] = a.x; twm[p][1] = a.y; twm[p][2] = a.z; twm[p][3] = a.w;
+            }
         }
+    }
+
+    // twiddle accessors (registers, or the table in read-only memory)
+    __device__ __forceinline__ void get_tw0(int d, uint32_t (&t)[8]) const {
+        if constexpr (TWREG) {
 #pragma unroll
-        for (int d = 0; d < ND0; ++d) {
-            const int n = (32 * (w + d * NW) + i32) % S0;
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) tw0[d][v >> 1] = tw_m(n * q32(v, g32));
+            for (int v = 0; v < 8; ++v) t[v] = tw0[d][v];
+        } else {
+            const u32x4 a = tq(2 * d), b = tq(2 * d + 1);
+            t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w;
+            t[4] = b.x; t[5] = b.y; t[6] = b.z; t[7] = b.w;
         }
+    }
+    __device__ __forceinline__ void get_tu0(int d, uint32_t (&t)[4]) const {
+        if constexpr (TWREG) {
 #pragma unroll
-        for (int d = 0; d < NDI; ++d) {
-            const int n = (16 * (w + d * NW) + j) % S0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tu0[d][e] = tw_m(n * (4 * g + e));
+            for (int c = 0; c < 4; ++c) t[c] = tu0[d][c];
+        } else {
+            const u32x4 a = tq(SH::Q_TU + d);
+            t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w;
         }
-        init_mid<1>();
+    }
+    __device__ __forceinline__ void get_twm(int p, uint32_t (&t)[4]) const {
+        if constexpr (TWREG) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t[c] = twm[p][c];
+        } else {
+            const u32x4 a = tq(SH::Q_MID + p);
+            t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w;
+        }
     }
 
     // Workgroup max (SUM = false) or sum (SUM = true).  Two alternating slot
@@ -339,17 +518,15 @@ struct Engine {
         for (int i = 0; i < NW; ++i) m = SUM ? m + r[i] : fmaxf(m, r[i]);
         return m;
     }
-    __device__ float block_max(float v) { return block_reduce<false>(v); }
 
     __device__ __forceinline__ uint32_t &at(int s, int pi) { return data[s * M + pi]; }
 
     // ---------------------------------------------------------- pass 0
-    // Operand gather: tile i of this wave covers butterflies (columns)
-    // c = 32 (w + i NW) + lane%32 of signal s = 32 (w + i NW) / S0 (uniform
-    // over the tile), offset n = c % S0; lane half h = lane/32 holds inputs
-    // m = 4h .. 4h+3 at n + m S0.
-    __device__ __forceinline__ int tile_sig(int i) { return (32 * (w + i * NW)) / S0; }
-    __device__ __forceinline__ int tile_n(int i) { return (32 * (w + i * NW)) % S0 + (lane & 31); }
+    // Tile i of this wave covers columns c = 32 (w + i NW) + lane%32 of
+    // signal s = 32 (w + i NW) / S0 (uniform over the tile), offset n = c % S0;
+    // lane half h = lane/32 holds inputs m = 4h .. 4h+3 at n + m S0.
+    __device__ __forceinline__ int tile_sig(int i) const { return (32 * (w + i * NW)) / S0; }
+    __device__ __forceinline__ int tile_n(int i) const { return (32 * (w + i * NW)) % S0 + (lane & 31); }
 
     // 16-bit activations through row pointers; `nval` valid samples per row.
     template <class RP>
@@ -358,7 +535,7 @@ struct Engine {
         const bool full = nval >= M / 2;
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
-            const int s = __builtin_amdgcn_readfirstlane(tile_sig(i));
+            const int s = tile_sig(i);
             const int off = tile_n(i) + 4 * h * S0;
             if (s < nsig) {
                 const RowPtrs rp = rows(sig0 + s);
@@ -399,50 +576,54 @@ struct Engine {
         }
     }
 
-    // zero-padded radix-16 DIF pass: DFT on the matrix cores, twiddle w_M^{n q},
-    // to LDS.  `op(i, e)` yields the packed scaled operand.  The matrix-core
-    // pass runs for every tile (operands of absent signals are zero); results
-    // land in that signal's slot of LDS, which no later pass reads.
+    // Zero-padded radix-16 DIF pass: DFT on the matrix cores, twiddle w_M^{n q},
+    // to LDS.  `op(i, e)` yields the packed scaled operand of tile i.
     template <class OP>
-    __device__ void pass0(const OP &op) {
+    __device__ void pass0(const OP &op, int nsig) {
         const int h = lane >> 5;
         const int pq = phys(2 * h * S0);  // q = const(v) + 2h, disjoint bits
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
             const int s = tile_sig(i);
-            const int pn = phys(tile_n(i)) ^ pq;
-            const half8 b = as_half8(op(i, 0), op(i, 1), op(i, 2), op(i, 3));
-            f16v z = {};
-            const f16v d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, b, z, 0, 0, 0);
+            if (s < nsig) {
+                uint32_t tw[8];
+                get_tw0(i % ND0, tw);
+                launder(tw);
+                const int pn = phys(tile_n(i)) ^ pq;
+                const half8 b = as_half8(op(i, 0), op(i, 1), op(i, 2), op(i, 3));
+                const f16v z = {};
+                const f16v d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, b, z, 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-                const int qc = 4 * (v >> 2) + ((v & 3) >> 1);  // q = qc + 2h
-                at(s, pn ^ phys(qc * S0)) = cmulh(pk(d[v], d[v + 1]), tw0[i % ND0][v >> 1]);
+                for (int v = 0; v < 16; v += 2) {
+                    const int qc = 4 * (v >> 2) + ((v & 3) >> 1);  // q = qc + 2h
+                    at(s, pn ^ phys(qc * S0)) = cmulh(pk(d[v], d[v + 1]), tw[v >> 1]);
+                }
             }
         }
         __syncthreads();
     }
 
-    // inverse pass 0: conjugate twiddle, inverse DFT-16 on the matrix cores
-    // keeping outputs m < 8; out(s, n, m, re, im) for m = 2g, 2g+1.
+    // Inverse of pass 0 keeping outputs m < 8: conjugated input times the
+    // twiddle, forward DFT-16 rows 0..7, conjugated result;
+    // out(s, n, m, re, im) for m = 2g, 2g+1.
     template <class OUT>
     __device__ void pass0_inv(const OUT &out, int nsig) {
-        const int pk4 = phys(4 * g * S0);
-        const int s_stride = (16 * NW) / S0;  // signals per tile step (0 if a signal spans steps)
-        (void)s_stride;
+        const int pg = phys(2 * g * S0);
 #pragma unroll
         for (int i = 0; i < TIW; ++i) {
-            const int s = __builtin_amdgcn_readfirstlane((16 * (w + i * NW)) / S0);
-            const int n = (16 * (w + i * NW)) % S0 + j;
+            const int s = (16 * (w + i * NW)) / S0;
             if (s < nsig) {
-                const int pn = phys(n) ^ pk4;
-                uint32_t x[4];
+                const int n = (16 * (w + i * NW)) % S0 + j;
+                const int pn = phys(n) ^ pg;
+                uint32_t tu[4], x[4];
+                get_tu0(i % NDI, tu);
+                launder(tu);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = cmulh_conj(at(s, pn ^ phys(e * S0)), tu0[i % NDI][e]);
-                f4 z = {0.f, 0.f, 0.f, 0.f};
-                const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ai0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
-                out(s, n, 2 * g, d[0], d[1]);
-                out(s, n, 2 * g + 1, d[2], d[3]);
+                for (int t = 0; t < 4; ++t) x[t] = cmulh_cx(at(s, pn ^ phys(tab::kChain[t] * S0)), tu[t]);
+                const f4 z = {0.f, 0.f, 0.f, 0.f};
+                const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
+                out(s, n, 2 * g, d[0], -d[1]);
+                out(s, n, 2 * g + 1, d[2], -d[3]);
             }
         }
     }
@@ -451,55 +632,47 @@ struct Engine {
     template <int P>
     __device__ __forceinline__ int base0() {
         constexpr int L = SH::L(P), S = L / 16;
-        const int b = 16 * opaque(w) + opaque(j);
+        const int b = 16 * w + j;
         return (b / S) * L + (b % S);
     }
 
-    template <int P>
-    __device__ void fwd_pass(int nsig) {
+    // INV = false: DIF pass, y_k = tw_k * sum_m W^{km} x_m.
+    // INV = true:  its inverse (up to the factor 16), x = conj(DFT(conj(y) tw)).
+    // Each lane reads and writes back the slots k = chain(g, 0..3).
+    template <int P, bool INV>
+    __device__ void mid_pass(int nsig) {
         constexpr int L = SH::L(P), S = L / 16;
-        const int b0 = base0<P>();
-        const int pr = phys(b0) ^ phys(4 * g * S);   // read  slots m = 4g + e
-        const int pw = phys(b0) ^ phys(2 * g * S);   // write slots k = 2g + {0, 1, 8, 9}
+        const int pb = phys(base0<P>()) ^ phys(2 * g * S);
+        uint32_t tw[4];
+        get_twm(P - 1, tw);
+        launder(tw);
         for (int s = 0; s < nsig; ++s) {
 #pragma unroll
             for (int ti = 0; ti < TPW; ++ti) {
-                const int ct = phys(ti * DELTA);
-                const half8 b = as_half8(at(s, pr ^ ct ^ phys(0 * S)), at(s, pr ^ ct ^ phys(1 * S)),
-                                         at(s, pr ^ ct ^ phys(2 * S)), at(s, pr ^ ct ^ phys(3 * S)));
-                f4 z = {0.f, 0.f, 0.f, 0.f};
-                const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Af0, b, z, 0, 0, 0);
-                const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Af1, b, z, 0, 0, 0);
-                at(s, pw ^ ct ^ phys(0 * S)) = cmulh(pk(d0[0], d0[1]), twf[P - 1][0]);
-                at(s, pw ^ ct ^ phys(1 * S)) = cmulh(pk(d0[2], d0[3]), twf[P - 1][1]);
-                at(s, pw ^ ct ^ phys(8 * S)) = cmulh(pk(d1[0], d1[1]), twf[P - 1][2]);
-                at(s, pw ^ ct ^ phys(9 * S)) = cmulh(pk(d1[2], d1[3]), twf[P - 1][3]);
-            }
-        }
-        __syncthreads();
-    }
-
-    template <int P>
-    __device__ void inv_pass(int nsig) {
-        constexpr int L = SH::L(P), S = L / 16;
-        const int b0 = base0<P>();
-        const int pr = phys(b0) ^ phys(4 * g * S);
-        const int pw = phys(b0) ^ phys(2 * g * S);
-        for (int s = 0; s < nsig; ++s) {
-#pragma unroll
-            for (int ti = 0; ti < TPW; ++ti) {
-                const int ct = phys(ti * DELTA);
+                const int ct = pb ^ phys(ti * DELTA);
+                int a[4];
                 uint32_t x[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = cmulh_conj(at(s, pr ^ ct ^ phys(e * S)), twi[P - 1][e]);
-                f4 z = {0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < 4; ++t) {
+                    a[t] = ct ^ phys(tab::kChain[t] * S);
+                    x[t] = at(s, a[t]);
+                    if (INV) x[t] = cmulh_cx(x[t], tw[t]);
+                }
                 const half8 b = as_half8(x[0], x[1], x[2], x[3]);
-                const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ai0, b, z, 0, 0, 0);
-                const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ai1, b, z, 0, 0, 0);
-                at(s, pw ^ ct ^ phys(0 * S)) = pk(d0[0], d0[1]);
-                at(s, pw ^ ct ^ phys(1 * S)) = pk(d0[2], d0[3]);
-                at(s, pw ^ ct ^ phys(8 * S)) = pk(d1[0], d1[1]);
-                at(s, pw ^ ct ^ phys(9 * S)) = pk(d1[2], d1[3]);
+                const f4 z = {0.f, 0.f, 0.f, 0.f};
+                const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, b, z, 0, 0, 0);
+                const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C1, b, z, 0, 0, 0);
+                if (!INV) {
+                    at(s, a[0]) = cmulh(pk(d0[0], d0[1]), tw[0]);
+                    at(s, a[1]) = cmulh(pk(d0[2], d0[3]), tw[1]);
+                    at(s, a[2]) = cmulh(pk(d1[0], d1[1]), tw[2]);
+                    at(s, a[3]) = cmulh(pk(d1[2], d1[3]), tw[3]);
+                } else {
+                    at(s, a[0]) = pk(d0[0], -d0[1]);
+                    at(s, a[1]) = pk(d0[2], -d0[3]);
+                    at(s, a[2]) = pk(d1[0], -d1[1]);
+                    at(s, a[3]) = pk(d1[2], -d1[3]);
+                }
             }
         }
         __syncthreads();
@@ -508,62 +681,60 @@ struct Engine {
     template <int P>
     __device__ void fwd_middle(int nsig) {
         if constexpr (P <= K) {
-            fwd_pass<P>(nsig);
+            mid_pass<P, false>(nsig);
             fwd_middle<P + 1>(nsig);
         }
     }
     template <int P>
     __device__ void inv_middle(int nsig) {
         if constexpr (P >= 1) {
-            inv_pass<P>(nsig);
+            mid_pass<P, true>(nsig);
             inv_middle<P - 1>(nsig);
         }
     }
 
     // ---------------------------------------------------------- last pass
-    static constexpr int NV = R == 16 ? 4 : (R == 8 ? 2 : R);
-    static constexpr int NLS = R == 16 ? TPW : (R == 8 ? T8W : BPTL);  // slots per round
-    static constexpr int NU = R >= 8 ? SIG * NLS : NLS;                 // (signal, slot) units
-
     __device__ __forceinline__ int lpos(int slot, int &s) {
-        // physical base of the slot's butterfly (R consecutive positions)
+        // physical base of the slot's group of R consecutive points
         if constexpr (R == 16) {
             s = -1;
-            return phys(16 * (16 * opaque(w) + opaque(j))) ^ phys(16 * slot * 16 * NW);
+            return phys(16 * (16 * w + j)) ^ phys(16 * slot * 16 * NW);
         } else if constexpr (R == 8) {
             s = -1;
-            return phys(8 * (16 * opaque(w) + opaque(j))) ^ phys(8 * slot * 16 * NW);
+            return phys(8 * (16 * w + j)) ^ phys(8 * slot * 16 * NW);
         } else {
-            const int beta = opaque(tid) + slot * NT;
+            const int beta = tid + slot * NT;
             s = beta / NBL;
             return phys(R * (beta % NBL));
         }
     }
 
-    // forward last-pass DFT of this slot (packed fp16 results)
+    // forward last-pass DFT of this slot (packed fp16 results, chained order
+    // for R = 16, natural for R = 8)
     __device__ __forceinline__ void last_fwd(int s, int pb, uint32_t (&y)[NV]) {
         if constexpr (R == 16) {
-            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-            const u4 v = *(const u4 *)&at(s, pb ^ (4 * g));
-            f4 z = {0.f, 0.f, 0.f, 0.f};
-            const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Af0, __builtin_bit_cast(half8, v), z, 0, 0, 0);
-            const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Af1, __builtin_bit_cast(half8, v), z, 0, 0, 0);
+            const u32x2 lo = *(const u32x2 *)&at(s, pb ^ (2 * g));
+            const u32x2 hi = *(const u32x2 *)&at(s, pb ^ (8 + 2 * g));
+            // (elements go through scalars: bit-casting an element expression
+            //  of an ext_vector directly reads element 0)
+            const uint32_t v0 = lo.x, v1 = lo.y, v2 = hi.x, v3 = hi.y;
+            const half8 b = as_half8(v0, v1, v2, v3);
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
+            const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, b, z, 0, 0, 0);
+            const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C1, b, z, 0, 0, 0);
             y[0] = pk(d0[0], d0[1]);
             y[1] = pk(d0[2], d0[3]);
             y[2] = pk(d1[0], d1[1]);
             y[3] = pk(d1[2], d1[3]);
         } else if constexpr (R == 8) {
-            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-            const u2 v = *(const u2 *)&at(s, pb ^ (2 * g));
-            f4 z = {0.f, 0.f, 0.f, 0.f};
-            const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8f, __builtin_bit_cast(half4, v), z, 0, 0, 0);
+            const u32x2 v = *(const u32x2 *)&at(s, pb ^ (2 * g));
+            const uint32_t v0 = v.x, v1 = v.y;
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
+            const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8, as_half4(v0, v1), z, 0, 0, 0);
             y[0] = pk(d[0], d[1]);
             y[1] = pk(d[2], d[3]);
         } else if constexpr (R == 4) {
-            // (vector elements are copied to scalars before the bit casts:
-            //  bit-casting an element expression directly reads element 0)
-            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-            const u4 v = *(const u4 *)&at(s, pb);
+            const u32x4 v = *(const u32x4 *)&at(s, pb);
             const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
             const h2 a = __builtin_bit_cast(h2, v0), b = __builtin_bit_cast(h2, v1),
                      c = __builtin_bit_cast(h2, v2), d = __builtin_bit_cast(h2, v3);
@@ -574,8 +745,7 @@ struct Engine {
             y[2] = __builtin_bit_cast(uint32_t, s0 - s1);
             y[3] = __builtin_bit_cast(uint32_t, d0 - d1mi);
         } else {
-            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-            const u2 v = *(const u2 *)&at(s, pb);
+            const u32x2 v = *(const u32x2 *)&at(s, pb);
             const uint32_t v0 = v.x, v1 = v.y;
             const h2 a = __builtin_bit_cast(h2, v0), b = __builtin_bit_cast(h2, v1);
             y[0] = __builtin_bit_cast(uint32_t, a + b);
@@ -583,48 +753,44 @@ struct Engine {
         }
     }
 
-    // inverse last-pass DFT of the (scaled) spectrum product, written in place
+    // Inverse last-pass DFT, written back in place.  For R >= 8 `y` holds
+    // conj(Y) and the forward matrix is used; for R <= 4 `y` holds Y.
     __device__ __forceinline__ void last_inv(int s, int pb, const uint32_t (&y)[NV]) {
         if constexpr (R == 16) {
-            f4 z = {0.f, 0.f, 0.f, 0.f};
             const half8 b = as_half8(y[0], y[1], y[2], y[3]);
-            const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ac0, b, z, 0, 0, 0);
-            const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ac1, b, z, 0, 0, 0);
-            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-            u2 lo = {pk(d0[0], d0[1]), pk(d0[2], d0[3])};
-            u2 hi = {pk(d1[0], d1[1]), pk(d1[2], d1[3])};
-            *(u2 *)&at(s, pb ^ (2 * g)) = lo;
-            *(u2 *)&at(s, pb ^ (8 + 2 * g)) = hi;
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
+            const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, b, z, 0, 0, 0);
+            const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C1, b, z, 0, 0, 0);
+            const u32x2 lo = {pk(d0[0], -d0[1]), pk(d0[2], -d0[3])};
+            const u32x2 hi = {pk(d1[0], -d1[1]), pk(d1[2], -d1[3])};
+            *(u32x2 *)&at(s, pb ^ (2 * g)) = lo;
+            *(u32x2 *)&at(s, pb ^ (8 + 2 * g)) = hi;
         } else if constexpr (R == 8) {
-            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-            const u2 yy = {y[0], y[1]};
-            f4 z = {0.f, 0.f, 0.f, 0.f};
-            const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8i, __builtin_bit_cast(half4, yy), z, 0, 0, 0);
-            u2 o = {pk(d[0], d[1]), pk(d[2], d[3])};
-            *(u2 *)&at(s, pb ^ (2 * g)) = o;
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
+            const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8, as_half4(y[0], y[1]), z, 0, 0, 0);
+            const u32x2 o = {pk(d[0], -d[1]), pk(d[2], -d[3])};
+            *(u32x2 *)&at(s, pb ^ (2 * g)) = o;
         } else if constexpr (R == 4) {
             const h2 a = __builtin_bit_cast(h2, y[0]), b = __builtin_bit_cast(h2, y[1]),
                      c = __builtin_bit_cast(h2, y[2]), d = __builtin_bit_cast(h2, y[3]);
             const h2 s0 = a + c, d0 = a - c, s1 = b + d, d1 = b - d;
             const h2 d1pi = {-d1.y, d1.x};  // (b - d) * (+i)
-            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-            u4 o = {__builtin_bit_cast(uint32_t, s0 + s1), __builtin_bit_cast(uint32_t, d0 + d1pi),
-                    __builtin_bit_cast(uint32_t, s0 - s1), __builtin_bit_cast(uint32_t, d0 - d1pi)};
-            *(u4 *)&at(s, pb) = o;
+            const u32x4 o = {__builtin_bit_cast(uint32_t, s0 + s1), __builtin_bit_cast(uint32_t, d0 + d1pi),
+                             __builtin_bit_cast(uint32_t, s0 - s1), __builtin_bit_cast(uint32_t, d0 - d1pi)};
+            *(u32x4 *)&at(s, pb) = o;
         } else {
             const h2 a = __builtin_bit_cast(h2, y[0]), b = __builtin_bit_cast(h2, y[1]);
-            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-            u2 o = {__builtin_bit_cast(uint32_t, a + b), __builtin_bit_cast(uint32_t, a - b)};
-            *(u2 *)&at(s, pb) = o;
+            const u32x2 o = {__builtin_bit_cast(uint32_t, a + b), __builtin_bit_cast(uint32_t, a - b)};
+            *(u32x2 *)&at(s, pb) = o;
         }
     }
 
-    __device__ __forceinline__ int fslot(int slot) {
+    __device__ __forceinline__ int fslot(int slot) const {
         if constexpr (R >= 8) return slot * NV;
         else return (slot % NSL) * NV;
     }
-    __device__ __forceinline__ bool slot_ok(int slot, int s, int nsig) {
-        if constexpr (R >= 8) return true;
+    __device__ __forceinline__ bool unit_ok(int u, int slot, int s, int nsig) const {
+        if constexpr (R >= 8) return u / NLS < nsig;
         else return slot * NT + tid < SIG * NBL && s < nsig;
     }
 
@@ -649,7 +815,7 @@ struct Engine {
         const float sf = ldexpf(1.f, 14 - ef);
         cF = ldexpf(1.f, -ef);
         const uint32_t ch = pk(1.0f / 16384.0f, 1.0f / 16384.0f);
-        pass0([&](int i, int e) -> uint32_t { return pk(fin[i][e].x * sf, 0.f); });
+        pass0([&](int i, int e) -> uint32_t { return pk(fin[i][e].x * sf, 0.f); }, 1);
         fwd_middle<1>(1);
 #pragma unroll
         for (int slot = 0; slot < NLS; ++slot) {
@@ -684,27 +850,31 @@ struct Engine {
                 for (int e = 0; e < 4; ++e) amax = fmaxf(amax, in_amax<KIND>(pin[i][e]));
         }
         // fp16 inputs are scaled in fp16, so the scale must be an fp16 power of two
-        const float su0 = pow2_scale(block_max(amax), hb);
+        const float su0 = pow2_scale(block_reduce<false>(amax), hb);
         const float su = (KIND == IN_F16) ? fminf(su0, 16384.0f) : su0;
         const uint32_t suh = pk(su, su);
-        pass0([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); });
+        pass0([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); }, nsig);
         fwd_middle<1>(nsig);
         // last pass: spectrum x filter spectrum, held in registers; its maximum
         // sets the scale of the inverse
+        uint32_t Fr[FN];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) Fr[i] = F[i];
+        launder(Fr);
         uint32_t P[NU][NV];
         float ymax = 0.f;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int slot = u % NLS, s0 = u / NLS;
+            const int slot = u % NLS;
             int s;
             const int pb = lpos(slot, s);
-            if (R >= 8) s = s0;
-            if ((R >= 8 && s < nsig) || (R < 8 && slot_ok(slot, s, nsig))) {
+            if (R >= 8) s = u / NLS;
+            if (unit_ok(u, slot, s, nsig)) {
                 uint32_t y[NV];
                 last_fwd(s, pb, y);
 #pragma unroll
                 for (int q = 0; q < NV; ++q) {
-                    P[u][q] = cmulh(y[q], F[fslot(slot) + q]);
+                    P[u][q] = cmulh(y[q], Fr[fslot(slot) + q]);
                     ymax = fmaxf(ymax, habs_max(P[u][q]));
                 }
             }
@@ -712,15 +882,17 @@ struct Engine {
         // Scale of the inverse: a power of two that keeps every inverse partial
         // sum below 2^15; applied to the fp16 product, so clamped to fp16's exact
         // powers of two (max|Y| < 2^16 bounds it below by 2^-15).
-        const float sy = fminf(fmaxf(pow2_scale(block_max(ymax), (LOG2M + 1) / 2), 1.0f / 32768.0f), 16384.0f);
-        const uint32_t syh = pk(sy, sy);
+        const float sy = fminf(fmaxf(pow2_scale(block_reduce<false>(ymax), (LOG2M + 1) / 2), 1.0f / 32768.0f),
+                               16384.0f);
+        // R >= 8 inverts through the forward matrix: feed conj(Y sy)
+        const uint32_t syh = R >= 8 ? pk(sy, -sy) : pk(sy, sy);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int slot = u % NLS, s0 = u / NLS;
+            const int slot = u % NLS;
             int s;
             const int pb = lpos(slot, s);
-            if (R >= 8) s = s0;
-            if ((R >= 8 && s < nsig) || (R < 8 && slot_ok(slot, s, nsig))) {
+            if (R >= 8) s = u / NLS;
+            if (unit_ok(u, slot, s, nsig)) {
                 uint32_t y[NV];
 #pragma unroll
                 for (int q = 0; q < NV; ++q) y[q] = pkmul(P[u][q], syh);
@@ -754,15 +926,12 @@ struct Engine {
                 const int pos = n + m * S0;
                 if (pos < nval) {
                     const RowPtrs rp = rows(r0 + s);
-                    if constexpr (KIND == IN_F16) {
-                        const h2 hv = __builtin_convertvector((f2){re, im}, h2);
-                        const _Float16 hre = hv.x, him = hv.y;
-                        rp.out0[pos] = __builtin_bit_cast(uint16_t, hre);
-                        if (rp.out1) rp.out1[pos] = __builtin_bit_cast(uint16_t, him);
-                    } else {
-                        rp.out0[pos] = f32_to_bf16_rne(re);
-                        if (rp.out1) rp.out1[pos] = f32_to_bf16_rne(im);
-                    }
+                    const f2 v = {re, im};
+                    uint32_t hv;
+                    if constexpr (KIND == IN_F16) hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+                    else hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+                    rp.out0[pos] = (uint16_t)hv;
+                    if (rp.out1) rp.out1[pos] = (uint16_t)(hv >> 16);
                 }
             };
             conv_round(out, nr, hb);
@@ -791,13 +960,6 @@ struct Engine {
         }
     }
 };
-
-// ceil(log2(n) / 2) for n >= 1
-__device__ __forceinline__ int half_bits(int n) {
-    int b = 0;
-    while ((1 << b) < n) ++b;
-    return (b + 1) / 2;
-}
 
 }  // namespace mf
 }  // namespace h3c
