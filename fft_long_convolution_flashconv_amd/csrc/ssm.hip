@@ -109,13 +109,22 @@ hipError_t launch_ssm_filter(const float *A, const float *Bm, const float *C, co
 
 // ---------------------------------------------------------------- state passing
 
-// Workspace layout (all fp32, 256-byte aligned blocks):
-//   fT  [H, T]            chunk filter with D folded into tap 0
-//   E   [H, S, 65]        Abar^l, l = 0..64            (complex)
-//   G   [H, S, T/64 + 1]  Abar^(64 i), i = 0..T/64     (complex)
-//   sc  [B, H, C, S]      per-chunk state contributions (complex)
+// Workspace layout (256-byte aligned blocks):
+//   fT  [H, T]            chunk filter with D folded into tap 0            fp32
+//   E   [H, S, 65]        Abar^l, l = 0..64                                complex
+//   G   [H, S, T/64 + 1]  Abar^(64 i), i = 0..T/64                         complex
+//   sc  [B, H, C, 64]     per-chunk state contributions                    complex
+// and for the matrix-core projections (16-bit activations), modes padded to 64:
+//   Et  [H, 128, 64]      row 2j+p, column l: part p of Abar_j^(63-l)      fp16
+//   Rt  [H, 64, 128]      row l, column 2j+p: 2 Re / -2 Im of C_j Abar_j^(l+1)  fp16
+//   Pc  [H, 64, 8]        Bbar_j Abar_j^(1024 (NCT-1-ih))                  complex
+//   Qc  [H, 64, 16]       Abar_j^(64 (TL-1-il)), zero for il >= TL         complex
+//   Px  [H, 64, 8]        Abar_j^(1024 ih)                                 complex
+//   Qx  [H, 64, 16]       Abar_j^(64 il), zero for il >= TL                complex
+//   aT  [H, 64]           Abar_j^T                                         complex
+// with T2 = T/64 columns i = 16 ih + il, NCT = ceil(T2/16), TL = min(T2, 16).
 struct SpLayout {
-    size_t fT, E, G, sc, total;
+    size_t fT, E, G, sc, Et, Rt, Pc, Qc, Px, Qx, aT, total;
 };
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -127,7 +136,14 @@ static SpLayout sp_layout(int64_t B, int64_t H, int64_t N, int64_t S, int64_t T)
     L.fT = o; o += al256((size_t)H * T * 4);
     L.E = o; o += al256((size_t)H * S * 65 * 8);
     L.G = o; o += al256((size_t)H * S * (T2 + 1) * 8);
-    L.sc = o; o += al256((size_t)B * H * C * S * 8);
+    L.sc = o; o += al256((size_t)B * H * C * 64 * 8);
+    L.Et = o; o += al256((size_t)H * 128 * 64 * 2);
+    L.Rt = o; o += al256((size_t)H * 64 * 128 * 2);
+    L.Pc = o; o += al256((size_t)H * 64 * 8 * 8);
+    L.Qc = o; o += al256((size_t)H * 64 * 16 * 8);
+    L.Px = o; o += al256((size_t)H * 64 * 8 * 8);
+    L.Qx = o; o += al256((size_t)H * 64 * 16 * 8);
+    L.aT = o; o += al256((size_t)H * 64 * 8);
     L.total = o;
     return L;
 }
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(256) void k_sp_contrib(const typename io_elem<IO>::
         const float *bb = Bm + ((size_t)h * S + tid) * 2;
         const float d = dt[h];
         s = cmul(s, mk(d * bb[0], d * bb[1]));
-        sc[(((size_t)b * H + h) * C + c) * S + tid] = s;
+        sc[(((size_t)b * H + h) * C + c) * 64 + tid] = s;
     }
 }
 
@@ -268,9 +284,9 @@ __global__ __launch_bounds__(256) void k_sp_correct(typename io_elem<IO>::T *__r
         if (j < S) {
             if (x_in) x = mk(x_in[(orow * S + j) * 2], x_in[(orow * S + j) * 2 + 1]);
             const cf aT = G[((size_t)h * S + j) * (T2 + 1) + T2];
-            for (int cc = 0; cc < c; ++cc) x = cadd(cmul(aT, x), sc[(orow * C + cc) * S + j]);
+            for (int cc = 0; cc < c; ++cc) x = cadd(cmul(aT, x), sc[(orow * C + cc) * 64 + j]);
             if (c == C - 1 && x_out) {
-                const cf xo = cadd(cmul(aT, x), sc[(orow * C + c) * S + j]);
+                const cf xo = cadd(cmul(aT, x), sc[(orow * C + c) * 64 + j]);
                 x_out[(orow * S + j) * 2] = xo.x;
                 x_out[(orow * S + j) * 2 + 1] = xo.y;
             }
@@ -300,6 +316,286 @@ __global__ __launch_bounds__(256) void k_sp_correct(typename io_elem<IO>::T *__r
         }
         const int t = 64 * i + l;
         st_io<IO>(yr + t, ld_io<IO>(yr + t) + 2.f * acc);
+    }
+}
+
+// ---------------------------------------------------------------- matrix-core projections
+// For 16-bit activations both projections of the state passing run as small
+// dense products on the matrix cores (fp16 operands, fp32 accumulation), with
+// the chunk index split as k = 64 i + l and i = 16 ih + il:
+//   s_j    = sum_ih Pc[j][ih] sum_il Qc[j][il] V[j][16 ih + il],
+//   V[j][i] = sum_l Abar_j^(63-l) u[64 i + l]                    (Et x U, K = l)
+//   corr[64 i + l] = sum_(j,p) Rt[l][2j+p] X[2j+p][i],           (Rt x X, K = 2j+p)
+//   X[j][i] = Abar_j^(64 i) x_j = Px[j][ih] Qx[j][il] x_j.
+// The operands of each product are scaled by a power of two into fp16 range
+// and the scale is undone on the fp32 results.
+
+// Abar^n = exp(n dt A) in fp64
+__device__ __forceinline__ void apow64(double are, double aim, double n, double &re, double &im) {
+    double sn, cs;
+    sincos(aim * n, &sn, &cs);
+    const double m = exp(are * n);
+    re = m * cs;
+    im = m * sn;
+}
+
+__device__ __forceinline__ uint16_t f16bits(double x) { return __builtin_bit_cast(uint16_t, (_Float16)(float)x); }
+
+__global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict__ A, const float *__restrict__ Bm,
+                                                       const float *__restrict__ Cc, const float *__restrict__ dt,
+                                                       uint16_t *__restrict__ Et, uint16_t *__restrict__ Rt,
+                                                       cf *__restrict__ Pc, cf *__restrict__ Qc,
+                                                       cf *__restrict__ Px, cf *__restrict__ Qx,
+                                                       cf *__restrict__ aT, int S, int T) {
+    const int h = blockIdx.x;
+    const double dth = (double)dt[h];
+    const int T2 = T / 64, NCT = (T2 + 15) / 16, TL = T2 < 16 ? T2 : 16;
+    uint16_t *Eh = Et + (size_t)h * 128 * 64;
+    uint16_t *Rh = Rt + (size_t)h * 64 * 128;
+    constexpr int PER = 64 + 64 + 8 + 16 + 8 + 16 + 1;
+    for (int e = threadIdx.x; e < 64 * PER; e += 256) {
+        const int j = e / PER, r = e % PER;
+        const bool on = j < S;
+        double are = 0.0, aim = 0.0, br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
+        if (on) {
+            const size_t o = ((size_t)h * S + j) * 2;
+            are = dth * (double)A[o];
+            aim = dth * (double)A[o + 1];
+            br = dth * (double)Bm[o];
+            bi = dth * (double)Bm[o + 1];
+            cr = (double)Cc[o];
+            ci = (double)Cc[o + 1];
+        }
+        double pr = 0.0, pi = 0.0;
+        if (r < 64) {  // Et: Abar^(63 - l)
+            const int l = r;
+            if (on) apow64(are, aim, (double)(63 - l), pr, pi);
+            Eh[(2 * j) * 64 + l] = f16bits(pr);
+            Eh[(2 * j + 1) * 64 + l] = f16bits(pi);
+        } else if (r < 128) {  // Rt: 2 C Abar^(l+1), real form
+            const int l = r - 64;
+            if (on) apow64(are, aim, (double)(l + 1), pr, pi);
+            const double zr = cr * pr - ci * pi, zi = cr * pi + ci * pr;
+            Rh[l * 128 + 2 * j] = f16bits(2.0 * zr);
+            Rh[l * 128 + 2 * j + 1] = f16bits(-2.0 * zi);
+        } else if (r < 136) {  // Pc: Bbar Abar^(1024 (NCT-1-ih))
+            const int ih = r - 128;
+            if (on && ih < NCT) apow64(are, aim, 1024.0 * (NCT - 1 - ih), pr, pi);
+            Pc[((size_t)h * 64 + j) * 8 + ih] = mk((float)(br * pr - bi * pi), (float)(br * pi + bi * pr));
+        } else if (r < 152) {  // Qc: Abar^(64 (TL-1-il))
+            const int il = r - 136;
+            if (on && il < TL) apow64(are, aim, 64.0 * (TL - 1 - il), pr, pi);
+            Qc[((size_t)h * 64 + j) * 16 + il] = mk((float)pr, (float)pi);
+        } else if (r < 160) {  // Px: Abar^(1024 ih)
+            const int ih = r - 152;
+            if (on && ih < NCT) apow64(are, aim, 1024.0 * ih, pr, pi);
+            Px[((size_t)h * 64 + j) * 8 + ih] = mk((float)pr, (float)pi);
+        } else if (r < 176) {  // Qx: Abar^(64 il)
+            const int il = r - 160;
+            if (on && il < TL) apow64(are, aim, 64.0 * il, pr, pi);
+            Qx[((size_t)h * 64 + j) * 16 + il] = mk((float)pr, (float)pi);
+        } else {  // Abar^T
+            if (on) apow64(are, aim, (double)T, pr, pi);
+            aT[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
+        }
+    }
+}
+
+__device__ __forceinline__ float sp_wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// 8 consecutive activations (16-byte aligned) as floats
+template <int IO>
+__device__ __forceinline__ void ld8(const typename io_elem<IO>::T *p, float (&x)[8]) {
+    static_assert(IO == IO_F16 || IO == IO_BF16, "16-bit activations");
+    const mf::u32x4 v = *(const mf::u32x4 *)p;
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if constexpr (IO == IO_F16) {
+            x[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(d[k] & 0xffffu));
+            x[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(d[k] >> 16));
+        } else {
+            x[2 * k] = __uint_as_float(d[k] << 16);
+            x[2 * k + 1] = __uint_as_float(d[k] & 0xffff0000u);
+        }
+    }
+}
+
+// State contribution of chunk-row (b, h, c) on the matrix cores.  Four waves;
+// wave w owns column tiles ct = w and w + 4 (T <= 8192 gives at most 8).
+template <int IO>
+__global__ __launch_bounds__(256) void k_sp_contrib_mfma(const typename io_elem<IO>::T *__restrict__ u,
+                                                        const uint16_t *__restrict__ Et,
+                                                        const cf *__restrict__ Pc, const cf *__restrict__ Qc,
+                                                        cf *__restrict__ sc, int H, int64_t N, int T) {
+    using namespace mf;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, C = gridDim.x;
+    const int T2 = T >> 6, NCT = (T2 + 15) >> 4;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, il = lane & 15, g = lane >> 4;
+    __shared__ float part[4][64][2];
+    __shared__ float red[4];
+    const typename io_elem<IO>::T *ur = u + ((size_t)b * H + h) * N + (size_t)c * T;
+    float xv[2][2][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int ct = w + 4 * q, i = 16 * ct + il;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ct < NCT && i < T2) {
+                ld8<IO>(ur + 64 * i + 32 * ks + 8 * g, xv[q][ks]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xv[q][ks][e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xv[q][ks][e]));
+        }
+    }
+    amax = sp_wave_max(amax);
+    if (lane == 0) red[w] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int ex = 0;
+    if (amax > 0.f) (void)frexpf(amax, &ex);
+    const float su = ldexpf(1.f, 14 - ex);  // scaled operands below 2^14
+    half8 Bop[2][2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            Bop[q][ks] = as_half8(pk(xv[q][ks][0] * su, xv[q][ks][1] * su), pk(xv[q][ks][2] * su, xv[q][ks][3] * su),
+                                  pk(xv[q][ks][4] * su, xv[q][ks][5] * su), pk(xv[q][ks][6] * su, xv[q][ks][7] * su));
+    const uint16_t *Eh = Et + (size_t)h * 128 * 64;
+    const cf *Pch = Pc + (size_t)h * 64 * 8, *Qch = Qc + (size_t)h * 64 * 16;
+#pragma unroll 2
+    for (int rt = 0; rt < 8; ++rt) {
+        half8 Aop[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            Aop[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Eh + (16 * rt + il) * 64 + 32 * ks + 8 * g));
+        const int j0 = 8 * rt + 2 * g, j1 = j0 + 1;
+        const cf q0 = Qch[j0 * 16 + il], q1 = Qch[j1 * 16 + il];
+        cf s0 = mk(0.f, 0.f), s1 = mk(0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int ct = w + 4 * q;
+            if (ct < NCT) {
+                const f4 z = {0.f, 0.f, 0.f, 0.f};
+                f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop[0], Bop[q][0], z, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop[1], Bop[q][1], d, 0, 0, 0);
+                s0 = cadd(s0, cmul(Pch[j0 * 8 + ct], cmul(q0, mk(d[0], d[1]))));
+                s1 = cadd(s1, cmul(Pch[j1 * 8 + ct], cmul(q1, mk(d[2], d[3]))));
+            }
+        }
+        // sum over the 16 columns il of each lane group
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            s0.x += __shfl_xor(s0.x, o, 64);
+            s0.y += __shfl_xor(s0.y, o, 64);
+            s1.x += __shfl_xor(s1.x, o, 64);
+            s1.y += __shfl_xor(s1.y, o, 64);
+        }
+        if (il == 0) {
+            part[w][j0][0] = s0.x;
+            part[w][j0][1] = s0.y;
+            part[w][j1][0] = s1.x;
+            part[w][j1][1] = s1.y;
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const float inv = 1.0f / su;
+        const float re = (part[0][tid][0] + part[1][tid][0]) + (part[2][tid][0] + part[3][tid][0]);
+        const float im = (part[0][tid][1] + part[1][tid][1]) + (part[2][tid][1] + part[3][tid][1]);
+        sc[(((size_t)b * H + h) * C + c) * 64 + tid] = mk(re * inv, im * inv);
+    }
+}
+
+// Carry the state into chunk-row (b, h, c) and add its free response on the
+// matrix cores.  The last chunk also writes x_out.
+template <int IO>
+__global__ __launch_bounds__(256) void k_sp_correct_mfma(typename io_elem<IO>::T *__restrict__ y,
+                                                        const uint16_t *__restrict__ Rt,
+                                                        const cf *__restrict__ Px, const cf *__restrict__ Qx,
+                                                        const cf *__restrict__ aT, const cf *__restrict__ sc,
+                                                        const float *__restrict__ x_in, float *__restrict__ x_out,
+                                                        int H, int64_t N, int S, int T) {
+    using namespace mf;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, C = gridDim.x;
+    const int T2 = T >> 6, NCT = (T2 + 15) >> 4;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, il = lane & 15, g = lane >> 4;
+    __shared__ cf xs[64];
+    __shared__ float amx;
+    const size_t orow = (size_t)b * H + h;
+    if (tid < 64) {
+        const int j = tid;
+        cf x = mk(0.f, 0.f);
+        if (x_in && j < S) x = mk(x_in[(orow * S + j) * 2], x_in[(orow * S + j) * 2 + 1]);
+        const cf a = aT[(size_t)h * 64 + j];
+        for (int cc = 0; cc < c; ++cc) x = cadd(cmul(a, x), sc[(orow * C + cc) * 64 + j]);
+        if (c == C - 1 && x_out && j < S) {
+            const cf xo = cadd(cmul(a, x), sc[(orow * C + c) * 64 + j]);
+            x_out[(orow * S + j) * 2] = xo.x;
+            x_out[(orow * S + j) * 2 + 1] = xo.y;
+        }
+        xs[j] = x;
+        const float m = sp_wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
+        if (lane == 0) amx = m;
+    }
+    __syncthreads();
+    const float amax = amx;
+    if (!(amax > 0.f)) return;
+    int ex = 0;
+    (void)frexpf(amax, &ex);
+    const float sx = ldexpf(1.f, 14 - ex);  // |X| <= |x| sx < 2^14 for stable modes
+    const float inv = 1.0f / sx;
+    const cf *Pxh = Px + (size_t)h * 64 * 8, *Qxh = Qx + (size_t)h * 64 * 16;
+    cf qx[4][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int j = 16 * ks + 4 * g + t;
+            qx[ks][t] = cscale(cmul(Qxh[j * 16 + il], xs[j]), sx);
+        }
+    const uint16_t *Rh = Rt + (size_t)h * 64 * 128;
+    typename io_elem<IO>::T *yr = y + orow * N + (size_t)c * T;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int ct = w + 4 * q;
+        if (ct >= NCT) break;
+        const int i = 16 * ct + il;
+        half8 Bop[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint32_t d4[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int j = 16 * ks + 4 * g + t;
+                const cf X = cmul(qx[ks][t], Pxh[j * 8 + ct]);
+                d4[t] = pk(X.x, X.y);
+            }
+            Bop[ks] = as_half8(d4[0], d4[1], d4[2], d4[3]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const half8 Aop = __builtin_bit_cast(half8, *(const u32x4 *)(Rh + (16 * rt + il) * 128 + 32 * ks + 8 * g));
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, Bop[ks], d, 0, 0, 0);
+            }
+            if (i < T2) {
+                typename io_elem<IO>::T *p = yr + 64 * i + 16 * rt + 4 * g;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) st_io<IO>(p + v, ld_io<IO>(p + v) + d[v] * inv);
+            }
+        }
     }
 }
 
@@ -364,7 +660,13 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
                        (int64_t)T);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sp_tables, dim3(H), dim3(256), 0, s, A, dt, E, G, S, T2);
+    if constexpr (IO != IO_F32) {
+        hipLaunchKernelGGL(k_sp_tables_mfma, dim3(H), dim3(256), 0, s, A, Bm, C, dt, (uint16_t *)(w + L.Et),
+                           (uint16_t *)(w + L.Rt), (cf *)(w + L.Pc), (cf *)(w + L.Qc), (cf *)(w + L.Px),
+                           (cf *)(w + L.Qx), (cf *)(w + L.aT), S, T);
+    } else {
+        hipLaunchKernelGGL(k_sp_tables, dim3(H), dim3(256), 0, s, A, dt, E, G, S, T2);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (fused_log2m(T)) {
         case 7: e = sp_conv<7, IO>(u, fT, y, B, H, N, T, s); break;
@@ -378,18 +680,29 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    const size_t sm_c = (size_t)T * 4 + 64 * 64 * 8 + 4 * 64 * 8;
-    const size_t sm_x = 64 * 64 * 8 + (size_t)64 * T2 * 8;
-    hipFuncSetAttribute((const void *)k_sp_contrib<IO>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)sm_c);
-    hipFuncSetAttribute((const void *)k_sp_correct<IO>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)sm_x);
-    hipLaunchKernelGGL((k_sp_contrib<IO>), dim3(C_, H, B), dim3(256), sm_c, s, (const T_ *)u, Bm, dt,
-                       E, G, sc, B, H, N, S, T);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_sp_correct<IO>), dim3(C_, H, B), dim3(256), sm_x, s, (T_ *)y, C, E, G, sc,
-                       x_in, x_out, B, H, N, S, T);
-    return hipGetLastError();
+    if constexpr (IO != IO_F32) {
+        hipLaunchKernelGGL((k_sp_contrib_mfma<IO>), dim3(C_, H, B), dim3(256), 0, s, (const T_ *)u,
+                           (const uint16_t *)(w + L.Et), (const cf *)(w + L.Pc), (const cf *)(w + L.Qc), sc, H,
+                           N, T);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_sp_correct_mfma<IO>), dim3(C_, H, B), dim3(256), 0, s, (T_ *)y,
+                           (const uint16_t *)(w + L.Rt), (const cf *)(w + L.Px), (const cf *)(w + L.Qx),
+                           (const cf *)(w + L.aT), (const cf *)sc, x_in, x_out, H, N, S, T);
+        return hipGetLastError();
+    } else {
+        const size_t sm_c = (size_t)T * 4 + 64 * 64 * 8 + 4 * 64 * 8;
+        const size_t sm_x = 64 * 64 * 8 + (size_t)64 * T2 * 8;
+        (void)hipFuncSetAttribute((const void *)k_sp_contrib<IO>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sm_c);
+        (void)hipFuncSetAttribute((const void *)k_sp_correct<IO>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sm_x);
+        hipLaunchKernelGGL((k_sp_contrib<IO>), dim3(C_, H, B), dim3(256), sm_c, s, (const T_ *)u, Bm, dt,
+                           E, G, sc, B, H, N, S, T);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_sp_correct<IO>), dim3(C_, H, B), dim3(256), sm_x, s, (T_ *)y, C, E, G, sc,
+                           x_in, x_out, B, H, N, S, T);
+        return hipGetLastError();
+    }
 }
 
 hipError_t launch_state_pass(const void *u, const float *A, const float *Bm, const float *C,

@@ -218,6 +218,37 @@ def test_state_pass_chunk_invariance_and_split():
     assert err <= 1e-5 and errx <= 1e-5
 
 
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("T,S", [(64, 16), (256, 64), (1024, 7), (2048, 64)])
+def test_state_pass_16bit_chunks_and_split(io, T, S):
+    """16-bit activations (matrix-core projections): every chunk length from
+    one 64-sample block to several column tiles, odd batch, partial mode
+    count, and two calls joined by the carried state."""
+    dev = device()
+    B, H, N = 3, 2, 4 * T
+    say("state_pass 16-bit io=%s B=%d H=%d N=%d S=%d T=%d" % (io, B, H, N, S, T))
+    u, p, D = _sp_inputs(B, H, N, S, io, seed=T + S)
+    d = {k: v.to(dev) for k, v in p.items()}
+    ud, Dd = u.to(dev), D.to(dev)
+    y, x = pkg.state_pass(ud, d["A"], d["Bm"], d["C"], d["dt"], Dd, T, return_state=True)
+    torch.cuda.synchronize()
+    ref, xr = _sp_ref(u, p, D)
+    err, errx = rel_l2(to_np(y), ref), rel_l2(x.cpu().numpy().astype(np.complex128), xr)
+    du = to_np(D)[None, :, None] * to_np(u)
+    err_conv = rel_l2(to_np(y) - du, ref - du)
+    say("  rel_l2=%.3e conv_only=%.3e state=%.3e" % (err, err_conv, errx))
+    assert err <= TOL[io] and err_conv <= TOL[io] and errx <= 1e-3
+    M = 3 * T
+    y1, x1 = pkg.state_pass(ud[..., :M].contiguous(), d["A"], d["Bm"], d["C"], d["dt"], Dd, T,
+                            return_state=True)
+    y2, x2 = pkg.state_pass(ud[..., M:].contiguous(), d["A"], d["Bm"], d["C"], d["dt"], Dd, T,
+                            x_in=x1, return_state=True)
+    err = rel_l2(np.concatenate([to_np(y1), to_np(y2)], axis=-1), ref)
+    errx = rel_l2(x2.cpu().numpy().astype(np.complex128), xr)
+    say("  split at %d rel_l2=%.3e state=%.3e" % (M, err, errx))
+    assert err <= TOL[io] and errx <= 1e-3
+
+
 def test_state_64k_workload():
     w = wl.WORKLOADS["state_64k"]
     dev = device()
