@@ -131,7 +131,7 @@ __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_h3_mix(
 // the matrix cores (see mfma_engine.h).
 
 template <int LOG2M, int IO>
-__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_fft_conv_mfma(
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M>::WPE))) void k_fft_conv_mfma(
     const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f,
     const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
     using T = typename io_elem<IO>::T;
@@ -147,24 +147,21 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_fft_conv_mfma(
     const T *uh = u + (size_t)h * N;
     T *yh = y + (size_t)h * N;
     const int hb = mf::half_bits(N);
-    auto ldf = [&](int pos) -> float {
-        float v = fh[pos];
-        if (pos == 0) v += dh;
-        return v;
-    };
+    auto ldf = [&](int pos) -> float { return fh[pos] + (pos == 0 ? dh : 0.f); };
     // complex signal `sig` = batch rows 2 sig (real part), 2 sig + 1 (imaginary)
-    auto rows = [&](int sig) -> mf::RowPtrs {
+    auto rows = [&](int sig) -> mf::RowBufs {
         const int b0 = 2 * sig;
-        const bool two = b0 + 1 < B;
-        const uint16_t *i0 = (const uint16_t *)(uh + (size_t)b0 * rs);
-        uint16_t *o0 = (uint16_t *)(yh + (size_t)b0 * rs);
-        return {i0, two ? i0 + rs : nullptr, o0, two ? o0 + rs : nullptr};
+        const int nb1 = (b0 + 1 < B) ? 2 * N : 0;
+        const T *i0 = uh + (size_t)b0 * rs;
+        T *o0 = yh + (size_t)b0 * rs;
+        return {mf::row_rsrc(i0, 2 * N), mf::row_rsrc(i0 + rs, nb1), mf::row_rsrc(o0, 2 * N),
+                mf::row_rsrc(o0 + rs, nb1)};
     };
-    E.run_raw(ldf, N, rows, (B + 1) / 2, N, hb);
+    E.run_raw(ldf, N, rows, (B + 1) / 2, hb);
 }
 
 template <int LOG2M, int IO>
-__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_h3_mix_mfma(
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M>::WPE))) void k_h3_mix_mfma(
     const typename io_elem<IO>::T *__restrict__ q, const typename io_elem<IO>::T *__restrict__ k,
     const typename io_elem<IO>::T *__restrict__ v, const float *__restrict__ w,
     const float *__restrict__ f, const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ out,
@@ -180,11 +177,7 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_h3_mix_mfma(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wd[i] = (i < L) ? w[(size_t)d * L + i] : 0.f;
     const int hb = mf::half_bits(N);
-    auto ldf = [&](int pos) -> float {
-        float x = fd[pos];
-        if (pos == 0) x += dd;
-        return x;
-    };
+    auto ldf = [&](int pos) -> float { return fd[pos] + (pos == 0 ? dd : 0.f); };
     const size_t rowstride = (size_t)N * Dm;
     auto mval = [&](size_t o, int t) -> float {
         float acc = 0.f;

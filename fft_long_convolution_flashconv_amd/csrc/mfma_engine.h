@@ -229,25 +229,41 @@ __device__ __forceinline__ float habs_max(uint32_t v) {
     return (float)__builtin_elementwise_max(a.x, a.y);
 }
 
-// Shared-memory index swizzle for packed-complex dwords: bits 4-5 are XORed
-// with a fold of bits 6 and up, so 16-dword groups stay contiguous while
-// strided operand gathers spread over the banks.  The map is linear over XOR,
-// so phys(a + b) = phys(a) ^ phys(b) whenever a and b have disjoint bits;
-// addresses are split that way into per-lane and compile-time parts.
+// Shared-memory index swizzle for packed-complex dwords, per transform size:
+// bit p >= 6 of an index, when set, flips the bits kSwz[LOG2M][p - 6] among
+// bits 1..5, so strided operand gathers and the contiguous last-pass groups
+// spread over the banks (masks chosen by a search over this engine's access
+// patterns against 32- and 64-bank models; bit 0, and bit 1 where the last
+// pass reads four dwords at once, are never flipped, so the groups a lane
+// reads with one 8- or 16-byte access stay contiguous).  The map is linear
+// over XOR, so phys(a ^ b) = phys(a) ^ phys(b); addresses are split that way
+// into per-lane and compile-time parts.
+constexpr int kSwz[15][8] = {
+    {}, {}, {}, {}, {}, {}, {}, {}, {},
+    {48, 18, 16},                        // 9
+    {4, 48, 16, 32},                     // 10
+    {4, 8, 48, 32, 16},                  // 11
+    {24, 4, 16, 48, 16, 32},             // 12
+    {16, 34, 16, 32, 48, 32, 16},        // 13
+    {4, 48, 16, 32, 16, 48, 16, 32},     // 14
+};
+template <int LOG2M>
 __host__ __device__ constexpr int phys(int i) {
-    int x = i >> 6;
-    x = (x ^ (x >> 2) ^ (x >> 4) ^ (x >> 6)) & 3;
-    return i ^ (x << 4);
+    int r = i;
+    for (int p = 6; p < LOG2M; ++p)
+        if ((i >> p) & 1) r ^= kSwz[LOG2M][p - 6];
+    return r;
 }
 
 // Workgroup shape per transform size: SIG signals in flight, NW waves.
 template <int LOG2M> struct Cfg;
-template <> struct Cfg<9> { static constexpr int SIG = 8, NW = 2; };
-template <> struct Cfg<10> { static constexpr int SIG = 4, NW = 4; };
-template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8; };
-template <> struct Cfg<12> { static constexpr int SIG = 2, NW = 8; };
-template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 8; };
-template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8; };
+// OCC = workgroups per compute unit the register budget is set for.
+template <> struct Cfg<9> { static constexpr int SIG = 8, NW = 2, OCC = 4; };
+template <> struct Cfg<10> { static constexpr int SIG = 4, NW = 4, OCC = 4; };
+template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8, OCC = 2; };
+template <> struct Cfg<12> { static constexpr int SIG = 2, NW = 8, OCC = 2; };
+template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 8, OCC = 2; };
+template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8, OCC = 2; };
 
 template <int LOG2M>
 struct Shape {
@@ -256,7 +272,8 @@ struct Shape {
     static constexpr int LR = LOG2M - 4 - 4 * K;       // log2 of the last radix
     static constexpr int R = 1 << LR;
     static constexpr int S0 = M / 16;                  // pass-0 columns per signal
-    static constexpr int SIG = Cfg<LOG2M>::SIG, NW = Cfg<LOG2M>::NW, NT = 64 * NW;
+    static constexpr int SIG = Cfg<LOG2M>::SIG, NW = Cfg<LOG2M>::NW, NT = 64 * NW, OCC = Cfg<LOG2M>::OCC;
+    static constexpr int WPE = (OCC * NW + 3) / 4;     // waves per SIMD at that occupancy
     static constexpr int T0 = SIG * S0 / 32;           // pass-0 tiles (32 columns) per round
     static constexpr int T0W = T0 / NW;
     static constexpr int TI = SIG * S0 / 16;           // inverse pass-0 tiles (16 columns)
@@ -279,6 +296,7 @@ struct Shape {
     static constexpr int Q_TU = 2 * ND0, Q_MID = 2 * ND0 + NDI, NQ = 2 * ND0 + NDI + K;
     static constexpr bool TWREG = 4 * NQ <= 24;        // twiddles held in registers
     static_assert(S0 >= 32, "pass-0 tiles must lie within one signal");
+    static_assert(K >= 1, "the inverse scale is applied by the first inverse middle pass");
     static_assert(T0 % NW == 0 && TI % NW == 0, "pass-0 tiles must split evenly over waves");
     static_assert(K == 0 || TM % NW == 0, "middle tiles must split evenly over waves");
     static_assert(R != 8 || TL8 % NW == 0, "radix-8 tiles must split evenly over waves");
@@ -391,13 +409,18 @@ __device__ __forceinline__ uint32_t in_scaled(const typename InT<KIND>::T &x, fl
     else return pk(x.x * s, x.y * s);
 }
 
-// Row pointers of one complex signal (two activation rows) for the 16-bit
-// activation kinds: in0/out0 carry the real part, in1/out1 (null when the
-// signal has one row) the imaginary part.
-struct RowPtrs {
-    const uint16_t *in0, *in1;
-    uint16_t *out0, *out1;
+// Rows of one complex signal for the 16-bit activation kinds, as raw buffer
+// resources (base in scalar registers, 32-bit per-lane offsets): in0/out0
+// carry the real part, in1/out1 the imaginary part.  The byte extent of each
+// resource is the valid part of its row, so loads past it return zero (the
+// zero padding of the transform) and stores past it are dropped; a signal
+// with one row gets empty in1/out1.
+struct RowBufs {
+    __amdgpu_buffer_rsrc_t in0, in1, out0, out1;
 };
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
 
 // ================================================================ engine
 
@@ -427,7 +450,11 @@ struct Engine {
     uint32_t twm[TWREG ? KM : 1][4];        // middle-pass twiddles
     uint32_t F[FN];                         // filter spectrum * cF (packed fp16)
     float cF;
-    IT pin[T0W][4], pnx[T0W][4];            // pass-0 operands: this round, next round
+    // Inputs of the next round are fetched during the current one, unless
+    // twiddles come from the table: loads retire in order, so every table
+    // load would then also wait for the whole prefetch.
+    static constexpr bool PREFETCH = TWREG;
+    IT pin[T0W][4], pnx[PREFETCH ? T0W : 1][4];  // pass-0 operands: this round, next round
     int rbank = 0;
 
     __device__ Engine(uint32_t *smem) {
@@ -519,7 +546,14 @@ struct Engine {
         return m;
     }
 
-    __device__ __forceinline__ uint32_t &at(int s, int pi) { return data[s * M + pi]; }
+    // LDS access by byte address.  Addresses are built as a per-lane base,
+    // laundered once per pass (so the compiler does not keep one register per
+    // tile and slot alive across the whole kernel), XORed with compile-time or
+    // wave-uniform parts; a compile-time signal offset is added last and folds
+    // into the instruction's offset field.
+    template <class V = uint32_t>
+    __device__ __forceinline__ V &lds(int b) { return *(V *)((char *)data + b); }
+    static constexpr int SB = M * 4;  // bytes per signal
 
     // ---------------------------------------------------------- pass 0
     // Tile i of this wave covers columns c = 32 (w + i NW) + lane%32 of
@@ -528,33 +562,22 @@ struct Engine {
     __device__ __forceinline__ int tile_sig(int i) const { return (32 * (w + i * NW)) / S0; }
     __device__ __forceinline__ int tile_n(int i) const { return (32 * (w + i * NW)) % S0 + (lane & 31); }
 
-    // 16-bit activations through row pointers; `nval` valid samples per row.
-    template <class RP>
-    __device__ __forceinline__ void fetch_raw(const RP &rows, int sig0, int nsig, int nval, uint32_t (&buf)[T0W][4]) {
+    // 16-bit activations through the rows' buffer resources (zero past each
+    // row's valid length).
+    template <class RB>
+    __device__ __forceinline__ void fetch_raw(const RB &rows, int sig0, int nsig, uint32_t (&buf)[T0W][4]) {
         const int h = lane >> 5;
-        const bool full = nval >= M / 2;
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
             const int s = tile_sig(i);
-            const int off = tile_n(i) + 4 * h * S0;
+            const int off = 2 * (tile_n(i) + 4 * h * S0);
             if (s < nsig) {
-                const RowPtrs rp = rows(sig0 + s);
-                if (full) {
+                const RowBufs rb = rows(sig0 + s);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = rp.in0[off + e * S0];
-                        const uint32_t hi = rp.in1 ? (uint32_t)rp.in1[off + e * S0] : 0u;
-                        buf[i][e] = lo | (hi << 16);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int pos = off + e * S0;
-                        const bool ok = pos < nval;
-                        const uint32_t lo = ok ? (uint32_t)rp.in0[pos] : 0u;
-                        const uint32_t hi = (ok && rp.in1) ? (uint32_t)rp.in1[pos] : 0u;
-                        buf[i][e] = lo | (hi << 16);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rb.in0, off, 2 * e * S0, 0);
+                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rb.in1, off, 2 * e * S0, 0);
+                    buf[i][e] = lo | (hi << 16);
                 }
             } else {
 #pragma unroll
@@ -581,7 +604,8 @@ struct Engine {
     template <class OP>
     __device__ void pass0(const OP &op, int nsig) {
         const int h = lane >> 5;
-        const int pq = phys(2 * h * S0);  // q = const(v) + 2h, disjoint bits
+        // lane part of the column (lane % 32) and of the output q = qc + 2h
+        const int lb = opaque(((lane & 31) ^ phys<LOG2M>(2 * h * S0)) << 2);
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
             const int s = tile_sig(i);
@@ -589,14 +613,14 @@ struct Engine {
                 uint32_t tw[8];
                 get_tw0(i % ND0, tw);
                 launder(tw);
-                const int pn = phys(tile_n(i)) ^ pq;
+                const int pn = lb ^ ((phys<LOG2M>((32 * (w + i * NW)) % S0) << 2) | (s * SB));
                 const half8 b = as_half8(op(i, 0), op(i, 1), op(i, 2), op(i, 3));
                 const f16v z = {};
                 const f16v d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, b, z, 0, 0, 0);
 #pragma unroll
                 for (int v = 0; v < 16; v += 2) {
                     const int qc = 4 * (v >> 2) + ((v & 3) >> 1);  // q = qc + 2h
-                    at(s, pn ^ phys(qc * S0)) = cmulh(pk(d[v], d[v + 1]), tw[v >> 1]);
+                    lds(pn ^ (phys<LOG2M>(qc * S0) << 2)) = cmulh(pk(d[v], d[v + 1]), tw[v >> 1]);
                 }
             }
         }
@@ -608,18 +632,18 @@ struct Engine {
     // out(s, n, m, re, im) for m = 2g, 2g+1.
     template <class OUT>
     __device__ void pass0_inv(const OUT &out, int nsig) {
-        const int pg = phys(2 * g * S0);
+        const int lb = opaque((j ^ phys<LOG2M>(2 * g * S0)) << 2);
 #pragma unroll
         for (int i = 0; i < TIW; ++i) {
             const int s = (16 * (w + i * NW)) / S0;
             if (s < nsig) {
-                const int n = (16 * (w + i * NW)) % S0 + j;
-                const int pn = phys(n) ^ pg;
+                const int n0 = (16 * (w + i * NW)) % S0, n = n0 + j;
+                const int pn = lb ^ ((phys<LOG2M>(n0) << 2) | (s * SB));
                 uint32_t tu[4], x[4];
                 get_tu0(i % NDI, tu);
                 launder(tu);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) x[t] = cmulh_cx(at(s, pn ^ phys(tab::kChain[t] * S0)), tu[t]);
+                for (int t = 0; t < 4; ++t) x[t] = cmulh_cx(lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2)), tu[t]);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
                 const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
                 out(s, n, 2 * g, d[0], -d[1]);
@@ -640,22 +664,25 @@ struct Engine {
     // INV = true:  its inverse (up to the factor 16), x = conj(DFT(conj(y) tw)).
     // Each lane reads and writes back the slots k = chain(g, 0..3).
     template <int P, bool INV>
-    __device__ void mid_pass(int nsig) {
+    __device__ void mid_pass(int nsig, uint32_t pre = 0u) {
         constexpr int L = SH::L(P), S = L / 16;
-        const int pb = phys(base0<P>()) ^ phys(2 * g * S);
+        const int pb = opaque((phys<LOG2M>(base0<P>()) ^ phys<LOG2M>(2 * g * S)) << 2);
         uint32_t tw[4];
         get_twm(P - 1, tw);
         launder(tw);
-        for (int s = 0; s < nsig; ++s) {
+#pragma unroll
+        for (int s = 0; s < SIG; ++s) {
+            if (s >= nsig) break;
 #pragma unroll
             for (int ti = 0; ti < TPW; ++ti) {
-                const int ct = pb ^ phys(ti * DELTA);
+                const int ct = pb ^ (phys<LOG2M>(ti * DELTA) << 2);
                 int a[4];
                 uint32_t x[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    a[t] = ct ^ phys(tab::kChain[t] * S);
-                    x[t] = at(s, a[t]);
+                    a[t] = (ct ^ (phys<LOG2M>(tab::kChain[t] * S) << 2)) + s * SB;
+                    x[t] = lds(a[t]);
+                    if (INV && P == K) x[t] = pkmul(x[t], pre);  // scale set after the last pass
                     if (INV) x[t] = cmulh_cx(x[t], tw[t]);
                 }
                 const half8 b = as_half8(x[0], x[1], x[2], x[3]);
@@ -663,15 +690,15 @@ struct Engine {
                 const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, b, z, 0, 0, 0);
                 const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C1, b, z, 0, 0, 0);
                 if (!INV) {
-                    at(s, a[0]) = cmulh(pk(d0[0], d0[1]), tw[0]);
-                    at(s, a[1]) = cmulh(pk(d0[2], d0[3]), tw[1]);
-                    at(s, a[2]) = cmulh(pk(d1[0], d1[1]), tw[2]);
-                    at(s, a[3]) = cmulh(pk(d1[2], d1[3]), tw[3]);
+                    lds(a[0]) = cmulh(pk(d0[0], d0[1]), tw[0]);
+                    lds(a[1]) = cmulh(pk(d0[2], d0[3]), tw[1]);
+                    lds(a[2]) = cmulh(pk(d1[0], d1[1]), tw[2]);
+                    lds(a[3]) = cmulh(pk(d1[2], d1[3]), tw[3]);
                 } else {
-                    at(s, a[0]) = pk(d0[0], -d0[1]);
-                    at(s, a[1]) = pk(d0[2], -d0[3]);
-                    at(s, a[2]) = pk(d1[0], -d1[1]);
-                    at(s, a[3]) = pk(d1[2], -d1[3]);
+                    lds(a[0]) = pk(d0[0], -d0[1]);
+                    lds(a[1]) = pk(d0[2], -d0[3]);
+                    lds(a[2]) = pk(d1[0], -d1[1]);
+                    lds(a[3]) = pk(d1[2], -d1[3]);
                 }
             }
         }
@@ -686,35 +713,38 @@ struct Engine {
         }
     }
     template <int P>
-    __device__ void inv_middle(int nsig) {
+    __device__ void inv_middle(int nsig, uint32_t pre) {
         if constexpr (P >= 1) {
-            mid_pass<P, true>(nsig);
-            inv_middle<P - 1>(nsig);
+            mid_pass<P, true>(nsig, pre);
+            inv_middle<P - 1>(nsig, pre);
         }
     }
 
     // ---------------------------------------------------------- last pass
-    __device__ __forceinline__ int lpos(int slot, int &s) {
-        // physical base of the slot's group of R consecutive points
-        if constexpr (R == 16) {
-            s = -1;
-            return phys(16 * (16 * w + j)) ^ phys(16 * slot * 16 * NW);
-        } else if constexpr (R == 8) {
-            s = -1;
-            return phys(8 * (16 * w + j)) ^ phys(8 * slot * 16 * NW);
-        } else {
-            const int beta = tid + slot * NT;
-            s = beta / NBL;
-            return phys(R * (beta % NBL));
-        }
+    // Unit u of a lane covers one group of R consecutive points.  lbase() is
+    // the lane's byte base (laundered by the caller), lpos(u) the unit's
+    // compile-time XOR part, lsig(u) its signal.  For R = 16 / 8 the base
+    // already points at the lane's first slot 2g; R <= 4 needs NBL >= NT.
+    __device__ __forceinline__ int lbase() const {
+        if constexpr (R == 16) return (phys<LOG2M>(16 * (16 * w + j)) ^ (2 * g)) << 2;
+        else if constexpr (R == 8) return (phys<LOG2M>(8 * (16 * w + j)) ^ (2 * g)) << 2;
+        else return phys<LOG2M>(R * tid) << 2;
     }
+    static constexpr int lpos(int u) {
+        if constexpr (R == 16) return phys<LOG2M>(16 * (u % NLS) * 16 * NW) << 2;
+        else if constexpr (R == 8) return phys<LOG2M>(8 * (u % NLS) * 16 * NW) << 2;
+        else return phys<LOG2M>(R * ((u % NSL) * NT)) << 2;
+    }
+    static constexpr int lsig(int u) { return R >= 8 ? u / NLS : u / NSL; }
+    static_assert(R >= 8 || NBL % NT == 0, "radix-2/4 last pass: butterflies must be a multiple of the threads");
 
     // forward last-pass DFT of this slot (packed fp16 results, chained order
     // for R = 16, natural for R = 8)
-    __device__ __forceinline__ void last_fwd(int s, int pb, uint32_t (&y)[NV]) {
+    // (pb = byte address of the unit including its signal offset)
+    __device__ __forceinline__ void last_fwd(int pb, uint32_t (&y)[NV]) {
         if constexpr (R == 16) {
-            const u32x2 lo = *(const u32x2 *)&at(s, pb ^ (2 * g));
-            const u32x2 hi = *(const u32x2 *)&at(s, pb ^ (8 + 2 * g));
+            const u32x2 lo = lds<u32x2>(pb);
+            const u32x2 hi = lds<u32x2>(pb ^ 32);  // slots 8 + 2g, 9 + 2g
             // (elements go through scalars: bit-casting an element expression
             //  of an ext_vector directly reads element 0)
             const uint32_t v0 = lo.x, v1 = lo.y, v2 = hi.x, v3 = hi.y;
@@ -727,14 +757,14 @@ struct Engine {
             y[2] = pk(d1[0], d1[1]);
             y[3] = pk(d1[2], d1[3]);
         } else if constexpr (R == 8) {
-            const u32x2 v = *(const u32x2 *)&at(s, pb ^ (2 * g));
+            const u32x2 v = lds<u32x2>(pb);
             const uint32_t v0 = v.x, v1 = v.y;
             const f4 z = {0.f, 0.f, 0.f, 0.f};
             const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8, as_half4(v0, v1), z, 0, 0, 0);
             y[0] = pk(d[0], d[1]);
             y[1] = pk(d[2], d[3]);
         } else if constexpr (R == 4) {
-            const u32x4 v = *(const u32x4 *)&at(s, pb);
+            const u32x4 v = lds<u32x4>(pb);
             const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
             const h2 a = __builtin_bit_cast(h2, v0), b = __builtin_bit_cast(h2, v1),
                      c = __builtin_bit_cast(h2, v2), d = __builtin_bit_cast(h2, v3);
@@ -745,7 +775,7 @@ struct Engine {
             y[2] = __builtin_bit_cast(uint32_t, s0 - s1);
             y[3] = __builtin_bit_cast(uint32_t, d0 - d1mi);
         } else {
-            const u32x2 v = *(const u32x2 *)&at(s, pb);
+            const u32x2 v = lds<u32x2>(pb);
             const uint32_t v0 = v.x, v1 = v.y;
             const h2 a = __builtin_bit_cast(h2, v0), b = __builtin_bit_cast(h2, v1);
             y[0] = __builtin_bit_cast(uint32_t, a + b);
@@ -753,9 +783,10 @@ struct Engine {
         }
     }
 
-    // Inverse last-pass DFT, written back in place.  For R >= 8 `y` holds
+    // Inverse last-pass DFT, written back in place; returns the largest
+    // magnitude of a real or imaginary part written.  For R >= 8 `y` holds
     // conj(Y) and the forward matrix is used; for R <= 4 `y` holds Y.
-    __device__ __forceinline__ void last_inv(int s, int pb, const uint32_t (&y)[NV]) {
+    __device__ __forceinline__ float last_inv(int pb, const uint32_t (&y)[NV]) {
         if constexpr (R == 16) {
             const half8 b = as_half8(y[0], y[1], y[2], y[3]);
             const f4 z = {0.f, 0.f, 0.f, 0.f};
@@ -763,25 +794,35 @@ struct Engine {
             const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C1, b, z, 0, 0, 0);
             const u32x2 lo = {pk(d0[0], -d0[1]), pk(d0[2], -d0[3])};
             const u32x2 hi = {pk(d1[0], -d1[1]), pk(d1[2], -d1[3])};
-            *(u32x2 *)&at(s, pb ^ (2 * g)) = lo;
-            *(u32x2 *)&at(s, pb ^ (8 + 2 * g)) = hi;
+            lds<u32x2>(pb) = lo;
+            lds<u32x2>(pb ^ 32) = hi;
+            return fmaxf(fmaxf(habs_max(lo.x), habs_max(lo.y)), fmaxf(habs_max(hi.x), habs_max(hi.y)));
         } else if constexpr (R == 8) {
             const f4 z = {0.f, 0.f, 0.f, 0.f};
             const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8, as_half4(y[0], y[1]), z, 0, 0, 0);
             const u32x2 o = {pk(d[0], -d[1]), pk(d[2], -d[3])};
-            *(u32x2 *)&at(s, pb ^ (2 * g)) = o;
+            lds<u32x2>(pb) = o;
+            return fmaxf(habs_max(o.x), habs_max(o.y));
         } else if constexpr (R == 4) {
             const h2 a = __builtin_bit_cast(h2, y[0]), b = __builtin_bit_cast(h2, y[1]),
                      c = __builtin_bit_cast(h2, y[2]), d = __builtin_bit_cast(h2, y[3]);
             const h2 s0 = a + c, d0 = a - c, s1 = b + d, d1 = b - d;
             const h2 d1pi = {-d1.y, d1.x};  // (b - d) * (+i)
-            const u32x4 o = {__builtin_bit_cast(uint32_t, s0 + s1), __builtin_bit_cast(uint32_t, d0 + d1pi),
-                             __builtin_bit_cast(uint32_t, s0 - s1), __builtin_bit_cast(uint32_t, d0 - d1pi)};
-            *(u32x4 *)&at(s, pb) = o;
+            const h2 o0 = s0 + s1, o1 = d0 + d1pi, o2 = s0 - s1, o3 = d0 - d1pi;
+            const u32x4 o = {__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
+                             __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3)};
+            lds<u32x4>(pb) = o;
+            const h2 m = __builtin_elementwise_max(
+                __builtin_elementwise_max(__builtin_elementwise_abs(o0), __builtin_elementwise_abs(o1)),
+                __builtin_elementwise_max(__builtin_elementwise_abs(o2), __builtin_elementwise_abs(o3)));
+            return fmaxf((float)m.x, (float)m.y);
         } else {
             const h2 a = __builtin_bit_cast(h2, y[0]), b = __builtin_bit_cast(h2, y[1]);
-            const u32x2 o = {__builtin_bit_cast(uint32_t, a + b), __builtin_bit_cast(uint32_t, a - b)};
-            *(u32x2 *)&at(s, pb) = o;
+            const h2 o0 = a + b, o1 = a - b;
+            const u32x2 o = {__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1)};
+            lds<u32x2>(pb) = o;
+            const h2 m = __builtin_elementwise_max(__builtin_elementwise_abs(o0), __builtin_elementwise_abs(o1));
+            return fmaxf((float)m.x, (float)m.y);
         }
     }
 
@@ -789,41 +830,52 @@ struct Engine {
         if constexpr (R >= 8) return slot * NV;
         else return (slot % NSL) * NV;
     }
-    __device__ __forceinline__ bool unit_ok(int u, int slot, int s, int nsig) const {
-        if constexpr (R >= 8) return u / NLS < nsig;
-        else return slot * NT + tid < SIG * NBL && s < nsig;
+    // ---------------------------------------------------------- filter
+    // Filter spectrum, kept in registers as packed fp16: F = DFT(f) * cF / R
+    // (conjugated for R >= 8) with cF = 2^-e where sum |f| < 2^e.  Every
+    // partial sum of the transform is bounded by sum |f|, so inputs scaled by
+    // 2^(14 - e) keep the whole transform below 2^14 and |F| below 1 / R,
+    // without a reduction over the spectrum itself.
+    // Issue the loads of the real filter (nf taps, branch-free: indices are
+    // clamped and the padding selected afterwards) into this lane's pass-0
+    // slots; kept apart from the transform so the activation loads can be
+    // issued behind them.
+    template <class LDF>
+    __device__ __forceinline__ void filter_fetch(const LDF &ldf, int nf, float (&fin)[T0W][4]) {
+        const int h = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < T0W; ++i) {
+            const int off = tile_n(i) + 4 * h * S0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pos = off + e * S0;
+                const float v = ldf(min(pos, nf - 1));
+                fin[i][e] = (tile_sig(i) == 0 && pos < nf) ? v : 0.f;
+            }
+        }
     }
 
-    // ---------------------------------------------------------- filter
-    // Filter spectrum, kept in registers as packed fp16: F = DFT(f) * cF with
-    // cF = 2^-e where sum |f| < 2^e.  Every partial sum of the transform is
-    // bounded by sum |f|, so inputs scaled by 2^(14 - e) keep the whole
-    // transform below 2^14 and F below 1, without a reduction over the
-    // spectrum itself.
-    template <class LDF>
-    __device__ void filter(const LDF &ldf, int nf) {
-        cf fin[T0W][4];
-        fetch_fp32([&](int, int pos) -> cf { return mk(pos < nf ? ldf(pos) : 0.f, 0.f); }, 0, 1, fin);
+    __device__ void filter(const float (&fin)[T0W][4], int nf) {
         float asum = 0.f;
 #pragma unroll
         for (int i = 0; i < T0W; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) asum += fabsf(fin[i][e].x);
+            for (int e = 0; e < 4; ++e) asum += fabsf(fin[i][e]);
         asum = block_reduce<true>(asum);
         int ef = 0;
         if (asum > 0.f) (void)frexpf(asum, &ef);
         const float sf = ldexpf(1.f, 14 - ef);
         cF = ldexpf(1.f, -ef);
-        const uint32_t ch = pk(1.0f / 16384.0f, 1.0f / 16384.0f);
-        pass0([&](int i, int e) -> uint32_t { return pk(fin[i][e].x * sf, 0.f); }, 1);
+        constexpr float c = 1.0f / (16384.0f * R);
+        const uint32_t ch = R >= 8 ? pk(c, -c) : pk(c, c);  // conjugate for R >= 8
+        pass0([&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); }, 1);
         fwd_middle<1>(1);
+        const int lb = opaque(lbase());
 #pragma unroll
         for (int slot = 0; slot < NLS; ++slot) {
             if (R >= 8 || slot < NSL) {
-                int s;
-                const int pb = lpos(slot, s);
                 uint32_t y[NV];
-                last_fwd(0, pb, y);
+                last_fwd(lb ^ lpos(slot), y);
 #pragma unroll
                 for (int q = 0; q < NV; ++q) F[fslot(slot) + q] = pkmul(y[q], ch);
             }
@@ -855,84 +907,70 @@ struct Engine {
         const uint32_t suh = pk(su, su);
         pass0([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); }, nsig);
         fwd_middle<1>(nsig);
-        // last pass: spectrum x filter spectrum, held in registers; its maximum
-        // sets the scale of the inverse
+        // Last pass, in place: forward DFT-R, product with the filter spectrum
+        // (stored as F cF / R, conjugated for R >= 8, so no product can
+        // overflow the inverse DFT-R), inverse DFT-R.  The maximum of what it
+        // writes sets the scale sy applied by the next inverse pass.
         uint32_t Fr[FN];
 #pragma unroll
         for (int i = 0; i < FN; ++i) Fr[i] = F[i];
         launder(Fr);
-        uint32_t P[NU][NV];
-        float ymax = 0.f;
+        float vmax = 0.f;
+        const int lb = opaque(lbase());
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int slot = u % NLS;
-            int s;
-            const int pb = lpos(slot, s);
-            if (R >= 8) s = u / NLS;
-            if (unit_ok(u, slot, s, nsig)) {
+            if (lsig(u) < nsig) {
+                const int pb = (lb ^ lpos(u)) + lsig(u) * SB;
                 uint32_t y[NV];
-                last_fwd(s, pb, y);
+                last_fwd(pb, y);
 #pragma unroll
-                for (int q = 0; q < NV; ++q) {
-                    P[u][q] = cmulh(y[q], Fr[fslot(slot) + q]);
-                    ymax = fmaxf(ymax, habs_max(P[u][q]));
-                }
+                for (int q = 0; q < NV; ++q)
+                    y[q] = R >= 8 ? cmulh_cx(y[q], Fr[fslot(slot) + q]) : cmulh(y[q], Fr[fslot(slot) + q]);
+                vmax = fmaxf(vmax, last_inv(pb, y));
             }
         }
-        // Scale of the inverse: a power of two that keeps every inverse partial
-        // sum below 2^15; applied to the fp16 product, so clamped to fp16's exact
-        // powers of two (max|Y| < 2^16 bounds it below by 2^-15).
-        const float sy = fminf(fmaxf(pow2_scale(block_reduce<false>(ymax), (LOG2M + 1) / 2), 1.0f / 32768.0f),
-                               16384.0f);
-        // R >= 8 inverts through the forward matrix: feed conj(Y sy)
-        const uint32_t syh = R >= 8 ? pk(sy, -sy) : pk(sy, sy);
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int slot = u % NLS;
-            int s;
-            const int pb = lpos(slot, s);
-            if (R >= 8) s = u / NLS;
-            if (unit_ok(u, slot, s, nsig)) {
-                uint32_t y[NV];
-#pragma unroll
-                for (int q = 0; q < NV; ++q) y[q] = pkmul(P[u][q], syh);
-                last_inv(s, pb, y);
-            }
-        }
-        __syncthreads();
-        inv_middle<K>(nsig);
-        const float os = 1.0f / ((float)M * su * sy * cF);
+        // The remaining inverse passes grow magnitudes by at most M / R: scale
+        // to keep every partial sum below 2^14, as an exact fp16 power of two.
+        const float vm = block_reduce<false>(vmax);
+        int ev = 0;
+        if (vm > 0.f) (void)frexpf(vm, &ev);
+        const float sy = fminf(fmaxf(ldexpf(1.f, 14 - ev - (LOG2M - SH::LR)), 1.0f / 16384.0f), 32768.0f);
+        inv_middle<K>(nsig, pk(sy, sy));
+        const float os = (float)R / ((float)M * su * sy * cF);
         pass0_inv([&](int s, int n, int m, float re, float im) { out(s, n, m, re * os, im * os); }, nsig);
     }
 
     // A whole channel of 16-bit activations: the filter spectrum, then
     // ceil(nsig / SIG) rounds of complex signals.  ldf(pos) gives the real
-    // filter (nf taps); rows(sig) the row pointers of signal `sig`; nval the
-    // sequence length.  The inputs of each round are fetched while the
+    // filter (nf taps); rows(sig) the buffer resources of signal `sig`.  The inputs of each round are fetched while the
     // previous round (or the filter) is being transformed.
-    template <class LDF, class RP>
-    __device__ void run_raw(const LDF &ldf, int nf, const RP &rows, int nsig, int nval, int hb) {
+    template <class LDF, class RB>
+    __device__ void run_raw(const LDF &ldf, int nf, const RB &rows, int nsig, int hb) {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
-        fetch_raw(rows, 0, min(SIG, nsig), nval, pnx);
-        filter(ldf, nf);
+        float fin[T0W][4];
+        filter_fetch(ldf, nf, fin);
+        if constexpr (PREFETCH) fetch_raw(rows, 0, min(SIG, nsig), pnx);
+        filter(fin, nf);
         for (int r0 = 0; r0 < nsig; r0 += SIG) {
             const int nr = min(SIG, nsig - r0);
+            if constexpr (PREFETCH) {
 #pragma unroll
-            for (int i = 0; i < T0W; ++i)
+                for (int i = 0; i < T0W; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pin[i][e] = pnx[i][e];
-            if (r0 + SIG < nsig) fetch_raw(rows, r0 + SIG, min(SIG, nsig - r0 - SIG), nval, pnx);
+                    for (int e = 0; e < 4; ++e) pin[i][e] = pnx[i][e];
+                if (r0 + SIG < nsig) fetch_raw(rows, r0 + SIG, min(SIG, nsig - r0 - SIG), pnx);
+            } else {
+                fetch_raw(rows, r0, nr, pin);
+            }
             auto out = [&](int s, int n, int m, float re, float im) {
-                const int pos = n + m * S0;
-                if (pos < nval) {
-                    const RowPtrs rp = rows(r0 + s);
-                    const f2 v = {re, im};
-                    uint32_t hv;
-                    if constexpr (KIND == IN_F16) hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
-                    else hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
-                    rp.out0[pos] = (uint16_t)hv;
-                    if (rp.out1) rp.out1[pos] = (uint16_t)(hv >> 16);
-                }
+                const RowBufs rb = rows(r0 + s);
+                const f2 v = {re, im};
+                uint32_t hv;
+                if constexpr (KIND == IN_F16) hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+                else hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * n, 2 * m * S0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * n, 2 * m * S0, 0);
             };
             conv_round(out, nr, hb);
         }
@@ -943,15 +981,21 @@ struct Engine {
     template <class LDF, class LD, class ST>
     __device__ void run_fp32(const LDF &ldf, int nf, const LD &ld, const ST &st, int nsig, int nval, int hb) {
         static_assert(KIND == IN_FP32, "fp32 inputs");
-        fetch_fp32(ld, 0, min(SIG, nsig), pnx);
-        filter(ldf, nf);
+        float fin[T0W][4];
+        filter_fetch(ldf, nf, fin);
+        if constexpr (PREFETCH) fetch_fp32(ld, 0, min(SIG, nsig), pnx);
+        filter(fin, nf);
         for (int r0 = 0; r0 < nsig; r0 += SIG) {
             const int nr = min(SIG, nsig - r0);
+            if constexpr (PREFETCH) {
 #pragma unroll
-            for (int i = 0; i < T0W; ++i)
+                for (int i = 0; i < T0W; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pin[i][e] = pnx[i][e];
-            if (r0 + SIG < nsig) fetch_fp32(ld, r0 + SIG, min(SIG, nsig - r0 - SIG), pnx);
+                    for (int e = 0; e < 4; ++e) pin[i][e] = pnx[i][e];
+                if (r0 + SIG < nsig) fetch_fp32(ld, r0 + SIG, min(SIG, nsig - r0 - SIG), pnx);
+            } else {
+                fetch_fp32(ld, r0, nr, pin);
+            }
             auto out = [&](int s, int n, int m, float re, float im) {
                 const int pos = n + m * S0;
                 if (pos < nval) st(r0 + s, pos, re, im);

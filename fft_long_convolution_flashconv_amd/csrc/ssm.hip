@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256) void k_sp_correct_mfma(typename io_elem<IO>::T
 
 // Same chunk convolution on the MFMA block-FFT engine (fp16 / bf16 I/O).
 template <int LOG2M, int IO>
-__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_sp_chunk_conv_mfma(
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M>::WPE))) void k_sp_chunk_conv_mfma(
     const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ fT,
     typename io_elem<IO>::T *__restrict__ y, int B, int H, int64_t N, int T) {
     using SH = mf::Shape<LOG2M>;
@@ -619,14 +619,16 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) void k_sp_chunk_conv_mfma(
         return ((size_t)b * H + h) * N + (size_t)c * T;
     };
     // complex signal `sig` = row chunks 2 sig (real part), 2 sig + 1 (imaginary)
-    auto rowp = [&](int sig) -> mf::RowPtrs {
+    auto rowp = [&](int sig) -> mf::RowBufs {
         const int r = 2 * sig;
-        const bool two = r + 1 < rows;
+        const int nb1 = (r + 1 < rows) ? 2 * T : 0;
         const uint16_t *ub = (const uint16_t *)u;
         uint16_t *yb = (uint16_t *)y;
-        return {ub + off(r), two ? ub + off(r + 1) : nullptr, yb + off(r), two ? yb + off(r + 1) : nullptr};
+        const size_t o1 = (r + 1 < rows) ? off(r + 1) : off(r);
+        return {mf::row_rsrc(ub + off(r), 2 * T), mf::row_rsrc(ub + o1, nb1), mf::row_rsrc(yb + off(r), 2 * T),
+                mf::row_rsrc(yb + o1, nb1)};
     };
-    E.run_raw([&](int pos) -> float { return fh[pos]; }, T, rowp, (rows + 1) / 2, T, hb);
+    E.run_raw([&](int pos) -> float { return fh[pos]; }, T, rowp, (rows + 1) / 2, hb);
 }
 
 template <int LOG2M, int IO>
