@@ -633,21 +633,36 @@ struct Engine {
     template <class OUT>
     __device__ void pass0_inv(const OUT &out, int nsig) {
         const int lb = opaque((j ^ phys<LOG2M>(2 * g * S0)) << 2);
+        // All twiddles and products first, then all stores: loads and stores
+        // retire in order, so a table load behind a store would wait for it.
+        uint32_t tua[NDI][4];
+#pragma unroll
+        for (int d = 0; d < NDI; ++d) get_tu0(d, tua[d]);
+        f4 res[TIW];
 #pragma unroll
         for (int i = 0; i < TIW; ++i) {
             const int s = (16 * (w + i * NW)) / S0;
+            res[i] = f4{0.f, 0.f, 0.f, 0.f};
             if (s < nsig) {
-                const int n0 = (16 * (w + i * NW)) % S0, n = n0 + j;
+                const int n0 = (16 * (w + i * NW)) % S0;
                 const int pn = lb ^ ((phys<LOG2M>(n0) << 2) | (s * SB));
                 uint32_t tu[4], x[4];
-                get_tu0(i % NDI, tu);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) tu[t] = tua[i % NDI][t];
                 launder(tu);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) x[t] = cmulh_cx(lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2)), tu[t]);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
-                const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
-                out(s, n, 2 * g, d[0], -d[1]);
-                out(s, n, 2 * g + 1, d[2], -d[3]);
+                res[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TIW; ++i) {
+            const int s = (16 * (w + i * NW)) / S0;
+            if (s < nsig) {
+                const int n = (16 * (w + i * NW)) % S0 + j;
+                out(s, n, 2 * g, res[i][0], -res[i][1]);
+                out(s, n, 2 * g + 1, res[i][2], -res[i][3]);
             }
         }
     }
