@@ -81,6 +81,8 @@ class Case:
                                       device=dev, dtype=torch.uint8)
             else:
                 s["y"] = torch.empty_like(s["q"])
+                s["ws"] = torch.empty(pkg.workspace_size(pkg.OP_H3_MIX, w.B, w.Dm, w.N), device=dev,
+                                      dtype=torch.uint8)
             self.sets.append(s)
         torch.cuda.synchronize()
 
@@ -93,7 +95,7 @@ class Case:
             pkg.state_pass(s["u"], s["A"], s["Bm"], s["C"], s["dt"], s["D"], w.T, out=s["y"],
                            workspace=s["ws"])
         else:
-            pkg.h3_mix(s["q"], s["k"], s["v"], s["w"], s["f"], s["D"], out=s["y"])
+            pkg.h3_mix(s["q"], s["k"], s["v"], s["w"], s["f"], s["D"], out=s["y"], workspace=s["ws"])
 
 
 def time_case(case: Case, steps: int, warmup: int):

@@ -57,7 +57,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.h3conv_fft_conv.argtypes = [P, P, P, P, I64, I64, I64, I, P]
     lib.h3conv_ssm_filter.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.h3conv_state_pass.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
-    lib.h3conv_h3_mix.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P]
+    lib.h3conv_h3_mix.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.h3conv_workspace_size.argtypes = [I, I64, I64, I64, I64, I64]
     lib.h3conv_workspace_size.restype = SZ
     lib.h3conv_status_string.argtypes = [I]
@@ -174,8 +174,11 @@ def state_pass(u, A, Bm, C, dt, D, T: int, x_in=None, return_state: bool = False
     return y
 
 
-def h3_mix(q, k, v, w, f, D, out=None):
-    """out = q * ((f * m)[:N] + D m), m = shift(k) * v; q,k,v [B,N,Dm], w [Dm,L], f [Dm,N], D [Dm]."""
+def h3_mix(q, k, v, w, f, D, out=None, workspace=None):
+    """out = q * ((f * m)[:N] + D m), m = shift(k) * v; q,k,v [B,N,Dm], w [Dm,L], f [Dm,N], D [Dm].
+
+    16-bit activations stage m and z channel-major in a workspace
+    (allocated here when not given)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype)
     if q.dtype not in _IO:
@@ -187,7 +190,12 @@ def h3_mix(q, k, v, w, f, D, out=None):
     L = w.shape[1]
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", q.dtype)
+    ws, nws = None, 0
+    if q.dtype != torch.float32:
+        ws = workspace if workspace is not None else torch.empty(
+            workspace_size(OP_H3_MIX, B, Dm, N), dtype=torch.uint8, device=q.device)
+        nws = ws.numel() * ws.element_size()
     _check(load().h3conv_h3_mix(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(f), _ptr(D), _ptr(o), B, N, Dm, L,
-                                _IO[q.dtype], _stream()),
+                                _IO[q.dtype], _ptr(ws) if ws is not None else None, nws, _stream()),
            "h3conv_h3_mix")
     return o

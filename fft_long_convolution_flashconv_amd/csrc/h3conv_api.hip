@@ -63,8 +63,10 @@ const char *h3conv_status_string(int status) {
 
 size_t h3conv_workspace_size(int op, int64_t B, int64_t H, int64_t N, int64_t S, int64_t T) {
     switch (op) {
-        case H3CONV_OP_FFT_CONV:
-        case H3CONV_OP_H3_MIX: return 0;
+        case H3CONV_OP_FFT_CONV: return 0;
+        case H3CONV_OP_H3_MIX:
+            if (B < 0 || H < 0 || N < 0) return (size_t)-1;
+            return h3c::h3_mix_workspace(B, N, H);
         case H3CONV_OP_STATE_PASS:
             if (B < 0 || H < 0 || N < 0 || S < 1 || S > H3CONV_MAX_STATE || T < 64 ||
                 T > H3CONV_MAX_FUSED_N || (T & (T - 1)) != 0 || N % T != 0)
@@ -147,7 +149,7 @@ h3conv_status h3conv_state_pass(const void *u, const float *A, const float *Bm, 
 
 h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const float *w,
                             const float *f, const float *D, void *out, int64_t B, int64_t N,
-                            int64_t Dm, int64_t L, int io, void *stream) {
+                            int64_t Dm, int64_t L, int io, void *ws, size_t ws_bytes, void *stream) {
     if (B < 0 || N < 0 || Dm < 0 || L < 1 || !valid_io(io)) return H3CONV_ERR_INVALID_ARG;
     if (B == 0 || N == 0 || Dm == 0) return H3CONV_OK;
     if (L > 4 || N > H3CONV_MAX_FUSED_N) return H3CONV_ERR_UNSUPPORTED;
@@ -161,9 +163,20 @@ h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const f
         overlap(out, n, w, (size_t)(Dm * L) * 4) || overlap(out, n, f, (size_t)(Dm * N) * 4) ||
         overlap(out, n, D, (size_t)Dm * 4))
         return H3CONV_ERR_INVALID_ARG;
+    if (io != H3CONV_F32) {
+        const size_t need = h3c::h3_mix_workspace(B, N, Dm);
+        if (!ws || ws_bytes < need) return H3CONV_ERR_WORKSPACE;
+        if (!aligned16(ws)) return H3CONV_ERR_INVALID_ARG;
+        const void *ins[] = {q, k, v, out};
+        for (const void *p : ins)
+            if (overlap(ws, need, p, n)) return H3CONV_ERR_INVALID_ARG;
+        if (overlap(ws, need, w, (size_t)(Dm * L) * 4) || overlap(ws, need, f, (size_t)(Dm * N) * 4) ||
+            overlap(ws, need, D, (size_t)Dm * 4))
+            return H3CONV_ERR_INVALID_ARG;
+    }
     h3conv_status st = device_check();
     if (st != H3CONV_OK) return st;
-    return from_hip(h3c::launch_h3_mix(q, k, v, w, f, D, out, (int)B, (int)N, (int)Dm, (int)L, io,
+    return from_hip(h3c::launch_h3_mix(q, k, v, w, f, D, out, (int)B, (int)N, (int)Dm, (int)L, io, ws,
                                        (hipStream_t)stream));
 }
 

@@ -19,7 +19,8 @@ hipError_t launch_fft_conv(const void *u, const float *f, const float *D, void *
 
 hipError_t launch_h3_mix(const void *q, const void *k, const void *v, const float *w,
                          const float *f, const float *D, void *out, int B, int N, int Dm, int L,
-                         int io, hipStream_t s);
+                         int io, void *ws, hipStream_t s);
+size_t h3_mix_workspace(int64_t B, int64_t N, int64_t Dm);
 
 hipError_t launch_ssm_filter(const float *A, const float *Bm, const float *C, const float *dt,
                              float *f, int H, int S, int64_t N, hipStream_t s);

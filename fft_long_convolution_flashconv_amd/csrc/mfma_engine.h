@@ -586,19 +586,6 @@ struct Engine {
         }
     }
 
-    // generic fp32 inputs: ld(sig, pos) -> cf, zero past the sequence
-    template <class LD>
-    __device__ __forceinline__ void fetch_fp32(const LD &ld, int sig0, int nsig, cf (&buf)[T0W][4]) {
-        const int h = lane >> 5;
-#pragma unroll
-        for (int i = 0; i < T0W; ++i) {
-            const int s = tile_sig(i);
-            const int off = tile_n(i) + 4 * h * S0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) buf[i][e] = (s < nsig) ? ld(sig0 + s, off + e * S0) : mk(0.f, 0.f);
-        }
-    }
-
     // Zero-padded radix-16 DIF pass: DFT on the matrix cores, twiddle w_M^{n q},
     // to LDS.  `op(i, e)` yields the packed scaled operand of tile i.
     template <class OP>
@@ -986,34 +973,6 @@ struct Engine {
                 else hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
                 __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * n, 2 * m * S0, 0);
                 __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * n, 2 * m * S0, 0);
-            };
-            conv_round(out, nr, hb);
-        }
-    }
-
-    // Same for fp32 inputs from a loader ld(sig, pos) (zero past the
-    // sequence) and a store st(sig, pos, re, im).
-    template <class LDF, class LD, class ST>
-    __device__ void run_fp32(const LDF &ldf, int nf, const LD &ld, const ST &st, int nsig, int nval, int hb) {
-        static_assert(KIND == IN_FP32, "fp32 inputs");
-        float fin[T0W][4];
-        filter_fetch(ldf, nf, fin);
-        if constexpr (PREFETCH) fetch_fp32(ld, 0, min(SIG, nsig), pnx);
-        filter(fin, nf);
-        for (int r0 = 0; r0 < nsig; r0 += SIG) {
-            const int nr = min(SIG, nsig - r0);
-            if constexpr (PREFETCH) {
-#pragma unroll
-                for (int i = 0; i < T0W; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pin[i][e] = pnx[i][e];
-                if (r0 + SIG < nsig) fetch_fp32(ld, r0 + SIG, min(SIG, nsig - r0 - SIG), pnx);
-            } else {
-                fetch_fp32(ld, r0, nr, pin);
-            }
-            auto out = [&](int s, int n, int m, float re, float im) {
-                const int pos = n + m * S0;
-                if (pos < nval) st(r0 + s, pos, re, im);
             };
             conv_round(out, nr, hb);
         }

@@ -125,16 +125,24 @@ h3conv_status h3conv_state_pass(const void *u, const float *A, const float *Bm, 
  *
  *   q, k, v [B,N,Dm] io dtype   w [Dm,L] fp32   f [Dm,N] fp32   D [Dm] fp32
  *   out     [B,N,Dm] io dtype (must not overlap any input)
+ *   ws, ws_bytes  for H3CONV_F16 / H3CONV_BF16: workspace of at least
+ *             h3conv_workspace_size(H3CONV_OP_H3_MIX, B, Dm, N, 0, 0) bytes,
+ *             16-byte aligned, overlapping nothing else (m and z are staged
+ *             there channel-major, as bf16); ignored for H3CONV_F32 (may be
+ *             NULL).  Too small or NULL: H3CONV_ERR_WORKSPACE.
  * Supported: 1 <= N <= H3CONV_MAX_FUSED_N, 1 <= L <= 4, B*Dm < 2^31.
  */
 h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const float *w,
                             const float *f, const float *D, void *out, int64_t B, int64_t N,
-                            int64_t Dm, int64_t L, int io, void *stream);
+                            int64_t Dm, int64_t L, int io, void *ws, size_t ws_bytes,
+                            void *stream);
 
 /*
  * Workspace bytes an operation needs for the given sizes (0 if none).
- * `op` is an h3conv_op; unused size arguments are ignored.  Returns
- * (size_t)-1 for sizes the operation does not support.
+ * `op` is an h3conv_op; unused size arguments are ignored.  For
+ * H3CONV_OP_H3_MIX, H is the model width Dm and the size is that of the
+ * 16-bit activation path (the fp32 path needs none).  Returns (size_t)-1 for
+ * sizes the operation does not support.
  */
 size_t h3conv_workspace_size(int op, int64_t B, int64_t H, int64_t N, int64_t S, int64_t T);
 

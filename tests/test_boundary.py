@@ -47,7 +47,8 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_size(lib):
     assert pkg.workspace_size(pkg.OP_FFT_CONV, 8, 768, 1024) == 0
-    assert pkg.workspace_size(pkg.OP_H3_MIX, 4, 2560, 2048) == 0
+    # 16-bit H3 mix stages m and z channel-major as bf16: two [B, Dm, N] buffers
+    assert pkg.workspace_size(pkg.OP_H3_MIX, 4, 2560, 2048) == 2 * 4 * 2560 * 2048 * 2
     n = pkg.workspace_size(pkg.OP_STATE_PASS, 2, 1024, 65536, 64, 8192)
     assert n > 0 and n % 256 == 0
     for bad in [(2, 4, 1000, 64, 8192), (2, 4, 8192, 65, 8192), (2, 4, 8192, 64, 100),
@@ -108,9 +109,9 @@ def test_state_pass_validation(lib):
     assert _sp(lib, B=0) == pkg.OK
 
 
-def _hm(lib, out=0x900000, B=2, N=64, Dm=8, L=4, io=2):
+def _hm(lib, out=0x900000, B=2, N=64, Dm=8, L=4, io=2, ws=0xa00000, nws=1 << 20):
     return lib.h3conv_h3_mix(0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, out,
-                             B, N, Dm, L, io, None)
+                             B, N, Dm, L, io, ws, nws, None)
 
 
 def test_h3_mix_validation(lib):
@@ -119,6 +120,9 @@ def test_h3_mix_validation(lib):
     assert _hm(lib, N=8193) == pkg.ERR_UNSUPPORTED
     assert _hm(lib, out=0x100000) == pkg.ERR_INVALID_ARG  # out aliases q
     assert _hm(lib, out=0x900008) == pkg.ERR_INVALID_ARG  # misaligned
+    assert _hm(lib, ws=None) == pkg.ERR_WORKSPACE          # 16-bit path needs a workspace
+    assert _hm(lib, nws=16) == pkg.ERR_WORKSPACE
+    assert _hm(lib, ws=0x100000) == pkg.ERR_INVALID_ARG    # workspace overlaps q
     assert _hm(lib, B=0) == pkg.OK
 
 
