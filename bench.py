@@ -12,7 +12,10 @@ the next of several independent input/output sets whose total exceeds 512 MB.
 
 Output: one JSON line with elements/s (B*H*N per second), the roofline of the
 dominant kernel against MI355X HBM3E (8 TB/s) measured with HIP events on the
-launch stream, and the fp64 CPU oracle timed on this host's cores.
+launch stream, and the fp64 CPU oracle timed on this host's cores.  The HBM
+traffic of the dominant kernel comes from the committed rocprofv3 counter
+summary (profiles/), and is reported only while the kernel sources still hash
+to the value recorded there.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --calib-copy    # plain 1 GiB device copy, for counter calibration
@@ -20,8 +23,10 @@ launch stream, and the fp64 CPU oracle timed on this host's cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,9 +43,39 @@ METRIC = "long-conv elements/s (B·H·N) + achieved HBM GB/s vs peak, N=1K–64K
 HBM_PEAK_GBS = 8000.0
 CACHE_BYTES = 512 << 20
 ESZ = {"f32": 4, "f16": 2, "bf16": 2}
-# dtype the convolution arithmetic runs in (activations are stored in the
-# workload's I/O dtype; every transform is computed in fp32)
-COMPUTE_DTYPE = "f32"
+# dtype the transforms compute in: for 16-bit activations the DFT blocks run
+# on the matrix cores with fp16 operands and fp32 accumulation, and twiddles,
+# scaling and the spectrum product are packed fp16; fp32 activations use the
+# fp32 vector engine
+COMPUTE_DTYPE = {"f16": "f16", "bf16": "f16", "f32": "f32"}
+# sources that define the dominant kernel, and the counter summary of it
+KERNEL_SOURCES = ("fft_long_convolution_flashconv_amd/csrc/mfma_engine.h",
+                  "fft_long_convolution_flashconv_amd/csrc/fftconv.hip",
+                  "fft_long_convolution_flashconv_amd/csrc/h3conv_device.h")
+PROFILE = "profiles/k_fft_conv_mfma_conv_1k.md"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch from the counter summary, if it covers this
+    workload and the current kernel sources (else None)."""
+    path = os.path.join(ROOT, PROFILE)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel source hash: `([0-9a-f]+)`", text)
+    m_wl = re.search(r"workload: `([a-z0-9_]+)`", text)
+    m_tr = re.search(r"traffic per launch: ([0-9]+) bytes", text)
+    if not (m_hash and m_wl and m_tr) or m_wl.group(1) != workload or m_hash.group(1) != kernel_source_hash():
+        return None
+    return int(m_tr.group(1))
 
 
 def log(*a):
@@ -99,22 +134,23 @@ class Case:
 
 
 def time_case(case: Case, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` steps.  HIP events on the launch
+    stream bracket the whole timed region (launches queue back to back, so
+    their elapsed time over `steps` is the average launch duration); the wall
+    clock is bracketed by device synchronisations."""
     for i in range(warmup):
         case.step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         case.step(warmup + i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    mean_ms = sum(per_launch_ms) / len(per_launch_ms)
-    return wall, mean_ms, per_launch_ms[len(per_launch_ms) // 2]
+    return wall, e0.elapsed_time(e1) / steps
 
 
 def cpu_baseline(w: wl.Workload, budget_s: float = 12.0) -> dict:
@@ -132,22 +168,29 @@ def cpu_baseline(w: wl.Workload, budget_s: float = 12.0) -> dict:
                               inp["dt"].double().numpy(), w.N) if "A" in inp else inp["f"].double().numpy()
         u = inp["u"].double().numpy()
         D = inp["D"].double().numpy()
-        # sample: whole batch rows for a growing number of channels until the budget is used
+        # sample: whole batch rows of a growing number of channels, then the
+        # sample repeated, until about `budget_s` seconds of CPU work
         H = w.H
-        t_one = None
         hs = 16
         while True:
             sel = np.arange(min(hs, H))
+            ua, fa, Da = np.ascontiguousarray(u[:, sel]), np.ascontiguousarray(f[sel]), D[sel]
             t0 = time.perf_counter()
-            oracle.causal_conv(np.ascontiguousarray(u[:, sel]), np.ascontiguousarray(f[sel]), D[sel])
+            oracle.causal_conv(ua, fa, Da)
             t_one = time.perf_counter() - t0
             if t_one > budget_s / 4 or hs >= H:
                 break
             hs = min(H, hs * 4)
-        n_el = w.B * len(sel) * w.N
-        return {"value": n_el / t_one, "unit": "elements/s", "cores": oracle.max_threads(), "kind": "oracle",
-                "sample": "direct O(N^2) causal conv (fp64) of all %d batch rows x %d of %d channels, N=%d "
-                          "(%.2f s)" % (w.B, len(sel), H, w.N, t_one)}
+        reps, total = 1, t_one
+        while total < budget_s:
+            t0 = time.perf_counter()
+            oracle.causal_conv(ua, fa, Da)
+            total += time.perf_counter() - t0
+            reps += 1
+        n_el = w.B * len(sel) * w.N * reps
+        return {"value": n_el / total, "unit": "elements/s", "cores": oracle.max_threads(), "kind": "oracle",
+                "sample": "direct O(N^2) causal conv (fp64) of all %d batch rows x %d of %d channels, N=%d, "
+                          "%d repetition(s), %.1f s" % (w.B, len(sel), H, w.N, reps, total)}
     raise ValueError(w.kind)
 
 
@@ -172,6 +215,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash and exit")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -181,13 +225,16 @@ def main():
     if a.calib_copy:
         calib_copy()
         return
+    if a.source_hash:
+        print(kernel_source_hash())
+        return
     dev = torch.device("cuda:0")
     pkg.load()
 
     w = wl.WORKLOADS[a.workload]
     log("bench: workload %s %s" % (w.name, w))
     case = Case(w, dev)
-    wall, mean_ms, med_ms = time_case(case, a.steps, a.warmup)
+    wall, mean_ms = time_case(case, a.steps, a.warmup)
     ms_per_step = wall * 1e3 / a.steps
     nbytes = algorithmic_bytes(w)
     achieved = nbytes / (mean_ms * 1e-3) / 1e9
@@ -202,14 +249,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": COMPUTE_DTYPE,
+        "dtype": COMPUTE_DTYPE[w.dtype],
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": w.name, "B": w.B, "H": w.H or w.Dm, "N": w.N, "io_dtype": w.dtype,
                    "kind": w.kind, "input_sets_rotated": case.nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel_mean_us": mean_ms * 1e3, "kernel_median_us": med_ms * 1e3,
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(w.name),
+                     "kernel_mean_us": mean_ms * 1e3, "algorithmic_bytes_per_launch": nbytes},
     }
     del case
     torch.cuda.empty_cache()
@@ -220,7 +266,7 @@ def main():
                 continue
             ww = wl.WORKLOADS[name]
             c = Case(ww, dev)
-            _, m_ms, md_ms = time_case(c, max(5, a.steps // 5), 3)
+            _, m_ms = time_case(c, max(5, a.steps // 5), 3)
             nb = algorithmic_bytes(ww)
             sec[name] = {"elements_per_s": ww.elements / (m_ms * 1e-3), "mean_us": m_ms * 1e3,
                          "algorithmic_bytes": nb, "GB_s": nb / (m_ms * 1e-3) / 1e9,
