@@ -21,13 +21,43 @@
 
 namespace h3c {
 
-// Abar^n = exp(n dt A) in fp64 (dt*Re A and dt*Im A are exact products of
-// fp32 values; the library's fp64 sincos reduces large phases accurately).
-__device__ __forceinline__ cf abar_pow(double are, double aim, double n) {
-    double s, c;
-    sincos(aim * n, &s, &c);
+// Abar^n = exp(n dt A) in fp64.  dt Re A and dt Im A are exact products of
+// fp32 values.  The phase n dt Im A reaches ~1e5 rad, so it is first reduced
+// by whole turns with a two-part 2 pi (the residual keeps the absolute error
+// of the fp64 product, ~1e-11 rad) and the sine and cosine then take their
+// short-argument path.
+__device__ __forceinline__ void apow64(double are, double aim, double n, double &re, double &im) {
+    constexpr double kTwoPiHi = 6.283185307179586232;   // 2 pi rounded to fp64
+    constexpr double kTwoPiLo = 2.4492935982947064e-16; // 2 pi - kTwoPiHi
+    const double ph = aim * n;
+    const double k = rint(ph * (1.0 / kTwoPiHi));
+    const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ph));
+    double sn, cs;
+    sincos(r, &sn, &cs);
     const double m = exp(are * n);
-    return mk((float)(m * c), (float)(m * s));
+    re = m * cs;
+    im = m * sn;
+}
+__device__ __forceinline__ cf abar_pow(double are, double aim, double n) {
+    double re, im;
+    apow64(are, aim, n, re, im);
+    return mk((float)re, (float)im);
+}
+
+// Runs of powers Abar^(n0 + k step), k < cnt: the first power and the step
+// are exact fp64 exponentials, the rest fp64 complex products (relative error
+// grows by ~1e-16 per step, so a run of <= 17 stays far below fp32 rounding).
+template <class EMIT>
+__device__ __forceinline__ void pow_run(double are, double aim, double n0, double step, int cnt, const EMIT &emit) {
+    double pr, pi, sr, si;
+    apow64(are, aim, n0, pr, pi);
+    apow64(are, aim, step, sr, si);
+    for (int k = 0; k < cnt; ++k) {
+        emit(k, pr, pi);
+        const double t = pr * sr - pi * si;
+        pi = pr * si + pi * sr;
+        pr = t;
+    }
 }
 
 // ---------------------------------------------------------------- filter
@@ -49,24 +79,26 @@ __global__ __launch_bounds__(256) void k_ssm_filter(const float *__restrict__ A,
     const int h = blockIdx.x;
     const double dth = (double)dt[h];
 
-    // WE table
-    for (int e = tid; e < S * 64; e += 256) {
-        const int j = e >> 6, l = e & 63;
+    // WE table: runs of 16 powers per (mode, quarter)
+    for (int e = tid; e < S * 4; e += 256) {
+        const int j = e >> 2, q = e & 3;
         const float *a = A + ((size_t)h * S + j) * 2;
         const float *b = Bm + ((size_t)h * S + j) * 2;
         const float *c = C + ((size_t)h * S + j) * 2;
-        const cf p = abar_pow(dth * (double)a[0], dth * (double)a[1], (double)l);
         const cf w = cmul(mk(c[0], c[1]), mk((float)(dth * b[0]), (float)(dth * b[1])));
-        WE[j][l] = cmul(w, p);
+        pow_run(dth * (double)a[0], dth * (double)a[1], 16.0 * q, 1.0, 16,
+                [&](int k, double pr, double pi) { WE[j][16 * q + k] = cmul(w, mk((float)pr, (float)pi)); });
     }
     for (int64_t seg = 0; seg < N; seg += FILT_SEG) {
         const int nseg = (int)((N - seg < FILT_SEG) ? (N - seg) : FILT_SEG);
         const int ni = (nseg + 63) / 64;
         __syncthreads();
-        for (int e = tid; e < S * ni; e += 256) {
-            const int j = e / ni, i = e % ni;
+        const int nr = (ni + 15) / 16;  // runs of 16 powers Abar^(seg + 64 i)
+        for (int e = tid; e < S * nr; e += 256) {
+            const int j = e / nr, q = e % nr;
             const float *a = A + ((size_t)h * S + j) * 2;
-            G[j][i] = abar_pow(dth * (double)a[0], dth * (double)a[1], (double)(seg + 64 * i));
+            pow_run(dth * (double)a[0], dth * (double)a[1], (double)(seg + 1024 * q), 64.0, min(16, ni - 16 * q),
+                    [&](int k, double pr, double pi) { G[j][16 * q + k] = mk((float)pr, (float)pi); });
         }
         __syncthreads();
         // tiles: l in {2 lp, 2 lp + 1}, i in {4 ip .. 4 ip + 3}
@@ -330,17 +362,16 @@ __global__ __launch_bounds__(256) void k_sp_correct(typename io_elem<IO>::T *__r
 // The operands of each product are scaled by a power of two into fp16 range
 // and the scale is undone on the fp32 results.
 
-// Abar^n = exp(n dt A) in fp64
-__device__ __forceinline__ void apow64(double are, double aim, double n, double &re, double &im) {
-    double sn, cs;
-    sincos(aim * n, &sn, &cs);
-    const double m = exp(are * n);
-    re = m * cs;
-    im = m * sn;
-}
 
 __device__ __forceinline__ uint16_t f16bits(double x) { return __builtin_bit_cast(uint16_t, (_Float16)(float)x); }
 
+// One workgroup per channel; eight runs of powers per mode (the modes past S
+// are written as zeros):
+//   runs 0..3  Abar^p, p = 16 q .. 16 q + 15 -> Et (l = 63 - p), Rt (l = p - 1)
+//   run 4      Abar^64                      -> Rt (l = 63)
+//   run 5      Abar^(64 k), k < 16         -> Qx[k], Qc[TL - 1 - k]
+//   run 6      Abar^(1024 k), k < 8        -> Px[k], Pc[NCT - 1 - k] (times Bbar)
+//   run 7      Abar^T                      -> aT
 __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict__ A, const float *__restrict__ Bm,
                                                        const float *__restrict__ Cc, const float *__restrict__ dt,
                                                        uint16_t *__restrict__ Et, uint16_t *__restrict__ Rt,
@@ -352,9 +383,8 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
     const int T2 = T / 64, NCT = (T2 + 15) / 16, TL = T2 < 16 ? T2 : 16;
     uint16_t *Eh = Et + (size_t)h * 128 * 64;
     uint16_t *Rh = Rt + (size_t)h * 64 * 128;
-    constexpr int PER = 64 + 64 + 8 + 16 + 8 + 16 + 1;
-    for (int e = threadIdx.x; e < 64 * PER; e += 256) {
-        const int j = e / PER, r = e % PER;
+    for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+        const int j = e >> 3, run = e & 7;
         const bool on = j < S;
         double are = 0.0, aim = 0.0, br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
         if (on) {
@@ -366,35 +396,42 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
             cr = (double)Cc[o];
             ci = (double)Cc[o + 1];
         }
-        double pr = 0.0, pi = 0.0;
-        if (r < 64) {  // Et: Abar^(63 - l)
-            const int l = r;
-            if (on) apow64(are, aim, (double)(63 - l), pr, pi);
-            Eh[(2 * j) * 64 + l] = f16bits(pr);
-            Eh[(2 * j + 1) * 64 + l] = f16bits(pi);
-        } else if (r < 128) {  // Rt: 2 C Abar^(l+1), real form
-            const int l = r - 64;
-            if (on) apow64(are, aim, (double)(l + 1), pr, pi);
-            const double zr = cr * pr - ci * pi, zi = cr * pi + ci * pr;
-            Rh[l * 128 + 2 * j] = f16bits(2.0 * zr);
-            Rh[l * 128 + 2 * j + 1] = f16bits(-2.0 * zi);
-        } else if (r < 136) {  // Pc: Bbar Abar^(1024 (NCT-1-ih))
-            const int ih = r - 128;
-            if (on && ih < NCT) apow64(are, aim, 1024.0 * (NCT - 1 - ih), pr, pi);
-            Pc[((size_t)h * 64 + j) * 8 + ih] = mk((float)(br * pr - bi * pi), (float)(br * pi + bi * pr));
-        } else if (r < 152) {  // Qc: Abar^(64 (TL-1-il))
-            const int il = r - 136;
-            if (on && il < TL) apow64(are, aim, 64.0 * (TL - 1 - il), pr, pi);
-            Qc[((size_t)h * 64 + j) * 16 + il] = mk((float)pr, (float)pi);
-        } else if (r < 160) {  // Px: Abar^(1024 ih)
-            const int ih = r - 152;
-            if (on && ih < NCT) apow64(are, aim, 1024.0 * ih, pr, pi);
-            Px[((size_t)h * 64 + j) * 8 + ih] = mk((float)pr, (float)pi);
-        } else if (r < 176) {  // Qx: Abar^(64 il)
-            const int il = r - 160;
-            if (on && il < TL) apow64(are, aim, 64.0 * il, pr, pi);
-            Qx[((size_t)h * 64 + j) * 16 + il] = mk((float)pr, (float)pi);
-        } else {  // Abar^T
+        // modes past S: all-zero tables (the power run is evaluated and masked)
+        const double on_d = on ? 1.0 : 0.0;
+        auto et_rt = [&](int p, double pr, double pi) {
+            pr *= on_d;
+            pi *= on_d;
+            if (p <= 63) {
+                Eh[(2 * j) * 64 + (63 - p)] = f16bits(pr);
+                Eh[(2 * j + 1) * 64 + (63 - p)] = f16bits(pi);
+            }
+            if (p >= 1) {
+                const int l = p - 1;
+                const double zr = cr * pr - ci * pi, zi = cr * pi + ci * pr;
+                Rh[l * 128 + 2 * j] = f16bits(2.0 * zr);
+                Rh[l * 128 + 2 * j + 1] = f16bits(-2.0 * zi);
+            }
+        };
+        if (run < 4) {
+            pow_run(are, aim, 16.0 * run, 1.0, 16, [&](int k, double pr, double pi) { et_rt(16 * run + k, pr, pi); });
+        } else if (run == 4) {
+            pow_run(are, aim, 64.0, 1.0, 1, [&](int, double pr, double pi) { et_rt(64, pr, pi); });
+        } else if (run == 5) {
+            pow_run(are, aim, 0.0, 64.0, 16, [&](int k, double pr, double pi) {
+                const bool ok = on && k < TL;
+                const cf v = ok ? mk((float)pr, (float)pi) : mk(0.f, 0.f);
+                Qx[((size_t)h * 64 + j) * 16 + k] = v;
+                Qc[((size_t)h * 64 + j) * 16 + (k < TL ? TL - 1 - k : k)] = v;
+            });
+        } else if (run == 6) {
+            pow_run(are, aim, 0.0, 1024.0, 8, [&](int k, double pr, double pi) {
+                const bool ok = on && k < NCT;
+                Px[((size_t)h * 64 + j) * 8 + k] = ok ? mk((float)pr, (float)pi) : mk(0.f, 0.f);
+                Pc[((size_t)h * 64 + j) * 8 + (k < NCT ? NCT - 1 - k : k)] =
+                    ok ? mk((float)(br * pr - bi * pi), (float)(br * pi + bi * pr)) : mk(0.f, 0.f);
+            });
+        } else {
+            double pr = 0.0, pi = 0.0;
             if (on) apow64(are, aim, (double)T, pr, pi);
             aT[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
         }
@@ -407,195 +444,229 @@ __device__ __forceinline__ float sp_wave_max(float v) {
     return v;
 }
 
-// 8 consecutive activations (16-byte aligned) as floats
-template <int IO>
-__device__ __forceinline__ void ld8(const typename io_elem<IO>::T *p, float (&x)[8]) {
-    static_assert(IO == IO_F16 || IO == IO_BF16, "16-bit activations");
-    const mf::u32x4 v = *(const mf::u32x4 *)p;
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        if constexpr (IO == IO_F16) {
-            x[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(d[k] & 0xffffu));
-            x[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(d[k] >> 16));
-        } else {
-            x[2 * k] = __uint_as_float(d[k] << 16);
-            x[2 * k + 1] = __uint_as_float(d[k] & 0xffff0000u);
-        }
-    }
-}
+// Both projections of one (batch row b, channel h), walking its chunks in
+// order and carrying the state in LDS.  Four waves; for each chunk c:
+//   1. the chunk's activations are staged in LDS as fp16 (bf16 inputs scaled
+//      by a power of two into fp16 range);
+//   2. contribution: wave w owns modes 16w .. 16w+15 (Et row tiles 2w, 2w+1)
+//      and all column tiles, so its Et operands stay in registers;
+//   3. correction with the state carried into the chunk: the operand X is
+//      built once in LDS, wave w owns output rows l = 16w .. 16w+15 (its Rt
+//      operands stay in registers), and y is updated in place;
+//   4. x <- Abar^T x + s.
+// The next chunk's activations are loaded while the current one is used.
+constexpr int SP_USTR = 72;   // staged chunk: 64 samples per row i, padded (bank spread)
+constexpr int SP_XSTR = 136;  // X operand: 128 (mode, part) entries per column i, padded
 
-// State contribution of chunk-row (b, h, c) on the matrix cores.  Four waves;
-// wave w owns column tiles ct = w and w + 4 (T <= 8192 gives at most 8).
 template <int IO>
-__global__ __launch_bounds__(256) void k_sp_contrib_mfma(const typename io_elem<IO>::T *__restrict__ u,
-                                                        const uint16_t *__restrict__ Et,
-                                                        const cf *__restrict__ Pc, const cf *__restrict__ Qc,
-                                                        cf *__restrict__ sc, int H, int64_t N, int T) {
+__global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>::T *__restrict__ u,
+                                                     typename io_elem<IO>::T *__restrict__ y,
+                                                     const uint16_t *__restrict__ Et,
+                                                     const uint16_t *__restrict__ Rt,
+                                                     const cf *__restrict__ Pc, const cf *__restrict__ Qc,
+                                                     const cf *__restrict__ Px, const cf *__restrict__ Qx,
+                                                     const cf *__restrict__ aT, const float *__restrict__ x_in,
+                                                     float *__restrict__ x_out, int H, int64_t N, int S, int T) {
     using namespace mf;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, C = gridDim.x;
-    const int T2 = T >> 6, NCT = (T2 + 15) >> 4;
+    using T_ = typename io_elem<IO>::T;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int C = (int)(N / T), T2 = T >> 6, NCT = (T2 + 15) >> 4;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, il = lane & 15, g = lane >> 4;
-    __shared__ float part[4][64][2];
-    __shared__ float red[4];
-    const typename io_elem<IO>::T *ur = u + ((size_t)b * H + h) * N + (size_t)c * T;
-    float xv[2][2][8];
-    float amax = 0.f;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int ct = w + 4 * q, i = 16 * ct + il;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ct < NCT && i < T2) {
-                ld8<IO>(ur + 64 * i + 32 * ks + 8 * g, xv[q][ks]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xv[q][ks][e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xv[q][ks][e]));
-        }
-    }
-    amax = sp_wave_max(amax);
-    if (lane == 0) red[w] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    int ex = 0;
-    if (amax > 0.f) (void)frexpf(amax, &ex);
-    const float su = ldexpf(1.f, 14 - ex);  // scaled operands below 2^14
-    half8 Bop[2][2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            Bop[q][ks] = as_half8(pk(xv[q][ks][0] * su, xv[q][ks][1] * su), pk(xv[q][ks][2] * su, xv[q][ks][3] * su),
-                                  pk(xv[q][ks][4] * su, xv[q][ks][5] * su), pk(xv[q][ks][6] * su, xv[q][ks][7] * su));
-    const uint16_t *Eh = Et + (size_t)h * 128 * 64;
-    const cf *Pch = Pc + (size_t)h * 64 * 8, *Qch = Qc + (size_t)h * 64 * 16;
-#pragma unroll 2
-    for (int rt = 0; rt < 8; ++rt) {
-        half8 Aop[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            Aop[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Eh + (16 * rt + il) * 64 + 32 * ks + 8 * g));
-        const int j0 = 8 * rt + 2 * g, j1 = j0 + 1;
-        const cf q0 = Qch[j0 * 16 + il], q1 = Qch[j1 * 16 + il];
-        cf s0 = mk(0.f, 0.f), s1 = mk(0.f, 0.f);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int ct = w + 4 * q;
-            if (ct < NCT) {
-                const f4 z = {0.f, 0.f, 0.f, 0.f};
-                f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop[0], Bop[q][0], z, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop[1], Bop[q][1], d, 0, 0, 0);
-                s0 = cadd(s0, cmul(Pch[j0 * 8 + ct], cmul(q0, mk(d[0], d[1]))));
-                s1 = cadd(s1, cmul(Pch[j1 * 8 + ct], cmul(q1, mk(d[2], d[3]))));
-            }
-        }
-        // sum over the 16 columns il of each lane group
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            s0.x += __shfl_xor(s0.x, o, 64);
-            s0.y += __shfl_xor(s0.y, o, 64);
-            s1.x += __shfl_xor(s1.x, o, 64);
-            s1.y += __shfl_xor(s1.y, o, 64);
-        }
-        if (il == 0) {
-            part[w][j0][0] = s0.x;
-            part[w][j0][1] = s0.y;
-            part[w][j1][0] = s1.x;
-            part[w][j1][1] = s1.y;
-        }
-    }
-    __syncthreads();
-    if (tid < 64) {
-        const float inv = 1.0f / su;
-        const float re = (part[0][tid][0] + part[1][tid][0]) + (part[2][tid][0] + part[3][tid][0]);
-        const float im = (part[0][tid][1] + part[1][tid][1]) + (part[2][tid][1] + part[3][tid][1]);
-        sc[(((size_t)b * H + h) * C + c) * 64 + tid] = mk(re * inv, im * inv);
-    }
-}
-
-// Carry the state into chunk-row (b, h, c) and add its free response on the
-// matrix cores.  The last chunk also writes x_out.
-template <int IO>
-__global__ __launch_bounds__(256) void k_sp_correct_mfma(typename io_elem<IO>::T *__restrict__ y,
-                                                        const uint16_t *__restrict__ Rt,
-                                                        const cf *__restrict__ Px, const cf *__restrict__ Qx,
-                                                        const cf *__restrict__ aT, const cf *__restrict__ sc,
-                                                        const float *__restrict__ x_in, float *__restrict__ x_out,
-                                                        int H, int64_t N, int S, int T) {
-    using namespace mf;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, C = gridDim.x;
-    const int T2 = T >> 6, NCT = (T2 + 15) >> 4;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, il = lane & 15, g = lane >> 4;
-    __shared__ cf xs[64];
-    __shared__ float amx;
+    __shared__ __attribute__((aligned(16))) uint16_t us[128 * SP_USTR];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[128 * SP_XSTR];
+    __shared__ cf pcs[64 * 8], pxs[64 * 8], qxs[64 * 16];
+    __shared__ cf xst[64], sst[64];
+    __shared__ float red[4], xmax;
     const size_t orow = (size_t)b * H + h;
-    if (tid < 64) {
-        const int j = tid;
-        cf x = mk(0.f, 0.f);
-        if (x_in && j < S) x = mk(x_in[(orow * S + j) * 2], x_in[(orow * S + j) * 2 + 1]);
-        const cf a = aT[(size_t)h * 64 + j];
-        for (int cc = 0; cc < c; ++cc) x = cadd(cmul(a, x), sc[(orow * C + cc) * 64 + j]);
-        if (c == C - 1 && x_out && j < S) {
-            const cf xo = cadd(cmul(a, x), sc[(orow * C + c) * 64 + j]);
-            x_out[(orow * S + j) * 2] = xo.x;
-            x_out[(orow * S + j) * 2 + 1] = xo.y;
-        }
-        xs[j] = x;
-        const float m = sp_wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
-        if (lane == 0) amx = m;
+    // tables and the initial state
+    for (int e = tid; e < 64 * 8; e += 256) {
+        pcs[e] = Pc[(size_t)h * 512 + e];
+        pxs[e] = Px[(size_t)h * 512 + e];
     }
-    __syncthreads();
-    const float amax = amx;
-    if (!(amax > 0.f)) return;
-    int ex = 0;
-    (void)frexpf(amax, &ex);
-    const float sx = ldexpf(1.f, 14 - ex);  // |X| <= |x| sx < 2^14 for stable modes
-    const float inv = 1.0f / sx;
-    const cf *Pxh = Px + (size_t)h * 64 * 8, *Qxh = Qx + (size_t)h * 64 * 16;
-    cf qx[4][4];
+    for (int e = tid; e < 64 * 16; e += 256) qxs[e] = Qx[(size_t)h * 1024 + e];
+    if (tid < 64) {
+        cf x = mk(0.f, 0.f);
+        if (x_in && tid < S) x = mk(x_in[(orow * S + tid) * 2], x_in[(orow * S + tid) * 2 + 1]);
+        xst[tid] = x;
+        const float m = sp_wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
+        if (tid == 0) xmax = m;
+    }
+    // matrix operands in registers
+    const uint16_t *Eh = Et + (size_t)h * 128 * 64, *Rh = Rt + (size_t)h * 64 * 128;
+    half8 Ea[2][2], Ra[4];
+    cf qc[2][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int rt = 2 * w + r;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            Ea[r][ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Eh + (16 * rt + il) * 64 + 32 * ks + 8 * g));
+        const int j0 = 8 * rt + 2 * g;
+        qc[r][0] = Qc[((size_t)h * 64 + j0) * 16 + il];
+        qc[r][1] = Qc[((size_t)h * 64 + j0 + 1) * 16 + il];
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
+        Ra[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Rh + (16 * w + il) * 128 + 32 * ks + 8 * g));
+    const cf aTj = (tid < 64) ? aT[(size_t)h * 64 + tid] : mk(0.f, 0.f);
+    // chunk loads: T / 8 groups of 8 activations (at most 4 per thread), and
+    // the 4 outputs per column tile this lane corrects (read-modify-write)
+    const int nq = T >> 3;
+    u32x4 pre[4];
+    u32x2 ypre[8];
+    auto load_chunk = [&](int c) {
+        const T_ *src = u + orow * N + (size_t)c * T;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int j = 16 * ks + 4 * g + t;
-            qx[ks][t] = cscale(cmul(Qxh[j * 16 + il], xs[j]), sx);
+        for (int k = 0; k < 4; ++k) {
+            const int q = tid + 256 * k;
+            if (q < nq) pre[k] = *(const u32x4 *)(src + 8 * q);
         }
-    const uint16_t *Rh = Rt + (size_t)h * 64 * 128;
-    typename io_elem<IO>::T *yr = y + orow * N + (size_t)c * T;
+        const T_ *yr = y + orow * N + (size_t)c * T;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int ct = w + 4 * q;
-        if (ct >= NCT) break;
-        const int i = 16 * ct + il;
-        half8 Bop[4];
+        for (int ct = 0; ct < 8; ++ct) {
+            const int i = 16 * ct + il;
+            if (ct < NCT && i < T2) ypre[ct] = *(const u32x2 *)(yr + 64 * i + 16 * w + 4 * g);
+        }
+    };
+    load_chunk(0);
+    __syncthreads();
+    for (int c = 0; c < C; ++c) {
+        // 1. stage (fp16, scaled for bf16 inputs)
+        float su = 1.f;
+        if constexpr (IO == IO_BF16) {
+            float m = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            uint32_t d4[4];
+            for (int k = 0; k < 4; ++k)
+                if (tid + 256 * k < nq) {
+                    const uint32_t d4[4] = {pre[k].x, pre[k].y, pre[k].z, pre[k].w};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int j = 16 * ks + 4 * g + t;
-                const cf X = cmul(qx[ks][t], Pxh[j * 8 + ct]);
-                d4[t] = pk(X.x, X.y);
-            }
-            Bop[ks] = as_half8(d4[0], d4[1], d4[2], d4[3]);
+                    for (int e = 0; e < 4; ++e)
+                        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(d4[e] << 16)), fabsf(__uint_as_float(d4[e] & 0xffff0000u))));
+                }
+            m = sp_wave_max(m);
+            if (lane == 0) red[w] = m;
+            __syncthreads();
+            m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            int ex = 0;
+            if (m > 0.f) (void)frexpf(m, &ex);
+            su = ldexpf(1.f, 14 - ex);
         }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f4 d = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < 4; ++k) {
+            const int q = tid + 256 * k;
+            if (q < nq) {
+                u32x4 v = pre[k];
+                if constexpr (IO == IO_BF16) {
+                    const uint32_t d4[4] = {v.x, v.y, v.z, v.w};
+                    uint32_t o4[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const half8 Aop = __builtin_bit_cast(half8, *(const u32x4 *)(Rh + (16 * rt + il) * 128 + 32 * ks + 8 * g));
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, Bop[ks], d, 0, 0, 0);
-            }
-            if (i < T2) {
-                typename io_elem<IO>::T *p = yr + 64 * i + 16 * rt + 4 * g;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) st_io<IO>(p + v, ld_io<IO>(p + v) + d[v] * inv);
+                    for (int e = 0; e < 4; ++e)
+                        o4[e] = pk(__uint_as_float(d4[e] << 16) * su, __uint_as_float(d4[e] & 0xffff0000u) * su);
+                    v = u32x4{o4[0], o4[1], o4[2], o4[3]};
+                }
+                *(u32x4 *)(us + (q >> 3) * SP_USTR + 8 * (q & 7)) = v;
             }
         }
+        u32x2 ycur[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) ycur[ct] = ypre[ct];
+        if (c + 1 < C) load_chunk(c + 1);
+        // correction operand X = Abar^(64 i) x sx, from the state carried in
+        const float xm = xmax;
+        const bool corr = xm > 0.f;
+        float sx = 1.f;
+        if (corr) {
+            int ex = 0;
+            (void)frexpf(xm, &ex);
+            sx = ldexpf(1.f, 14 - ex);  // |X| <= |x| sx < 2^14 for stable modes
+            for (int e = tid; e < 64 * T2; e += 256) {
+                const int j = e & 63, i = e >> 6;
+                const cf X = cscale(cmul(cmul(pxs[j * 8 + (i >> 4)], qxs[j * 16 + (i & 15)]), xst[j]), sx);
+                *(uint32_t *)(xs + i * SP_XSTR + 2 * j) = pk(X.x, X.y);
+            }
+        }
+        __syncthreads();
+        // 2. contribution
+        cf acc[2][2] = {{mk(0.f, 0.f), mk(0.f, 0.f)}, {mk(0.f, 0.f), mk(0.f, 0.f)}};
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int i = 16 * ct + il;
+            half8 Bop[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x4 z4 = {0u, 0u, 0u, 0u};
+                const u32x4 v = (i < T2) ? *(const u32x4 *)(us + i * SP_USTR + 32 * ks + 8 * g) : z4;
+                Bop[ks] = __builtin_bit_cast(half8, v);
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const f4 z = {0.f, 0.f, 0.f, 0.f};
+                f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ea[r][0], Bop[0], z, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ea[r][1], Bop[1], d, 0, 0, 0);
+                const int j0 = 8 * (2 * w + r) + 2 * g;
+                acc[r][0] = cadd(acc[r][0], cmul(pcs[j0 * 8 + ct], cmul(qc[r][0], mk(d[0], d[1]))));
+                acc[r][1] = cadd(acc[r][1], cmul(pcs[(j0 + 1) * 8 + ct], cmul(qc[r][1], mk(d[2], d[3]))));
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    acc[r][q].x += __shfl_xor(acc[r][q].x, o, 64);
+                    acc[r][q].y += __shfl_xor(acc[r][q].y, o, 64);
+                }
+        if (il == 0) {
+            const float inv = 1.0f / su;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int j0 = 8 * (2 * w + r) + 2 * g;
+                sst[j0] = cscale(acc[r][0], inv);
+                sst[j0 + 1] = cscale(acc[r][1], inv);
+            }
+        }
+        // 3. correction: y += 2 Re(C Abar^(t+1) x), rows l = 16 w + 4 g + v
+        if (corr) {
+            const float inv = 1.0f / sx;
+            T_ *yr = y + orow * N + (size_t)c * T;
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                if (ct >= NCT) break;
+                const int i = 16 * ct + il;
+                f4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const u32x4 z4 = {0u, 0u, 0u, 0u};
+                    const u32x4 v = (i < T2) ? *(const u32x4 *)(xs + i * SP_XSTR + 32 * ks + 8 * g) : z4;
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ra[ks], __builtin_bit_cast(half8, v), d, 0, 0, 0);
+                }
+                if (i < T2) {
+                    T_ *p = yr + 64 * i + 16 * w + 4 * g;
+                    const uint32_t y01 = ycur[ct].x, y23 = ycur[ct].y;
+                    const T_ *yv = (const T_ *)&y01;
+                    const T_ *yw = (const T_ *)&y23;
+                    T_ o[4];
+                    o[0] = yv[0]; o[1] = yv[1]; o[2] = yw[0]; o[3] = yw[1];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) st_io<IO>(o + v, ld_io<IO>(o + v) + d[v] * inv);
+                    const uint32_t a = *(const uint32_t *)&o[0], bb = *(const uint32_t *)&o[2];
+                    *(u32x2 *)p = u32x2{a, bb};
+                }
+            }
+        }
+        __syncthreads();
+        // 4. carry the state
+        if (tid < 64) {
+            const cf x = cadd(cmul(aTj, xst[tid]), sst[tid]);
+            xst[tid] = x;
+            const float m = sp_wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
+            if (tid == 0) xmax = m;
+        }
+        __syncthreads();
+    }
+    if (x_out && tid < S) {
+        x_out[(orow * S + tid) * 2] = xst[tid].x;
+        x_out[(orow * S + tid) * 2 + 1] = xst[tid].y;
     }
 }
 
@@ -683,13 +754,10 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
     }
     if (e != hipSuccess) return e;
     if constexpr (IO != IO_F32) {
-        hipLaunchKernelGGL((k_sp_contrib_mfma<IO>), dim3(C_, H, B), dim3(256), 0, s, (const T_ *)u,
-                           (const uint16_t *)(w + L.Et), (const cf *)(w + L.Pc), (const cf *)(w + L.Qc), sc, H,
-                           N, T);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_sp_correct_mfma<IO>), dim3(C_, H, B), dim3(256), 0, s, (T_ *)y,
-                           (const uint16_t *)(w + L.Rt), (const cf *)(w + L.Px), (const cf *)(w + L.Qx),
-                           (const cf *)(w + L.aT), (const cf *)sc, x_in, x_out, H, N, S, T);
+        hipLaunchKernelGGL((k_sp_proj_mfma<IO>), dim3(H, B), dim3(256), 0, s, (const T_ *)u, (T_ *)y,
+                           (const uint16_t *)(w + L.Et), (const uint16_t *)(w + L.Rt), (const cf *)(w + L.Pc),
+                           (const cf *)(w + L.Qc), (const cf *)(w + L.Px), (const cf *)(w + L.Qx),
+                           (const cf *)(w + L.aT), x_in, x_out, H, N, S, T);
         return hipGetLastError();
     } else {
         const size_t sm_c = (size_t)T * 4 + 64 * 64 * 8 + 4 * 64 * 8;
