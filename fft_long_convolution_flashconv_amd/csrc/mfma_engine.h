@@ -197,19 +197,29 @@ __device__ __forceinline__ uint32_t pk(float re, float im) {
     const f2 v = {re, im};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
 }
-// x * w
-__device__ __forceinline__ uint32_t cmulh(uint32_t xx, uint32_t ww) {
-    const h2 x = __builtin_bit_cast(h2, xx), w = __builtin_bit_cast(h2, ww);
-    const h2 t = x.xx * w;
-    const h2 nw = {-w.y, w.x};
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(x.yy, nw, t));
+// x * w and conj(x) * w on packed fp16 complex, two instructions each with
+// the half selection and negation in op_sel / neg modifiers.  Written as
+// instructions so that the twiddle operand stays as it is: as plain vector
+// code the compiler hoists the swapped copy of a loop-invariant twiddle out
+// of every loop and keeps both copies in registers.  Their operands are
+// never matrix-core results directly (those pass through a compiler-emitted
+// conversion first).  conj(x) * w feeds matrix-core operands, and the
+// compiler does not insert the wait states between a vector write and a
+// matrix-core read for an instruction it did not emit, so that variant ends
+// with its own.
+__device__ __forceinline__ uint32_t cmulh(uint32_t x, uint32_t w) {
+    uint32_t t, r;
+    asm("v_pk_mul_f16 %0, %1, %2 op_sel_hi:[0,1]" : "=v"(t) : "v"(x), "v"(w));
+    asm("v_pk_fma_f16 %0, %1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_lo:[1,0,0]"
+        : "=v"(r) : "v"(x), "v"(w), "v"(t));
+    return r;
 }
-// conj(x) * w
-__device__ __forceinline__ uint32_t cmulh_cx(uint32_t xx, uint32_t ww) {
-    const h2 x = __builtin_bit_cast(h2, xx), w = __builtin_bit_cast(h2, ww);
-    const h2 t = x.xx * w;
-    const h2 sw = {w.y, -w.x};
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(x.yy, sw, t));
+__device__ __forceinline__ uint32_t cmulh_cx(uint32_t x, uint32_t w) {
+    uint32_t t, r;
+    asm("v_pk_mul_f16 %0, %1, %2 op_sel_hi:[0,1]" : "=v"(t) : "v"(x), "v"(w));
+    asm("v_pk_fma_f16 %0, %1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_hi:[1,0,0]\n\ts_nop 4"
+        : "=v"(r) : "v"(x), "v"(w), "v"(t));
+    return r;
 }
 // both halves times the matching halves of a packed factor
 __device__ __forceinline__ uint32_t pkmul(uint32_t xx, uint32_t ss) {
@@ -367,16 +377,6 @@ __device__ __forceinline__ float pow2_scale(float amax, int hb) {
 __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
     return x;
-}
-
-// Fresh copies of loop-invariant packed operands right before a pass: without
-// it the compiler hoists the half swaps that the complex multiply applies to
-// them out of every loop and keeps the swapped copies in extra registers; on
-// a fresh copy the swaps fold into op_sel / neg modifiers instead.
-template <int N>
-__device__ __forceinline__ void launder(uint32_t (&v)[N]) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
 }
 
 // ceil(log2(n) / 2) for n >= 1
@@ -599,7 +599,6 @@ struct Engine {
             if (s < nsig) {
                 uint32_t tw[8];
                 get_tw0(i % ND0, tw);
-                launder(tw);
                 const int pn = lb ^ ((phys<LOG2M>((32 * (w + i * NW)) % S0) << 2) | (s * SB));
                 const half8 b = as_half8(op(i, 0), op(i, 1), op(i, 2), op(i, 3));
                 const f16v z = {};
@@ -636,7 +635,6 @@ struct Engine {
                 uint32_t tu[4], x[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) tu[t] = tua[i % NDI][t];
-                launder(tu);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) x[t] = cmulh_cx(lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2)), tu[t]);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
@@ -671,7 +669,6 @@ struct Engine {
         const int pb = opaque((phys<LOG2M>(base0<P>()) ^ phys<LOG2M>(2 * g * S)) << 2);
         uint32_t tw[4];
         get_twm(P - 1, tw);
-        launder(tw);
 #pragma unroll
         for (int s = 0; s < SIG; ++s) {
             if (s >= nsig) break;
@@ -916,7 +913,6 @@ struct Engine {
         uint32_t Fr[FN];
 #pragma unroll
         for (int i = 0; i < FN; ++i) Fr[i] = F[i];
-        launder(Fr);
         float vmax = 0.f;
         const int lb = opaque(lbase());
 #pragma unroll
@@ -971,8 +967,8 @@ struct Engine {
                 uint32_t hv;
                 if constexpr (KIND == IN_F16) hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
                 else hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * n, 2 * m * S0, 0);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * n, 2 * m * S0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, 0);
             };
             conv_round(out, nr, hb);
         }
