@@ -563,7 +563,10 @@ struct Engine {
     __device__ __forceinline__ int tile_n(int i) const { return (32 * (w + i * NW)) % S0 + (lane & 31); }
 
     // 16-bit activations through the rows' buffer resources (zero past each
-    // row's valid length).
+    // row's valid length).  The compile-time part of the offset goes in the
+    // scalar offset, which gfx950 includes in the range check of a raw buffer
+    // access (checked on the device: a load whose per-lane offset is in range
+    // but whose total offset is not returns zero).
     template <class RB>
     __device__ __forceinline__ void fetch_raw(const RB &rows, int sig0, int nsig, uint32_t (&buf)[T0W][4]) {
         const int h = lane >> 5;
