@@ -353,16 +353,36 @@ __device__ const TwTab<LOG2M> kTw = make_tw<LOG2M>();
 
 // ================================================================ helpers
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+// Wave-wide max (SUM = false) or sum of a non-negative value with DPP row
+// operations (no LDS round trips): pairs and quads, half-row and row
+// mirrors, then the row broadcasts; the result is in lane 63.
+template <bool SUM>
+__device__ __forceinline__ float wave_reduce(float v) {
+    auto step = [&](float x, float y) { return SUM ? x + y : fmaxf(x, y); };
+    auto dpp = [&](float x, int ctrl_sel, int rmask) -> float {
+        const int xi = __builtin_bit_cast(int, x);
+        int r = 0;
+        switch (ctrl_sel) {  // the control word must be a constant
+            case 0: r = __builtin_amdgcn_update_dpp(0, xi, 0xb1, 0xf, 0xf, false); break;   // quad_perm [1,0,3,2]
+            case 1: r = __builtin_amdgcn_update_dpp(0, xi, 0x4e, 0xf, 0xf, false); break;   // quad_perm [2,3,0,1]
+            case 2: r = __builtin_amdgcn_update_dpp(0, xi, 0x141, 0xf, 0xf, false); break;  // row_half_mirror
+            case 3: r = __builtin_amdgcn_update_dpp(0, xi, 0x140, 0xf, 0xf, false); break;  // row_mirror
+            case 4: r = __builtin_amdgcn_update_dpp(0, xi, 0x142, 0xa, 0xf, false); break;  // row_bcast:15
+            default: r = __builtin_amdgcn_update_dpp(0, xi, 0x143, 0xc, 0xf, false); break; // row_bcast:31
+        }
+        (void)rmask;
+        return __builtin_bit_cast(float, r);
+    };
+    v = step(v, dpp(v, 0, 0xf));
+    v = step(v, dpp(v, 1, 0xf));
+    v = step(v, dpp(v, 2, 0xf));
+    v = step(v, dpp(v, 3, 0xf));
+    v = step(v, dpp(v, 4, 0xa));
+    v = step(v, dpp(v, 5, 0xc));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce<false>(v); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce<true>(v); }
 
 // Power-of-two scale 2^(8 - e - hb) where amax < 2^e: after a transform that
 // can grow magnitudes by at most 2^(2 hb), values stay below 2^(8 + hb).
