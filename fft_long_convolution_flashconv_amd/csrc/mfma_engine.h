@@ -205,8 +205,8 @@ __device__ __forceinline__ uint32_t pk(float re, float im) {
 // never matrix-core results directly (those pass through a compiler-emitted
 // conversion first).  conj(x) * w feeds matrix-core operands, and the
 // compiler does not insert the wait states between a vector write and a
-// matrix-core read for an instruction it did not emit, so that variant ends
-// with its own.
+// matrix-core read for an instruction it did not emit, so that variant works
+// on a whole operand at once and ends with its own.
 __device__ __forceinline__ uint32_t cmulh(uint32_t x, uint32_t w) {
     uint32_t t, r;
     asm("v_pk_mul_f16 %0, %1, %2 op_sel_hi:[0,1]" : "=v"(t) : "v"(x), "v"(w));
@@ -214,12 +214,33 @@ __device__ __forceinline__ uint32_t cmulh(uint32_t x, uint32_t w) {
         : "=v"(r) : "v"(x), "v"(w), "v"(t));
     return r;
 }
-__device__ __forceinline__ uint32_t cmulh_cx(uint32_t x, uint32_t w) {
-    uint32_t t, r;
-    asm("v_pk_mul_f16 %0, %1, %2 op_sel_hi:[0,1]" : "=v"(t) : "v"(x), "v"(w));
-    asm("v_pk_fma_f16 %0, %1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_hi:[1,0,0]\n\ts_nop 4"
-        : "=v"(r) : "v"(x), "v"(w), "v"(t));
-    return r;
+// conj(x[i]) * w[i] for the N operand dwords of one matrix-core product, in
+// one block so that the wait states at its end cover every result.
+template <int N>
+__device__ __forceinline__ void cmulh_cx_n(uint32_t (&x)[N], const uint32_t (&w)[N]) {
+    static_assert(N == 2 || N == 4, "two or four operand dwords");
+    uint32_t t[N];
+    if constexpr (N == 4) {
+        asm("v_pk_mul_f16 %4, %0, %8 op_sel_hi:[0,1]\n\t"
+            "v_pk_mul_f16 %5, %1, %9 op_sel_hi:[0,1]\n\t"
+            "v_pk_mul_f16 %6, %2, %10 op_sel_hi:[0,1]\n\t"
+            "v_pk_mul_f16 %7, %3, %11 op_sel_hi:[0,1]\n\t"
+            "v_pk_fma_f16 %0, %0, %8, %4 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_hi:[1,0,0]\n\t"
+            "v_pk_fma_f16 %1, %1, %9, %5 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_hi:[1,0,0]\n\t"
+            "v_pk_fma_f16 %2, %2, %10, %6 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_hi:[1,0,0]\n\t"
+            "v_pk_fma_f16 %3, %3, %11, %7 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_hi:[1,0,0]\n\t"
+            "s_nop 4"
+            : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+            : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
+    } else {
+        asm("v_pk_mul_f16 %2, %0, %4 op_sel_hi:[0,1]\n\t"
+            "v_pk_mul_f16 %3, %1, %5 op_sel_hi:[0,1]\n\t"
+            "v_pk_fma_f16 %0, %0, %4, %2 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_hi:[1,0,0]\n\t"
+            "v_pk_fma_f16 %1, %1, %5, %3 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_hi:[1,0,0]\n\t"
+            "s_nop 4"
+            : "+v"(x[0]), "+v"(x[1]), "=&v"(t[0]), "=&v"(t[1])
+            : "v"(w[0]), "v"(w[1]));
+    }
 }
 // both halves times the matching halves of a packed factor
 __device__ __forceinline__ uint32_t pkmul(uint32_t xx, uint32_t ss) {
@@ -659,7 +680,8 @@ struct Engine {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) tu[t] = tua[i % NDI][t];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) x[t] = cmulh_cx(lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2)), tu[t]);
+                for (int t = 0; t < 4; ++t) x[t] = lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2));
+                cmulh_cx_n(x, tu);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
                 res[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
             }
@@ -705,8 +727,8 @@ struct Engine {
                     a[t] = (ct ^ (phys<LOG2M>(tab::kChain[t] * S) << 2)) + s * SB;
                     x[t] = lds(a[t]);
                     if (INV && P == K) x[t] = pkmul(x[t], pre);  // scale set after the last pass
-                    if (INV) x[t] = cmulh_cx(x[t], tw[t]);
                 }
+                if (INV) cmulh_cx_n(x, tw);
                 const half8 b = as_half8(x[0], x[1], x[2], x[3]);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
                 const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, b, z, 0, 0, 0);
@@ -945,9 +967,15 @@ struct Engine {
                 const int pb = (lb ^ lpos(u)) + lsig(u) * SB;
                 uint32_t y[NV];
                 last_fwd(pb, y);
+                if constexpr (R >= 8) {
+                    uint32_t fr[NV];
 #pragma unroll
-                for (int q = 0; q < NV; ++q)
-                    y[q] = R >= 8 ? cmulh_cx(y[q], Fr[fslot(slot) + q]) : cmulh(y[q], Fr[fslot(slot) + q]);
+                    for (int q = 0; q < NV; ++q) fr[q] = Fr[fslot(slot) + q];
+                    cmulh_cx_n(y, fr);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NV; ++q) y[q] = cmulh(y[q], Fr[fslot(slot) + q]);
+                }
                 vmax = fmaxf(vmax, last_inv(pb, y));
             }
         }
