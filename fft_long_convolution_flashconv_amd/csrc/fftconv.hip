@@ -143,21 +143,21 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
     const int h = blockIdx.x;
     const float *fh = f + (size_t)h * N;
     const float dh = D[h];
-    const size_t rs = (size_t)H * N;          // stride between batch rows
-    const T *uh = u + (size_t)h * N;
-    T *yh = y + (size_t)h * N;
+    // bytes between batch rows; opaque, so that a signal's offset stays one
+    // short product (the compiler would otherwise refactor every row address
+    // into a full 64-bit multiply by N)
+    const uint64_t rsb = mf::opaque_u64(2ull * (uint64_t)H * (uint64_t)N);
+    const char *uh = (const char *)(u + (size_t)h * N);
+    char *yh = (char *)(y + (size_t)h * N);
     const int hb = mf::half_bits(N);
-    auto ldf = [&](int pos) -> float { return fh[pos] + (pos == 0 ? dh : 0.f); };
     // complex signal `sig` = batch rows 2 sig (real part), 2 sig + 1 (imaginary)
     auto rows = [&](int sig) -> mf::RowBufs {
-        const int b0 = 2 * sig;
-        const int nb1 = (b0 + 1 < B) ? 2 * N : 0;
-        const T *i0 = uh + (size_t)b0 * rs;
-        T *o0 = yh + (size_t)b0 * rs;
-        return {mf::row_rsrc(i0, 2 * N), mf::row_rsrc(i0 + rs, nb1), mf::row_rsrc(o0, 2 * N),
-                mf::row_rsrc(o0 + rs, nb1)};
+        const uint64_t o = (uint64_t)(uint32_t)sig * (2 * rsb);
+        const int nb1 = (2 * sig + 1 < B) ? 2 * N : 0;
+        return {mf::row_rsrc(uh + o, 2 * N), mf::row_rsrc(uh + o + rsb, nb1), mf::row_rsrc(yh + o, 2 * N),
+                mf::row_rsrc(yh + o + rsb, nb1)};
     };
-    E.run_raw(ldf, N, rows, (B + 1) / 2, hb);
+    E.run_raw(mf::row_rsrc(fh, 4 * N), dh, rows, (B + 1) / 2, hb);
 }
 
 template <int LOG2M, int IO>

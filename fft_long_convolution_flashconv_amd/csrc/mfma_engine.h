@@ -25,8 +25,10 @@
 //               which writes only the first N outputs.
 // Spectra stay in digit-reversed order; the filter spectrum goes through the
 // same passes, so the pointwise product needs no reordering.  Inverse DFTs use
-// the forward matrices: IDFT(x) = conj(DFT(conj(x))), with the conjugations
-// folded into the twiddle multiply and the fp32 -> fp16 conversion.
+// the forward matrices: IDFT(x) = conj(DFT(conj(x))); the inverse passes keep
+// the signal conjugated, so the conjugations between them cancel and only the
+// first (in the product with the filter spectrum) and the last (in the output
+// scaling) remain, both free as instruction modifiers.
 //
 // Range: the activations of each round of signals are scaled by a power of
 // two chosen from their maximum so that no fp16 intermediate can overflow
@@ -242,6 +244,34 @@ __device__ __forceinline__ void cmulh_cx_n(uint32_t (&x)[N], const uint32_t (&w)
             : "v"(w[0]), "v"(w[1]));
     }
 }
+// x[i] * w[i] for the N operand dwords of one matrix-core product (the same
+// layout and closing wait states as above).
+template <int N>
+__device__ __forceinline__ void cmulh_n(uint32_t (&x)[N], const uint32_t (&w)[N]) {
+    static_assert(N == 2 || N == 4, "two or four operand dwords");
+    uint32_t t[N];
+    if constexpr (N == 4) {
+        asm("v_pk_mul_f16 %4, %0, %8 op_sel_hi:[0,1]\n\t"
+            "v_pk_mul_f16 %5, %1, %9 op_sel_hi:[0,1]\n\t"
+            "v_pk_mul_f16 %6, %2, %10 op_sel_hi:[0,1]\n\t"
+            "v_pk_mul_f16 %7, %3, %11 op_sel_hi:[0,1]\n\t"
+            "v_pk_fma_f16 %0, %0, %8, %4 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_lo:[1,0,0]\n\t"
+            "v_pk_fma_f16 %1, %1, %9, %5 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_lo:[1,0,0]\n\t"
+            "v_pk_fma_f16 %2, %2, %10, %6 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_lo:[1,0,0]\n\t"
+            "v_pk_fma_f16 %3, %3, %11, %7 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_lo:[1,0,0]\n\t"
+            "s_nop 4"
+            : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+            : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
+    } else {
+        asm("v_pk_mul_f16 %2, %0, %4 op_sel_hi:[0,1]\n\t"
+            "v_pk_mul_f16 %3, %1, %5 op_sel_hi:[0,1]\n\t"
+            "v_pk_fma_f16 %0, %0, %4, %2 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_lo:[1,0,0]\n\t"
+            "v_pk_fma_f16 %1, %1, %5, %3 op_sel:[1,1,0] op_sel_hi:[1,0,1] neg_lo:[1,0,0]\n\t"
+            "s_nop 4"
+            : "+v"(x[0]), "+v"(x[1]), "=&v"(t[0]), "=&v"(t[1])
+            : "v"(w[0]), "v"(w[1]));
+    }
+}
 // both halves times the matching halves of a packed factor
 __device__ __forceinline__ uint32_t pkmul(uint32_t xx, uint32_t ss) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, xx) * __builtin_bit_cast(h2, ss));
@@ -291,7 +321,7 @@ template <int LOG2M> struct Cfg;
 // OCC = workgroups per compute unit the register budget is set for.
 template <> struct Cfg<9> { static constexpr int SIG = 8, NW = 2, OCC = 4; };
 template <> struct Cfg<10> { static constexpr int SIG = 4, NW = 4, OCC = 4; };
-template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8, OCC = 2; };
+template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8, OCC = 3; };
 template <> struct Cfg<12> { static constexpr int SIG = 2, NW = 8, OCC = 2; };
 template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 8, OCC = 2; };
 template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8, OCC = 2; };
@@ -376,31 +406,40 @@ __device__ const TwTab<LOG2M> kTw = make_tw<LOG2M>();
 
 // Wave-wide max (SUM = false) or sum of a non-negative value with DPP row
 // operations (no LDS round trips): pairs and quads, half-row and row
-// mirrors, then the row broadcasts; the result is in lane 63.
+// mirrors, then the row broadcasts; the result is in lane 63.  The max works
+// on the bit patterns as integers (the same order for non-negative floats),
+// with 0 as the identity, so that the full-row steps become one max
+// instruction with a DPP source operand.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ int dpp_max_step(int x) {
+    return max(x, __builtin_amdgcn_update_dpp(0, x, CTRL, RMASK, 0xf, false));
+}
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float dpp_sum_step(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, RMASK, 0xf, false));
+}
 template <bool SUM>
 __device__ __forceinline__ float wave_reduce(float v) {
-    auto step = [&](float x, float y) { return SUM ? x + y : fmaxf(x, y); };
-    auto dpp = [&](float x, int ctrl_sel, int rmask) -> float {
-        const int xi = __builtin_bit_cast(int, x);
-        int r = 0;
-        switch (ctrl_sel) {  // the control word must be a constant
-            case 0: r = __builtin_amdgcn_update_dpp(0, xi, 0xb1, 0xf, 0xf, false); break;   // quad_perm [1,0,3,2]
-            case 1: r = __builtin_amdgcn_update_dpp(0, xi, 0x4e, 0xf, 0xf, false); break;   // quad_perm [2,3,0,1]
-            case 2: r = __builtin_amdgcn_update_dpp(0, xi, 0x141, 0xf, 0xf, false); break;  // row_half_mirror
-            case 3: r = __builtin_amdgcn_update_dpp(0, xi, 0x140, 0xf, 0xf, false); break;  // row_mirror
-            case 4: r = __builtin_amdgcn_update_dpp(0, xi, 0x142, 0xa, 0xf, false); break;  // row_bcast:15
-            default: r = __builtin_amdgcn_update_dpp(0, xi, 0x143, 0xc, 0xf, false); break; // row_bcast:31
-        }
-        (void)rmask;
-        return __builtin_bit_cast(float, r);
-    };
-    v = step(v, dpp(v, 0, 0xf));
-    v = step(v, dpp(v, 1, 0xf));
-    v = step(v, dpp(v, 2, 0xf));
-    v = step(v, dpp(v, 3, 0xf));
-    v = step(v, dpp(v, 4, 0xa));
-    v = step(v, dpp(v, 5, 0xc));
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror,
+    // row_bcast:15 (rows 1, 3), row_bcast:31 (rows 2, 3)
+    if constexpr (SUM) {
+        v = dpp_sum_step<0xb1, 0xf>(v);
+        v = dpp_sum_step<0x4e, 0xf>(v);
+        v = dpp_sum_step<0x141, 0xf>(v);
+        v = dpp_sum_step<0x140, 0xf>(v);
+        v = dpp_sum_step<0x142, 0xa>(v);
+        v = dpp_sum_step<0x143, 0xc>(v);
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    } else {
+        int x = __builtin_bit_cast(int, v);
+        x = dpp_max_step<0xb1, 0xf>(x);
+        x = dpp_max_step<0x4e, 0xf>(x);
+        x = dpp_max_step<0x141, 0xf>(x);
+        x = dpp_max_step<0x140, 0xf>(x);
+        x = dpp_max_step<0x142, 0xa>(x);
+        x = dpp_max_step<0x143, 0xc>(x);
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 63));
+    }
 }
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce<false>(v); }
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce<true>(v); }
@@ -417,6 +456,12 @@ __device__ __forceinline__ float pow2_scale(float amax, int hb) {
 // registers) across the whole kernel
 __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
+    return x;
+}
+
+// opaque copy of a wave-uniform 64-bit value (kept in scalar registers)
+__device__ __forceinline__ uint64_t opaque_u64(uint64_t x) {
+    asm volatile("" : "+s"(x));
     return x;
 }
 
@@ -657,9 +702,12 @@ struct Engine {
         __syncthreads();
     }
 
-    // Inverse of pass 0 keeping outputs m < 8: conjugated input times the
-    // twiddle, forward DFT-16 rows 0..7, conjugated result;
-    // out(s, n, m, re, im) for m = 2g, 2g+1.
+    // Inverse of pass 0 keeping outputs m < 8.  The inverse passes keep the
+    // signal conjugated in LDS (IDFT(x) = conj(DFT(conj(x))), and the
+    // conjugations between consecutive passes cancel), so this pass is the
+    // twiddle times the stored value, forward DFT-16 rows 0..7, and the one
+    // remaining conjugation in the output; out(s, n, m, re, im) for
+    // m = 2g, 2g+1.
     template <class OUT>
     __device__ void pass0_inv(const OUT &out, int nsig) {
         const int lb = opaque((j ^ phys<LOG2M>(2 * g * S0)) << 2);
@@ -681,7 +729,7 @@ struct Engine {
                 for (int t = 0; t < 4; ++t) tu[t] = tua[i % NDI][t];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) x[t] = lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2));
-                cmulh_cx_n(x, tu);
+                cmulh_n(x, tu);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
                 res[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
             }
@@ -706,7 +754,8 @@ struct Engine {
     }
 
     // INV = false: DIF pass, y_k = tw_k * sum_m W^{km} x_m.
-    // INV = true:  its inverse (up to the factor 16), x = conj(DFT(conj(y) tw)).
+    // INV = true:  its inverse (up to the factor 16) on conjugated data:
+    // conj(x) = DFT(conj(y) tw), i.e. twiddle first, then the forward DFT.
     // Each lane reads and writes back the slots k = chain(g, 0..3).
     template <int P, bool INV>
     __device__ void mid_pass(int nsig, uint32_t pre = 0u) {
@@ -728,7 +777,7 @@ struct Engine {
                     x[t] = lds(a[t]);
                     if (INV && P == K) x[t] = pkmul(x[t], pre);  // scale set after the last pass
                 }
-                if (INV) cmulh_cx_n(x, tw);
+                if (INV) cmulh_n(x, tw);
                 const half8 b = as_half8(x[0], x[1], x[2], x[3]);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
                 const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, b, z, 0, 0, 0);
@@ -739,10 +788,10 @@ struct Engine {
                     lds(a[2]) = cmulh(pk(d1[0], d1[1]), tw[2]);
                     lds(a[3]) = cmulh(pk(d1[2], d1[3]), tw[3]);
                 } else {
-                    lds(a[0]) = pk(d0[0], -d0[1]);
-                    lds(a[1]) = pk(d0[2], -d0[3]);
-                    lds(a[2]) = pk(d1[0], -d1[1]);
-                    lds(a[3]) = pk(d1[2], -d1[3]);
+                    lds(a[0]) = pk(d0[0], d0[1]);
+                    lds(a[1]) = pk(d0[2], d0[3]);
+                    lds(a[2]) = pk(d1[0], d1[1]);
+                    lds(a[3]) = pk(d1[2], d1[3]);
                 }
             }
         }
@@ -827,32 +876,33 @@ struct Engine {
         }
     }
 
-    // Inverse last-pass DFT, written back in place; returns the largest
-    // magnitude of a real or imaginary part written.  For R >= 8 `y` holds
-    // conj(Y) and the forward matrix is used; for R <= 4 `y` holds Y.
+    // Inverse last-pass DFT, written back in place conjugated (the inverse
+    // passes work on conjugated data): `y` holds conj(Y) and the forward DFT
+    // gives conj(IDFT(Y)) R.  Returns the largest magnitude of a real or
+    // imaginary part written.
     __device__ __forceinline__ float last_inv(int pb, const uint32_t (&y)[NV]) {
         if constexpr (R == 16) {
             const half8 b = as_half8(y[0], y[1], y[2], y[3]);
             const f4 z = {0.f, 0.f, 0.f, 0.f};
             const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, b, z, 0, 0, 0);
             const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C1, b, z, 0, 0, 0);
-            const u32x2 lo = {pk(d0[0], -d0[1]), pk(d0[2], -d0[3])};
-            const u32x2 hi = {pk(d1[0], -d1[1]), pk(d1[2], -d1[3])};
+            const u32x2 lo = {pk(d0[0], d0[1]), pk(d0[2], d0[3])};
+            const u32x2 hi = {pk(d1[0], d1[1]), pk(d1[2], d1[3])};
             lds<u32x2>(pb) = lo;
             lds<u32x2>(pb ^ 32) = hi;
             return fmaxf(fmaxf(habs_max(lo.x), habs_max(lo.y)), fmaxf(habs_max(hi.x), habs_max(hi.y)));
         } else if constexpr (R == 8) {
             const f4 z = {0.f, 0.f, 0.f, 0.f};
             const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8, as_half4(y[0], y[1]), z, 0, 0, 0);
-            const u32x2 o = {pk(d[0], -d[1]), pk(d[2], -d[3])};
+            const u32x2 o = {pk(d[0], d[1]), pk(d[2], d[3])};
             lds<u32x2>(pb) = o;
             return fmaxf(habs_max(o.x), habs_max(o.y));
         } else if constexpr (R == 4) {
             const h2 a = __builtin_bit_cast(h2, y[0]), b = __builtin_bit_cast(h2, y[1]),
                      c = __builtin_bit_cast(h2, y[2]), d = __builtin_bit_cast(h2, y[3]);
             const h2 s0 = a + c, d0 = a - c, s1 = b + d, d1 = b - d;
-            const h2 d1pi = {-d1.y, d1.x};  // (b - d) * (+i)
-            const h2 o0 = s0 + s1, o1 = d0 + d1pi, o2 = s0 - s1, o3 = d0 - d1pi;
+            const h2 d1mi = {d1.y, -d1.x};  // (b - d) * (-i)
+            const h2 o0 = s0 + s1, o1 = d0 + d1mi, o2 = s0 - s1, o3 = d0 - d1mi;
             const u32x4 o = {__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
                              __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3)};
             lds<u32x4>(pb) = o;
@@ -875,31 +925,33 @@ struct Engine {
         else return (slot % NSL) * NV;
     }
     // ---------------------------------------------------------- filter
-    // Filter spectrum, kept in registers as packed fp16: F = DFT(f) * cF / R
-    // (conjugated for R >= 8) with cF = 2^-e where sum |f| < 2^e.  Every
+    // Filter spectrum, kept in registers as packed fp16: conj(F) = conj(DFT(f))
+    // * cF / R with cF = 2^-e where sum |f| < 2^e.  Every
     // partial sum of the transform is bounded by sum |f|, so inputs scaled by
     // 2^(14 - e) keep the whole transform below 2^14 and |F| below 1 / R,
     // without a reduction over the spectrum itself.
-    // Issue the loads of the real filter (nf taps, branch-free: indices are
-    // clamped and the padding selected afterwards) into this lane's pass-0
-    // slots; kept apart from the transform so the activation loads can be
-    // issued behind them.
-    template <class LDF>
-    __device__ __forceinline__ void filter_fetch(const LDF &ldf, int nf, float (&fin)[T0W][4]) {
+    // Issue the loads of the real filter into this lane's pass-0 slots, kept
+    // apart from the transform so the activation loads can be issued behind
+    // them.  `frs` covers the filter's taps (reads past them return zero:
+    // the padding); d0 is added to tap 0 (the skip term D u folded in).
+    __device__ __forceinline__ void filter_fetch(__amdgpu_buffer_rsrc_t frs, float d0, float (&fin)[T0W][4]) {
         const int h = lane >> 5;
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
             const int off = tile_n(i) + 4 * h * S0;
+            if (tile_sig(i) == 0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int pos = off + e * S0;
-                const float v = ldf(min(pos, nf - 1));
-                fin[i][e] = (tile_sig(i) == 0 && pos < nf) ? v : 0.f;
+                for (int e = 0; e < 4; ++e)
+                    fin[i][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(frs, 4 * off, 4 * e * S0, 0));
+                if (off == 0) fin[i][0] += d0;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fin[i][e] = 0.f;
             }
         }
     }
 
-    __device__ void filter(const float (&fin)[T0W][4], int nf) {
+    __device__ void filter(const float (&fin)[T0W][4]) {
         float asum = 0.f;
 #pragma unroll
         for (int i = 0; i < T0W; ++i)
@@ -911,7 +963,7 @@ struct Engine {
         const float sf = ldexpf(1.f, 14 - ef);
         cF = ldexpf(1.f, -ef);
         constexpr float c = 1.0f / (16384.0f * R);
-        const uint32_t ch = R >= 8 ? pk(c, -c) : pk(c, c);  // conjugate for R >= 8
+        const uint32_t ch = pk(c, -c);  // conjugate
         pass0([&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); }, 1);
         fwd_middle<1>(1);
         const int lb = opaque(lbase());
@@ -952,8 +1004,8 @@ struct Engine {
         pass0([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); }, nsig);
         fwd_middle<1>(nsig);
         // Last pass, in place: forward DFT-R, product with the filter spectrum
-        // (stored as F cF / R, conjugated for R >= 8, so no product can
-        // overflow the inverse DFT-R), inverse DFT-R.  The maximum of what it
+        // (stored as conj(F) cF / R, so no product can overflow the inverse
+        // DFT-R), inverse DFT-R on conjugated values.  The maximum of what it
         // writes sets the scale sy applied by the next inverse pass.
         uint32_t Fr[FN];
 #pragma unroll
@@ -965,17 +1017,11 @@ struct Engine {
             const int slot = u % NLS;
             if (lsig(u) < nsig) {
                 const int pb = (lb ^ lpos(u)) + lsig(u) * SB;
-                uint32_t y[NV];
+                uint32_t y[NV], fr[NV];
                 last_fwd(pb, y);
-                if constexpr (R >= 8) {
-                    uint32_t fr[NV];
 #pragma unroll
-                    for (int q = 0; q < NV; ++q) fr[q] = Fr[fslot(slot) + q];
-                    cmulh_cx_n(y, fr);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < NV; ++q) y[q] = cmulh(y[q], Fr[fslot(slot) + q]);
-                }
+                for (int q = 0; q < NV; ++q) fr[q] = Fr[fslot(slot) + q];
+                cmulh_cx_n(y, fr);  // conj(Y) = conj(X) conj(F)
                 vmax = fmaxf(vmax, last_inv(pb, y));
             }
         }
@@ -991,16 +1037,17 @@ struct Engine {
     }
 
     // A whole channel of 16-bit activations: the filter spectrum, then
-    // ceil(nsig / SIG) rounds of complex signals.  ldf(pos) gives the real
-    // filter (nf taps); rows(sig) the buffer resources of signal `sig`.  The inputs of each round are fetched while the
-    // previous round (or the filter) is being transformed.
-    template <class LDF, class RB>
-    __device__ void run_raw(const LDF &ldf, int nf, const RB &rows, int nsig, int hb) {
+    // ceil(nsig / SIG) rounds of complex signals.  `frs` covers the real
+    // filter's taps and d0 is added to tap 0; rows(sig) gives the buffer
+    // resources of signal `sig`.  The inputs of each round are fetched while
+    // the previous round (or the filter) is being transformed.
+    template <class RB>
+    __device__ void run_raw(__amdgpu_buffer_rsrc_t frs, float d0, const RB &rows, int nsig, int hb) {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         float fin[T0W][4];
-        filter_fetch(ldf, nf, fin);
+        filter_fetch(frs, d0, fin);
         if constexpr (PREFETCH) fetch_raw(rows, 0, min(SIG, nsig), pnx);
-        filter(fin, nf);
+        filter(fin);
         for (int r0 = 0; r0 < nsig; r0 += SIG) {
             const int nr = min(SIG, nsig - r0);
             if constexpr (PREFETCH) {

@@ -699,7 +699,7 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
         return {mf::row_rsrc(ub + off(r), 2 * T), mf::row_rsrc(ub + o1, nb1), mf::row_rsrc(yb + off(r), 2 * T),
                 mf::row_rsrc(yb + o1, nb1)};
     };
-    E.run_raw([&](int pos) -> float { return fh[pos]; }, T, rowp, (rows + 1) / 2, hb);
+    E.run_raw(mf::row_rsrc(fh, 4 * T), 0.f, rowp, (rows + 1) / 2, hb);
 }
 
 template <int LOG2M, int IO>
