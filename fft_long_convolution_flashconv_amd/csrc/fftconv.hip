@@ -150,11 +150,13 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
     const char *uh = (const char *)(u + (size_t)h * N);
     char *yh = (char *)(y + (size_t)h * N);
     const int hb = mf::half_bits(N);
-    // complex signal `sig` = batch rows 2 sig (real part), 2 sig + 1 (imaginary)
+    // complex signal `sig` = batch rows 2 sig (real part), 2 sig + 1
+    // (imaginary); rows past B get empty resources
     auto rows = [&](int sig) -> mf::RowBufs {
         const uint64_t o = (uint64_t)(uint32_t)sig * (2 * rsb);
+        const int nb0 = (2 * sig < B) ? 2 * N : 0;
         const int nb1 = (2 * sig + 1 < B) ? 2 * N : 0;
-        return {mf::row_rsrc(uh + o, 2 * N), mf::row_rsrc(uh + o + rsb, nb1), mf::row_rsrc(yh + o, 2 * N),
+        return {mf::row_rsrc(uh + o, nb0), mf::row_rsrc(uh + o + rsb, nb1), mf::row_rsrc(yh + o, nb0),
                 mf::row_rsrc(yh + o + rsb, nb1)};
     };
     E.run_raw(mf::row_rsrc(fh, 4 * N), dh, rows, (B + 1) / 2, hb);

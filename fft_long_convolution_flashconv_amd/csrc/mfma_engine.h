@@ -318,13 +318,14 @@ __host__ __device__ constexpr int phys(int i) {
 
 // Workgroup shape per transform size: SIG signals in flight, NW waves.
 template <int LOG2M> struct Cfg;
-// OCC = workgroups per compute unit the register budget is set for.
-template <> struct Cfg<9> { static constexpr int SIG = 8, NW = 2, OCC = 4; };
-template <> struct Cfg<10> { static constexpr int SIG = 4, NW = 4, OCC = 4; };
-template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8, OCC = 3; };
-template <> struct Cfg<12> { static constexpr int SIG = 2, NW = 8, OCC = 2; };
-template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 8, OCC = 2; };
-template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8, OCC = 2; };
+// OCC = workgroups per compute unit the register budget is set for; BD =
+// most dwords a lane reads from LDS ahead of the first write in a pass.
+template <> struct Cfg<9> { static constexpr int SIG = 8, NW = 2, OCC = 4, BD = 16; };
+template <> struct Cfg<10> { static constexpr int SIG = 4, NW = 4, OCC = 4, BD = 16; };
+template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8, OCC = 3, BD = 8; };
+template <> struct Cfg<12> { static constexpr int SIG = 2, NW = 8, OCC = 2, BD = 16; };
+template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 8, OCC = 2, BD = 16; };
+template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8, OCC = 2, BD = 8; };
 
 template <int LOG2M>
 struct Shape {
@@ -334,6 +335,7 @@ struct Shape {
     static constexpr int R = 1 << LR;
     static constexpr int S0 = M / 16;                  // pass-0 columns per signal
     static constexpr int SIG = Cfg<LOG2M>::SIG, NW = Cfg<LOG2M>::NW, NT = 64 * NW, OCC = Cfg<LOG2M>::OCC;
+    static constexpr int BD = Cfg<LOG2M>::BD;
     static constexpr int WPE = (OCC * NW + 3) / 4;     // waves per SIMD at that occupancy
     static constexpr int T0 = SIG * S0 / 32;           // pass-0 tiles (32 columns) per round
     static constexpr int T0W = T0 / NW;
@@ -528,7 +530,8 @@ struct Engine {
     uint32_t *data;  // [SIG][M] packed complex (swizzled)
     float *red;      // [2][NW] reduction slots
     int tid, w, lane, j, g;
-    const u32x4 *twt;                       // this thread's column of the twiddle table
+    __amdgpu_buffer_rsrc_t twr;             // the twiddle table
+    int two;                                // this thread's byte offset in it
     half8 A0, C0, C1;                       // DFT-16: zero-padded 32x32x16; chained 16x16x32
     half4 A8;                               // DFT-8: 16x16x16
     uint32_t tw0[TWREG ? ND0 : 1][8];       // pass-0 twiddles (when held in registers)
@@ -553,7 +556,13 @@ struct Engine {
         g = lane >> 4;
     }
 
-    __device__ __forceinline__ u32x4 tq(int c) const { return twt[c * NT]; }
+    // Quad c of this thread's twiddles.  The offset goes through an opaque
+    // copy so that a load stays where it is used: the table is the same for
+    // every round, and the compiler would otherwise hoist the loads out of
+    // the round loop and hold (or spill) all of them throughout.
+    __device__ __forceinline__ u32x4 tq(int c) const {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(twr, opaque(two), c * NT * 16, 0));
+    }
 
     __device__ void init() {
         const u32x4 *mt = (const u32x4 *)&tab::kMat.q[0][0][0];
@@ -565,7 +574,8 @@ struct Engine {
             const uint32_t a0 = a.x, a1 = a.y;
             A8 = as_half4(a0, a1);
         }
-        twt = (const u32x4 *)&tab::kTw<LOG2M>.q[0][0][0] + tid;
+        twr = row_rsrc(&tab::kTw<LOG2M>.q[0][0][0], (int)sizeof(tab::TwTab<LOG2M>));
+        two = tid * 16;
         if constexpr (TWREG) {
 #pragma unroll
             for (int d = 0; d < ND0; ++d) {
@@ -649,43 +659,40 @@ struct Engine {
     __device__ __forceinline__ int tile_n(int i) const { return (32 * (w + i * NW)) % S0 + (lane & 31); }
 
     // 16-bit activations through the rows' buffer resources (zero past each
-    // row's valid length).  The compile-time part of the offset goes in the
-    // scalar offset, which gfx950 includes in the range check of a raw buffer
-    // access (checked on the device: a load whose per-lane offset is in range
-    // but whose total offset is not returns zero).
+    // row's valid length; a row that does not exist has an empty resource,
+    // so a round is always SIG signals, the missing ones all zero).  The
+    // compile-time part of the offset goes in the scalar offset, which gfx950
+    // includes in the range check of a raw buffer access (checked on the
+    // device: a load whose per-lane offset is in range but whose total offset
+    // is not returns zero).
     template <class RB>
-    __device__ __forceinline__ void fetch_raw(const RB &rows, int sig0, int nsig, uint32_t (&buf)[T0W][4]) {
+    __device__ __forceinline__ void fetch_raw(const RB &rows, int sig0, uint32_t (&buf)[T0W][4]) {
         const int h = lane >> 5;
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
-            const int s = tile_sig(i);
             const int off = 2 * (tile_n(i) + 4 * h * S0);
-            if (s < nsig) {
-                const RowBufs rb = rows(sig0 + s);
+            const RowBufs rb = rows(sig0 + tile_sig(i));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rb.in0, off, 2 * e * S0, 0);
-                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rb.in1, off, 2 * e * S0, 0);
-                    buf[i][e] = lo | (hi << 16);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) buf[i][e] = 0u;
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rb.in0, off, 2 * e * S0, 0);
+                const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rb.in1, off, 2 * e * S0, 0);
+                buf[i][e] = lo | (hi << 16);
             }
         }
     }
 
-    // Zero-padded radix-16 DIF pass: DFT on the matrix cores, twiddle w_M^{n q},
-    // to LDS.  `op(i, e)` yields the packed scaled operand of tile i.
-    template <class OP>
-    __device__ void pass0(const OP &op, int nsig) {
+    // Zero-padded radix-16 DIF pass over the first NS signals: DFT on the
+    // matrix cores, twiddle w_M^{n q}, to LDS.  `op(i, e)` yields the packed
+    // scaled operand of tile i.
+    template <int NS, class OP>
+    __device__ void pass0(const OP &op) {
         const int h = lane >> 5;
         // lane part of the column (lane % 32) and of the output q = qc + 2h
         const int lb = opaque(((lane & 31) ^ phys<LOG2M>(2 * h * S0)) << 2);
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
             const int s = tile_sig(i);
-            if (s < nsig) {
+            if (NS == SIG || s < NS) {
                 uint32_t tw[8];
                 get_tw0(i % ND0, tw);
                 const int pn = lb ^ ((phys<LOG2M>((32 * (w + i * NW)) % S0) << 2) | (s * SB));
@@ -706,42 +713,71 @@ struct Engine {
     // signal conjugated in LDS (IDFT(x) = conj(DFT(conj(x))), and the
     // conjugations between consecutive passes cancel), so this pass is the
     // twiddle times the stored value, forward DFT-16 rows 0..7, and the one
-    // remaining conjugation in the output; out(s, n, m, re, im) for
-    // m = 2g, 2g+1.
-    template <class OUT>
-    __device__ void pass0_inv(const OUT &out, int nsig) {
+    // remaining conjugation in the output, scaled by os and converted to
+    // the activation type; st(s, n, m, v) stores the packed pair v (row 2s
+    // in the low half, row 2s + 1 in the high half) of output m = 2g, 2g+1.
+    template <class ST>
+    __device__ void pass0_inv(const ST &st, float os) {
         const int lb = opaque((j ^ phys<LOG2M>(2 * g * S0)) << 2);
         // All twiddles and products first, then all stores: loads and stores
         // retire in order, so a table load behind a store would wait for it.
-        uint32_t tua[NDI][4];
+        // The LDS reads go in batches of BD / 4 tiles (an empty asm with a
+        // memory clobber keeps a batch's reads from moving up into the
+        // previous one, where they would only hold registers).
+        // (twiddles from the table: per batch, issued with its LDS reads)
+        constexpr int NTA = TWREG ? NDI : 1;
+        uint32_t tua[NTA][4];
+        if constexpr (TWREG) {
 #pragma unroll
-        for (int d = 0; d < NDI; ++d) get_tu0(d, tua[d]);
-        f4 res[TIW];
+            for (int d = 0; d < NDI; ++d) get_tu0(d, tua[d]);
+        }
+        constexpr int BI = TIW < SH::BD / 4 ? TIW : SH::BD / 4;
+        static_assert(TIW % BI == 0, "inverse pass-0 tiles split into equal batches");
+        uint32_t ov[TIW][2];
+        auto cv = [&](float re, float im) -> uint32_t {
+            const f2 v = {re * os, im * os};
+            if constexpr (KIND == IN_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+            else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+        };
 #pragma unroll
-        for (int i = 0; i < TIW; ++i) {
-            const int s = (16 * (w + i * NW)) / S0;
-            res[i] = f4{0.f, 0.f, 0.f, 0.f};
-            if (s < nsig) {
+        for (int i0 = 0; i0 < TIW; i0 += BI) {
+            uint32_t xb[BI][4], tb[TWREG ? 1 : BI][4];
+            if constexpr (!TWREG) {
+#pragma unroll
+                for (int k = 0; k < BI; ++k) get_tu0((i0 + k) % NDI, tb[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < BI; ++k) {
+                const int i = i0 + k;
+                const int s = (16 * (w + i * NW)) / S0;
                 const int n0 = (16 * (w + i * NW)) % S0;
                 const int pn = lb ^ ((phys<LOG2M>(n0) << 2) | (s * SB));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) xb[k][t] = lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2));
+            }
+#pragma unroll
+            for (int k = 0; k < BI; ++k) {
+                const int i = i0 + k;
                 uint32_t tu[4], x[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) tu[t] = tua[i % NDI][t];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) x[t] = lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2));
+                for (int t = 0; t < 4; ++t) {
+                    tu[t] = TWREG ? tua[i % NTA][t] : tb[TWREG ? 0 : k][t];
+                    x[t] = xb[k][t];
+                }
                 cmulh_n(x, tu);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
-                res[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
+                const f4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
+                ov[i][0] = cv(r[0], -r[1]);
+                ov[i][1] = cv(r[2], -r[3]);
             }
+            asm volatile("" ::: "memory");
         }
 #pragma unroll
         for (int i = 0; i < TIW; ++i) {
             const int s = (16 * (w + i * NW)) / S0;
-            if (s < nsig) {
-                const int n = (16 * (w + i * NW)) % S0 + j;
-                out(s, n, 2 * g, res[i][0], -res[i][1]);
-                out(s, n, 2 * g + 1, res[i][2], -res[i][3]);
-            }
+            const int n = (16 * (w + i * NW)) % S0 + j;
+            st(s, n, 2 * g, ov[i][0]);
+            st(s, n, 2 * g + 1, ov[i][1]);
         }
     }
 
@@ -756,25 +792,38 @@ struct Engine {
     // INV = false: DIF pass, y_k = tw_k * sum_m W^{km} x_m.
     // INV = true:  its inverse (up to the factor 16) on conjugated data:
     // conj(x) = DFT(conj(y) tw), i.e. twiddle first, then the forward DFT.
-    // Each lane reads and writes back the slots k = chain(g, 0..3).
-    template <int P, bool INV>
-    __device__ void mid_pass(int nsig, uint32_t pre = 0u) {
+    // Each lane reads and writes back the slots k = chain(g, 0..3) of its
+    // tiles (signal s < NS, tile ti < TPW).  The reads of a batch of tiles
+    // are all issued before its first write: the compiler cannot tell that
+    // one tile's writes never touch another's slots, so it would otherwise
+    // wait out every tile's read latency in turn.
+    template <int P, bool INV, int NS>
+    __device__ void mid_pass(uint32_t pre = 0u) {
         constexpr int L = SH::L(P), S = L / 16;
+        constexpr int NTL = NS * TPW, BT = NTL < SH::BD / 4 ? NTL : SH::BD / 4;
+        static_assert(NTL % BT == 0, "tiles split into equal batches");
         const int pb = opaque((phys<LOG2M>(base0<P>()) ^ phys<LOG2M>(2 * g * S)) << 2);
         uint32_t tw[4];
         get_twm(P - 1, tw);
+        auto addr = [&](int tile, int t) {
+            const int s = tile / TPW, ti = tile % TPW;
+            return ((pb ^ (phys<LOG2M>(ti * DELTA) << 2)) ^ (phys<LOG2M>(tab::kChain[t] * S) << 2)) + s * SB;
+        };
 #pragma unroll
-        for (int s = 0; s < SIG; ++s) {
-            if (s >= nsig) break;
+        for (int b0 = 0; b0 < NTL; b0 += BT) {
+            uint32_t xb[BT][4];
 #pragma unroll
-            for (int ti = 0; ti < TPW; ++ti) {
-                const int ct = pb ^ (phys<LOG2M>(ti * DELTA) << 2);
+            for (int k = 0; k < BT; ++k)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) xb[k][t] = lds(addr(b0 + k, t));
+#pragma unroll
+            for (int k = 0; k < BT; ++k) {
                 int a[4];
                 uint32_t x[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    a[t] = (ct ^ (phys<LOG2M>(tab::kChain[t] * S) << 2)) + s * SB;
-                    x[t] = lds(a[t]);
+                    a[t] = addr(b0 + k, t);
+                    x[t] = xb[k][t];
                     if (INV && P == K) x[t] = pkmul(x[t], pre);  // scale set after the last pass
                 }
                 if (INV) cmulh_n(x, tw);
@@ -798,18 +847,18 @@ struct Engine {
         __syncthreads();
     }
 
-    template <int P>
-    __device__ void fwd_middle(int nsig) {
+    template <int P, int NS>
+    __device__ void fwd_middle() {
         if constexpr (P <= K) {
-            mid_pass<P, false>(nsig);
-            fwd_middle<P + 1>(nsig);
+            mid_pass<P, false, NS>();
+            fwd_middle<P + 1, NS>();
         }
     }
     template <int P>
-    __device__ void inv_middle(int nsig, uint32_t pre) {
+    __device__ void inv_middle(uint32_t pre) {
         if constexpr (P >= 1) {
-            mid_pass<P, true>(nsig, pre);
-            inv_middle<P - 1>(nsig, pre);
+            mid_pass<P, true, SIG>(pre);
+            inv_middle<P - 1>(pre);
         }
     }
 
@@ -831,17 +880,32 @@ struct Engine {
     static constexpr int lsig(int u) { return R >= 8 ? u / NLS : u / NSL; }
     static_assert(R >= 8 || NBL % NT == 0, "radix-2/4 last pass: butterflies must be a multiple of the threads");
 
-    // forward last-pass DFT of this slot (packed fp16 results, chained order
-    // for R = 16, natural for R = 8)
-    // (pb = byte address of the unit including its signal offset)
-    __device__ __forceinline__ void last_fwd(int pb, uint32_t (&y)[NV]) {
+    // dwords a lane reads for one last-pass unit
+    static constexpr int NVD = (R == 16 || R == 4) ? 4 : 2;
+    // read one unit (pb = byte address of the unit including its signal offset)
+    __device__ __forceinline__ void last_load(int pb, uint32_t (&v)[NVD]) {
+        // (elements go through scalars: bit-casting an element expression of
+        //  an ext_vector directly reads element 0)
         if constexpr (R == 16) {
             const u32x2 lo = lds<u32x2>(pb);
             const u32x2 hi = lds<u32x2>(pb ^ 32);  // slots 8 + 2g, 9 + 2g
-            // (elements go through scalars: bit-casting an element expression
-            //  of an ext_vector directly reads element 0)
             const uint32_t v0 = lo.x, v1 = lo.y, v2 = hi.x, v3 = hi.y;
-            const half8 b = as_half8(v0, v1, v2, v3);
+            v[0] = v0; v[1] = v1; v[2] = v2; v[3] = v3;
+        } else if constexpr (R == 4) {
+            const u32x4 a = lds<u32x4>(pb);
+            const uint32_t v0 = a.x, v1 = a.y, v2 = a.z, v3 = a.w;
+            v[0] = v0; v[1] = v1; v[2] = v2; v[3] = v3;
+        } else {
+            const u32x2 a = lds<u32x2>(pb);
+            const uint32_t v0 = a.x, v1 = a.y;
+            v[0] = v0; v[1] = v1;
+        }
+    }
+    // forward last-pass DFT of one unit's values (packed fp16 results,
+    // chained order for R = 16, natural for R = 8)
+    __device__ __forceinline__ void last_fwd(const uint32_t (&v)[NVD], uint32_t (&y)[NV]) {
+        if constexpr (R == 16) {
+            const half8 b = as_half8(v[0], v[1], v[2], v[3]);
             const f4 z = {0.f, 0.f, 0.f, 0.f};
             const f4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, b, z, 0, 0, 0);
             const f4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(C1, b, z, 0, 0, 0);
@@ -850,17 +914,13 @@ struct Engine {
             y[2] = pk(d1[0], d1[1]);
             y[3] = pk(d1[2], d1[3]);
         } else if constexpr (R == 8) {
-            const u32x2 v = lds<u32x2>(pb);
-            const uint32_t v0 = v.x, v1 = v.y;
             const f4 z = {0.f, 0.f, 0.f, 0.f};
-            const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8, as_half4(v0, v1), z, 0, 0, 0);
+            const f4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(A8, as_half4(v[0], v[1]), z, 0, 0, 0);
             y[0] = pk(d[0], d[1]);
             y[1] = pk(d[2], d[3]);
         } else if constexpr (R == 4) {
-            const u32x4 v = lds<u32x4>(pb);
-            const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
-            const h2 a = __builtin_bit_cast(h2, v0), b = __builtin_bit_cast(h2, v1),
-                     c = __builtin_bit_cast(h2, v2), d = __builtin_bit_cast(h2, v3);
+            const h2 a = __builtin_bit_cast(h2, v[0]), b = __builtin_bit_cast(h2, v[1]),
+                     c = __builtin_bit_cast(h2, v[2]), d = __builtin_bit_cast(h2, v[3]);
             const h2 s0 = a + c, d0 = a - c, s1 = b + d, d1 = b - d;
             const h2 d1mi = {d1.y, -d1.x};  // (b - d) * (-i)
             y[0] = __builtin_bit_cast(uint32_t, s0 + s1);
@@ -868,12 +928,15 @@ struct Engine {
             y[2] = __builtin_bit_cast(uint32_t, s0 - s1);
             y[3] = __builtin_bit_cast(uint32_t, d0 - d1mi);
         } else {
-            const u32x2 v = lds<u32x2>(pb);
-            const uint32_t v0 = v.x, v1 = v.y;
-            const h2 a = __builtin_bit_cast(h2, v0), b = __builtin_bit_cast(h2, v1);
+            const h2 a = __builtin_bit_cast(h2, v[0]), b = __builtin_bit_cast(h2, v[1]);
             y[0] = __builtin_bit_cast(uint32_t, a + b);
             y[1] = __builtin_bit_cast(uint32_t, a - b);
         }
+    }
+    __device__ __forceinline__ void last_fwd(int pb, uint32_t (&y)[NV]) {
+        uint32_t v[NVD];
+        last_load(pb, v);
+        last_fwd(v, y);
     }
 
     // Inverse last-pass DFT, written back in place conjugated (the inverse
@@ -964,8 +1027,8 @@ struct Engine {
         cF = ldexpf(1.f, -ef);
         constexpr float c = 1.0f / (16384.0f * R);
         const uint32_t ch = pk(c, -c);  // conjugate
-        pass0([&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); }, 1);
-        fwd_middle<1>(1);
+        pass0<1>([&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); });
+        fwd_middle<1, 1>();
         const int lb = opaque(lbase());
 #pragma unroll
         for (int slot = 0; slot < NLS; ++slot) {
@@ -980,7 +1043,7 @@ struct Engine {
 
     // ---------------------------------------------------------- conv round
     template <class OUT>
-    __device__ void conv_round(const OUT &out, int nsig, int hb) {
+    __device__ void conv_round(const OUT &out, int hb) {
         float amax;
         if constexpr (KIND == IN_F16) {
             h2 am = {(_Float16)0.f, (_Float16)0.f};
@@ -1001,8 +1064,8 @@ struct Engine {
         const float su0 = pow2_scale(block_reduce<false>(amax), hb);
         const float su = (KIND == IN_F16) ? fminf(su0, 16384.0f) : su0;
         const uint32_t suh = pk(su, su);
-        pass0([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); }, nsig);
-        fwd_middle<1>(nsig);
+        pass0<SIG>([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); });
+        fwd_middle<1, SIG>();
         // Last pass, in place: forward DFT-R, product with the filter spectrum
         // (stored as conj(F) cF / R, so no product can overflow the inverse
         // DFT-R), inverse DFT-R on conjugated values.  The maximum of what it
@@ -1010,15 +1073,23 @@ struct Engine {
         uint32_t Fr[FN];
 #pragma unroll
         for (int i = 0; i < FN; ++i) Fr[i] = F[i];
+        // Units go in batches whose reads are all issued before the first
+        // write (as in the middle passes).
         float vmax = 0.f;
         const int lb = opaque(lbase());
+        constexpr int UB = NU * NVD <= SH::BD ? NU : SH::BD / NVD;
+        static_assert(NU % UB == 0, "last-pass units split into equal batches");
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int slot = u % NLS;
-            if (lsig(u) < nsig) {
+        for (int u0 = 0; u0 < NU; u0 += UB) {
+            uint32_t vb[UB][NVD];
+#pragma unroll
+            for (int k = 0; k < UB; ++k) last_load((lb ^ lpos(u0 + k)) + lsig(u0 + k) * SB, vb[k]);
+#pragma unroll
+            for (int k = 0; k < UB; ++k) {
+                const int u = u0 + k, slot = u % NLS;
                 const int pb = (lb ^ lpos(u)) + lsig(u) * SB;
                 uint32_t y[NV], fr[NV];
-                last_fwd(pb, y);
+                last_fwd(vb[k], y);
 #pragma unroll
                 for (int q = 0; q < NV; ++q) fr[q] = Fr[fslot(slot) + q];
                 cmulh_cx_n(y, fr);  // conj(Y) = conj(X) conj(F)
@@ -1031,44 +1102,40 @@ struct Engine {
         int ev = 0;
         if (vm > 0.f) (void)frexpf(vm, &ev);
         const float sy = fminf(fmaxf(ldexpf(1.f, 14 - ev - (LOG2M - SH::LR)), 1.0f / 16384.0f), 32768.0f);
-        inv_middle<K>(nsig, pk(sy, sy));
+        inv_middle<K>(pk(sy, sy));
         const float os = (float)R / ((float)M * su * sy * cF);
-        pass0_inv([&](int s, int n, int m, float re, float im) { out(s, n, m, re * os, im * os); }, nsig);
+        pass0_inv(out, os);
     }
 
     // A whole channel of 16-bit activations: the filter spectrum, then
     // ceil(nsig / SIG) rounds of complex signals.  `frs` covers the real
     // filter's taps and d0 is added to tap 0; rows(sig) gives the buffer
-    // resources of signal `sig`.  The inputs of each round are fetched while
-    // the previous round (or the filter) is being transformed.
+    // resources of signal `sig`, empty ones for the rows past the last (a
+    // round always transforms SIG signals).  The inputs of each round are
+    // fetched while the previous round (or the filter) is being transformed.
     template <class RB>
     __device__ void run_raw(__amdgpu_buffer_rsrc_t frs, float d0, const RB &rows, int nsig, int hb) {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         float fin[T0W][4];
         filter_fetch(frs, d0, fin);
-        if constexpr (PREFETCH) fetch_raw(rows, 0, min(SIG, nsig), pnx);
+        if constexpr (PREFETCH) fetch_raw(rows, 0, pnx);
         filter(fin);
         for (int r0 = 0; r0 < nsig; r0 += SIG) {
-            const int nr = min(SIG, nsig - r0);
             if constexpr (PREFETCH) {
 #pragma unroll
                 for (int i = 0; i < T0W; ++i)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) pin[i][e] = pnx[i][e];
-                if (r0 + SIG < nsig) fetch_raw(rows, r0 + SIG, min(SIG, nsig - r0 - SIG), pnx);
+                if (r0 + SIG < nsig) fetch_raw(rows, r0 + SIG, pnx);
             } else {
-                fetch_raw(rows, r0, nr, pin);
+                fetch_raw(rows, r0, pin);
             }
-            auto out = [&](int s, int n, int m, float re, float im) {
+            auto out = [&](int s, int n, int m, uint32_t hv) {
                 const RowBufs rb = rows(r0 + s);
-                const f2 v = {re, im};
-                uint32_t hv;
-                if constexpr (KIND == IN_F16) hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
-                else hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
                 __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, 0);
             };
-            conv_round(out, nr, hb);
+            conv_round(out, hb);
         }
     }
 };

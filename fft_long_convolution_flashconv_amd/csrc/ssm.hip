@@ -689,14 +689,17 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
         const int b = r / C, c = r % C;
         return ((size_t)b * H + h) * N + (size_t)c * T;
     };
-    // complex signal `sig` = row chunks 2 sig (real part), 2 sig + 1 (imaginary)
+    // complex signal `sig` = row chunks 2 sig (real part), 2 sig + 1
+    // (imaginary); chunks past the last get empty resources
     auto rowp = [&](int sig) -> mf::RowBufs {
         const int r = 2 * sig;
+        const int nb0 = (r < rows) ? 2 * T : 0;
         const int nb1 = (r + 1 < rows) ? 2 * T : 0;
         const uint16_t *ub = (const uint16_t *)u;
         uint16_t *yb = (uint16_t *)y;
-        const size_t o1 = (r + 1 < rows) ? off(r + 1) : off(r);
-        return {mf::row_rsrc(ub + off(r), 2 * T), mf::row_rsrc(ub + o1, nb1), mf::row_rsrc(yb + off(r), 2 * T),
+        const size_t o0 = (r < rows) ? off(r) : 0;
+        const size_t o1 = (r + 1 < rows) ? off(r + 1) : o0;
+        return {mf::row_rsrc(ub + o0, nb0), mf::row_rsrc(ub + o1, nb1), mf::row_rsrc(yb + o0, nb0),
                 mf::row_rsrc(yb + o1, nb1)};
     };
     E.run_raw(mf::row_rsrc(fh, 4 * T), 0.f, rowp, (rows + 1) / 2, hb);
