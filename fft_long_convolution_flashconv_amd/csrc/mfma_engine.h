@@ -325,7 +325,7 @@ template <> struct Cfg<10> { static constexpr int SIG = 4, NW = 4, OCC = 4, BD =
 template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8, OCC = 3, BD = 8; };
 template <> struct Cfg<12> { static constexpr int SIG = 2, NW = 8, OCC = 2, BD = 16; };
 template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 8, OCC = 2, BD = 16; };
-template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8, OCC = 2, BD = 8; };
+template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8, OCC = 2, BD = 16; };
 
 template <int LOG2M>
 struct Shape {
@@ -503,6 +503,10 @@ __device__ __forceinline__ uint32_t in_scaled(const typename InT<KIND>::T &x, fl
 // resource is the valid part of its row, so loads past it return zero (the
 // zero padding of the transform) and stores past it are dropped; a signal
 // with one row gets empty in1/out1.
+// Cache policy of the activation loads and stores: non-temporal (each value
+// is read or written once), so they do not displace the tables and filters
+// in L2 and leave no dirty lines in it for the end of the kernel to write back.
+constexpr int kNT = 2;
 struct RowBufs {
     __amdgpu_buffer_rsrc_t in0, in1, out0, out1;
 };
@@ -674,8 +678,8 @@ struct Engine {
             const RowBufs rb = rows(sig0 + tile_sig(i));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rb.in0, off, 2 * e * S0, 0);
-                const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rb.in1, off, 2 * e * S0, 0);
+                const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rb.in0, off, 2 * e * S0, kNT);
+                const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rb.in1, off, 2 * e * S0, kNT);
                 buf[i][e] = lo | (hi << 16);
             }
         }
@@ -1132,8 +1136,8 @@ struct Engine {
             }
             auto out = [&](int s, int n, int m, uint32_t hv) {
                 const RowBufs rb = rows(r0 + s);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, kNT);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, kNT);
             };
             conv_round(out, hb);
         }
