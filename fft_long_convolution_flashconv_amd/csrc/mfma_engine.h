@@ -348,8 +348,13 @@ struct Shape {
     static constexpr int NBL = M / R;                  // radix-2/4 last-pass butterflies per signal
     static constexpr int NSL = (NBL > NT) ? NBL / NT : 1;            // distinct positions per thread
     static constexpr int BPTL = (SIG * NBL + NT - 1) / NT;           // butterflies per thread
-    static constexpr int DATA = SIG * M;
-    static constexpr int LDS_DWORDS = SIG * M + 64;
+    // The filter is transformed together with the first round's signals, in
+    // a signal slot of its own, when that slot fits the LDS budget of OCC
+    // workgroups per compute unit (160 KiB); otherwise it is transformed on
+    // its own first, in the signals' slots.
+    static constexpr bool FUSEF = ((SIG + 1) * M + 64) * 4 * OCC <= 160 * 1024;
+    static constexpr int DATA = (SIG + (FUSEF ? 1 : 0)) * M;
+    static constexpr int LDS_DWORDS = DATA + 64;
     static constexpr int DELTA = 256 * NW;             // butterfly-base step between a wave's tiles
     // distinct column offsets a thread meets in pass 0 (32-column tiles) and
     // in its inverse (16-column tiles)
@@ -547,7 +552,7 @@ struct Engine {
     // twiddles come from the table: loads retire in order, so every table
     // load would then also wait for the whole prefetch.
     static constexpr bool PREFETCH = TWREG;
-    IT pin[T0W][4], pnx[PREFETCH ? T0W : 1][4];  // pass-0 operands: this round, next round
+    IT pin[T0W][4];  // pass-0 operands of the current (or, prefetched, the next) round
     int rbank = 0;
 
     __device__ Engine(uint32_t *smem) {
@@ -631,12 +636,13 @@ struct Engine {
     }
 
     // Workgroup max (SUM = false) or sum (SUM = true).  Two alternating slot
-    // banks: a wave can only write a bank again after the next reduction's
-    // barrier, which every wave reaches only after reading that bank.
+    // banks (of 2 NW floats, room for the joint reduction below): a wave can
+    // only write a bank again after the next reduction's barrier, which every
+    // wave reaches only after reading that bank.
     template <bool SUM>
     __device__ float block_reduce(float v) {
         v = SUM ? wave_sum(v) : wave_max(v);
-        float *r = red + rbank * NW;
+        float *r = red + rbank * 2 * NW;
         rbank ^= 1;
         if (lane == 0) r[w] = v;
         __syncthreads();
@@ -644,6 +650,26 @@ struct Engine {
 #pragma unroll
         for (int i = 0; i < NW; ++i) m = SUM ? m + r[i] : fmaxf(m, r[i]);
         return m;
+    }
+
+    // Workgroup sum of a and max of b with one barrier (same bank scheme).
+    __device__ f2 block_reduce_sm(float a, float b) {
+        a = wave_sum(a);
+        b = wave_max(b);
+        float *r = red + rbank * 2 * NW;
+        rbank ^= 1;
+        if (lane == 0) {
+            r[w] = a;
+            r[NW + w] = b;
+        }
+        __syncthreads();
+        float sa = 0.f, mb = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            sa += r[i];
+            mb = fmaxf(mb, r[NW + i]);
+        }
+        return f2{sa, mb};
     }
 
     // LDS access by byte address.  Addresses are built as a per-lane base,
@@ -687,28 +713,34 @@ struct Engine {
 
     // Zero-padded radix-16 DIF pass over the first NS signals: DFT on the
     // matrix cores, twiddle w_M^{n q}, to LDS.  `op(i, e)` yields the packed
-    // scaled operand of tile i.
-    template <int NS, class OP>
-    __device__ void pass0(const OP &op) {
+    // scaled operand of tile i.  With FILT, the tiles of signal 0's columns
+    // are also done for the filter operand fop(i, e), into slot SIG.
+    template <int NS, bool FILT = false, class OP, class FOP>
+    __device__ void pass0(const OP &op, const FOP &fop) {
         const int h = lane >> 5;
         // lane part of the column (lane % 32) and of the output q = qc + 2h
         const int lb = opaque(((lane & 31) ^ phys<LOG2M>(2 * h * S0)) << 2);
+        auto tile = [&](int i, int s, const half8 b) {
+            uint32_t tw[8];
+            get_tw0(i % ND0, tw);
+            const int pn = lb ^ ((phys<LOG2M>((32 * (w + i * NW)) % S0) << 2) | (s * SB));
+            const f16v z = {};
+            const f16v d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, b, z, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const int qc = 4 * (v >> 2) + ((v & 3) >> 1);  // q = qc + 2h
+                lds(pn ^ (phys<LOG2M>(qc * S0) << 2)) = cmulh(pk(d[v], d[v + 1]), tw[v >> 1]);
+            }
+        };
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
             const int s = tile_sig(i);
-            if (NS == SIG || s < NS) {
-                uint32_t tw[8];
-                get_tw0(i % ND0, tw);
-                const int pn = lb ^ ((phys<LOG2M>((32 * (w + i * NW)) % S0) << 2) | (s * SB));
-                const half8 b = as_half8(op(i, 0), op(i, 1), op(i, 2), op(i, 3));
-                const f16v z = {};
-                const f16v d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, b, z, 0, 0, 0);
+            if (NS == SIG || s < NS) tile(i, s, as_half8(op(i, 0), op(i, 1), op(i, 2), op(i, 3)));
+        }
+        if constexpr (FILT) {
 #pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const int qc = 4 * (v >> 2) + ((v & 3) >> 1);  // q = qc + 2h
-                    lds(pn ^ (phys<LOG2M>(qc * S0) << 2)) = cmulh(pk(d[v], d[v + 1]), tw[v >> 1]);
-                }
-            }
+            for (int i = 0; i < T0W; ++i)
+                if (tile_sig(i) == 0) tile(i, SIG, as_half8(fop(i, 0), fop(i, 1), fop(i, 2), fop(i, 3)));
         }
         __syncthreads();
     }
@@ -805,7 +837,6 @@ struct Engine {
     __device__ void mid_pass(uint32_t pre = 0u) {
         constexpr int L = SH::L(P), S = L / 16;
         constexpr int NTL = NS * TPW, BT = NTL < SH::BD / 4 ? NTL : SH::BD / 4;
-        static_assert(NTL % BT == 0, "tiles split into equal batches");
         const int pb = opaque((phys<LOG2M>(base0<P>()) ^ phys<LOG2M>(2 * g * S)) << 2);
         uint32_t tw[4];
         get_twm(P - 1, tw);
@@ -818,10 +849,13 @@ struct Engine {
             uint32_t xb[BT][4];
 #pragma unroll
             for (int k = 0; k < BT; ++k)
+                if (b0 + k < NTL) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) xb[k][t] = lds(addr(b0 + k, t));
+                    for (int t = 0; t < 4; ++t) xb[k][t] = lds(addr(b0 + k, t));
+                }
 #pragma unroll
             for (int k = 0; k < BT; ++k) {
+                if (b0 + k >= NTL) break;
                 int a[4];
                 uint32_t x[4];
 #pragma unroll
@@ -1018,36 +1052,51 @@ struct Engine {
         }
     }
 
-    __device__ void filter(const float (&fin)[T0W][4]) {
+    __device__ __forceinline__ float filter_asum(const float (&fin)[T0W][4]) const {
         float asum = 0.f;
 #pragma unroll
         for (int i = 0; i < T0W; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) asum += fabsf(fin[i][e]);
-        asum = block_reduce<true>(asum);
+        return asum;
+    }
+    // input scale of the filter from the workgroup's sum |f|; sets cF
+    __device__ __forceinline__ float filter_scale(float asum) {
         int ef = 0;
         if (asum > 0.f) (void)frexpf(asum, &ef);
-        const float sf = ldexpf(1.f, 14 - ef);
         cF = ldexpf(1.f, -ef);
+        return ldexpf(1.f, 14 - ef);
+    }
+    // last pass of the filter transform (signal slot `s`): the spectrum into F
+    __device__ __forceinline__ void filter_last(int s) {
         constexpr float c = 1.0f / (16384.0f * R);
         const uint32_t ch = pk(c, -c);  // conjugate
-        pass0<1>([&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); });
-        fwd_middle<1, 1>();
         const int lb = opaque(lbase());
 #pragma unroll
         for (int slot = 0; slot < NLS; ++slot) {
             if (R >= 8 || slot < NSL) {
                 uint32_t y[NV];
-                last_fwd(lb ^ lpos(slot), y);
+                last_fwd((lb ^ lpos(slot)) + s * SB, y);
 #pragma unroll
                 for (int q = 0; q < NV; ++q) F[fslot(slot) + q] = pkmul(y[q], ch);
             }
         }
     }
+    // the filter on its own, in signal slot 0
+    __device__ void filter(const float (&fin)[T0W][4]) {
+        const float sf = filter_scale(block_reduce<true>(filter_asum(fin)));
+        auto fop = [&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); };
+        pass0<1>(fop, fop);
+        fwd_middle<1, 1>();
+        filter_last(0);
+    }
 
     // ---------------------------------------------------------- conv round
-    template <class OUT>
-    __device__ void conv_round(const OUT &out, int hb) {
+    // One round of SIG signals from pin.  FILT: the filter (fin) is
+    // transformed alongside, in slot SIG, and its spectrum taken into F
+    // before the products.  prefetch() is called once pin has been consumed.
+    template <bool FILT, class OUT, class PF>
+    __device__ void conv_round(const OUT &out, int hb, const float (&fin)[T0W][4], const PF &prefetch) {
         float amax;
         if constexpr (KIND == IN_F16) {
             h2 am = {(_Float16)0.f, (_Float16)0.f};
@@ -1064,12 +1113,23 @@ struct Engine {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) amax = fmaxf(amax, in_amax<KIND>(pin[i][e]));
         }
+        float sf = 0.f, am;
+        if constexpr (FILT) {
+            const f2 r = block_reduce_sm(filter_asum(fin), amax);
+            sf = filter_scale(r.x);
+            am = r.y;
+        } else {
+            am = block_reduce<false>(amax);
+        }
         // fp16 inputs are scaled in fp16, so the scale must be an fp16 power of two
-        const float su0 = pow2_scale(block_reduce<false>(amax), hb);
+        const float su0 = pow2_scale(am, hb);
         const float su = (KIND == IN_F16) ? fminf(su0, 16384.0f) : su0;
         const uint32_t suh = pk(su, su);
-        pass0<SIG>([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); });
-        fwd_middle<1, SIG>();
+        pass0<SIG, FILT>([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); },
+                         [&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); });
+        prefetch();
+        fwd_middle<1, SIG + (FILT ? 1 : 0)>();
+        if constexpr (FILT) filter_last(SIG);
         // Last pass, in place: forward DFT-R, product with the filter spectrum
         // (stored as conj(F) cF / R, so no product can overflow the inverse
         // DFT-R), inverse DFT-R on conjugated values.  The maximum of what it
@@ -1122,24 +1182,31 @@ struct Engine {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         float fin[T0W][4];
         filter_fetch(frs, d0, fin);
-        if constexpr (PREFETCH) fetch_raw(rows, 0, pnx);
-        filter(fin);
-        for (int r0 = 0; r0 < nsig; r0 += SIG) {
-            if constexpr (PREFETCH) {
-#pragma unroll
-                for (int i = 0; i < T0W; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pin[i][e] = pnx[i][e];
-                if (r0 + SIG < nsig) fetch_raw(rows, r0 + SIG, pnx);
-            } else {
-                fetch_raw(rows, r0, pin);
-            }
-            auto out = [&](int s, int n, int m, uint32_t hv) {
-                const RowBufs rb = rows(r0 + s);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, kNT);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, kNT);
-            };
-            conv_round(out, hb);
+        if constexpr (PREFETCH || SH::FUSEF) fetch_raw(rows, 0, pin);
+        // output of round r0: packed pair v of rows 2 (r0 + s), 2 (r0 + s) + 1
+        auto store = [&](int r0, int s, int n, int m, uint32_t hv) {
+            const RowBufs rb = rows(r0 + s);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, kNT);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, kNT);
+        };
+        // with PREFETCH, the next round's inputs are loaded into pin as soon
+        // as pass 0 has consumed this round's
+        auto prefetch = [&](int r0) {
+            if (PREFETCH && r0 + SIG < nsig) fetch_raw(rows, r0 + SIG, pin);
+        };
+        int r1 = 0;
+        if constexpr (SH::FUSEF) {
+            // first round with the filter alongside
+            conv_round<true>([&](int s, int n, int m, uint32_t hv) { store(0, s, n, m, hv); }, hb, fin,
+                             [&]() { prefetch(0); });
+            r1 = SIG;
+        } else {
+            filter(fin);
+        }
+        for (int r0 = r1; r0 < nsig; r0 += SIG) {
+            if (!PREFETCH && (!SH::FUSEF || r0 > 0)) fetch_raw(rows, r0, pin);
+            conv_round<false>([&](int s, int n, int m, uint32_t hv) { store(r0, s, n, m, hv); }, hb, fin,
+                              [&]() { prefetch(r0); });
         }
     }
 };
