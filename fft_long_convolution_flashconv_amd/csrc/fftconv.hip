@@ -143,17 +143,17 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
     const int h = blockIdx.x;
     const float *fh = f + (size_t)h * N;
     const float dh = D[h];
-    // bytes between batch rows; opaque, so that a signal's offset stays one
-    // short product (the compiler would otherwise refactor every row address
-    // into a full 64-bit multiply by N)
-    const uint64_t rsb = mf::opaque_u64(2ull * (uint64_t)H * (uint64_t)N);
+    // bytes between batch rows; every row offset of a launch fits 32 bits
+    // (the launcher splits larger batches), so a row's address is one 32-bit
+    // product and one 64-bit add
+    const uint32_t rsb = mf::opaque_u32(2u * (uint32_t)H * (uint32_t)N);
     const char *uh = (const char *)(u + (size_t)h * N);
     char *yh = (char *)(y + (size_t)h * N);
     const int hb = mf::half_bits(N);
     // complex signal `sig` = batch rows 2 sig (real part), 2 sig + 1
     // (imaginary); rows past B get empty resources
     auto rows = [&](int sig) -> mf::RowBufs {
-        const uint64_t o = (uint64_t)(uint32_t)sig * (2 * rsb);
+        const uint32_t o = (uint32_t)(2 * sig) * rsb;
         const int nb0 = (2 * sig < B) ? 2 * N : 0;
         const int nb1 = (2 * sig + 1 < B) ? 2 * N : 0;
         return {mf::row_rsrc(uh + o, nb0), mf::row_rsrc(uh + o + rsb, nb1), mf::row_rsrc(yh + o, nb0),
@@ -166,9 +166,21 @@ template <int LOG2M, int IO>
 static hipError_t launch_fc_mfma(const void *u, const float *f, const float *D, void *y, int B,
                                  int H, int N, hipStream_t s) {
     using T = typename io_elem<IO>::T;
-    hipLaunchKernelGGL((k_fft_conv_mfma<LOG2M, IO>), dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
-                       (const T *)u, f, D, (T *)y, B, H, N);
-    return hipGetLastError();
+    // Row byte offsets inside one launch are 32-bit, including the empty rows
+    // a last partial round addresses (up to 2 SIG + 2 past the batch): larger
+    // batches go in slices of an even number of rows.
+    const uint64_t rowb = 2ull * (uint64_t)H * (uint64_t)N;
+    const uint64_t pad = 2 * mf::Shape<LOG2M>::SIG + 2;
+    if ((pad + 2) * rowb >= (1ull << 32)) return hipErrorInvalidValue;
+    const int bmax = (int)std::min<uint64_t>((uint64_t)B, (((1ull << 32) - 1) / rowb - pad) & ~1ull);
+    for (int b0 = 0; b0 < B; b0 += bmax) {
+        const size_t o = (size_t)b0 * H * N;
+        hipLaunchKernelGGL((k_fft_conv_mfma<LOG2M, IO>), dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
+                           (const T *)u + o, f, D, (T *)y + o, std::min(bmax, B - b0), H, N);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int LOG2M, int IO>

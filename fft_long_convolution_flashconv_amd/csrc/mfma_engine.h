@@ -466,8 +466,8 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
-// opaque copy of a wave-uniform 64-bit value (kept in scalar registers)
-__device__ __forceinline__ uint64_t opaque_u64(uint64_t x) {
+// opaque copy of a wave-uniform value (kept in scalar registers)
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
     asm volatile("" : "+s"(x));
     return x;
 }
@@ -559,7 +559,9 @@ struct Engine {
         data = smem;
         red = (float *)(smem + SH::DATA);
         tid = threadIdx.x;
-        w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        // (masked so the compiler knows w < NW: with the launch's NT threads it
+        //  changes nothing, and tile-to-signal maps become compile-time)
+        w = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
         lane = tid & 63;
         j = lane & 15;
         g = lane >> 4;
