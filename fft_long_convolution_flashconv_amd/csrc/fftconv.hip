@@ -267,91 +267,142 @@ static hipError_t hm_dispatch(int log2m, const void *q, const void *k, const voi
 //   conv     z_T = (f_d * m_T)[:N] + D[d] m_T                  (fft conv, in ws)
 //   gate-out out[b, t, d] = q[b, t, d] * z_T[b, d, t]
 // The intermediates are bf16 (fp32 range, so no product can overflow them).
-// A block covers 64 channels x 64 steps of one batch row; thread (d, tg)
-// owns 16 consecutive steps of one channel, so channel-last accesses are
-// coalesced across the 64 channels of a wave and channel-major ones are
-// 32 contiguous bytes per thread.
-constexpr int HM_TD = 64, HM_TT = 64, HM_TR = 16;
+// Both gates transpose a tile of HM_TT steps x HM_TD channels of one batch
+// row through LDS, so every global access is 16 bytes per lane along the
+// contiguous dimension; the channel tile is the fastest grid index, so the
+// workgroups in flight together cover whole channel-last rows.  `vec` (set
+// by the launcher when N, Dm and the pointers allow 16-byte accesses) picks
+// the vector accesses; otherwise, and at ragged tile edges, they go element
+// by element.
+constexpr int HM_TT = 64, HM_TD = 128;
 
 template <int IO>
-__global__ __launch_bounds__(256) void k_h3_gate_in(const typename io_elem<IO>::T *__restrict__ k,
-                                                   const typename io_elem<IO>::T *__restrict__ v,
-                                                   const float *__restrict__ w, uint16_t *__restrict__ mT,
-                                                   int N, int Dm, int L) {
-    const int d = blockIdx.y * HM_TD + (threadIdx.x & 63);
-    const int t0 = blockIdx.x * HM_TT + (threadIdx.x >> 6) * HM_TR;
-    const int b = blockIdx.z;
-    if (d >= Dm || t0 >= N) return;
-    float wd[4];
+__device__ __forceinline__ float hm_f(uint16_t x) {
+    if constexpr (IO == IO_F16) return (float)__builtin_bit_cast(_Float16, x);
+    else return __uint_as_float((uint32_t)x << 16);
+}
+template <int IO>
+__device__ __forceinline__ uint16_t hm_h(float x) {
+    if constexpr (IO == IO_F16) return __builtin_bit_cast(uint16_t, (_Float16)x);
+    else return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// 8 consecutive 16-bit values at p (n of them valid), zero-filled
+__device__ __forceinline__ mf::u32x4 hm_load8(const uint16_t *p, int n, bool vec) {
+    if (vec && n >= 8) return *(const mf::u32x4 *)p;
+    uint16_t e[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wd[i] = (i < L) ? w[(size_t)d * L + i] : 0.f;
-    const size_t base = (size_t)b * N * Dm + d;
-    float kk[HM_TR + 3];
+    for (int i = 0; i < 8; ++i) e[i] = i < n ? p[i] : (uint16_t)0;
+    mf::u32x4 r;
 #pragma unroll
-    for (int r = 0; r < HM_TR + 3; ++r) {
-        const int t = t0 + r - 3;
-        kk[r] = (t >= 0 && t < N) ? ld_io<IO>(k + base + (size_t)t * Dm) : 0.f;
-    }
-    uint16_t mo[HM_TR];
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
+    return r;
+}
+__device__ __forceinline__ void hm_store8(uint16_t *p, int n, bool vec, const uint16_t (&e)[8]) {
+    if (vec && n >= 8) {
+        mf::u32x4 r;
 #pragma unroll
-    for (int r = 0; r < HM_TR; ++r) {
-        const int t = t0 + r;
-        float m = 0.f;
-        if (t < N) {
-            const float sh = fmaf(wd[0], kk[r + 3], fmaf(wd[1], kk[r + 2], fmaf(wd[2], kk[r + 1], wd[3] * kk[r])));
-            m = sh * ld_io<IO>(v + base + (size_t)t * Dm);
-        }
-        mo[r] = __builtin_bit_cast(uint16_t, (__bf16)m);
-    }
-    uint16_t *dst = mT + ((size_t)b * Dm + d) * N + t0;
-    if (t0 + HM_TR <= N && (N & 7) == 0) {
-        mf::u32x4 lo, hi;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            lo[q] = (uint32_t)mo[2 * q] | ((uint32_t)mo[2 * q + 1] << 16);
-            hi[q] = (uint32_t)mo[8 + 2 * q] | ((uint32_t)mo[8 + 2 * q + 1] << 16);
-        }
-        *(mf::u32x4 *)dst = lo;
-        *(mf::u32x4 *)(dst + 8) = hi;
+        for (int i = 0; i < 4; ++i) r[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
+        *(mf::u32x4 *)p = r;
     } else {
 #pragma unroll
-        for (int r = 0; r < HM_TR; ++r)
-            if (t0 + r < N) dst[r] = mo[r];
+        for (int i = 0; i < 8; ++i)
+            if (i < n) p[i] = e[i];
     }
 }
 
 template <int IO>
-__global__ __launch_bounds__(256) void k_h3_gate_out(const typename io_elem<IO>::T *__restrict__ q,
-                                                    const uint16_t *__restrict__ zT,
-                                                    typename io_elem<IO>::T *__restrict__ out, int N, int Dm) {
-    const int d = blockIdx.y * HM_TD + (threadIdx.x & 63);
-    const int t0 = blockIdx.x * HM_TT + (threadIdx.x >> 6) * HM_TR;
-    const int b = blockIdx.z;
-    if (d >= Dm || t0 >= N) return;
-    const uint16_t *src = zT + ((size_t)b * Dm + d) * N + t0;
-    float z[HM_TR];
-    if (t0 + HM_TR <= N && (N & 7) == 0) {
-        const mf::u32x4 lo = *(const mf::u32x4 *)src, hi = *(const mf::u32x4 *)(src + 8);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t a = lo[c], e = hi[c];
-            z[2 * c] = __uint_as_float(a << 16);
-            z[2 * c + 1] = __uint_as_float(a & 0xffff0000u);
-            z[8 + 2 * c] = __uint_as_float(e << 16);
-            z[8 + 2 * c + 1] = __uint_as_float(e & 0xffff0000u);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < HM_TR; ++r) z[r] = (t0 + r < N) ? __uint_as_float((uint32_t)src[r] << 16) : 0.f;
+__global__ __launch_bounds__(256) void k_h3_gate_in(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                                   const float *__restrict__ w, uint16_t *__restrict__ mT,
+                                                   int N, int Dm, int L, int vec) {
+    constexpr int PD = HM_TD + 8;  // LDS row stride (16-bit units), rows 16-byte aligned
+    __shared__ __attribute__((aligned(16))) uint16_t ks[(HM_TT + 3) * PD];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[HM_TT * PD];
+    const int tid = threadIdx.x;
+    const int d0 = blockIdx.x * HM_TD, t0 = blockIdx.y * HM_TT, b = blockIdx.z;
+    const uint16_t *kb = k + (size_t)b * N * Dm, *vb = v + (size_t)b * N * Dm;
+    // rows t0 - 3 .. t0 + TT - 1 of k (the short filter's history) and
+    // t0 .. t0 + TT - 1 of v, 16 chunks of 8 channels per row
+    for (int ci = tid; ci < (HM_TT + 3) * (HM_TD / 8); ci += 256) {
+        const int r = ci / (HM_TD / 8), c = ci % (HM_TD / 8);
+        const int t = t0 - 3 + r, d = d0 + 8 * c;
+        mf::u32x4 x = {0u, 0u, 0u, 0u};
+        if (t >= 0 && t < N && d < Dm) x = hm_load8(kb + (size_t)t * Dm + d, Dm - d, vec);
+        *(mf::u32x4 *)&ks[r * PD + 8 * c] = x;
     }
-    const size_t base = (size_t)b * N * Dm + d;
+    for (int ci = tid; ci < HM_TT * (HM_TD / 8); ci += 256) {
+        const int r = ci / (HM_TD / 8), c = ci % (HM_TD / 8);
+        const int t = t0 + r, d = d0 + 8 * c;
+        mf::u32x4 x = {0u, 0u, 0u, 0u};
+        if (t < N && d < Dm) x = hm_load8(vb + (size_t)t * Dm + d, Dm - d, vec);
+        *(mf::u32x4 *)&vs[r * PD + 8 * c] = x;
+    }
+    __syncthreads();
+    // thread: channel dl, steps 32 h .. 32 h + 31 of the tile
+    const int dl = tid % HM_TD, h = tid / HM_TD, d = d0 + dl;
+    if (d >= Dm) return;
+    float wd[4];
 #pragma unroll
-    for (int r = 0; r < HM_TR; ++r) {
-        const int t = t0 + r;
-        if (t < N) {
-            const size_t o = base + (size_t)t * Dm;
-            st_io<IO>(out + o, ld_io<IO>(q + o) * z[r]);
+    for (int i = 0; i < 4; ++i) wd[i] = (i < L) ? w[(size_t)d * L + i] : 0.f;
+    float k1 = hm_f<IO>(ks[(32 * h + 2) * PD + dl]), k2 = hm_f<IO>(ks[(32 * h + 1) * PD + dl]),
+          k3 = hm_f<IO>(ks[(32 * h) * PD + dl]);  // k at t - 1, t - 2, t - 3
+    uint16_t *dst = mT + ((size_t)b * Dm + d) * N + t0 + 32 * h;
+    const int nt = N - (t0 + 32 * h);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        uint16_t mo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int r = 32 * h + 8 * c + e;
+            const float k0 = hm_f<IO>(ks[(r + 3) * PD + dl]);
+            const float sh = fmaf(wd[0], k0, fmaf(wd[1], k1, fmaf(wd[2], k2, wd[3] * k3)));
+            mo[e] = __builtin_bit_cast(uint16_t, (__bf16)(sh * hm_f<IO>(vs[r * PD + dl])));
+            k3 = k2;
+            k2 = k1;
+            k1 = k0;
         }
+        if (nt - 8 * c > 0) hm_store8(dst + 8 * c, nt - 8 * c, vec, mo);
+    }
+}
+
+template <int IO>
+__global__ __launch_bounds__(256) void k_h3_gate_out(const uint16_t *__restrict__ q, const uint16_t *__restrict__ zT,
+                                                    uint16_t *__restrict__ out, int N, int Dm, int vec) {
+    constexpr int PZ = HM_TT + 1;  // odd row stride: the transposed reads spread over the banks
+    __shared__ uint16_t zs[HM_TD * PZ];
+    const int tid = threadIdx.x;
+    const int d0 = blockIdx.x * HM_TD, t0 = blockIdx.y * HM_TT, b = blockIdx.z;
+    // rows d0 .. d0 + TD - 1 of z_T, 8 chunks of 8 steps per row
+    for (int ci = tid; ci < HM_TD * (HM_TT / 8); ci += 256) {
+        const int r = ci / (HM_TT / 8), c = ci % (HM_TT / 8);
+        const int d = d0 + r, t = t0 + 8 * c;
+        mf::u32x4 x = {0u, 0u, 0u, 0u};
+        if (d < Dm && t < N) x = hm_load8(zT + ((size_t)b * Dm + d) * N + t, N - t, vec);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            zs[r * PZ + 8 * c + 2 * e] = (uint16_t)(x[e] & 0xffffu);
+            zs[r * PZ + 8 * c + 2 * e + 1] = (uint16_t)(x[e] >> 16);
+        }
+    }
+    __syncthreads();
+    // thread: 8 channels 8 c .. 8 c + 7, steps tl, tl + 16, ...
+    const int c = tid % (HM_TD / 8), d = d0 + 8 * c;
+    if (d >= Dm) return;
+    const uint16_t *qb = q + (size_t)b * N * Dm;
+    uint16_t *ob = out + (size_t)b * N * Dm;
+    for (int tl = tid / (HM_TD / 8); tl < HM_TT; tl += 256 / (HM_TD / 8)) {
+        const int t = t0 + tl;
+        if (t >= N) break;
+        const size_t o = (size_t)t * Dm + d;
+        const mf::u32x4 x = hm_load8(qb + o, Dm - d, vec);
+        uint16_t r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t qe = (uint16_t)((e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xffffu));
+            const float z = __uint_as_float((uint32_t)zs[(8 * c + e) * PZ + tl] << 16);
+            r[e] = hm_h<IO>(hm_f<IO>(qe) * z);
+        }
+        hm_store8(ob + o, Dm - d, vec, r);
     }
 }
 
@@ -367,14 +418,17 @@ static hipError_t hm_16bit(const void *q, const void *k, const void *v, const fl
     const size_t one = h3_mix_workspace(B, N, Dm) / 2;
     uint16_t *mT = (uint16_t *)ws;
     uint16_t *zT = (uint16_t *)((char *)ws + one);
-    const dim3 grid((N + HM_TT - 1) / HM_TT, (Dm + HM_TD - 1) / HM_TD, B);
-    hipLaunchKernelGGL((k_h3_gate_in<IO>), grid, dim3(256), 0, s, (const T *)k, (const T *)v, w, mT, N, Dm, L);
+    const dim3 grid((Dm + HM_TD - 1) / HM_TD, (N + HM_TT - 1) / HM_TT, B);
+    const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)ws;
+    const int vec = (N % 8 == 0 && Dm % 8 == 0 && (al & 15) == 0 && (one & 15) == 0) ? 1 : 0;
+    hipLaunchKernelGGL((k_h3_gate_in<IO>), grid, dim3(256), 0, s, (const uint16_t *)k, (const uint16_t *)v, w, mT,
+                       N, Dm, L, vec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = fc_dispatch<IO_BF16>(fused_log2m(N), mT, f, D, zT, B, Dm, N, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_h3_gate_out<IO>), grid, dim3(256), 0, s, (const T *)q, (const uint16_t *)zT, (T *)out,
-                       N, Dm);
+    hipLaunchKernelGGL((k_h3_gate_out<IO>), grid, dim3(256), 0, s, (const uint16_t *)q, (const uint16_t *)zT,
+                       (uint16_t *)out, N, Dm, vec);
     return hipGetLastError();
 }
 
