@@ -315,9 +315,15 @@ template <int IO>
 __global__ __launch_bounds__(256) void k_h3_gate_in(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
                                                    const float *__restrict__ w, uint16_t *__restrict__ mT,
                                                    int N, int Dm, int L, int vec) {
-    constexpr int PD = HM_TD + 8;  // LDS row stride (16-bit units), rows 16-byte aligned
+    // LDS row stride (16-bit units): rows 4-byte aligned, and 8 rows apart
+    // land 8 banks apart, so the reads below spread over the banks
+    constexpr int PD = HM_TD + 2;
     __shared__ __attribute__((aligned(16))) uint16_t ks[(HM_TT + 3) * PD];
     __shared__ __attribute__((aligned(16))) uint16_t vs[HM_TT * PD];
+    auto put = [&](uint16_t *row, const mf::u32x4 &x) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ((uint32_t *)row)[e] = x[e];
+    };
     const int tid = threadIdx.x;
     const int d0 = blockIdx.x * HM_TD, t0 = blockIdx.y * HM_TT, b = blockIdx.z;
     const uint16_t *kb = k + (size_t)b * N * Dm, *vb = v + (size_t)b * N * Dm;
@@ -328,32 +334,32 @@ __global__ __launch_bounds__(256) void k_h3_gate_in(const uint16_t *__restrict__
         const int t = t0 - 3 + r, d = d0 + 8 * c;
         mf::u32x4 x = {0u, 0u, 0u, 0u};
         if (t >= 0 && t < N && d < Dm) x = hm_load8(kb + (size_t)t * Dm + d, Dm - d, vec);
-        *(mf::u32x4 *)&ks[r * PD + 8 * c] = x;
+        put(&ks[r * PD + 8 * c], x);
     }
     for (int ci = tid; ci < HM_TT * (HM_TD / 8); ci += 256) {
         const int r = ci / (HM_TD / 8), c = ci % (HM_TD / 8);
         const int t = t0 + r, d = d0 + 8 * c;
         mf::u32x4 x = {0u, 0u, 0u, 0u};
         if (t < N && d < Dm) x = hm_load8(vb + (size_t)t * Dm + d, Dm - d, vec);
-        *(mf::u32x4 *)&vs[r * PD + 8 * c] = x;
+        put(&vs[r * PD + 8 * c], x);
     }
     __syncthreads();
-    // thread: channel dl, steps 32 h .. 32 h + 31 of the tile
-    const int dl = tid % HM_TD, h = tid / HM_TD, d = d0 + dl;
-    if (d >= Dm) return;
-    float wd[4];
+    // thread: steps 8 c .. 8 c + 7 of channel dl; the 8 lanes of a channel
+    // write one contiguous 128-byte run of its m_T row
+    const int c = tid % (HM_TT / 8);
+    for (int dl = tid / (HM_TT / 8); dl < HM_TD; dl += 256 / (HM_TT / 8)) {
+        const int d = d0 + dl;
+        if (d >= Dm) break;
+        float wd[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wd[i] = (i < L) ? w[(size_t)d * L + i] : 0.f;
-    float k1 = hm_f<IO>(ks[(32 * h + 2) * PD + dl]), k2 = hm_f<IO>(ks[(32 * h + 1) * PD + dl]),
-          k3 = hm_f<IO>(ks[(32 * h) * PD + dl]);  // k at t - 1, t - 2, t - 3
-    uint16_t *dst = mT + ((size_t)b * Dm + d) * N + t0 + 32 * h;
-    const int nt = N - (t0 + 32 * h);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+        for (int i = 0; i < 4; ++i) wd[i] = (i < L) ? w[(size_t)d * L + i] : 0.f;
+        // k at t - 1, t - 2, t - 3 for t = t0 + 8 c (tile row r + 3 holds step t0 + r)
+        float k1 = hm_f<IO>(ks[(8 * c + 2) * PD + dl]), k2 = hm_f<IO>(ks[(8 * c + 1) * PD + dl]),
+              k3 = hm_f<IO>(ks[(8 * c) * PD + dl]);
         uint16_t mo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int r = 32 * h + 8 * c + e;
+            const int r = 8 * c + e;
             const float k0 = hm_f<IO>(ks[(r + 3) * PD + dl]);
             const float sh = fmaf(wd[0], k0, fmaf(wd[1], k1, fmaf(wd[2], k2, wd[3] * k3)));
             mo[e] = __builtin_bit_cast(uint16_t, (__bf16)(sh * hm_f<IO>(vs[r * PD + dl])));
@@ -361,7 +367,8 @@ __global__ __launch_bounds__(256) void k_h3_gate_in(const uint16_t *__restrict__
             k2 = k1;
             k1 = k0;
         }
-        if (nt - 8 * c > 0) hm_store8(dst + 8 * c, nt - 8 * c, vec, mo);
+        const int nt = N - (t0 + 8 * c);
+        if (nt > 0) hm_store8(mT + ((size_t)b * Dm + d) * N + t0 + 8 * c, nt, vec, mo);
     }
 }
 
