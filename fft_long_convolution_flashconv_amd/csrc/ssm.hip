@@ -62,79 +62,106 @@ __device__ __forceinline__ void pow_run(double are, double aim, double n0, doubl
 
 // ---------------------------------------------------------------- filter
 
-constexpr int FILT_SEG = 8192;  // outputs per table segment (128 x 64)
+// One workgroup per channel, 8 waves.  With k = 64 i + l the filter is the
+// real part of a complex matrix product,
+//   f[64 i + l] = 2 sum_j Re(W[j][l] G[j][i]),  W[j][l] = w_j Abar_j^l,
+//   G[j][i] = Abar_j^(64 i)                    (w_j = C_j Bbar_j),
+// i.e. the real product of [Gr | Gi] (i x 2S) and [Wr ; -Wi] (2S x l), run on
+// the matrix cores in fp32 (16x16x4 products; K = 128 with modes j >= S
+// zeroed).  W is built once; G for 64 values of i at a time (4096 outputs).
+// LDS rows are 80 floats apart, so the four rows one operand read touches
+// fall 16 banks apart.
+constexpr int FILT_PR = 80;
 
-// One workgroup per channel.  LDS: WE[j][l] = w_j Abar_j^l (w_j = C_j Bbar_j),
-// G[j][i] = Abar_j^(seg + 64 i).  Each thread computes a 2 x 4 tile (two l,
-// four i) of outputs per step so a pair of table loads feeds several products.
-__global__ __launch_bounds__(256) void k_ssm_filter(const float *__restrict__ A,
+__global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
                                                    const float *__restrict__ Bm,
                                                    const float *__restrict__ C,
                                                    const float *__restrict__ dt,
                                                    const float *__restrict__ D, float *__restrict__ f,
                                                    int S, int64_t N, int64_t ldf) {
-    __shared__ cf WE[64][65];
-    __shared__ cf G[64][129];
-    const int tid = threadIdx.x;
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    __shared__ float Wr[64 * FILT_PR], Wn[64 * FILT_PR];  // W[j][l]: real part, minus imaginary part
+    __shared__ float Gr[64 * FILT_PR], Gi[64 * FILT_PR];  // G[j][i - i0]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int h = blockIdx.x;
     const double dth = (double)dt[h];
 
-    // WE table: runs of 16 powers per (mode, quarter)
-    for (int e = tid; e < S * 4; e += 256) {
+    // W: runs of 16 powers per (mode, quarter); modes j >= S are zero
+    for (int e = tid; e < 64 * 4; e += 512) {
         const int j = e >> 2, q = e & 3;
-        const float *a = A + ((size_t)h * S + j) * 2;
-        const float *b = Bm + ((size_t)h * S + j) * 2;
-        const float *c = C + ((size_t)h * S + j) * 2;
-        const cf w = cmul(mk(c[0], c[1]), mk((float)(dth * b[0]), (float)(dth * b[1])));
-        pow_run(dth * (double)a[0], dth * (double)a[1], 16.0 * q, 1.0, 16,
-                [&](int k, double pr, double pi) { WE[j][16 * q + k] = cmul(w, mk((float)pr, (float)pi)); });
-    }
-    for (int64_t seg = 0; seg < N; seg += FILT_SEG) {
-        const int nseg = (int)((N - seg < FILT_SEG) ? (N - seg) : FILT_SEG);
-        const int ni = (nseg + 63) / 64;
-        __syncthreads();
-        const int nr = (ni + 15) / 16;  // runs of 16 powers Abar^(seg + 64 i)
-        for (int e = tid; e < S * nr; e += 256) {
-            const int j = e / nr, q = e % nr;
+        if (j < S) {
             const float *a = A + ((size_t)h * S + j) * 2;
-            pow_run(dth * (double)a[0], dth * (double)a[1], (double)(seg + 1024 * q), 64.0, min(16, ni - 16 * q),
-                    [&](int k, double pr, double pi) { G[j][16 * q + k] = mk((float)pr, (float)pi); });
+            const float *b = Bm + ((size_t)h * S + j) * 2;
+            const float *c = C + ((size_t)h * S + j) * 2;
+            const cf wj = cmul(mk(c[0], c[1]), mk((float)(dth * b[0]), (float)(dth * b[1])));
+            pow_run(dth * (double)a[0], dth * (double)a[1], 16.0 * q, 1.0, 16, [&](int k, double pr, double pi) {
+                const cf v = cmul(wj, mk((float)pr, (float)pi));
+                Wr[j * FILT_PR + 16 * q + k] = v.x;
+                Wn[j * FILT_PR + 16 * q + k] = -v.y;
+            });
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) Wr[j * FILT_PR + 16 * q + k] = Wn[j * FILT_PR + 16 * q + k] = 0.f;
+        }
+    }
+    const int64_t ntot = (N + 63) / 64;  // values of i
+    // this wave's output tiles: i in [16 (w / 2), +16), l-tiles 2 (w % 2) + {0, 1}
+    const int it = w >> 1, lt0 = 2 * (w & 1);
+    for (int64_t i0 = 0; i0 < ntot; i0 += 64) {
+        __syncthreads();  // the previous block of G has been read
+        for (int e = tid; e < 64 * 4; e += 512) {
+            const int j = e >> 2, q = e & 3;
+            if (j < S) {
+                const float *a = A + ((size_t)h * S + j) * 2;
+                pow_run(dth * (double)a[0], dth * (double)a[1], (double)(64 * (i0 + 16 * q)), 64.0, 16,
+                        [&](int k, double pr, double pi) {
+                            Gr[j * FILT_PR + 16 * q + k] = (float)pr;
+                            Gi[j * FILT_PR + 16 * q + k] = (float)pi;
+                        });
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) Gr[j * FILT_PR + 16 * q + k] = Gi[j * FILT_PR + 16 * q + k] = 0.f;
+            }
         }
         __syncthreads();
-        // tiles: l in {2 lp, 2 lp + 1}, i in {4 ip .. 4 ip + 3}
-        const int ntile = 32 * ((ni + 3) / 4);
-        for (int t = tid; t < ntile; t += 256) {
-            const int lp = t & 31, ip = t >> 5;
-            float acc[2][4] = {};
-            for (int j = 0; j < S; ++j) {
-                const cf e0 = WE[j][2 * lp], e1 = WE[j][2 * lp + 1];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int i = 4 * ip + q;
-                    const cf g = G[j][i < ni ? i : 0];
-                    acc[0][q] = fmaf(e0.x, g.x, fmaf(-e0.y, g.y, acc[0][q]));
-                    acc[1][q] = fmaf(e1.x, g.x, fmaf(-e1.y, g.y, acc[1][q]));
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int k = 64 * (4 * ip + q) + 2 * lp + r;
-                    if (k < nseg) {
-                        float v = 2.f * acc[r][q];
-                        if (D != nullptr && seg + k == 0) v += D[h];
-                        f[(size_t)h * ldf + seg + k] = v;
-                    }
-                }
-            }
+        // out[i][l] over K = 128 in steps of 4: lane holds A[i = lane % 16][k = lane / 16]
+        // and B[k = lane / 16][l = lane % 16]
+        f4v acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const int col = lane & 15, kr = lane >> 4;
+#pragma unroll 8
+        for (int k0 = 0; k0 < 64; k0 += 4) {
+            const int j = k0 + kr;
+            const float ar = Gr[j * FILT_PR + 16 * it + col];
+            const float b0 = Wr[j * FILT_PR + 16 * lt0 + col], b1 = Wr[j * FILT_PR + 16 * (lt0 + 1) + col];
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar, b0, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(ar, b1, acc[1], 0, 0, 0);
         }
+#pragma unroll 8
+        for (int k0 = 0; k0 < 64; k0 += 4) {
+            const int j = k0 + kr;
+            const float ai = Gi[j * FILT_PR + 16 * it + col];
+            const float b0 = Wn[j * FILT_PR + 16 * lt0 + col], b1 = Wn[j * FILT_PR + 16 * (lt0 + 1) + col];
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(ai, b0, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(ai, b1, acc[1], 0, 0, 0);
+        }
+        // accumulator v of tile t: i = i0 + 16 it + 4 (lane / 16) + v, l = 16 (lt0 + t) + lane % 16
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t k = 64 * (i0 + 16 * it + 4 * kr + v) + 16 * (lt0 + t) + col;
+                if (k < N) {
+                    float val = 2.f * acc[t][v];
+                    if (D != nullptr && k == 0) val += D[h];
+                    f[(size_t)h * ldf + k] = val;
+                }
+            }
     }
 }
 
 hipError_t launch_ssm_filter(const float *A, const float *Bm, const float *C, const float *dt,
                              float *f, int H, int S, int64_t N, hipStream_t s) {
-    hipLaunchKernelGGL(k_ssm_filter, dim3(H), dim3(256), 0, s, A, Bm, C, dt, (const float *)nullptr,
+    hipLaunchKernelGGL(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, (const float *)nullptr,
                        f, S, N, N);
     return hipGetLastError();
 }
@@ -732,7 +759,7 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
     cf *sc = (cf *)(w + L.sc);
     const int C_ = (int)(N / T), T2 = T / 64;
 
-    hipLaunchKernelGGL(k_ssm_filter, dim3(H), dim3(256), 0, s, A, Bm, C, dt, D, fT, S, (int64_t)T,
+    hipLaunchKernelGGL(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, S, (int64_t)T,
                        (int64_t)T);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
