@@ -477,13 +477,15 @@ __device__ __forceinline__ float sp_wave_max(float v) {
 //      by a power of two into fp16 range);
 //   2. contribution: wave w owns modes 16w .. 16w+15 (Et row tiles 2w, 2w+1)
 //      and all column tiles, so its Et operands stay in registers;
-//   3. correction with the state carried into the chunk: the operand X is
-//      built once in LDS, wave w owns output rows l = 16w .. 16w+15 (its Rt
-//      operands stay in registers), and y is updated in place;
+//   3. correction with the state carried into the chunk,
+//        y[64 i + l] += 2 Re sum_j (C_j Abar_j^(l+1) x_j) Abar_j^(64 i):
+//      the power table G = Abar^(64 i) is the B operand, built once in LDS;
+//      wave w owns output rows l = 16w .. 16w+15 and scales its Rt operands
+//      (in registers) by the state, and y is updated in place;
 //   4. x <- Abar^T x + s.
 // The next chunk's activations are loaded while the current one is used.
 constexpr int SP_USTR = 72;   // staged chunk: 64 samples per row i, padded (bank spread)
-constexpr int SP_XSTR = 136;  // X operand: 128 (mode, part) entries per column i, padded
+constexpr int SP_XSTR = 136;  // G operand: 128 (mode, part) entries per column i, padded
 
 template <int IO>
 __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>::T *__restrict__ u,
@@ -511,6 +513,13 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
         pxs[e] = Px[(size_t)h * 512 + e];
     }
     for (int e = tid; e < 64 * 16; e += 256) qxs[e] = Qx[(size_t)h * 1024 + e];
+    __syncthreads();
+    // G[(j, part)][i] = Abar_j^(64 i) as fp16 (|G| <= 1 for stable modes)
+    for (int e = tid; e < 64 * T2; e += 256) {
+        const int j = e & 63, i = e >> 6;
+        const cf X = cmul(pxs[j * 8 + (i >> 4)], qxs[j * 16 + (i & 15)]);
+        *(uint32_t *)(xs + i * SP_XSTR + 2 * j) = pk(X.x, X.y);
+    }
     if (tid < 64) {
         cf x = mk(0.f, 0.f);
         if (x_in && tid < S) x = mk(x_in[(orow * S + tid) * 2], x_in[(orow * S + tid) * 2 + 1]);
@@ -536,6 +545,21 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
     for (int ks = 0; ks < 4; ++ks)
         Ra[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Rh + (16 * w + il) * 128 + 32 * ks + 8 * g));
     const cf aTj = (tid < 64) ? aT[(size_t)h * 64 + tid] : mk(0.f, 0.f);
+    // max |Rt entry| < 2^er over the workgroup (sets the state scale below)
+    __shared__ float rmax[4];
+    int er = 0;
+    {
+        float m = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)Ra[ks][e]));
+        m = sp_wave_max(m);
+        if (lane == 0) rmax[w] = m;
+        __syncthreads();
+        m = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
+        if (m > 0.f) (void)frexpf(m, &er);
+    }
     // chunk loads: T / 8 groups of 8 activations (at most 4 per thread), and
     // the 4 outputs per column tile this lane corrects (read-modify-write)
     const int nq = T >> 3;
@@ -598,18 +622,31 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) ycur[ct] = ypre[ct];
         if (c + 1 < C) load_chunk(c + 1);
-        // correction operand X = Abar^(64 i) x sx, from the state carried in
+        // correction operand: this wave's Rt rows times the state carried in,
+        // (2 Re R, -2 Im R) (x) -> (2 Re (R x), -2 Im (R x)), with x scaled by
+        // sx = 2^(14 - e - er), max |x| < 2^e, so every product stays below 2^14
         const float xm = xmax;
         const bool corr = xm > 0.f;
         float sx = 1.f;
+        half8 Rx[4];
         if (corr) {
             int ex = 0;
             (void)frexpf(xm, &ex);
-            sx = ldexpf(1.f, 14 - ex);  // |X| <= |x| sx < 2^14 for stable modes
-            for (int e = tid; e < 64 * T2; e += 256) {
-                const int j = e & 63, i = e >> 6;
-                const cf X = cscale(cmul(cmul(pxs[j * 8 + (i >> 4)], qxs[j * 16 + (i & 15)]), xst[j]), sx);
-                *(uint32_t *)(xs + i * SP_XSTR + 2 * j) = pk(X.x, X.y);
+            sx = ldexpf(1.f, 14 - ex - er);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x4 r4 = __builtin_bit_cast(u32x4, Ra[ks]);
+                uint32_t o4[4] = {r4.x, r4.y, r4.z, r4.w}, xc[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const cf x = xst[16 * ks + 4 * g + q];  // mode of slot pair q
+                    xc[q] = pk(x.x * sx, -x.y * sx);
+                }
+                // (a + i b) conj(x sx) with (a, b) = (2 Re R, -2 Im R); the
+                // results are matrix-core operands (the helper ends with the
+                // wait states that needs)
+                cmulh_n(o4, xc);
+                Rx[ks] = __builtin_bit_cast(half8, u32x4{o4[0], o4[1], o4[2], o4[3]});
             }
         }
         __syncthreads();
@@ -665,7 +702,7 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
                 for (int ks = 0; ks < 4; ++ks) {
                     const u32x4 z4 = {0u, 0u, 0u, 0u};
                     const u32x4 v = (i < T2) ? *(const u32x4 *)(xs + i * SP_XSTR + 32 * ks + 8 * g) : z4;
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ra[ks], __builtin_bit_cast(half8, v), d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Rx[ks], __builtin_bit_cast(half8, v), d, 0, 0, 0);
                 }
                 if (i < T2) {
                     T_ *p = yr + 64 * i + 16 * w + 4 * g;
