@@ -408,10 +408,15 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
     const int h = blockIdx.x;
     const double dth = (double)dt[h];
     const int T2 = T / 64, NCT = (T2 + 15) / 16, TL = T2 < 16 ? T2 : 16;
-    uint16_t *Eh = Et + (size_t)h * 128 * 64;
-    uint16_t *Rh = Rt + (size_t)h * 64 * 128;
+    // Et and Rt are built in LDS and written out with 16-byte stores.  The
+    // lanes of a wave take 64 modes of one run, so the runs' different code
+    // paths never diverge within a wave; Et rows are padded to 66 entries so
+    // those lanes' writes spread over the banks.
+    constexpr int EST = 66;
+    __shared__ __attribute__((aligned(16))) uint16_t Eh[128 * EST];
+    __shared__ __attribute__((aligned(16))) uint16_t Rh[64 * 128];
     for (int e = threadIdx.x; e < 64 * 8; e += 256) {
-        const int j = e >> 3, run = e & 7;
+        const int j = e & 63, run = e >> 6;
         const bool on = j < S;
         double are = 0.0, aim = 0.0, br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
         if (on) {
@@ -429,8 +434,8 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
             pr *= on_d;
             pi *= on_d;
             if (p <= 63) {
-                Eh[(2 * j) * 64 + (63 - p)] = f16bits(pr);
-                Eh[(2 * j + 1) * 64 + (63 - p)] = f16bits(pi);
+                Eh[(2 * j) * EST + (63 - p)] = f16bits(pr);
+                Eh[(2 * j + 1) * EST + (63 - p)] = f16bits(pi);
             }
             if (p >= 1) {
                 const int l = p - 1;
@@ -462,6 +467,14 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
             if (on) apow64(are, aim, (double)T, pr, pi);
             aT[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
         }
+    }
+    __syncthreads();
+    using u32x4 = mf::u32x4;
+    u32x4 *eo = (u32x4 *)(Et + (size_t)h * 128 * 64), *ro = (u32x4 *)(Rt + (size_t)h * 64 * 128);
+    for (int e = threadIdx.x; e < 128 * 64 / 8; e += 256) {
+        const uint32_t *er = (const uint32_t *)(Eh + (e >> 3) * EST + 8 * (e & 7));
+        eo[e] = u32x4{er[0], er[1], er[2], er[3]};
+        ro[e] = ((const u32x4 *)Rh)[e];
     }
 }
 
