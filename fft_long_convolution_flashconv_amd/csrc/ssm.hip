@@ -485,23 +485,26 @@ __device__ __forceinline__ float sp_wave_max(float v) {
 }
 
 // Both projections of one (batch row b, channel h), walking its chunks in
-// order and carrying the state in LDS.  Four waves; for each chunk c:
+// order and carrying the state in LDS.  Eight waves; for each chunk c (the
+// correction goes first, so that its stores are issued before the next
+// chunk's loads and are long complete when those are waited for):
 //   1. the chunk's activations are staged in LDS as fp16 (bf16 inputs scaled
 //      by a power of two into fp16 range);
-//   2. contribution: wave w owns modes 16w .. 16w+15 (Et row tiles 2w, 2w+1)
-//      and all column tiles, so its Et operands stay in registers;
+//   2. contribution: wave w owns modes 8w .. 8w+7 (Et row tile w) and all
+//      column tiles, so its Et operands stay in registers;
 //   3. correction with the state carried into the chunk,
 //        y[64 i + l] += 2 Re sum_j (C_j Abar_j^(l+1) x_j) Abar_j^(64 i):
 //      the power table G = Abar^(64 i) is the B operand, built once in LDS;
-//      wave w owns output rows l = 16w .. 16w+15 and scales its Rt operands
-//      (in registers) by the state, and y is updated in place;
+//      wave w owns output rows l = 16 (w % 4) .. +15 and column tiles
+//      4 (w / 4) .. +3, scales its Rt operands (in registers) by the state,
+//      and updates y in place;
 //   4. x <- Abar^T x + s.
 // The next chunk's activations are loaded while the current one is used.
 constexpr int SP_USTR = 72;   // staged chunk: 64 samples per row i, padded (bank spread)
 constexpr int SP_XSTR = 136;  // G operand: 128 (mode, part) entries per column i, padded
 
 template <int IO>
-__global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>::T *__restrict__ u,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_sp_proj_mfma(const typename io_elem<IO>::T *__restrict__ u,
                                                      typename io_elem<IO>::T *__restrict__ y,
                                                      const uint16_t *__restrict__ Et,
                                                      const uint16_t *__restrict__ Rt,
@@ -511,24 +514,30 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
                                                      float *__restrict__ x_out, int H, int64_t N, int S, int T) {
     using namespace mf;
     using T_ = typename io_elem<IO>::T;
+    constexpr int NWV = 8;
     const int h = blockIdx.x, b = blockIdx.y;
     const int C = (int)(N / T), T2 = T >> 6, NCT = (T2 + 15) >> 4;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, il = lane & 15, g = lane >> 4;
+    const int lr = w & 3, ch = w >> 2;  // correction rows 16 lr .., column tiles 4 ch ..
     __shared__ __attribute__((aligned(16))) uint16_t us[128 * SP_USTR];
     __shared__ __attribute__((aligned(16))) uint16_t xs[128 * SP_XSTR];
     __shared__ cf pcs[64 * 8], pxs[64 * 8], qxs[64 * 16];
     __shared__ cf xst[64], sst[64];
-    __shared__ float red[4], xmax;
+    __shared__ float red[NWV], rmax[NWV], xmax;
     const size_t orow = (size_t)b * H + h;
     // tables and the initial state
-    for (int e = tid; e < 64 * 8; e += 256) {
+    for (int e = tid; e < 64 * 8; e += 512) {
         pcs[e] = Pc[(size_t)h * 512 + e];
         pxs[e] = Px[(size_t)h * 512 + e];
     }
-    for (int e = tid; e < 64 * 16; e += 256) qxs[e] = Qx[(size_t)h * 1024 + e];
+    for (int e = tid; e < 64 * 16; e += 512) qxs[e] = Qx[(size_t)h * 1024 + e];
+    // rows i >= T2 of both operands stay zero, so the column-tile loops need
+    // no tests (the tables are zero past the chunk's tiles as well)
+    for (int e = tid; e < 128 * SP_USTR / 8; e += 512) ((u32x4 *)us)[e] = u32x4{0u, 0u, 0u, 0u};
+    for (int e = tid; e < 128 * SP_XSTR / 8; e += 512) ((u32x4 *)xs)[e] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     // G[(j, part)][i] = Abar_j^(64 i) as fp16 (|G| <= 1 for stable modes)
-    for (int e = tid; e < 64 * T2; e += 256) {
+    for (int e = tid; e < 64 * T2; e += 512) {
         const int j = e & 63, i = e >> 6;
         const cf X = cmul(pxs[j * 8 + (i >> 4)], qxs[j * 16 + (i & 15)]);
         *(uint32_t *)(xs + i * SP_XSTR + 2 * j) = pk(X.x, X.y);
@@ -542,24 +551,17 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
     }
     // matrix operands in registers
     const uint16_t *Eh = Et + (size_t)h * 128 * 64, *Rh = Rt + (size_t)h * 64 * 128;
-    half8 Ea[2][2], Ra[4];
-    cf qc[2][2];
+    half8 Ea[2], Ra[4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int rt = 2 * w + r;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            Ea[r][ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Eh + (16 * rt + il) * 64 + 32 * ks + 8 * g));
-        const int j0 = 8 * rt + 2 * g;
-        qc[r][0] = Qc[((size_t)h * 64 + j0) * 16 + il];
-        qc[r][1] = Qc[((size_t)h * 64 + j0 + 1) * 16 + il];
-    }
+    for (int ks = 0; ks < 2; ++ks)
+        Ea[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Eh + (16 * w + il) * 64 + 32 * ks + 8 * g));
+    const int j0 = 8 * w + 2 * g;  // modes of this lane's accumulator pairs: j0, j0 + 1
+    const cf qc0 = Qc[((size_t)h * 64 + j0) * 16 + il], qc1 = Qc[((size_t)h * 64 + j0 + 1) * 16 + il];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-        Ra[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Rh + (16 * w + il) * 128 + 32 * ks + 8 * g));
+        Ra[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Rh + (16 * lr + il) * 128 + 32 * ks + 8 * g));
     const cf aTj = (tid < 64) ? aT[(size_t)h * 64 + tid] : mk(0.f, 0.f);
     // max |Rt entry| < 2^er over the workgroup (sets the state scale below)
-    __shared__ float rmax[4];
     int er = 0;
     {
         float m = 0.f;
@@ -570,26 +572,28 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
         m = sp_wave_max(m);
         if (lane == 0) rmax[w] = m;
         __syncthreads();
-        m = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
+        m = 0.f;
+#pragma unroll
+        for (int k = 0; k < NWV; ++k) m = fmaxf(m, rmax[k]);
         if (m > 0.f) (void)frexpf(m, &er);
     }
-    // chunk loads: T / 8 groups of 8 activations (at most 4 per thread), and
-    // the 4 outputs per column tile this lane corrects (read-modify-write)
+    // chunk loads: T / 8 groups of 8 activations (at most 2 per thread), and
+    // the 4 outputs per column tile this lane corrects (read-modify-write).
     const int nq = T >> 3;
-    u32x4 pre[4];
-    u32x2 ypre[8];
+    u32x4 pre[2];
+    u32x2 ypre[4];
     auto load_chunk = [&](int c) {
         const T_ *src = u + orow * N + (size_t)c * T;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int q = tid + 256 * k;
+        for (int k = 0; k < 2; ++k) {
+            const int q = tid + 512 * k;
             if (q < nq) pre[k] = *(const u32x4 *)(src + 8 * q);
         }
         const T_ *yr = y + orow * N + (size_t)c * T;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int i = 16 * ct + il;
-            if (ct < NCT && i < T2) ypre[ct] = *(const u32x2 *)(yr + 64 * i + 16 * w + 4 * g);
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int ct = 4 * ch + c4, i = 16 * ct + il;
+            if (ct < NCT && i < T2) ypre[c4] = *(const u32x2 *)(yr + 64 * i + 16 * lr + 4 * g);
         }
     };
     load_chunk(0);
@@ -600,8 +604,8 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
         if constexpr (IO == IO_BF16) {
             float m = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (tid + 256 * k < nq) {
+            for (int k = 0; k < 2; ++k)
+                if (tid + 512 * k < nq) {
                     const uint32_t d4[4] = {pre[k].x, pre[k].y, pre[k].z, pre[k].w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -610,14 +614,16 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
             m = sp_wave_max(m);
             if (lane == 0) red[w] = m;
             __syncthreads();
-            m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            m = 0.f;
+#pragma unroll
+            for (int k = 0; k < NWV; ++k) m = fmaxf(m, red[k]);
             int ex = 0;
             if (m > 0.f) (void)frexpf(m, &ex);
             su = ldexpf(1.f, 14 - ex);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int q = tid + 256 * k;
+        for (int k = 0; k < 2; ++k) {
+            const int q = tid + 512 * k;
             if (q < nq) {
                 u32x4 v = pre[k];
                 if constexpr (IO == IO_BF16) {
@@ -631,10 +637,14 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
                 *(u32x4 *)(us + (q >> 3) * SP_USTR + 8 * (q & 7)) = v;
             }
         }
-        u32x2 ycur[8];
+        // (taken into registers of their own here, at the top of the pass,
+        //  so that no later use waits behind the stores issued meanwhile)
+        u32x2 ycur[4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) ycur[ct] = ypre[ct];
-        if (c + 1 < C) load_chunk(c + 1);
+        for (int c4 = 0; c4 < 4; ++c4) {
+            ycur[c4] = ypre[c4];
+            asm volatile("" : "+v"(ycur[c4]));
+        }
         // correction operand: this wave's Rt rows times the state carried in,
         // (2 Re R, -2 Im R) (x) -> (2 Re (R x), -2 Im (R x)), with x scaled by
         // sx = 2^(14 - e - er), max |x| < 2^e, so every product stays below 2^14
@@ -663,73 +673,66 @@ __global__ __launch_bounds__(256) void k_sp_proj_mfma(const typename io_elem<IO>
             }
         }
         __syncthreads();
-        // 2. contribution
-        cf acc[2][2] = {{mk(0.f, 0.f), mk(0.f, 0.f)}, {mk(0.f, 0.f), mk(0.f, 0.f)}};
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int i = 16 * ct + il;
-            half8 Bop[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 z4 = {0u, 0u, 0u, 0u};
-                const u32x4 v = (i < T2) ? *(const u32x4 *)(us + i * SP_USTR + 32 * ks + 8 * g) : z4;
-                Bop[ks] = __builtin_bit_cast(half8, v);
-            }
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const f4 z = {0.f, 0.f, 0.f, 0.f};
-                f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ea[r][0], Bop[0], z, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ea[r][1], Bop[1], d, 0, 0, 0);
-                const int j0 = 8 * (2 * w + r) + 2 * g;
-                acc[r][0] = cadd(acc[r][0], cmul(pcs[j0 * 8 + ct], cmul(qc[r][0], mk(d[0], d[1]))));
-                acc[r][1] = cadd(acc[r][1], cmul(pcs[(j0 + 1) * 8 + ct], cmul(qc[r][1], mk(d[2], d[3]))));
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    acc[r][q].x += __shfl_xor(acc[r][q].x, o, 64);
-                    acc[r][q].y += __shfl_xor(acc[r][q].y, o, 64);
-                }
-        if (il == 0) {
-            const float inv = 1.0f / su;
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int j0 = 8 * (2 * w + r) + 2 * g;
-                sst[j0] = cscale(acc[r][0], inv);
-                sst[j0 + 1] = cscale(acc[r][1], inv);
-            }
-        }
-        // 3. correction: y += 2 Re(C Abar^(t+1) x), rows l = 16 w + 4 g + v
+        // 3. correction: y += 2 Re(C Abar^(t+1) x), rows l = 16 lr + 4 g + v
         if (corr) {
             const float inv = 1.0f / sx;
             T_ *yr = y + orow * N + (size_t)c * T;
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-                if (ct >= NCT) break;
-                const int i = 16 * ct + il;
-                f4 d = {0.f, 0.f, 0.f, 0.f};
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const int ct = 4 * ch + c4, i = 16 * ct + il;
+                {
+                    f4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const u32x4 z4 = {0u, 0u, 0u, 0u};
-                    const u32x4 v = (i < T2) ? *(const u32x4 *)(xs + i * SP_XSTR + 32 * ks + 8 * g) : z4;
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Rx[ks], __builtin_bit_cast(half8, v), d, 0, 0, 0);
-                }
-                if (i < T2) {
-                    T_ *p = yr + 64 * i + 16 * w + 4 * g;
-                    const uint32_t y01 = ycur[ct].x, y23 = ycur[ct].y;
-                    const T_ *yv = (const T_ *)&y01;
-                    const T_ *yw = (const T_ *)&y23;
-                    T_ o[4];
-                    o[0] = yv[0]; o[1] = yv[1]; o[2] = yw[0]; o[3] = yw[1];
+                    for (int ks = 0; ks < 4; ++ks)
+                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            Rx[ks], __builtin_bit_cast(half8, *(const u32x4 *)(xs + i * SP_XSTR + 32 * ks + 8 * g)), d, 0, 0, 0);
+                    if (i < T2) {
+                        T_ *p = yr + 64 * i + 16 * lr + 4 * g;
+                        const uint32_t y01 = ycur[c4].x, y23 = ycur[c4].y;
+                        const T_ *yv = (const T_ *)&y01;
+                        const T_ *yw = (const T_ *)&y23;
+                        T_ o[4];
+                        o[0] = yv[0]; o[1] = yv[1]; o[2] = yw[0]; o[3] = yw[1];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) st_io<IO>(o + v, ld_io<IO>(o + v) + d[v] * inv);
-                    const uint32_t a = *(const uint32_t *)&o[0], bb = *(const uint32_t *)&o[2];
-                    *(u32x2 *)p = u32x2{a, bb};
+                        for (int v = 0; v < 4; ++v) st_io<IO>(o + v, ld_io<IO>(o + v) + d[v] * inv);
+                        const uint32_t a = *(const uint32_t *)&o[0], bb = *(const uint32_t *)&o[2];
+                        *(u32x2 *)p = u32x2{a, bb};
+                    }
                 }
             }
+        }
+        // next chunk's loads (unconditional, the last pass reloading its own
+        // chunk: in a branch of their own they end up after the last barrier)
+        load_chunk(c + 1 < C ? c + 1 : c);
+        // 2. contribution (column tiles unrolled, so their reads and products
+        //    overlap; the per-lane factor qc is applied once at the end)
+        cf acc0 = mk(0.f, 0.f), acc1 = mk(0.f, 0.f);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const int i = 16 * ct + il;
+            half8 Bop[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                Bop[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(us + i * SP_USTR + 32 * ks + 8 * g));
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
+            f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ea[0], Bop[0], z, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ea[1], Bop[1], d, 0, 0, 0);
+            acc0 = cadd(acc0, cmul(pcs[j0 * 8 + ct], mk(d[0], d[1])));
+            acc1 = cadd(acc1, cmul(pcs[(j0 + 1) * 8 + ct], mk(d[2], d[3])));
+        }
+        acc0 = cmul(qc0, acc0);
+        acc1 = cmul(qc1, acc1);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            acc0.x += __shfl_xor(acc0.x, o, 64);
+            acc0.y += __shfl_xor(acc0.y, o, 64);
+            acc1.x += __shfl_xor(acc1.x, o, 64);
+            acc1.y += __shfl_xor(acc1.y, o, 64);
+        }
+        if (il == 0) {
+            const float inv = 1.0f / su;
+            sst[j0] = cscale(acc0, inv);
+            sst[j0 + 1] = cscale(acc1, inv);
         }
         __syncthreads();
         // 4. carry the state
@@ -834,7 +837,7 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
     }
     if (e != hipSuccess) return e;
     if constexpr (IO != IO_F32) {
-        hipLaunchKernelGGL((k_sp_proj_mfma<IO>), dim3(H, B), dim3(256), 0, s, (const T_ *)u, (T_ *)y,
+        hipLaunchKernelGGL((k_sp_proj_mfma<IO>), dim3(H, B), dim3(512), 0, s, (const T_ *)u, (T_ *)y,
                            (const uint16_t *)(w + L.Et), (const uint16_t *)(w + L.Rt), (const cf *)(w + L.Pc),
                            (const cf *)(w + L.Qc), (const cf *)(w + L.Px), (const cf *)(w + L.Qx),
                            (const cf *)(w + L.aT), x_in, x_out, H, N, S, T);
