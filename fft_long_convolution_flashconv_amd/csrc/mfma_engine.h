@@ -545,7 +545,11 @@ struct Engine {
     half4 A8;                               // DFT-8: 16x16x16
     uint32_t tw0[TWREG ? ND0 : 1][8];       // pass-0 twiddles (when held in registers)
     uint32_t tu0[TWREG ? NDI : 1][4];       // inverse pass-0 twiddles
-    uint32_t twm[TWREG ? KM : 1][4];        // middle-pass twiddles
+    // middle-pass twiddles: always in registers (4 K dwords; each is used by
+    // a forward and an inverse pass, and a table load at a pass's start
+    // would put its latency on the critical path)
+    static constexpr bool MIDREG = true;
+    uint32_t twm[KM][4];
     uint32_t F[FN];                         // filter spectrum * cF (packed fp16)
     float cF;
     // Inputs of the next round are fetched during the current one, unless
@@ -599,6 +603,8 @@ struct Engine {
                 const u32x4 a = tq(SH::Q_TU + d);
                 tu0[d][0] = a.x; tu0[d][1] = a.y; tu0[d][2] = a.z; tu0[d][3] = a.w;
             }
+        }
+        if constexpr (MIDREG) {
 #pragma unroll
             for (int p = 0; p < K; ++p) {
                 const u32x4 a = tq(SH::Q_MID + p);
@@ -628,7 +634,7 @@ struct Engine {
         }
     }
     __device__ __forceinline__ void get_twm(int p, uint32_t (&t)[4]) const {
-        if constexpr (TWREG) {
+        if constexpr (MIDREG) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) t[c] = twm[p][c];
         } else {
