@@ -72,7 +72,7 @@ def profiled_traffic(workload: str):
     text = open(path).read()
     m_hash = re.search(r"kernel source hash: `([0-9a-f]+)`", text)
     m_wl = re.search(r"workload: `([a-z0-9_]+)`", text)
-    m_tr = re.search(r"traffic per launch: ([0-9]+) bytes", text)
+    m_tr = re.search(r"traffic per launch(?: of `[^`]*`)?: ([0-9]+) bytes", text)
     if not (m_hash and m_wl and m_tr) or m_wl.group(1) != workload or m_hash.group(1) != kernel_source_hash():
         return None
     return int(m_tr.group(1))
