@@ -512,6 +512,16 @@ __device__ __forceinline__ uint32_t in_scaled(const typename InT<KIND>::T &x, fl
 // is read or written once), so they do not displace the tables and filters
 // in L2 and leave no dirty lines in it for the end of the kernel to write back.
 constexpr int kNT = 2;
+
+// Wave priorities (s_setprio).  The instruction arbiter otherwise favours
+// the oldest waves, so the workgroups sharing a compute unit run one after
+// the other: the last one works alone at the end, too few waves to keep the
+// unit busy.  A wave runs at kPrioLoad from its start (or the start of a
+// round) until pass 0 has consumed the round's inputs, then at kPrioWork:
+// a younger workgroup gets its loads out and its first pass done ahead of
+// the older ones' later passes, and the workgroups of a unit stay closer
+// together.
+constexpr int kPrioLoad = 3, kPrioWork = 2;
 struct RowBufs {
     __amdgpu_buffer_rsrc_t in0, in1, out0, out1;
 };
@@ -1105,6 +1115,7 @@ struct Engine {
     // before the products.  prefetch() is called once pin has been consumed.
     template <bool FILT, class OUT, class PF>
     __device__ void conv_round(const OUT &out, int hb, const float (&fin)[T0W][4], const PF &prefetch) {
+        __builtin_amdgcn_s_setprio(kPrioLoad);
         float amax;
         if constexpr (KIND == IN_F16) {
             h2 am = {(_Float16)0.f, (_Float16)0.f};
@@ -1136,6 +1147,7 @@ struct Engine {
         pass0<SIG, FILT>([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); },
                          [&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); });
         prefetch();
+        __builtin_amdgcn_s_setprio(kPrioWork);
         fwd_middle<1, SIG + (FILT ? 1 : 0)>();
         if constexpr (FILT) filter_last(SIG);
         // Last pass, in place: forward DFT-R, product with the filter spectrum
@@ -1189,6 +1201,7 @@ struct Engine {
     __device__ void run_raw(__amdgpu_buffer_rsrc_t frs, float d0, const RB &rows, int nsig, int hb) {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         float fin[T0W][4];
+        __builtin_amdgcn_s_setprio(kPrioLoad);
         filter_fetch(frs, d0, fin);
         if constexpr (PREFETCH || SH::FUSEF) fetch_raw(rows, 0, pin);
         // output of round r0: packed pair v of rows 2 (r0 + s), 2 (r0 + s) + 1
@@ -1212,6 +1225,7 @@ struct Engine {
             filter(fin);
         }
         for (int r0 = r1; r0 < nsig; r0 += SIG) {
+            __builtin_amdgcn_s_setprio(kPrioLoad);
             if (!PREFETCH && (!SH::FUSEF || r0 > 0)) fetch_raw(rows, r0, pin);
             conv_round<false>([&](int s, int n, int m, uint32_t hv) { store(r0, s, n, m, hv); }, hb, fin,
                               [&]() { prefetch(r0); });
