@@ -44,22 +44,6 @@ __device__ __forceinline__ cf abar_pow(double are, double aim, double n) {
     return mk((float)re, (float)im);
 }
 
-// Runs of powers Abar^(n0 + k step), k < cnt: the first power and the step
-// are exact fp64 exponentials, the rest fp64 complex products (relative error
-// grows by ~1e-16 per step, so a run of <= 17 stays far below fp32 rounding).
-template <class EMIT>
-__device__ __forceinline__ void pow_run(double are, double aim, double n0, double step, int cnt, const EMIT &emit) {
-    double pr, pi, sr, si;
-    apow64(are, aim, n0, pr, pi);
-    apow64(are, aim, step, sr, si);
-    for (int k = 0; k < cnt; ++k) {
-        emit(k, pr, pi);
-        const double t = pr * sr - pi * si;
-        pi = pr * si + pi * sr;
-        pr = t;
-    }
-}
-
 // ---------------------------------------------------------------- filter
 
 // One workgroup per channel, 8 waves.  With k = 64 i + l the filter is the
@@ -69,9 +53,10 @@ __device__ __forceinline__ void pow_run(double are, double aim, double n0, doubl
 // i.e. the real product of [Gr | Gi] (i x 2S) and [Wr ; -Wi] (2S x l), run on
 // the matrix cores in fp32 (16x16x4 products; K = 128 with modes j >= S
 // zeroed).  W is built once; G for 64 values of i at a time (4096 outputs).
-// LDS rows are 80 floats apart, so the four rows one operand read touches
-// fall 16 banks apart.
-constexpr int FILT_PR = 80;
+// LDS rows are 72 floats apart, so the four rows one operand read touches
+// fall 8 banks apart and the 64 lanes of a read cover every bank twice (and
+// two workgroups of 8 waves fit a compute unit).
+constexpr int FILT_PR = 72;
 
 __global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
                                                    const float *__restrict__ Bm,
@@ -85,20 +70,40 @@ __global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int h = blockIdx.x;
     const double dth = (double)dt[h];
+    // The fp64 exponentials per mode, one wave each: Abar^1, Abar^16,
+    // Abar^64, Abar^1024.  Every run below starts from products of these
+    // (a handful of fp64 complex products: relative error ~1e-16 each).
+    __shared__ double2 pw[4][64];
+    if (w < 4) {
+        constexpr double kPow[4] = {1.0, 16.0, 64.0, 1024.0};
+        double re = 0.0, im = 0.0;
+        if (lane < S) {
+            const float *a = A + ((size_t)h * S + lane) * 2;
+            apow64(dth * (double)a[0], dth * (double)a[1], kPow[w], re, im);
+        }
+        pw[w][lane] = double2{re, im};
+    }
+    __syncthreads();
+    auto dmul = [](double2 x, double2 y) { return double2{x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x}; };
 
-    // W: runs of 16 powers per (mode, quarter); modes j >= S are zero
+    // W: runs of 16 powers per (mode, quarter) from Abar^(16 q), step Abar;
+    // modes j >= S are zero
     for (int e = tid; e < 64 * 4; e += 512) {
         const int j = e >> 2, q = e & 3;
         if (j < S) {
-            const float *a = A + ((size_t)h * S + j) * 2;
             const float *b = Bm + ((size_t)h * S + j) * 2;
             const float *c = C + ((size_t)h * S + j) * 2;
             const cf wj = cmul(mk(c[0], c[1]), mk((float)(dth * b[0]), (float)(dth * b[1])));
-            pow_run(dth * (double)a[0], dth * (double)a[1], 16.0 * q, 1.0, 16, [&](int k, double pr, double pi) {
-                const cf v = cmul(wj, mk((float)pr, (float)pi));
+            double2 p = double2{1.0, 0.0};
+            for (int r = 0; r < q; ++r) p = dmul(p, pw[1][j]);
+            const double2 st = pw[0][j];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const cf v = cmul(wj, mk((float)p.x, (float)p.y));
                 Wr[j * FILT_PR + 16 * q + k] = v.x;
                 Wn[j * FILT_PR + 16 * q + k] = -v.y;
-            });
+                p = dmul(p, st);
+            }
         } else {
 #pragma unroll
             for (int k = 0; k < 16; ++k) Wr[j * FILT_PR + 16 * q + k] = Wn[j * FILT_PR + 16 * q + k] = 0.f;
@@ -107,17 +112,30 @@ __global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
     const int64_t ntot = (N + 63) / 64;  // values of i
     // this wave's output tiles: i in [16 (w / 2), +16), l-tiles 2 (w % 2) + {0, 1}
     const int it = w >> 1, lt0 = 2 * (w & 1);
+    // G run (j, q) of the block at i0 starts at Abar^(64 (i0 + 16 q)): from
+    // (Abar^1024)^q, advanced by Abar^4096 from one block to the next
+    // (threads e < 256 keep their run across the blocks)
+    double2 gs = double2{1.0, 0.0}, gadv = double2{1.0, 0.0}, gst = double2{1.0, 0.0};
+    if (tid < 256 && (tid >> 2) < S) {
+        const int j = tid >> 2, q = tid & 3;
+        for (int r = 0; r < q; ++r) gs = dmul(gs, pw[3][j]);
+        gadv = dmul(pw[3][j], pw[3][j]);
+        gadv = dmul(gadv, gadv);
+        gst = pw[2][j];
+    }
     for (int64_t i0 = 0; i0 < ntot; i0 += 64) {
         __syncthreads();  // the previous block of G has been read
         for (int e = tid; e < 64 * 4; e += 512) {
             const int j = e >> 2, q = e & 3;
             if (j < S) {
-                const float *a = A + ((size_t)h * S + j) * 2;
-                pow_run(dth * (double)a[0], dth * (double)a[1], (double)(64 * (i0 + 16 * q)), 64.0, 16,
-                        [&](int k, double pr, double pi) {
-                            Gr[j * FILT_PR + 16 * q + k] = (float)pr;
-                            Gi[j * FILT_PR + 16 * q + k] = (float)pi;
-                        });
+                double2 p = gs;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    Gr[j * FILT_PR + 16 * q + k] = (float)p.x;
+                    Gi[j * FILT_PR + 16 * q + k] = (float)p.y;
+                    p = dmul(p, gst);
+                }
+                gs = dmul(gs, gadv);
             } else {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) Gr[j * FILT_PR + 16 * q + k] = Gi[j * FILT_PR + 16 * q + k] = 0.f;
@@ -392,7 +410,9 @@ __global__ __launch_bounds__(256) void k_sp_correct(typename io_elem<IO>::T *__r
 
 __device__ __forceinline__ uint16_t f16bits(double x) { return __builtin_bit_cast(uint16_t, (_Float16)(float)x); }
 
-// One workgroup per channel; eight runs of powers per mode (the modes past S
+// One workgroup per channel.  Each wave first takes one fp64 exponential per
+// mode (Abar^1, Abar^16, Abar^64, Abar^1024); every power below is a short
+// product of these.  Then eight runs of powers per mode (the modes past S
 // are written as zeros):
 //   runs 0..3  Abar^p, p = 16 q .. 16 q + 15 -> Et (l = 63 - p), Rt (l = p - 1)
 //   run 4      Abar^64                      -> Rt (l = 63)
@@ -415,14 +435,32 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
     constexpr int EST = 66;
     __shared__ __attribute__((aligned(16))) uint16_t Eh[128 * EST];
     __shared__ __attribute__((aligned(16))) uint16_t Rh[64 * 128];
+    __shared__ double2 pw[4][64];
+    {
+        constexpr double kPow[4] = {1.0, 16.0, 64.0, 1024.0};
+        const int w = threadIdx.x >> 6, j = threadIdx.x & 63;
+        double re = 0.0, im = 0.0;
+        if (j < S) {
+            const size_t o = ((size_t)h * S + j) * 2;
+            apow64(dth * (double)A[o], dth * (double)A[o + 1], kPow[w], re, im);
+        }
+        pw[w][j] = double2{re, im};
+    }
+    __syncthreads();
+    auto dmul = [](double2 x, double2 y) { return double2{x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x}; };
+    // cnt powers st^k times p, k < cnt
+    auto run_ = [&](double2 p, double2 st, int cnt, auto &&emit) {
+        for (int k = 0; k < cnt; ++k) {
+            emit(k, p.x, p.y);
+            p = dmul(p, st);
+        }
+    };
     for (int e = threadIdx.x; e < 64 * 8; e += 256) {
         const int j = e & 63, run = e >> 6;
         const bool on = j < S;
-        double are = 0.0, aim = 0.0, br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
+        double br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
         if (on) {
             const size_t o = ((size_t)h * S + j) * 2;
-            are = dth * (double)A[o];
-            aim = dth * (double)A[o + 1];
             br = dth * (double)Bm[o];
             bi = dth * (double)Bm[o + 1];
             cr = (double)Cc[o];
@@ -444,28 +482,32 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
                 Rh[l * 128 + 2 * j + 1] = f16bits(-2.0 * zi);
             }
         };
+        const double2 one = double2{1.0, 0.0};
         if (run < 4) {
-            pow_run(are, aim, 16.0 * run, 1.0, 16, [&](int k, double pr, double pi) { et_rt(16 * run + k, pr, pi); });
+            double2 p = one;
+            for (int r = 0; r < run; ++r) p = dmul(p, pw[1][j]);
+            run_(p, pw[0][j], 16, [&](int k, double pr, double pi) { et_rt(16 * run + k, pr, pi); });
         } else if (run == 4) {
-            pow_run(are, aim, 64.0, 1.0, 1, [&](int, double pr, double pi) { et_rt(64, pr, pi); });
+            et_rt(64, pw[2][j].x, pw[2][j].y);
         } else if (run == 5) {
-            pow_run(are, aim, 0.0, 64.0, 16, [&](int k, double pr, double pi) {
+            run_(one, pw[2][j], 16, [&](int k, double pr, double pi) {
                 const bool ok = on && k < TL;
                 const cf v = ok ? mk((float)pr, (float)pi) : mk(0.f, 0.f);
                 Qx[((size_t)h * 64 + j) * 16 + k] = v;
                 Qc[((size_t)h * 64 + j) * 16 + (k < TL ? TL - 1 - k : k)] = v;
             });
         } else if (run == 6) {
-            pow_run(are, aim, 0.0, 1024.0, 8, [&](int k, double pr, double pi) {
+            run_(one, pw[3][j], 8, [&](int k, double pr, double pi) {
                 const bool ok = on && k < NCT;
                 Px[((size_t)h * 64 + j) * 8 + k] = ok ? mk((float)pr, (float)pi) : mk(0.f, 0.f);
                 Pc[((size_t)h * 64 + j) * 8 + (k < NCT ? NCT - 1 - k : k)] =
                     ok ? mk((float)(br * pr - bi * pi), (float)(br * pi + bi * pr)) : mk(0.f, 0.f);
             });
         } else {
-            double pr = 0.0, pi = 0.0;
-            if (on) apow64(are, aim, (double)T, pr, pi);
-            aT[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
+            // Abar^T, T = 64 2^m: squarings of Abar^64
+            double2 p = pw[2][j];
+            for (int t = 64; t < T; t <<= 1) p = dmul(p, p);
+            aT[(size_t)h * 64 + j] = on ? mk((float)p.x, (float)p.y) : mk(0.f, 0.f);
         }
     }
     __syncthreads();
