@@ -57,23 +57,20 @@ __device__ __forceinline__ cf abar_pow(double are, double aim, double n) {
 // fall 8 banks apart and the 64 lanes of a read cover every bank twice (and
 // two workgroups of 8 waves fit a compute unit).
 constexpr int FILT_PR = 72;
+constexpr int FILT_LDS = 4 * 64 * FILT_PR;  // floats: Wr, Wn, Gr, Gi
 
-__global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
-                                                   const float *__restrict__ Bm,
-                                                   const float *__restrict__ C,
-                                                   const float *__restrict__ dt,
-                                                   const float *__restrict__ D, float *__restrict__ f,
-                                                   int S, int64_t N, int64_t ldf) {
-    typedef float f4v __attribute__((ext_vector_type(4)));
-    __shared__ float Wr[64 * FILT_PR], Wn[64 * FILT_PR];  // W[j][l]: real part, minus imaginary part
-    __shared__ float Gr[64 * FILT_PR], Gi[64 * FILT_PR];  // G[j][i - i0]
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int h = blockIdx.x;
-    const double dth = (double)dt[h];
-    // The fp64 exponentials per mode, one wave each: Abar^1, Abar^16,
-    // Abar^64, Abar^1024.  Every run below starts from products of these
-    // (a handful of fp64 complex products: relative error ~1e-16 each).
-    __shared__ double2 pw[4][64];
+__device__ __forceinline__ double2 dmul(double2 x, double2 y) {
+    return double2{x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x};
+}
+
+// The fp64 exponentials per mode of channel h, one wave each (waves 0..3):
+// pw[0..3][j] = Abar_j^1, ^16, ^64, ^1024 (zero for j >= S).  Every power
+// the filter and the state-passing tables use is a short product of these
+// (a handful of fp64 complex products: relative error ~1e-16 each).  The
+// caller synchronises before reading pw.
+__device__ __forceinline__ void ssm_powers(const float *__restrict__ A, double dth, int S, int h,
+                                           double2 (*pw)[64]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (w < 4) {
         constexpr double kPow[4] = {1.0, 16.0, 64.0, 1024.0};
         double re = 0.0, im = 0.0;
@@ -83,8 +80,17 @@ __global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
         }
         pw[w][lane] = double2{re, im};
     }
-    __syncthreads();
-    auto dmul = [](double2 x, double2 y) { return double2{x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x}; };
+}
+
+// The filter of channel h (512 threads) from its powers pw; lds holds
+// FILT_LDS floats.
+__device__ __forceinline__ void ssm_filter_body(const float *__restrict__ Bm, const float *__restrict__ C, double dth,
+                                const float *__restrict__ D, float *__restrict__ f, int S, int64_t N, int64_t ldf,
+                                int h, const double2 (*pw)[64], float *lds) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    float *const Wr = lds, *const Wn = lds + 64 * FILT_PR;  // W[j][l]: real part, minus imaginary part
+    float *const Gr = lds + 2 * 64 * FILT_PR, *const Gi = lds + 3 * 64 * FILT_PR;  // G[j][i - i0]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
     // W: runs of 16 powers per (mode, quarter) from Abar^(16 q), step Abar;
     // modes j >= S are zero
@@ -175,6 +181,21 @@ __global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
                 }
             }
     }
+}
+
+__global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
+                                                   const float *__restrict__ Bm,
+                                                   const float *__restrict__ C,
+                                                   const float *__restrict__ dt,
+                                                   const float *__restrict__ D, float *__restrict__ f,
+                                                   int S, int64_t N, int64_t ldf) {
+    __shared__ float lds[FILT_LDS];
+    __shared__ double2 pw[4][64];
+    const int h = blockIdx.x;
+    const double dth = (double)dt[h];
+    ssm_powers(A, dth, S, h, pw);
+    __syncthreads();
+    ssm_filter_body(Bm, C, dth, D, f, S, N, ldf, h, pw, lds);
 }
 
 hipError_t launch_ssm_filter(const float *A, const float *Bm, const float *C, const float *dt,
@@ -410,44 +431,29 @@ __global__ __launch_bounds__(256) void k_sp_correct(typename io_elem<IO>::T *__r
 
 __device__ __forceinline__ uint16_t f16bits(double x) { return __builtin_bit_cast(uint16_t, (_Float16)(float)x); }
 
-// One workgroup per channel.  Each wave first takes one fp64 exponential per
-// mode (Abar^1, Abar^16, Abar^64, Abar^1024); every power below is a short
-// product of these.  Then eight runs of powers per mode (the modes past S
-// are written as zeros):
+// The tables of channel h from its powers pw (ssm_powers), by the workgroup's
+// NT threads: eight runs of powers per mode (the modes past S are written as
+// zeros):
 //   runs 0..3  Abar^p, p = 16 q .. 16 q + 15 -> Et (l = 63 - p), Rt (l = p - 1)
 //   run 4      Abar^64                      -> Rt (l = 63)
 //   run 5      Abar^(64 k), k < 16         -> Qx[k], Qc[TL - 1 - k]
 //   run 6      Abar^(1024 k), k < 8        -> Px[k], Pc[NCT - 1 - k] (times Bbar)
 //   run 7      Abar^T                      -> aT
-__global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict__ A, const float *__restrict__ Bm,
-                                                       const float *__restrict__ Cc, const float *__restrict__ dt,
-                                                       uint16_t *__restrict__ Et, uint16_t *__restrict__ Rt,
-                                                       cf *__restrict__ Pc, cf *__restrict__ Qc,
-                                                       cf *__restrict__ Px, cf *__restrict__ Qx,
-                                                       cf *__restrict__ aT, int S, int T) {
-    const int h = blockIdx.x;
-    const double dth = (double)dt[h];
+constexpr int SP_EST = 66;                                // Et row stride in LDS (16-bit units)
+constexpr int SP_TAB_LDS = 128 * SP_EST * 2 + 64 * 128 * 2;  // bytes: Et, then Rt
+
+template <int NT>
+__device__ __forceinline__ void sp_tables_body(const float *__restrict__ Bm, const float *__restrict__ Cc, double dth,
+                               uint16_t *__restrict__ Et, uint16_t *__restrict__ Rt, cf *__restrict__ Pc,
+                               cf *__restrict__ Qc, cf *__restrict__ Px, cf *__restrict__ Qx, cf *__restrict__ aT,
+                               int S, int T, int h, const double2 (*pw)[64], uint16_t *lds) {
     const int T2 = T / 64, NCT = (T2 + 15) / 16, TL = T2 < 16 ? T2 : 16;
     // Et and Rt are built in LDS and written out with 16-byte stores.  The
     // lanes of a wave take 64 modes of one run, so the runs' different code
     // paths never diverge within a wave; Et rows are padded to 66 entries so
     // those lanes' writes spread over the banks.
-    constexpr int EST = 66;
-    __shared__ __attribute__((aligned(16))) uint16_t Eh[128 * EST];
-    __shared__ __attribute__((aligned(16))) uint16_t Rh[64 * 128];
-    __shared__ double2 pw[4][64];
-    {
-        constexpr double kPow[4] = {1.0, 16.0, 64.0, 1024.0};
-        const int w = threadIdx.x >> 6, j = threadIdx.x & 63;
-        double re = 0.0, im = 0.0;
-        if (j < S) {
-            const size_t o = ((size_t)h * S + j) * 2;
-            apow64(dth * (double)A[o], dth * (double)A[o + 1], kPow[w], re, im);
-        }
-        pw[w][j] = double2{re, im};
-    }
-    __syncthreads();
-    auto dmul = [](double2 x, double2 y) { return double2{x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x}; };
+    constexpr int EST = SP_EST;
+    uint16_t *const Eh = lds, *const Rh = lds + 128 * EST;
     // cnt powers st^k times p, k < cnt
     auto run_ = [&](double2 p, double2 st, int cnt, auto &&emit) {
         for (int k = 0; k < cnt; ++k) {
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
             p = dmul(p, st);
         }
     };
-    for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+    for (int e = threadIdx.x; e < 64 * 8; e += NT) {
         const int j = e & 63, run = e >> 6;
         const bool on = j < S;
         double br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
@@ -513,11 +519,32 @@ __global__ __launch_bounds__(256) void k_sp_tables_mfma(const float *__restrict_
     __syncthreads();
     using u32x4 = mf::u32x4;
     u32x4 *eo = (u32x4 *)(Et + (size_t)h * 128 * 64), *ro = (u32x4 *)(Rt + (size_t)h * 64 * 128);
-    for (int e = threadIdx.x; e < 128 * 64 / 8; e += 256) {
+    for (int e = threadIdx.x; e < 128 * 64 / 8; e += NT) {
         const uint32_t *er = (const uint32_t *)(Eh + (e >> 3) * EST + 8 * (e & 7));
         eo[e] = u32x4{er[0], er[1], er[2], er[3]};
         ro[e] = ((const u32x4 *)Rh)[e];
     }
+}
+
+// The per-channel parameters of the 16-bit state passing in one launch, one
+// workgroup of 8 waves per channel: the powers, the chunk filter (with D
+// folded into tap 0) and then, in the same LDS, the projection tables.
+__global__ __launch_bounds__(512) void k_sp_params(const float *__restrict__ A, const float *__restrict__ Bm,
+                                                  const float *__restrict__ Cc, const float *__restrict__ dt,
+                                                  const float *__restrict__ D, float *__restrict__ fT,
+                                                  uint16_t *__restrict__ Et, uint16_t *__restrict__ Rt,
+                                                  cf *__restrict__ Pc, cf *__restrict__ Qc, cf *__restrict__ Px,
+                                                  cf *__restrict__ Qx, cf *__restrict__ aT, int S, int T) {
+    static_assert(SP_TAB_LDS <= FILT_LDS * 4, "the tables fit the filter's LDS");
+    __shared__ __attribute__((aligned(16))) float lds[FILT_LDS];
+    __shared__ double2 pw[4][64];
+    const int h = blockIdx.x;
+    const double dth = (double)dt[h];
+    ssm_powers(A, dth, S, h, pw);
+    __syncthreads();
+    ssm_filter_body(Bm, Cc, dth, D, fT, S, (int64_t)T, (int64_t)T, h, pw, lds);
+    __syncthreads();  // (the filter's operands have been read)
+    sp_tables_body<512>(Bm, Cc, dth, Et, Rt, Pc, Qc, Px, Qx, aT, S, T, h, pw, (uint16_t *)lds);
 }
 
 __device__ __forceinline__ float sp_wave_max(float v) {
@@ -854,15 +881,15 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
     cf *sc = (cf *)(w + L.sc);
     const int C_ = (int)(N / T), T2 = T / 64;
 
-    hipLaunchKernelGGL(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, S, (int64_t)T,
-                       (int64_t)T);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
     if constexpr (IO != IO_F32) {
-        hipLaunchKernelGGL(k_sp_tables_mfma, dim3(H), dim3(256), 0, s, A, Bm, C, dt, (uint16_t *)(w + L.Et),
+        hipLaunchKernelGGL(k_sp_params, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, (uint16_t *)(w + L.Et),
                            (uint16_t *)(w + L.Rt), (cf *)(w + L.Pc), (cf *)(w + L.Qc), (cf *)(w + L.Px),
                            (cf *)(w + L.Qx), (cf *)(w + L.aT), S, T);
     } else {
+        hipLaunchKernelGGL(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, S, (int64_t)T,
+                           (int64_t)T);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(k_sp_tables, dim3(H), dim3(256), 0, s, A, dt, E, G, S, T2);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
