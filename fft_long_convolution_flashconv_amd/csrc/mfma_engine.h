@@ -516,8 +516,9 @@ constexpr int kNT = 2;
 // Wave priorities (s_setprio).  The instruction arbiter otherwise favours
 // the oldest waves, so the workgroups sharing a compute unit run one after
 // the other: the last one works alone at the end, too few waves to keep the
-// unit busy.  A wave runs at kPrioLoad from its start (or the start of a
-// round) until pass 0 has consumed the round's inputs, then at kPrioWork:
+// unit busy.  A wave runs at kPrioLoad from its start (through the filter
+// transform, where that comes first) or the start of a round until pass 0
+// has consumed the round's inputs, then at kPrioWork:
 // a younger workgroup gets its loads out and its first pass done ahead of
 // the older ones' later passes, and the workgroups of a unit stay closer
 // together.
