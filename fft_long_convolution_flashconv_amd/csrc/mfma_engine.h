@@ -352,8 +352,9 @@ struct Shape {
     // a signal slot of its own, when that slot fits the LDS budget of OCC
     // workgroups per compute unit (160 KiB); otherwise it is transformed on
     // its own first, in the signals' slots.
-    static constexpr bool FUSEF = ((SIG + 1) * M + 64) * 4 * OCC <= 160 * 1024;
-    static constexpr int DATA = (SIG + (FUSEF ? 1 : 0)) * M;
+    static constexpr int PAD = 16;                     // dwords after each signal slot
+    static constexpr bool FUSEF = ((SIG + 1) * (M + PAD) + 64) * 4 * OCC <= 160 * 1024;
+    static constexpr int DATA = (SIG + (FUSEF ? 1 : 0)) * (M + PAD);
     static constexpr int LDS_DWORDS = DATA + 64;
     static constexpr int DELTA = 256 * NW;             // butterfly-base step between a wave's tiles
     // distinct column offsets a thread meets in pass 0 (32-column tiles) and
@@ -698,7 +699,12 @@ struct Engine {
     // into the instruction's offset field.
     template <class V = uint32_t>
     __device__ __forceinline__ V &lds(int b) { return *(V *)((char *)data + b); }
-    static constexpr int SB = M * 4;  // bytes per signal
+    // Bytes per signal slot: M points and PAD more dwords, so that the same
+    // point of two slots falls in different banks (the compiler merges such
+    // pairs of reads into one two-address instruction, whose two dwords a
+    // power-of-two slot stride would put in one bank).  The slot offset is
+    // added after every XOR of the swizzle.
+    static constexpr int SB = (M + SH::PAD) * 4;
 
     // ---------------------------------------------------------- pass 0
     // Tile i of this wave covers columns c = 32 (w + i NW) + lane%32 of
@@ -742,13 +748,13 @@ struct Engine {
         auto tile = [&](int i, int s, const half8 b) {
             uint32_t tw[8];
             get_tw0(i % ND0, tw);
-            const int pn = lb ^ ((phys<LOG2M>((32 * (w + i * NW)) % S0) << 2) | (s * SB));
+            const int pn = lb ^ (phys<LOG2M>((32 * (w + i * NW)) % S0) << 2);
             const f16v z = {};
             const f16v d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, b, z, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; v += 2) {
                 const int qc = 4 * (v >> 2) + ((v & 3) >> 1);  // q = qc + 2h
-                lds(pn ^ (phys<LOG2M>(qc * S0) << 2)) = cmulh(pk(d[v], d[v + 1]), tw[v >> 1]);
+                lds((pn ^ (phys<LOG2M>(qc * S0) << 2)) + s * SB) = cmulh(pk(d[v], d[v + 1]), tw[v >> 1]);
             }
         };
 #pragma unroll
@@ -806,9 +812,9 @@ struct Engine {
                 const int i = i0 + k;
                 const int s = (16 * (w + i * NW)) / S0;
                 const int n0 = (16 * (w + i * NW)) % S0;
-                const int pn = lb ^ ((phys<LOG2M>(n0) << 2) | (s * SB));
+                const int pn = lb ^ (phys<LOG2M>(n0) << 2);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) xb[k][t] = lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2));
+                for (int t = 0; t < 4; ++t) xb[k][t] = lds((pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2)) + s * SB);
             }
 #pragma unroll
             for (int k = 0; k < BI; ++k) {
