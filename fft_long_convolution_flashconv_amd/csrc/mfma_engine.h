@@ -292,13 +292,15 @@ __device__ __forceinline__ float habs_max(uint32_t v) {
 
 // Shared-memory index swizzle for packed-complex dwords, per transform size:
 // bit p >= 6 of an index, when set, flips the bits kSwz[LOG2M][p - 6] among
-// bits 1..5, so strided operand gathers and the contiguous last-pass groups
-// spread over the banks (masks chosen by a search over this engine's access
-// patterns against 32- and 64-bank models; bit 0, and bit 1 where the last
-// pass reads four dwords at once, are never flipped, so the groups a lane
-// reads with one 8- or 16-byte access stay contiguous).  The map is linear
-// over XOR, so phys(a ^ b) = phys(a) ^ phys(b); addresses are split that way
-// into per-lane and compile-time parts.
+// bits 1..5, and bit 5 flips the bits kSwz5[LOG2M] among bits 1..4, so
+// strided operand gathers and the contiguous last-pass groups spread over the
+// banks (masks chosen by a search over this engine's access patterns, every
+// wave of a workgroup, against 32- and 64-bank models; bit 0, and bit 1 where
+// the last pass reads four dwords at once, are never flipped, so the groups a
+// lane reads with one access stay contiguous).  Indices below 32 map to
+// themselves: a lane's column within a 32-column tile is used as is.  The map is linear over XOR, so
+// phys(a ^ b) = phys(a) ^ phys(b); addresses are split that way into
+// per-lane and compile-time parts.
 constexpr int kSwz[15][8] = {
     {}, {}, {}, {}, {}, {}, {}, {}, {},
     {48, 18, 16},                        // 9
@@ -308,9 +310,10 @@ constexpr int kSwz[15][8] = {
     {16, 34, 16, 32, 48, 32, 16},        // 13
     {4, 48, 16, 32, 16, 48, 16, 32},     // 14
 };
+constexpr int kSwz5[15] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 8, 0, 0, 16, 8, 0};
 template <int LOG2M>
 __host__ __device__ constexpr int phys(int i) {
-    int r = i;
+    int r = (i >> 5) & 1 ? i ^ kSwz5[LOG2M] : i;
     for (int p = 6; p < LOG2M; ++p)
         if ((i >> p) & 1) r ^= kSwz[LOG2M][p - 6];
     return r;
