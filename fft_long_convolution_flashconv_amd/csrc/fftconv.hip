@@ -328,20 +328,34 @@ __global__ __launch_bounds__(256) void k_h3_gate_in(const uint16_t *__restrict__
     const int d0 = blockIdx.x * HM_TD, t0 = blockIdx.y * HM_TT, b = blockIdx.z;
     const uint16_t *kb = k + (size_t)b * N * Dm, *vb = v + (size_t)b * N * Dm;
     // rows t0 - 3 .. t0 + TT - 1 of k (the short filter's history) and
-    // t0 .. t0 + TT - 1 of v, 16 chunks of 8 channels per row
-    for (int ci = tid; ci < (HM_TT + 3) * (HM_TD / 8); ci += 256) {
-        const int r = ci / (HM_TD / 8), c = ci % (HM_TD / 8);
+    // t0 .. t0 + TT - 1 of v, 16 chunks of 8 channels per row; every load of
+    // the tile is issued before the first LDS write
+    constexpr int CR = HM_TD / 8, NKC = (HM_TT + 3) * CR, NVC = HM_TT * CR;
+    constexpr int NK = (NKC + 255) / 256, NV = (NVC + 255) / 256;
+    mf::u32x4 xk[NK], xv[NV];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int ci = tid + 256 * j, r = ci / CR, c = ci % CR;
         const int t = t0 - 3 + r, d = d0 + 8 * c;
-        mf::u32x4 x = {0u, 0u, 0u, 0u};
-        if (t >= 0 && t < N && d < Dm) x = hm_load8(kb + (size_t)t * Dm + d, Dm - d, vec);
-        put(&ks[r * PD + 8 * c], x);
+        xk[j] = mf::u32x4{0u, 0u, 0u, 0u};
+        if (ci < NKC && t >= 0 && t < N && d < Dm) xk[j] = hm_load8(kb + (size_t)t * Dm + d, Dm - d, vec);
     }
-    for (int ci = tid; ci < HM_TT * (HM_TD / 8); ci += 256) {
-        const int r = ci / (HM_TD / 8), c = ci % (HM_TD / 8);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int ci = tid + 256 * j, r = ci / CR, c = ci % CR;
         const int t = t0 + r, d = d0 + 8 * c;
-        mf::u32x4 x = {0u, 0u, 0u, 0u};
-        if (t < N && d < Dm) x = hm_load8(vb + (size_t)t * Dm + d, Dm - d, vec);
-        put(&vs[r * PD + 8 * c], x);
+        xv[j] = mf::u32x4{0u, 0u, 0u, 0u};
+        if (ci < NVC && t < N && d < Dm) xv[j] = hm_load8(vb + (size_t)t * Dm + d, Dm - d, vec);
+    }
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int ci = tid + 256 * j;
+        if (ci < NKC) put(&ks[(ci / CR) * PD + 8 * (ci % CR)], xk[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int ci = tid + 256 * j;
+        if (ci < NVC) put(&vs[(ci / CR) * PD + 8 * (ci % CR)], xv[j]);
     }
     __syncthreads();
     // thread: steps 8 c .. 8 c + 7 of channel dl; the 8 lanes of a channel
@@ -379,33 +393,51 @@ __global__ __launch_bounds__(256) void k_h3_gate_out(const uint16_t *__restrict_
     __shared__ uint16_t zs[HM_TD * PZ];
     const int tid = threadIdx.x;
     const int d0 = blockIdx.x * HM_TD, t0 = blockIdx.y * HM_TT, b = blockIdx.z;
-    // rows d0 .. d0 + TD - 1 of z_T, 8 chunks of 8 steps per row
-    for (int ci = tid; ci < HM_TD * (HM_TT / 8); ci += 256) {
-        const int r = ci / (HM_TT / 8), c = ci % (HM_TT / 8);
+    // rows d0 .. d0 + TD - 1 of z_T, 8 chunks of 8 steps per row, all
+    // loaded before the first LDS write
+    constexpr int CT = HM_TT / 8, NZ = HM_TD * CT / 256;
+    static_assert(HM_TD * CT % 256 == 0, "whole chunks per thread");
+    mf::u32x4 xz[NZ];
+#pragma unroll
+    for (int j = 0; j < NZ; ++j) {
+        const int ci = tid + 256 * j, r = ci / CT, c = ci % CT;
         const int d = d0 + r, t = t0 + 8 * c;
-        mf::u32x4 x = {0u, 0u, 0u, 0u};
-        if (d < Dm && t < N) x = hm_load8(zT + ((size_t)b * Dm + d) * N + t, N - t, vec);
+        xz[j] = mf::u32x4{0u, 0u, 0u, 0u};
+        if (d < Dm && t < N) xz[j] = hm_load8(zT + ((size_t)b * Dm + d) * N + t, N - t, vec);
+    }
+#pragma unroll
+    for (int j = 0; j < NZ; ++j) {
+        const int ci = tid + 256 * j, r = ci / CT, c = ci % CT;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            zs[r * PZ + 8 * c + 2 * e] = (uint16_t)(x[e] & 0xffffu);
-            zs[r * PZ + 8 * c + 2 * e + 1] = (uint16_t)(x[e] >> 16);
+            zs[r * PZ + 8 * c + 2 * e] = (uint16_t)(xz[j][e] & 0xffffu);
+            zs[r * PZ + 8 * c + 2 * e + 1] = (uint16_t)(xz[j][e] >> 16);
         }
     }
-    __syncthreads();
-    // thread: 8 channels 8 c .. 8 c + 7, steps tl, tl + 16, ...
-    const int c = tid % (HM_TD / 8), d = d0 + 8 * c;
-    if (d >= Dm) return;
+    // thread: 8 channels 8 c .. 8 c + 7, steps tl, tl + 16, ...; its q
+    // loads are issued before the barrier
+    constexpr int TS = 256 / (HM_TD / 8), NQ = HM_TT / TS;
+    const int c = tid % (HM_TD / 8), d = d0 + 8 * c, tl0 = tid / (HM_TD / 8);
     const uint16_t *qb = q + (size_t)b * N * Dm;
     uint16_t *ob = out + (size_t)b * N * Dm;
-    for (int tl = tid / (HM_TD / 8); tl < HM_TT; tl += 256 / (HM_TD / 8)) {
-        const int t = t0 + tl;
+    mf::u32x4 xq[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int t = t0 + tl0 + TS * j;
+        xq[j] = mf::u32x4{0u, 0u, 0u, 0u};
+        if (d < Dm && t < N) xq[j] = hm_load8(qb + (size_t)t * Dm + d, Dm - d, vec);
+    }
+    __syncthreads();
+    if (d >= Dm) return;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int tl = tl0 + TS * j, t = t0 + tl;
         if (t >= N) break;
         const size_t o = (size_t)t * Dm + d;
-        const mf::u32x4 x = hm_load8(qb + o, Dm - d, vec);
         uint16_t r[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint16_t qe = (uint16_t)((e & 1) ? (x[e >> 1] >> 16) : (x[e >> 1] & 0xffffu));
+            const uint16_t qe = (uint16_t)((e & 1) ? (xq[j][e >> 1] >> 16) : (xq[j][e >> 1] & 0xffffu));
             const float z = __uint_as_float((uint32_t)zs[(8 * c + e) * PZ + tl] << 16);
             r[e] = hm_h<IO>(hm_f<IO>(qe) * z);
         }

@@ -292,6 +292,26 @@ def test_h3_mix_small(io, L):
     assert err <= TOL[io]
 
 
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_h3_mix_vector_ragged_tiles(io):
+    # N and d_model multiples of 8 (16-byte gate accesses) but not of the
+    # gates' 64-step x 128-channel tiles
+    dev = device()
+    B, N, Dm, L = 2, 520, 136, 4
+    say("h3_mix io=%s B=%d N=%d Dm=%d L=%d" % (io, B, N, Dm, L))
+    g = wl.gen(9000 + len(io))
+    q, k, v = (wl.normal((B, N, Dm), g, dtype=DT[io]) for _ in range(3))
+    w = wl.normal((Dm, L), g, std=0.5)
+    f = wl.random_env_filter(Dm, N, g)
+    D = wl.normal((Dm,), g)
+    out = pkg.h3_mix(*(t.to(dev) for t in (q, k, v, w, f, D)))
+    torch.cuda.synchronize()
+    ref = oracle.h3_mix(q, k, v, w, f, D)
+    err = rel_l2(to_np(out), ref)
+    say("  rel_l2=%.3e" % err)
+    assert err <= TOL[io]
+
+
 def test_h3_mix_2k_workload():
     w = wl.WORKLOADS["h3_mix_2k"]
     dev = device()
