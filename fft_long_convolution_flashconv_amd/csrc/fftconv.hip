@@ -357,16 +357,24 @@ __global__ __launch_bounds__(256) void k_h3_gate_in(const uint16_t *__restrict__
         const int ci = tid + 256 * j;
         if (ci < NVC) put(&vs[(ci / CR) * PD + 8 * (ci % CR)], xv[j]);
     }
-    __syncthreads();
-    // thread: steps 8 c .. 8 c + 7 of channel dl; the 8 lanes of a channel
-    // write one contiguous 128-byte run of its m_T row
-    const int c = tid % (HM_TT / 8);
-    for (int dl = tid / (HM_TT / 8); dl < HM_TD; dl += 256 / (HM_TT / 8)) {
-        const int d = d0 + dl;
-        if (d >= Dm) break;
-        float wd[4];
+    // thread: steps 8 c .. 8 c + 7 of channels dl0, dl0 + DS, ...; the 8
+    // lanes of a channel write one contiguous 128-byte run of its m_T row.
+    // The short-filter taps are loaded before the barrier too.
+    constexpr int DS = 256 / (HM_TT / 8), ND = HM_TD / DS;
+    const int c = tid % (HM_TT / 8), dl0 = tid / (HM_TT / 8);
+    float wt[ND][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wd[i] = (i < L) ? w[(size_t)d * L + i] : 0.f;
+    for (int j = 0; j < ND; ++j) {
+        const int d = d0 + dl0 + DS * j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wt[j][i] = (i < L && d < Dm) ? w[(size_t)d * L + i] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+        const int dl = dl0 + DS * j, d = d0 + dl;
+        if (d >= Dm) break;
+        const float(&wd)[4] = wt[j];
         // k at t - 1, t - 2, t - 3 for t = t0 + 8 c (tile row r + 3 holds step t0 + r)
         float k1 = hm_f<IO>(ks[(8 * c + 2) * PD + dl]), k2 = hm_f<IO>(ks[(8 * c + 1) * PD + dl]),
               k3 = hm_f<IO>(ks[(8 * c) * PD + dl]);
