@@ -288,8 +288,15 @@ __device__ __forceinline__ uint16_t hm_h(float x) {
 }
 
 // 8 consecutive 16-bit values at p (n of them valid), zero-filled
+// NTA: non-temporal access.  The block's own inputs (q, k, v) and output
+// are touched once, and non-temporal stores of the output leave no dirty L2
+// lines behind; the bf16 intermediates m_T and z_T keep the default policy.
+template <bool NTA>
 __device__ __forceinline__ mf::u32x4 hm_load8(const uint16_t *p, int n, bool vec) {
-    if (vec && n >= 8) return *(const mf::u32x4 *)p;
+    if (vec && n >= 8) {
+        if constexpr (NTA) return __builtin_nontemporal_load((const mf::u32x4 *)p);
+        else return *(const mf::u32x4 *)p;
+    }
     uint16_t e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) e[i] = i < n ? p[i] : (uint16_t)0;
@@ -298,12 +305,14 @@ __device__ __forceinline__ mf::u32x4 hm_load8(const uint16_t *p, int n, bool vec
     for (int i = 0; i < 4; ++i) r[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
     return r;
 }
+template <bool NTA>
 __device__ __forceinline__ void hm_store8(uint16_t *p, int n, bool vec, const uint16_t (&e)[8]) {
     if (vec && n >= 8) {
         mf::u32x4 r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
-        *(mf::u32x4 *)p = r;
+        if constexpr (NTA) __builtin_nontemporal_store(r, (mf::u32x4 *)p);
+        else *(mf::u32x4 *)p = r;
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -338,14 +347,14 @@ __global__ __launch_bounds__(256) void k_h3_gate_in(const uint16_t *__restrict__
         const int ci = tid + 256 * j, r = ci / CR, c = ci % CR;
         const int t = t0 - 3 + r, d = d0 + 8 * c;
         xk[j] = mf::u32x4{0u, 0u, 0u, 0u};
-        if (ci < NKC && t >= 0 && t < N && d < Dm) xk[j] = hm_load8(kb + (size_t)t * Dm + d, Dm - d, vec);
+        if (ci < NKC && t >= 0 && t < N && d < Dm) xk[j] = hm_load8<true>(kb + (size_t)t * Dm + d, Dm - d, vec);
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int ci = tid + 256 * j, r = ci / CR, c = ci % CR;
         const int t = t0 + r, d = d0 + 8 * c;
         xv[j] = mf::u32x4{0u, 0u, 0u, 0u};
-        if (ci < NVC && t < N && d < Dm) xv[j] = hm_load8(vb + (size_t)t * Dm + d, Dm - d, vec);
+        if (ci < NVC && t < N && d < Dm) xv[j] = hm_load8<true>(vb + (size_t)t * Dm + d, Dm - d, vec);
     }
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(256) void k_h3_gate_in(const uint16_t *__restrict__
             k1 = k0;
         }
         const int nt = N - (t0 + 8 * c);
-        if (nt > 0) hm_store8(mT + ((size_t)b * Dm + d) * N + t0 + 8 * c, nt, vec, mo);
+        if (nt > 0) hm_store8<false>(mT + ((size_t)b * Dm + d) * N + t0 + 8 * c, nt, vec, mo);
     }
 }
 
@@ -411,7 +420,7 @@ __global__ __launch_bounds__(256) void k_h3_gate_out(const uint16_t *__restrict_
         const int ci = tid + 256 * j, r = ci / CT, c = ci % CT;
         const int d = d0 + r, t = t0 + 8 * c;
         xz[j] = mf::u32x4{0u, 0u, 0u, 0u};
-        if (d < Dm && t < N) xz[j] = hm_load8(zT + ((size_t)b * Dm + d) * N + t, N - t, vec);
+        if (d < Dm && t < N) xz[j] = hm_load8<false>(zT + ((size_t)b * Dm + d) * N + t, N - t, vec);
     }
 #pragma unroll
     for (int j = 0; j < NZ; ++j) {
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(256) void k_h3_gate_out(const uint16_t *__restrict_
     for (int j = 0; j < NQ; ++j) {
         const int t = t0 + tl0 + TS * j;
         xq[j] = mf::u32x4{0u, 0u, 0u, 0u};
-        if (d < Dm && t < N) xq[j] = hm_load8(qb + (size_t)t * Dm + d, Dm - d, vec);
+        if (d < Dm && t < N) xq[j] = hm_load8<true>(qb + (size_t)t * Dm + d, Dm - d, vec);
     }
     __syncthreads();
     if (d >= Dm) return;
@@ -449,7 +458,7 @@ __global__ __launch_bounds__(256) void k_h3_gate_out(const uint16_t *__restrict_
             const float z = __uint_as_float((uint32_t)zs[(8 * c + e) * PZ + tl] << 16);
             r[e] = hm_h<IO>(hm_f<IO>(qe) * z);
         }
-        hm_store8(ob + o, Dm - d, vec, r);
+        hm_store8<true>(ob + o, Dm - d, vec, r);
     }
 }
 
