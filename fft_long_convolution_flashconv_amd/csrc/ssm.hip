@@ -554,7 +554,9 @@ __device__ __forceinline__ float sp_wave_max(float v) {
 }
 
 // Both projections of one (batch row b, channel h), walking its chunks in
-// order and carrying the state in LDS.  Eight waves; for each chunk c (the
+// order; every wave carries its own copy of the state (lane l: mode l), so
+// the state update needs no barrier of its own.  Eight waves; for each chunk
+// c (the
 // correction goes first, so that its stores are issued before the next
 // chunk's loads and are long complete when those are waited for):
 //   1. the chunk's activations are staged in LDS as fp16 (bf16 inputs scaled
@@ -567,8 +569,10 @@ __device__ __forceinline__ float sp_wave_max(float v) {
 //      wave w owns output rows l = 16 (w % 4) .. +15 and column tiles
 //      4 (w / 4) .. +3, scales its Rt operands (in registers) by the state,
 //      and updates y in place;
-//   4. x <- Abar^T x + s.
-// The next chunk's activations are loaded while the current one is used.
+//   4. x <- Abar^T x + s, in every wave at the top of the next chunk (the
+//      contributions s are complete at the chunk's last barrier).
+// Two barriers per chunk: after staging, and after the contribution.  The
+// next chunk's activations are loaded while the current one is used.
 constexpr int SP_USTR = 72;   // staged chunk: 64 samples per row i, padded (bank spread)
 constexpr int SP_XSTR = 136;  // G operand: 128 (mode, part) entries per column i, padded
 
@@ -591,8 +595,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     __shared__ __attribute__((aligned(16))) uint16_t us[128 * SP_USTR];
     __shared__ __attribute__((aligned(16))) uint16_t xs[128 * SP_XSTR];
     __shared__ cf pcs[64 * 8], pxs[64 * 8], qxs[64 * 16];
-    __shared__ cf xst[64], sst[64];
-    __shared__ float red[NWV], rmax[NWV], xmax;
+    __shared__ cf xw[NWV][64], sst[64];
+    __shared__ float red[NWV], rmax[NWV];
     const size_t orow = (size_t)b * H + h;
     // tables and the initial state
     for (int e = tid; e < 64 * 8; e += 512) {
@@ -611,13 +615,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
         const cf X = cmul(pxs[j * 8 + (i >> 4)], qxs[j * 16 + (i & 15)]);
         *(uint32_t *)(xs + i * SP_XSTR + 2 * j) = pk(X.x, X.y);
     }
-    if (tid < 64) {
-        cf x = mk(0.f, 0.f);
-        if (x_in && tid < S) x = mk(x_in[(orow * S + tid) * 2], x_in[(orow * S + tid) * 2 + 1]);
-        xst[tid] = x;
-        const float m = sp_wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
-        if (tid == 0) xmax = m;
-    }
+    // every wave carries its own copy of the state: lane l holds mode l
+    cf xl = mk(0.f, 0.f);
+    if (x_in && lane < S) xl = mk(x_in[(orow * S + lane) * 2], x_in[(orow * S + lane) * 2 + 1]);
     // matrix operands in registers
     const uint16_t *Eh = Et + (size_t)h * 128 * 64, *Rh = Rt + (size_t)h * 64 * 128;
     half8 Ea[2], Ra[4];
@@ -629,7 +629,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
         Ra[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Rh + (16 * lr + il) * 128 + 32 * ks + 8 * g));
-    const cf aTj = (tid < 64) ? aT[(size_t)h * 64 + tid] : mk(0.f, 0.f);
+    const cf aTl = aT[(size_t)h * 64 + lane];
     // max |Rt entry| < 2^er over the workgroup (sets the state scale below)
     int er = 0;
     {
@@ -717,7 +717,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
         // correction operand: this wave's Rt rows times the state carried in,
         // (2 Re R, -2 Im R) (x) -> (2 Re (R x), -2 Im (R x)), with x scaled by
         // sx = 2^(14 - e - er), max |x| < 2^e, so every product stays below 2^14
-        const float xm = xmax;
+        // 4. (for the previous chunk) x <- Abar^T x + s, in every wave; the
+        //    contributions s were completed at the previous chunk's last barrier
+        if (c > 0) xl = cadd(cmul(aTl, xl), sst[lane]);
+        const float xm = sp_wave_max(fmaxf(fabsf(xl.x), fabsf(xl.y)));
+        xw[w][lane] = xl;
         const bool corr = xm > 0.f;
         float sx = 1.f;
         half8 Rx[4];
@@ -731,7 +735,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
                 uint32_t o4[4] = {r4.x, r4.y, r4.z, r4.w}, xc[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const cf x = xst[16 * ks + 4 * g + q];  // mode of slot pair q
+                    const cf x = xw[w][16 * ks + 4 * g + q];  // mode of slot pair q
                     xc[q] = pk(x.x * sx, -x.y * sx);
                 }
                 // (a + i b) conj(x sx) with (a, b) = (2 Re R, -2 Im R); the
@@ -804,18 +808,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
             sst[j0 + 1] = cscale(acc1, inv);
         }
         __syncthreads();
-        // 4. carry the state
-        if (tid < 64) {
-            const cf x = cadd(cmul(aTj, xst[tid]), sst[tid]);
-            xst[tid] = x;
-            const float m = sp_wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
-            if (tid == 0) xmax = m;
-        }
-        __syncthreads();
     }
-    if (x_out && tid < S) {
-        x_out[(orow * S + tid) * 2] = xst[tid].x;
-        x_out[(orow * S + tid) * 2 + 1] = xst[tid].y;
+    if (x_out && w == 0) {
+        xl = cadd(cmul(aTl, xl), sst[lane]);
+        if (lane < S) {
+            x_out[(orow * S + lane) * 2] = xl.x;
+            x_out[(orow * S + lane) * 2 + 1] = xl.y;
+        }
     }
 }
 
