@@ -130,7 +130,9 @@ __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_h3_mix(
 // fp16 / bf16 activations, 2N >= 256: same per-channel structure, transforms on
 // the matrix cores (see mfma_engine.h).
 
-template <int LOG2M, int IO>
+// SPOL: cache policy of the output stores (non-temporal unless the output
+// is read again right away)
+template <int LOG2M, int IO, int SPOL>
 __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M>::WPE))) void k_fft_conv_mfma(
     const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f,
     const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
@@ -159,10 +161,10 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
         return {mf::row_rsrc(uh + o, nb0), mf::row_rsrc(uh + o + rsb, nb1), mf::row_rsrc(yh + o, nb0),
                 mf::row_rsrc(yh + o + rsb, nb1)};
     };
-    E.run_raw(mf::row_rsrc(fh, 4 * N), dh, rows, (B + 1) / 2, hb);
+    E.template run_raw<SPOL>(mf::row_rsrc(fh, 4 * N), dh, rows, (B + 1) / 2, hb);
 }
 
-template <int LOG2M, int IO>
+template <int LOG2M, int IO, int SPOL>
 static hipError_t launch_fc_mfma(const void *u, const float *f, const float *D, void *y, int B,
                                  int H, int N, hipStream_t s) {
     using T = typename io_elem<IO>::T;
@@ -175,7 +177,7 @@ static hipError_t launch_fc_mfma(const void *u, const float *f, const float *D, 
     const int bmax = (int)std::min<uint64_t>((uint64_t)B, (((1ull << 32) - 1) / rowb - pad) & ~1ull);
     for (int b0 = 0; b0 < B; b0 += bmax) {
         const size_t o = (size_t)b0 * H * N;
-        hipLaunchKernelGGL((k_fft_conv_mfma<LOG2M, IO>), dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
+        hipLaunchKernelGGL((k_fft_conv_mfma<LOG2M, IO, SPOL>), dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
                            (const T *)u + o, f, D, (T *)y + o, std::min(bmax, B - b0), H, N);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -192,17 +194,17 @@ static hipError_t launch_fc(const void *u, const float *f, const float *D, void 
     return hipGetLastError();
 }
 
-template <int IO>
+template <int IO, int SPOL = mf::kNT>
 static hipError_t fc_dispatch(int log2m, const void *u, const float *f, const float *D, void *y,
                               int B, int H, int N, hipStream_t s) {
     if constexpr (IO != IO_F32) {
         switch (log2m) {
-            case 9: return launch_fc_mfma<9, IO>(u, f, D, y, B, H, N, s);
-            case 10: return launch_fc_mfma<10, IO>(u, f, D, y, B, H, N, s);
-            case 11: return launch_fc_mfma<11, IO>(u, f, D, y, B, H, N, s);
-            case 12: return launch_fc_mfma<12, IO>(u, f, D, y, B, H, N, s);
-            case 13: return launch_fc_mfma<13, IO>(u, f, D, y, B, H, N, s);
-            case 14: return launch_fc_mfma<14, IO>(u, f, D, y, B, H, N, s);
+            case 9: return launch_fc_mfma<9, IO, SPOL>(u, f, D, y, B, H, N, s);
+            case 10: return launch_fc_mfma<10, IO, SPOL>(u, f, D, y, B, H, N, s);
+            case 11: return launch_fc_mfma<11, IO, SPOL>(u, f, D, y, B, H, N, s);
+            case 12: return launch_fc_mfma<12, IO, SPOL>(u, f, D, y, B, H, N, s);
+            case 13: return launch_fc_mfma<13, IO, SPOL>(u, f, D, y, B, H, N, s);
+            case 14: return launch_fc_mfma<14, IO, SPOL>(u, f, D, y, B, H, N, s);
             default: break;
         }
     }
@@ -481,7 +483,9 @@ static hipError_t hm_16bit(const void *q, const void *k, const void *v, const fl
                        N, Dm, L, vec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = fc_dispatch<IO_BF16>(fused_log2m(N), mT, f, D, zT, B, Dm, N, s);
+    // z_T is read back by the output gate right away: its stores keep the
+    // default cache policy
+    e = fc_dispatch<IO_BF16, 0>(fused_log2m(N), mT, f, D, zT, B, Dm, N, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_h3_gate_out<IO>), grid, dim3(256), 0, s, (const uint16_t *)q, (const uint16_t *)zT,
                        (uint16_t *)out, N, Dm, vec);

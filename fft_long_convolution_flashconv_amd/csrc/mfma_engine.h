@@ -1207,7 +1207,8 @@ struct Engine {
     // resources of signal `sig`, empty ones for the rows past the last (a
     // round always transforms SIG signals).  The inputs of each round are
     // fetched while the previous round (or the filter) is being transformed.
-    template <class RB>
+    // SPOL: cache policy of the output stores.
+    template <int SPOL = kNT, class RB>
     __device__ void run_raw(__amdgpu_buffer_rsrc_t frs, float d0, const RB &rows, int nsig, int hb) {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         float fin[T0W][4];
@@ -1217,8 +1218,8 @@ struct Engine {
         // output of round r0: packed pair v of rows 2 (r0 + s), 2 (r0 + s) + 1
         auto store = [&](int r0, int s, int n, int m, uint32_t hv) {
             const RowBufs rb = rows(r0 + s);
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, kNT);
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, kNT);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, SPOL);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, SPOL);
         };
         // with PREFETCH, the next round's inputs are loaded into pin as soon
         // as pass 0 has consumed this round's
