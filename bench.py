@@ -218,7 +218,7 @@ def main():
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash and exit")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(channels shard with no communication; see the design notes). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

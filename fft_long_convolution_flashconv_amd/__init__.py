@@ -50,8 +50,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise RuntimeError("libh3conv.so not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
-                           "or `python fft_long_convolution_flashconv_amd/build.py` (looked for %s)" % path)
+        raise RuntimeError("libh3conv.so not built: run `python fft_long_convolution_flashconv_amd/build.py` "
+                           "(looked for %s)" % path)
     lib = ctypes.CDLL(path)
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.h3conv_fft_conv.argtypes = [P, P, P, P, I64, I64, I64, I, P]

@@ -2,7 +2,7 @@
 
 Every ``csrc/*.hip`` file is compiled to an object in parallel, then linked
 into one shared library next to this file.  The build always runs when
-called (it is the "does it build" check); loaders only import what exists.
+called, also where a built library exists; loaders only load what exists.
 """
 from __future__ import annotations
 
