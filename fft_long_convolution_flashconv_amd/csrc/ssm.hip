@@ -651,21 +651,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int nq = T >> 3;
     u32x4 pre[2];
     u32x2 ypre[4];
-    auto load_chunk = [&](int c) {
-        const T_ *src = u + orow * N + (size_t)c * T;
+    // Loads go through buffer resources: a chunk past the last (the loads
+    // issued during the last chunk) or outputs that no correction will use
+    // (chunk 0 without x_in) get an empty resource, whose loads read zero and
+    // touch no memory, with no branch around them.
+    auto load_chunk = [&](int c, bool uv, bool yv) {
+        const __amdgpu_buffer_rsrc_t ur = row_rsrc(u + orow * N + (size_t)c * T, uv ? 2 * T : 0);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int q = tid + 512 * k;
-            if (q < nq) pre[k] = *(const u32x4 *)(src + 8 * q);
+            if (q < nq) pre[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ur, 16 * q, 0, 0));
         }
-        const T_ *yr = y + orow * N + (size_t)c * T;
+        const __amdgpu_buffer_rsrc_t yrs = row_rsrc(y + orow * N + (size_t)c * T, yv ? 2 * T : 0);
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             const int ct = 4 * ch + c4, i = 16 * ct + il;
-            if (ct < NCT && i < T2) ypre[c4] = *(const u32x2 *)(yr + 64 * i + 16 * lr + 4 * g);
+            if (ct < NCT && i < T2)
+                ypre[c4] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yrs, 2 * (64 * i + 16 * lr + 4 * g), 0, 0));
         }
     };
-    load_chunk(0);
+    load_chunk(0, true, x_in != nullptr);
     __syncthreads();
     for (int c = 0; c < C; ++c) {
         // 1. stage (fp16, scaled for bf16 inputs)
@@ -774,9 +779,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
                 }
             }
         }
-        // next chunk's loads (unconditional, the last pass reloading its own
-        // chunk: in a branch of their own they end up after the last barrier)
-        load_chunk(c + 1 < C ? c + 1 : c);
+        // next chunk's loads (issued on every pass, with empty resources on
+        // the last: in a branch of their own they end up after the barrier)
+        load_chunk(c + 1 < C ? c + 1 : c, c + 1 < C, c + 1 < C);
         // 2. contribution (column tiles unrolled, so their reads and products
         //    overlap; the per-lane factor qc is applied once at the end)
         cf acc0 = mk(0.f, 0.f), acc1 = mk(0.f, 0.f);
