@@ -429,7 +429,14 @@ __global__ __launch_bounds__(256) void k_sp_correct(typename io_elem<IO>::T *__r
 // and the scale is undone on the fp32 results.
 
 
-__device__ __forceinline__ uint16_t f16bits(double x) { return __builtin_bit_cast(uint16_t, (_Float16)(float)x); }
+// fp64 -> fp32 -> fp16 with the two hardware conversions (the empty asm keeps
+// the compiler from fusing them into one software-rounded fp64 -> fp16
+// conversion, about forty instructions)
+__device__ __forceinline__ uint16_t f16bits(double x) {
+    float f = (float)x;
+    asm volatile("" : "+v"(f));
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
 
 // The tables of channel h from its powers pw (ssm_powers), by the workgroup's
 // NT threads: eight runs of powers per mode (the modes past S are written as
