@@ -219,7 +219,7 @@ def test_state_pass_chunk_invariance_and_split():
 
 
 @pytest.mark.parametrize("io", ["f16", "bf16"])
-@pytest.mark.parametrize("T,S", [(64, 16), (256, 64), (1024, 7), (2048, 64)])
+@pytest.mark.parametrize("T,S", [(64, 16), (256, 64), (1024, 7), (2048, 64), (4096, 64), (8192, 33)])
 def test_state_pass_16bit_chunks_and_split(io, T, S):
     """16-bit activations (matrix-core projections): every chunk length from
     one 64-sample block to several column tiles, odd batch, partial mode
@@ -247,6 +247,23 @@ def test_state_pass_16bit_chunks_and_split(io, T, S):
     errx = rel_l2(x2.cpu().numpy().astype(np.complex128), xr)
     say("  split at %d rel_l2=%.3e state=%.3e" % (M, err, errx))
     assert err <= TOL[io] and errx <= 1e-3
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_state_pass_zero_state_equals_none(io):
+    """An all-zero x_in gives exactly the result of no x_in (the carried
+    state starts at zero either way)."""
+    dev = device()
+    B, H, N, S, T = 2, 3, 2048, 64, 512
+    say("state_pass zero x_in io=%s B=%d H=%d N=%d S=%d T=%d" % (io, B, H, N, S, T))
+    u, p, D = _sp_inputs(B, H, N, S, io, seed=77)
+    d = {k: v.to(dev) for k, v in p.items()}
+    ud, Dd = u.to(dev), D.to(dev)
+    y0, x0 = pkg.state_pass(ud, d["A"], d["Bm"], d["C"], d["dt"], Dd, T, return_state=True)
+    xz = torch.zeros(B, H, S, dtype=torch.complex64, device=dev)
+    y1, x1 = pkg.state_pass(ud, d["A"], d["Bm"], d["C"], d["dt"], Dd, T, x_in=xz, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(x0, x1)
 
 
 def test_state_64k_workload():
