@@ -152,6 +152,33 @@ def _ssm_conv_workload(name, nrows):
     assert err <= TOL[w.dtype] and err_conv <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_fft_conv_batch_past_32bit_offsets(io):
+    """A batch whose rows span more than 4 GiB: the launcher splits it into
+    slices whose row offsets fit 32 bits (checked on rows either side of the
+    split and at the ends, odd batch)."""
+    dev = device()
+    B, H, N = 4099, 64, 8192
+    say("fft_conv io=%s B=%d H=%d N=%d (%.1f GiB per activation tensor)" % (io, B, H, N, B * H * N * 2 / 2**30))
+    gen = torch.Generator(device=dev).manual_seed(4099)
+    u = torch.randn((B, H, N), generator=gen, device=dev, dtype=DT[io])
+    g = wl.gen(4099)
+    f = wl.random_env_filter(H, N, g)
+    D = wl.normal((H,), g)
+    y = pkg.fft_conv(u, f.to(dev), D.to(dev))
+    torch.cuda.synchronize()
+    bs = torch.tensor([0, 1, 2044, 2045, 4089, 4090, 4091, 4097, 4098])
+    hs = torch.tensor([0, 63, 17, 40, 5, 31, 62, 1, 33])
+    u_s = u[bs.to(dev), hs.to(dev)].cpu()[None]
+    ref = oracle.causal_conv(to_np(u_s), to_np(f[hs]), to_np(D[hs]))[0]
+    got = to_np(y[bs.to(dev), hs.to(dev)])
+    del u, y
+    err = rel_l2(got, ref)
+    per_row = max(rel_l2(got[i], ref[i]) for i in range(len(bs)))
+    say("  rel_l2=%.3e max_row=%.3e" % (err, per_row))
+    assert err <= TOL[io] and per_row <= TOL[io]
+
+
 def test_conv_1k_workload():
     _ssm_conv_workload("conv_1k", 32)
 
