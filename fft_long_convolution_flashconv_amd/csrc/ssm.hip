@@ -563,9 +563,8 @@ __device__ __forceinline__ float sp_wave_max(float v) {
 // Both projections of one (batch row b, channel h), walking its chunks in
 // order; every wave carries its own copy of the state (lane l: mode l), so
 // the state update needs no barrier of its own.  Eight waves; for each chunk
-// c (the
-// correction goes first, so that its stores are issued before the next
-// chunk's loads and are long complete when those are waited for):
+// c (the correction goes first, so that its stores are issued before the
+// next chunk's loads and are long complete when those are waited for):
 //   1. the chunk's activations are staged in LDS as fp16 (bf16 inputs scaled
 //      by a power of two into fp16 range);
 //   2. contribution: wave w owns modes 8w .. 8w+7 (Et row tile w) and all
