@@ -358,6 +358,15 @@ struct Shape {
     static constexpr int PAD = 16;                     // dwords after each signal slot
     static constexpr bool FUSEF = ((SIG + 1) * (M + PAD) + 64) * 4 * OCC <= 160 * 1024;
     static constexpr int DATA = (SIG + (FUSEF ? 1 : 0)) * (M + PAD);
+    // Reduction slots (after the signal data, two alternating banks): per
+    // round, the per-signal input maxima (one slot per pass-0 tile, or per
+    // wave when a round holds one signal) and the filter sums of the waves.
+    static constexpr int NSLOT = SIG == 1 ? NW : T0;
+    static constexpr int RBK = (NSLOT + NW > 2 * NW) ? NSLOT + NW : 2 * NW;
+    static_assert(2 * RBK <= 64, "two reduction banks fit the 64 slots");
+    // With several signals per round, the pass-0 tiles of one wave belong to
+    // different signals (32 NW columns >= one signal's S0 columns).
+    static_assert(SIG == 1 || 32 * NW >= S0, "a wave's pass-0 tiles cover distinct signals");
     static constexpr int LDS_DWORDS = DATA + 64;
     static constexpr int DELTA = 256 * NW;             // butterfly-base step between a wave's tiles
     // distinct column offsets a thread meets in pass 0 (32-column tiles) and
@@ -455,6 +464,29 @@ __device__ __forceinline__ float wave_reduce(float v) {
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce<false>(v); }
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce<true>(v); }
 
+// Max of two pairs of 16-bit magnitudes, half by half.  The bit patterns of
+// non-negative fp16 or bf16 values order like the values themselves, so the
+// pairs are compared as unsigned 16-bit integers.
+__device__ __forceinline__ uint32_t pkmax_u16(uint32_t a, uint32_t b) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
+}
+template <int CTRL, int RMASK>
+__device__ __forceinline__ uint32_t dpp_pkmax_step(uint32_t x) {
+    return pkmax_u16(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, RMASK, 0xf, false));
+}
+// wave-wide half-by-half max of packed 16-bit magnitudes (same DPP steps as
+// wave_reduce; 0 is the identity), wave-uniform result
+__device__ __forceinline__ uint32_t wave_pkmax(uint32_t x) {
+    x = dpp_pkmax_step<0xb1, 0xf>(x);
+    x = dpp_pkmax_step<0x4e, 0xf>(x);
+    x = dpp_pkmax_step<0x141, 0xf>(x);
+    x = dpp_pkmax_step<0x140, 0xf>(x);
+    x = dpp_pkmax_step<0x142, 0xa>(x);
+    x = dpp_pkmax_step<0x143, 0xc>(x);
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Power-of-two scale 2^(8 - e - hb) where amax < 2^e: after a transform that
 // can grow magnitudes by at most 2^(2 hb), values stay below 2^(8 + hb).
 __device__ __forceinline__ float pow2_scale(float amax, int hb) {
@@ -498,12 +530,13 @@ __device__ __forceinline__ float in_amax(const typename InT<KIND>::T &x) {
         return fmaxf(fabsf(__uint_as_float(x << 16)), fabsf(__uint_as_float(x & 0xffff0000u)));
     else return fmaxf(fabsf(x.x), fabsf(x.y));
 }
-// scaled packed fp16 operand value; `sh` is the scale as a packed fp16 pair
+// scaled packed fp16 operand value: the real half times s.x, the imaginary
+// half times s.y; `sh` is the same pair as packed fp16
 template <int KIND>
-__device__ __forceinline__ uint32_t in_scaled(const typename InT<KIND>::T &x, float s, uint32_t sh) {
+__device__ __forceinline__ uint32_t in_scaled(const typename InT<KIND>::T &x, f2 s, uint32_t sh) {
     if constexpr (KIND == IN_F16) return pkmul(x, sh);
-    else if constexpr (KIND == IN_BF16) return pk(__uint_as_float(x << 16) * s, __uint_as_float(x & 0xffff0000u) * s);
-    else return pk(x.x * s, x.y * s);
+    else if constexpr (KIND == IN_BF16) return pk(__uint_as_float(x << 16) * s.x, __uint_as_float(x & 0xffff0000u) * s.y);
+    else return pk(x.x * s.x, x.y * s.y);
 }
 
 // Rows of one complex signal for the 16-bit activation kinds, as raw buffer
@@ -662,10 +695,12 @@ struct Engine {
     // banks (of 2 NW floats, room for the joint reduction below): a wave can
     // only write a bank again after the next reduction's barrier, which every
     // wave reaches only after reading that bank.
+    static constexpr int NSLOT = SH::NSLOT, RBK = SH::RBK;
+
     template <bool SUM>
     __device__ float block_reduce(float v) {
         v = SUM ? wave_sum(v) : wave_max(v);
-        float *r = red + rbank * 2 * NW;
+        float *r = red + rbank * RBK;
         rbank ^= 1;
         if (lane == 0) r[w] = v;
         __syncthreads();
@@ -679,7 +714,7 @@ struct Engine {
     __device__ f2 block_reduce_sm(float a, float b) {
         a = wave_sum(a);
         b = wave_max(b);
-        float *r = red + rbank * 2 * NW;
+        float *r = red + rbank * RBK;
         rbank ^= 1;
         if (lane == 0) {
             r[w] = a;
@@ -693,6 +728,72 @@ struct Engine {
             mb = fmaxf(mb, r[NW + i]);
         }
         return f2{sa, mb};
+    }
+
+    // Per-signal, per-half maxima of the round's inputs: sm[s] holds max |re|
+    // (low half) and max |im| (high half) of signal s as 16-bit bit patterns
+    // (wave-uniform); with FILT, also the workgroup's sum of `fs` (the
+    // filter's |f|).  One barrier.  A signal's two halves are separate rows,
+    // so each gets a scale of its own from these.
+    template <bool FILT>
+    __device__ float block_scales(uint32_t (&sm)[SIG], float fs) {
+        uint32_t tm[T0W];
+#pragma unroll
+        for (int i = 0; i < T0W; ++i) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = pkmax_u16(m, pin[i][e] & 0x7fff7fffu);
+            tm[i] = m;
+        }
+        if constexpr (SIG == 1) {
+#pragma unroll
+            for (int i = 1; i < T0W; ++i) tm[0] = pkmax_u16(tm[0], tm[i]);
+        }
+        constexpr int NR = SIG == 1 ? 1 : T0W;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) tm[i] = wave_pkmax(tm[i]);
+        if constexpr (FILT) fs = wave_sum(fs);
+        uint32_t *r = (uint32_t *)(red + rbank * RBK);
+        rbank ^= 1;
+        if (lane == 0) {
+            // slot of tile i of wave w: its pass-0 tile index w + i NW, whose
+            // signal is 32 (w + i NW) / S0 (with one signal: the wave)
+#pragma unroll
+            for (int i = 0; i < NR; ++i) r[SIG == 1 ? w : w + i * NW] = tm[i];
+            if constexpr (FILT) ((float *)r)[NSLOT + w] = fs;
+        }
+        __syncthreads();
+        constexpr int PER = NSLOT / SIG;
+#pragma unroll
+        for (int sg = 0; sg < SIG; ++sg) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) m = pkmax_u16(m, r[sg * PER + k]);
+            sm[sg] = (uint32_t)__builtin_amdgcn_readfirstlane((int)m);
+        }
+        float sa = 0.f;
+        if constexpr (FILT) {
+#pragma unroll
+            for (int k = 0; k < NW; ++k) sa += ((const float *)r)[NSLOT + k];
+        }
+        return sa;
+    }
+
+    // the magnitude whose 16-bit pattern is the low (H = 0) or high half of v
+    template <int H>
+    __device__ __forceinline__ static float half_mag(uint32_t v) {
+        const uint32_t b = H ? (v >> 16) : (v & 0xffffu);
+        if constexpr (KIND == IN_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+        else return __uint_as_float(b << 16);
+    }
+    // entry s of a per-signal array for a wave-uniform signal index
+    template <class V>
+    __device__ __forceinline__ static V pick(const V (&a)[SIG], int s) {
+        V r = a[0];
+#pragma unroll
+        for (int k = 1; k < SIG; ++k)
+            if (s == k) r = a[k];
+        return r;
     }
 
     // LDS access by byte address.  Addresses are built as a per-lane base,
@@ -781,7 +882,7 @@ struct Engine {
     // the activation type; st(s, n, m, v) stores the packed pair v (row 2s
     // in the low half, row 2s + 1 in the high half) of output m = 2g, 2g+1.
     template <class ST>
-    __device__ void pass0_inv(const ST &st, float os) {
+    __device__ void pass0_inv(const ST &st, const f2 (&osg)[SIG]) {
         const int lb = opaque((j ^ phys<LOG2M>(2 * g * S0)) << 2);
         // All twiddles and products first, then all stores: loads and stores
         // retire in order, so a table load behind a store would wait for it.
@@ -798,8 +899,13 @@ struct Engine {
         constexpr int BI = TIW < SH::BD / 4 ? TIW : SH::BD / 4;
         static_assert(TIW % BI == 0, "inverse pass-0 tiles split into equal batches");
         uint32_t ov[TIW][2];
-        auto cv = [&](float re, float im) -> uint32_t {
-            const f2 v = {re * os, im * os};
+        // output scale of each tile's signal: real half (row 2s), imaginary
+        // half (row 2s + 1)
+        f2 os[TIW];
+#pragma unroll
+        for (int i = 0; i < TIW; ++i) os[i] = pick(osg, (16 * (w + i * NW)) / S0);
+        auto cv = [&](float re, float im, f2 o) -> uint32_t {
+            const f2 v = {re * o.x, im * o.y};
             if constexpr (KIND == IN_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
             else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
         };
@@ -831,8 +937,8 @@ struct Engine {
                 cmulh_n(x, tu);
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
                 const f4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
-                ov[i][0] = cv(r[0], -r[1]);
-                ov[i][1] = cv(r[2], -r[3]);
+                ov[i][0] = cv(r[0], -r[1], os[i]);
+                ov[i][1] = cv(r[2], -r[3], os[i]);
             }
             asm volatile("" ::: "memory");
         }
@@ -1125,36 +1231,33 @@ struct Engine {
     // before the products.  prefetch() is called once pin has been consumed.
     template <bool FILT, class OUT, class PF>
     __device__ void conv_round(const OUT &out, int hb, const float (&fin)[T0W][4], const PF &prefetch) {
+        static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         __builtin_amdgcn_s_setprio(kPrioLoad);
-        float amax;
-        if constexpr (KIND == IN_F16) {
-            h2 am = {(_Float16)0.f, (_Float16)0.f};
-#pragma unroll
-            for (int i = 0; i < T0W; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    am = __builtin_elementwise_max(am, __builtin_elementwise_abs(__builtin_bit_cast(h2, pin[i][e])));
-            amax = fmaxf((float)am.x, (float)am.y);
-        } else {
-            amax = 0.f;
-#pragma unroll
-            for (int i = 0; i < T0W; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) amax = fmaxf(amax, in_amax<KIND>(pin[i][e]));
+        // Every row gets a scale of its own: a signal's real and imaginary
+        // halves are different rows, and one scale for both would leave a
+        // small row with rounding errors of the size of its partner's values.
+        uint32_t sm[SIG];
+        float sf = 0.f;
+        {
+            const float fa = block_scales<FILT>(sm, FILT ? filter_asum(fin) : 0.f);
+            if constexpr (FILT) sf = filter_scale(fa);
         }
-        float sf = 0.f, am;
-        if constexpr (FILT) {
-            const f2 r = block_reduce_sm(filter_asum(fin), amax);
-            sf = filter_scale(r.x);
-            am = r.y;
-        } else {
-            am = block_reduce<false>(amax);
+        // fp16 inputs are scaled in fp16, so a scale must be an fp16 power of two
+        auto in_scale = [&](float am) -> float {
+            const float s0 = pow2_scale(am, hb);
+            return (KIND == IN_F16) ? fminf(s0, 16384.0f) : s0;
+        };
+        f2 su[SIG];
+#pragma unroll
+        for (int sg = 0; sg < SIG; ++sg) su[sg] = f2{in_scale(half_mag<0>(sm[sg])), in_scale(half_mag<1>(sm[sg]))};
+        f2 sut[T0W];
+        uint32_t suh[T0W];
+#pragma unroll
+        for (int i = 0; i < T0W; ++i) {
+            sut[i] = pick(su, tile_sig(i));
+            suh[i] = pk(sut[i].x, sut[i].y);
         }
-        // fp16 inputs are scaled in fp16, so the scale must be an fp16 power of two
-        const float su0 = pow2_scale(am, hb);
-        const float su = (KIND == IN_F16) ? fminf(su0, 16384.0f) : su0;
-        const uint32_t suh = pk(su, su);
-        pass0<SIG, FILT>([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], su, suh); },
+        pass0<SIG, FILT>([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], sut[i], suh[i]); },
                          [&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); });
         prefetch();
         __builtin_amdgcn_s_setprio(kPrioWork);
@@ -1197,8 +1300,13 @@ struct Engine {
         if (vm > 0.f) (void)frexpf(vm, &ev);
         const float sy = fminf(fmaxf(ldexpf(1.f, 14 - ev - (LOG2M - SH::LR)), 1.0f / 16384.0f), 32768.0f);
         inv_middle<K>(pk(sy, sy));
-        const float os = (float)R / ((float)M * su * sy * cF);
-        pass0_inv(out, os);
+        // output scales; a row whose inputs are all zero is written as zeros
+        const float ob = (float)R / ((float)M * sy * cF);
+        f2 osg[SIG];
+#pragma unroll
+        for (int sg = 0; sg < SIG; ++sg)
+            osg[sg] = f2{(sm[sg] & 0xffffu) ? ob / su[sg].x : 0.f, (sm[sg] >> 16) ? ob / su[sg].y : 0.f};
+        pass0_inv(out, osg);
     }
 
     // A whole channel of 16-bit activations: the filter spectrum, then

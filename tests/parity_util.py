@@ -34,10 +34,11 @@ def cplx(t: torch.Tensor) -> np.ndarray:
     return a[..., 0] + 1j * a[..., 1]
 
 
-def sample_rows(n: int, k: int, seed: int) -> np.ndarray:
-    """k distinct indices in [0, n) including the first and last."""
-    rng = np.random.default_rng(seed)
-    idx = set([0, n - 1])
-    while len(idx) < min(k, n):
-        idx.add(int(rng.integers(0, n)))
-    return np.array(sorted(idx))
+def row_rel_l2(got, ref) -> np.ndarray:
+    """Relative L2 error of every row (last axis) of got against ref; rows
+    whose reference is all zero report their absolute norm."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return num / np.where(den > 0, den, 1.0)

@@ -81,3 +81,65 @@ def test_zero_input_and_zero_filter():
     u = torch.randn(B, H, N, device=dev).half()
     y = pkg.fft_conv(u, torch.zeros(H, N, device=dev), torch.zeros(H, device=dev))
     assert torch.count_nonzero(y) == 0
+
+
+# Rows of very different magnitude in one batch.  The 16-bit engine packs two
+# rows into the real and imaginary parts of one complex signal, so without a
+# scale of their own a small row would carry rounding errors of the order of
+# its partner's values.  Every row must meet the bar relative to its own
+# magnitude, and an all-zero row must come out exactly zero.
+_MIXED = {"f16": [1.0, 1e-3, 0.0, 1.0, 30.0, 1e-2, 1.0, 0.0, 1e-4],
+          "bf16": [1.0, 1e-6, 0.0, 1.0, 1e8, 1e-2, 1e-12, 0.0, 3.0]}
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("N", [200, 1024, 4096, 8192])
+def test_rows_of_different_magnitude(io, N):
+    from parity_util import row_rel_l2
+    sc = _MIXED[io]
+    B, H = len(sc), 2
+    label = "mixed-magnitude rows io=%s B=%d H=%d N=%d" % (io, B, H, N)
+    say(label)
+    g = wl.gen(31 * N)
+    u = (torch.randn(B, H, N, generator=g, dtype=torch.float64) *
+         torch.tensor(sc, dtype=torch.float64)[:, None, None]).to(DT[io])
+    f = wl.random_env_filter(H, N, g)
+    D = wl.normal((H,), g)
+    dev = device()
+    y = to_np(pkg.fft_conv(u.to(dev), f.to(dev), D.to(dev)))
+    ref = oracle.causal_conv(u, f, D)
+    rows = row_rel_l2(y.reshape(B * H, N), ref.reshape(B * H, N)).reshape(B, H)
+    say("  per-row rel_l2 max by batch row: " + " ".join("%.1e" % r for r in rows.max(axis=1)))
+    for b, s in enumerate(sc):
+        if s == 0.0:
+            assert np.count_nonzero(y[b]) == 0, (label, b)
+        else:
+            assert rows[b].max() <= TOL[io], (label, b, s, float(rows[b].max()))
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_state_pass_rows_of_different_magnitude(io):
+    """State passing pairs chunk rows of consecutive (batch, chunk) index,
+    across batch rows when the chunk count is odd."""
+    from parity_util import cplx, row_rel_l2
+    sc = [1.0, 1e-3, 0.0]
+    B, H, S, T = len(sc), 2, 16, 1024
+    N = 3 * T
+    label = "state_pass mixed-magnitude rows io=%s B=%d H=%d N=%d T=%d" % (io, B, H, N, T)
+    say(label)
+    g = wl.gen(4242)
+    u = (torch.randn(B, H, N, generator=g, dtype=torch.float64) *
+         torch.tensor(sc, dtype=torch.float64)[:, None, None]).to(DT[io])
+    p = wl.diag_ssm_params(H, S, g)
+    D = wl.normal((H,), g)
+    dev = device()
+    d = {k: v.to(dev) for k, v in p.items()}
+    y = to_np(pkg.state_pass(u.to(dev), d["A"], d["Bm"], d["C"], d["dt"], D.to(dev), T))
+    ref = oracle.ssm_recurrence(u, cplx(p["A"]), cplx(p["Bm"]), cplx(p["C"]), to_np(p["dt"]), to_np(D))
+    rows = row_rel_l2(y.reshape(B * H, N), ref.reshape(B * H, N)).reshape(B, H)
+    say("  per-row rel_l2 max by batch row: " + " ".join("%.1e" % r for r in rows.max(axis=1)))
+    for b, s in enumerate(sc):
+        if s == 0.0:
+            assert np.count_nonzero(y[b]) == 0, (label, b)
+        else:
+            assert rows[b].max() <= TOL[io], (label, b, s, float(rows[b].max()))

@@ -13,7 +13,7 @@ import torch
 import fft_long_convolution_flashconv_amd as pkg
 from fft_long_convolution_flashconv_amd import workloads as wl
 import oracle
-from parity_util import TOL, cplx, device, rel_l2, sample_rows, say, to_np
+from parity_util import TOL, cplx, device, rel_l2, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -128,30 +128,6 @@ def test_ssm_filter(S, N):
     assert err <= 1e-5
 
 
-def _ssm_conv_workload(name, nrows):
-    w = wl.WORKLOADS[name]
-    dev = device()
-    say("workload %s B=%d H=%d N=%d %s (full-size run, %d sampled rows)" % (name, w.B, w.H, w.N, w.dtype, nrows))
-    inp = wl.make_inputs(w)
-    d = {k: v.to(dev) for k, v in inp.items()}
-    f = pkg.ssm_filter(d["A"], d["Bm"], d["C"], d["dt"], w.N)
-    y = pkg.fft_conv(d["u"], f, d["D"])
-    torch.cuda.synchronize()
-    rows = sample_rows(w.B * w.H, nrows, seed=w.seed)
-    bs, hs = rows // w.H, rows % w.H
-    f_ref = oracle.ssm_filter(cplx(inp["A"][hs]), cplx(inp["Bm"][hs]), cplx(inp["C"][hs]),
-                              to_np(inp["dt"][hs]), w.N)
-    u_s = inp["u"][bs, hs][None]                          # [1, R, N]
-    ref = oracle.causal_conv(u_s, f_ref, to_np(inp["D"][hs]))[0]
-    got = to_np(y[torch.as_tensor(bs), torch.as_tensor(hs)])
-    err = rel_l2(got, ref)
-    du = to_np(inp["D"][hs])[:, None] * to_np(u_s[0])
-    err_conv = rel_l2(got - du, ref - du)
-    per_row = max(rel_l2(got[i], ref[i]) for i in range(len(rows)))
-    say("  rel_l2=%.3e conv_only=%.3e max_row=%.3e" % (err, err_conv, per_row))
-    assert err <= TOL[w.dtype] and err_conv <= TOL[w.dtype]
-
-
 @pytest.mark.parametrize("io", ["f16", "bf16"])
 def test_fft_conv_batch_past_32bit_offsets(io):
     """A batch whose rows span more than 4 GiB: the launcher splits it into
@@ -177,14 +153,6 @@ def test_fft_conv_batch_past_32bit_offsets(io):
     per_row = max(rel_l2(got[i], ref[i]) for i in range(len(bs)))
     say("  rel_l2=%.3e max_row=%.3e" % (err, per_row))
     assert err <= TOL[io] and per_row <= TOL[io]
-
-
-def test_conv_1k_workload():
-    _ssm_conv_workload("conv_1k", 32)
-
-
-def test_conv_8k_workload():
-    _ssm_conv_workload("conv_8k", 12)
 
 
 # ------------------------------------------------------------------ state passing
@@ -293,28 +261,6 @@ def test_state_pass_zero_state_equals_none(io):
     assert torch.equal(y0, y1) and torch.equal(x0, x1)
 
 
-def test_state_64k_workload():
-    w = wl.WORKLOADS["state_64k"]
-    dev = device()
-    say("workload %s B=%d H=%d N=%d T=%d %s (full-size run, sampled rows)" % (w.name, w.B, w.H, w.N, w.T, w.dtype))
-    inp = wl.make_inputs(w)
-    d = {k: v.to(dev) for k, v in inp.items()}
-    y, x = pkg.state_pass(d["u"], d["A"], d["Bm"], d["C"], d["dt"], d["D"], w.T, return_state=True)
-    torch.cuda.synchronize()
-    rows = sample_rows(w.B * w.H, 8, seed=w.seed)
-    bs, hs = rows // w.H, rows % w.H
-    u_s = inp["u"][bs, hs][None]
-    ref, xr = oracle.ssm_recurrence(to_np(u_s), cplx(inp["A"][hs]), cplx(inp["Bm"][hs]), cplx(inp["C"][hs]),
-                                    to_np(inp["dt"][hs]), to_np(inp["D"][hs]), return_state=True)
-    got = to_np(y[torch.as_tensor(bs), torch.as_tensor(hs)])
-    gx = x[torch.as_tensor(bs), torch.as_tensor(hs)].cpu().numpy().astype(np.complex128)
-    err, errx = rel_l2(got, ref[0]), rel_l2(gx, xr[0])
-    du = to_np(inp["D"][hs])[:, None] * to_np(u_s[0])
-    err_conv = rel_l2(got - du, ref[0] - du)
-    say("  rel_l2=%.3e conv_only=%.3e state=%.3e" % (err, err_conv, errx))
-    assert err <= TOL[w.dtype] and err_conv <= TOL[w.dtype] and errx <= 1e-3
-
-
 # ------------------------------------------------------------------ H3 mix
 
 @pytest.mark.parametrize("io", ["f32", "f16", "bf16"])
@@ -354,23 +300,3 @@ def test_h3_mix_vector_ragged_tiles(io):
     err = rel_l2(to_np(out), ref)
     say("  rel_l2=%.3e" % err)
     assert err <= TOL[io]
-
-
-def test_h3_mix_2k_workload():
-    w = wl.WORKLOADS["h3_mix_2k"]
-    dev = device()
-    say("workload %s B=%d N=%d Dm=%d %s (full-size run, sampled channels)" % (w.name, w.B, w.N, w.Dm, w.dtype))
-    inp = wl.make_inputs(w)
-    d = {k: v.to(dev) for k, v in inp.items()}
-    f = pkg.ssm_filter(d["A"], d["Bm"], d["C"], d["dt"], w.N)
-    out = pkg.h3_mix(d["q"], d["k"], d["v"], d["w"], f, d["D"])
-    torch.cuda.synchronize()
-    ch = sample_rows(w.Dm, 12, seed=w.seed)
-    f_ref = oracle.ssm_filter(cplx(inp["A"][ch]), cplx(inp["Bm"][ch]), cplx(inp["C"][ch]),
-                              to_np(inp["dt"][ch]), w.N)
-    sel = lambda t: t[:, :, torch.as_tensor(ch)].contiguous()
-    ref = oracle.h3_mix(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), inp["w"][ch], f_ref, inp["D"][ch])
-    got = to_np(out[:, :, torch.as_tensor(ch, device=dev)])
-    err = rel_l2(got, ref)
-    say("  rel_l2=%.3e" % err)
-    assert err <= TOL[w.dtype]
