@@ -34,8 +34,8 @@ MAX_STATE = 64
 _IO = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
 
-EXPORTS = ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_h3_mix",
-           "h3conv_workspace_size", "h3conv_status_string", "h3conv_version")
+EXPORTS = ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass",
+           "h3conv_ssm_step", "h3conv_h3_mix", "h3conv_workspace_size", "h3conv_status_string", "h3conv_version")
 
 
 class H3ConvError(RuntimeError):
@@ -57,13 +57,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.h3conv_fft_conv.argtypes = [P, P, P, P, I64, I64, I64, I, P]
     lib.h3conv_ssm_filter.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.h3conv_state_pass.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
+    lib.h3conv_ssm_step.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I, P]
     lib.h3conv_h3_mix.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.h3conv_workspace_size.argtypes = [I, I64, I64, I64, I64, I64]
     lib.h3conv_workspace_size.restype = SZ
     lib.h3conv_status_string.argtypes = [I]
     lib.h3conv_status_string.restype = ctypes.c_char_p
     lib.h3conv_version.restype = I
-    for name in ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_h3_mix"):
+    for name in ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass",
+                 "h3conv_ssm_step", "h3conv_h3_mix"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -93,39 +95,67 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, dtype=None):
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    """Type, dtype, exact shape and contiguity of one tensor argument (the
+    device is checked for all arguments of a call together, by _same_device)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
-        raise ValueError("%s must be on a HIP device" % name)
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
 
 
-def _cplx_param(t: torch.Tensor, name: str) -> torch.Tensor:
+def _same_device(**ts):
+    """Every tensor on one HIP device, which is the current one (the library
+    launches on the current device and its current stream)."""
+    devs = {n: t.device for n, t in ts.items() if t is not None}
+    for n, d in devs.items():
+        if d.type != "cuda":
+            raise ValueError("%s must be on a HIP device, got %s" % (n, d))
+    if len(set(devs.values())) > 1:
+        raise ValueError("all tensors must be on one device, got %s" % devs)
+    d = next(iter(devs.values()))
+    cur = torch.cuda.current_device()
+    if d.index is not None and d.index != cur:
+        raise ValueError("tensors are on %s but the current device is cuda:%d" % (d, cur))
+
+
+def _cplx_param(t: torch.Tensor, name: str, shape=None) -> torch.Tensor:
     """Complex parameters are accepted as complex64 [...] or float32 [..., 2]."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
     if t.is_complex():
+        if t.dtype != torch.complex64:
+            raise ValueError("%s must be complex64 or float32 [..., 2], got %s" % (name, t.dtype))
         t = torch.view_as_real(t)
-    _need(t, name, torch.float32)
-    if t.shape[-1] != 2:
+    _need(t, name, torch.float32, None if shape is None else tuple(shape) + (2,))
+    if t.dim() < 1 or t.shape[-1] != 2:
         raise ValueError("%s must be complex or have a trailing dimension of 2" % name)
     return t
+
+
+def _io(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _IO:
+        raise ValueError("%s must be float32, float16 or bfloat16, got %s" % (name, t.dtype))
+    return _IO[t.dtype]
 
 
 def fft_conv(u: torch.Tensor, f: torch.Tensor, D: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """y[b,h,:] = causal (f[h] * u[b,h])[:N] + D[h] u[b,h]; u [B,H,N] f32/f16/bf16, f [H,N] f32, D [H] f32."""
     _need(u, "u")
-    if u.dtype not in _IO:
-        raise ValueError("u must be float32, float16 or bfloat16")
+    io = _io(u, "u")
+    if u.dim() != 3:
+        raise ValueError("u must be [B,H,N], got %s" % (tuple(u.shape),))
     B, H, N = u.shape
-    _need(f, "f", torch.float32); _need(D, "D", torch.float32)
-    if tuple(f.shape) != (H, N) or tuple(D.shape) != (H,):
-        raise ValueError("f must be [H,N] and D [H]")
+    _need(f, "f", torch.float32, (H, N)); _need(D, "D", torch.float32, (H,))
+    if out is not None:
+        _need(out, "out", u.dtype, (B, H, N))
+    _same_device(u=u, f=f, D=D, out=out)
     y = torch.empty_like(u) if out is None else out
-    _need(y, "out", u.dtype)
-    _check(load().h3conv_fft_conv(_ptr(u), _ptr(f), _ptr(D), _ptr(y), B, H, N, _IO[u.dtype], _stream()),
+    _check(load().h3conv_fft_conv(_ptr(u), _ptr(f), _ptr(D), _ptr(y), B, H, N, io, _stream()),
            "h3conv_fft_conv")
     return y
 
@@ -133,14 +163,41 @@ def fft_conv(u: torch.Tensor, f: torch.Tensor, D: torch.Tensor, out: torch.Tenso
 def ssm_filter(A: torch.Tensor, Bm: torch.Tensor, C: torch.Tensor, dt: torch.Tensor, N: int,
                out: torch.Tensor | None = None) -> torch.Tensor:
     """f[h,k] = 2 Re(sum_j C exp(dt A k) dt B), k < N; A, Bm, C [H,S] complex, dt [H] f32."""
-    A = _cplx_param(A, "A"); Bm = _cplx_param(Bm, "Bm"); C = _cplx_param(C, "C")
-    _need(dt, "dt", torch.float32)
+    A = _cplx_param(A, "A")
+    if A.dim() != 3:
+        raise ValueError("A must be [H,S] complex")
     H, S = A.shape[0], A.shape[1]
-    f = torch.empty(H, N, device=A.device, dtype=torch.float32) if out is None else out
-    _need(f, "out", torch.float32)
+    Bm = _cplx_param(Bm, "Bm", (H, S)); C = _cplx_param(C, "C", (H, S))
+    _need(dt, "dt", torch.float32, (H,))
+    if out is not None:
+        _need(out, "out", torch.float32, (H, int(N)))
+    _same_device(A=A, Bm=Bm, C=C, dt=dt, out=out)
+    f = torch.empty(H, int(N), device=A.device, dtype=torch.float32) if out is None else out
     _check(load().h3conv_ssm_filter(_ptr(A), _ptr(Bm), _ptr(C), _ptr(dt), _ptr(f), H, S, int(N), _stream()),
            "h3conv_ssm_filter")
     return f
+
+
+def _sp_args(u, A, Bm, C, dt, D, x_in, out, workspace):
+    _need(u, "u")
+    io = _io(u, "u")
+    if u.dim() != 3:
+        raise ValueError("u must be [B,H,N], got %s" % (tuple(u.shape),))
+    B, H, N = u.shape
+    A = _cplx_param(A, "A")
+    if A.dim() != 3 or A.shape[0] != H:
+        raise ValueError("A must be [H,S] complex with H = %d, got %s" % (H, tuple(A.shape)))
+    S = A.shape[1]
+    Bm = _cplx_param(Bm, "Bm", (H, S)); C = _cplx_param(C, "C", (H, S))
+    _need(dt, "dt", torch.float32, (H,)); _need(D, "D", torch.float32, (H,))
+    if x_in is not None:
+        x_in = _cplx_param(x_in, "x_in", (B, H, S))
+    if out is not None:
+        _need(out, "out", u.dtype, (B, H, N))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _same_device(u=u, A=A, Bm=Bm, C=C, dt=dt, D=D, x_in=x_in, out=out, workspace=workspace)
+    return io, B, H, N, S, A, Bm, C, x_in
 
 
 def state_pass(u, A, Bm, C, dt, D, T: int, x_in=None, return_state: bool = False,
@@ -149,28 +206,46 @@ def state_pass(u, A, Bm, C, dt, D, T: int, x_in=None, return_state: bool = False
 
     Returns y, or (y, x_out) with x_out [B,H,S] complex64 if ``return_state``.
     """
-    _need(u, "u")
-    if u.dtype not in _IO:
-        raise ValueError("u must be float32, float16 or bfloat16")
-    A = _cplx_param(A, "A"); Bm = _cplx_param(Bm, "Bm"); C = _cplx_param(C, "C")
-    _need(dt, "dt", torch.float32); _need(D, "D", torch.float32)
-    B, H, N = u.shape
-    S = A.shape[1]
-    if x_in is not None:
-        x_in = _cplx_param(x_in, "x_in")
+    io, B, H, N, S, A, Bm, C, x_in = _sp_args(u, A, Bm, C, dt, D, x_in, out, workspace)
     y = torch.empty_like(u) if out is None else out
-    _need(y, "out", u.dtype)
     x_out = torch.empty(B, H, S, 2, device=u.device, dtype=torch.float32) if return_state else None
-    need = workspace_size(OP_STATE_PASS, B, H, N, S, T)
+    need = workspace_size(OP_STATE_PASS, B, H, N, S, T) if N > 0 else 0
     ws = workspace
     if ws is None or ws.numel() * ws.element_size() < need:
         ws = torch.empty(max(need, 1), device=u.device, dtype=torch.uint8)
     _check(load().h3conv_state_pass(_ptr(u), _ptr(A), _ptr(Bm), _ptr(C), _ptr(dt), _ptr(D), _ptr(x_in),
-                                     _ptr(x_out), _ptr(y), B, H, N, S, int(T), _IO[u.dtype], _ptr(ws),
+                                     _ptr(x_out), _ptr(y), B, H, N, S, int(T), io, _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream()),
            "h3conv_state_pass")
     if return_state:
         return y, torch.view_as_complex(x_out)
+    return y
+
+
+def ssm_step(u, A, Bm, C, dt, D, x, out=None):
+    """K recurrent steps per row: x <- exp(dt A) x + dt B u_t, y_t = 2 Re(C.x) + D u_t.
+
+    u [B,H,K] f32/f16/bf16; A, Bm, C [H,S] complex; dt, D [H]; x [B,H,S]
+    complex64 (or float32 [B,H,S,2]), updated in place.  Returns y [B,H,K]."""
+    _need(u, "u")
+    io = _io(u, "u")
+    if u.dim() != 3:
+        raise ValueError("u must be [B,H,K], got %s" % (tuple(u.shape),))
+    B, H, K = u.shape
+    A = _cplx_param(A, "A")
+    if A.dim() != 3 or A.shape[0] != H:
+        raise ValueError("A must be [H,S] complex with H = %d, got %s" % (H, tuple(A.shape)))
+    S = A.shape[1]
+    Bm = _cplx_param(Bm, "Bm", (H, S)); C = _cplx_param(C, "C", (H, S))
+    _need(dt, "dt", torch.float32, (H,)); _need(D, "D", torch.float32, (H,))
+    xv = _cplx_param(x, "x", (B, H, S))
+    if out is not None:
+        _need(out, "out", u.dtype, (B, H, K))
+    _same_device(u=u, A=A, Bm=Bm, C=C, dt=dt, D=D, x=xv, out=out)
+    y = torch.empty_like(u) if out is None else out
+    _check(load().h3conv_ssm_step(_ptr(u), _ptr(A), _ptr(Bm), _ptr(C), _ptr(dt), _ptr(D), _ptr(xv), _ptr(y),
+                                   B, H, K, S, io, _stream()),
+           "h3conv_ssm_step")
     return y
 
 
@@ -179,23 +254,29 @@ def h3_mix(q, k, v, w, f, D, out=None, workspace=None):
 
     16-bit activations stage m and z channel-major in a workspace
     (allocated here when not given)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype)
-    if q.dtype not in _IO:
-        raise ValueError("q, k, v must be float32, float16 or bfloat16")
+    _need(q, "q")
+    io = _io(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [B,N,Dm], got %s" % (tuple(q.shape),))
     B, N, Dm = q.shape
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must have the same shape")
-    _need(w, "w", torch.float32); _need(f, "f", torch.float32); _need(D, "D", torch.float32)
+    _need(k, "k", q.dtype, (B, N, Dm)); _need(v, "v", q.dtype, (B, N, Dm))
+    _need(w, "w", torch.float32)
+    if w.dim() != 2 or w.shape[0] != Dm:
+        raise ValueError("w must be [Dm,L] with Dm = %d, got %s" % (Dm, tuple(w.shape)))
     L = w.shape[1]
+    _need(f, "f", torch.float32, (Dm, N)); _need(D, "D", torch.float32, (Dm,))
+    if out is not None:
+        _need(out, "out", q.dtype, (B, N, Dm))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _same_device(q=q, k=k, v=v, w=w, f=f, D=D, out=out, workspace=workspace)
     o = torch.empty_like(q) if out is None else out
-    _need(o, "out", q.dtype)
     ws, nws = None, 0
     if q.dtype != torch.float32:
         ws = workspace if workspace is not None else torch.empty(
-            workspace_size(OP_H3_MIX, B, Dm, N), dtype=torch.uint8, device=q.device)
+            max(workspace_size(OP_H3_MIX, B, Dm, N), 1), dtype=torch.uint8, device=q.device)
         nws = ws.numel() * ws.element_size()
     _check(load().h3conv_h3_mix(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(f), _ptr(D), _ptr(o), B, N, Dm, L,
-                                _IO[q.dtype], _ptr(ws) if ws is not None else None, nws, _stream()),
+                                io, _ptr(ws) if ws is not None else None, nws, _stream()),
            "h3conv_h3_mix")
     return o

@@ -164,22 +164,45 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
     E.template run_raw<SPOL>(mf::row_rsrc(fh, 4 * N), dh, rows, (B + 1) / 2, hb);
 }
 
+// Row byte offsets inside one launch of the 16-bit engine are 32-bit,
+// including the empty rows a last partial round addresses (up to 2 SIG + 2
+// past the batch): larger batches go in slices of an even number of rows,
+// and a slice must hold at least two.
+template <int LOG2M>
+static constexpr uint64_t fc_row_pad() { return 2 * mf::Shape<LOG2M>::SIG + 2; }
+
+static uint64_t fc_pad_for(int log2m) {
+    switch (log2m) {
+        case 9: return fc_row_pad<9>();
+        case 10: return fc_row_pad<10>();
+        case 11: return fc_row_pad<11>();
+        case 12: return fc_row_pad<12>();
+        case 13: return fc_row_pad<13>();
+        case 14: return fc_row_pad<14>();
+        default: return 0;  // fp32 engine: 64-bit offsets
+    }
+}
+
+bool fft_conv_rows_fit(int64_t H, int64_t N, int io) {
+    if (io == IO_F32 || H <= 0 || N <= 0) return true;
+    const uint64_t pad = fc_pad_for(fused_log2m(N));
+    if (pad == 0) return true;
+    const uint64_t rowb = 2ull * (uint64_t)H * (uint64_t)N;
+    return (pad + 2) * rowb < (1ull << 32);
+}
+
 template <int LOG2M, int IO, int SPOL>
 static hipError_t launch_fc_mfma(const void *u, const float *f, const float *D, void *y, int B,
                                  int H, int N, hipStream_t s) {
     using T = typename io_elem<IO>::T;
-    // Row byte offsets inside one launch are 32-bit, including the empty rows
-    // a last partial round addresses (up to 2 SIG + 2 past the batch): larger
-    // batches go in slices of an even number of rows.
     const uint64_t rowb = 2ull * (uint64_t)H * (uint64_t)N;
-    const uint64_t pad = 2 * mf::Shape<LOG2M>::SIG + 2;
-    if ((pad + 2) * rowb >= (1ull << 32)) return hipErrorInvalidValue;
+    const uint64_t pad = fc_row_pad<LOG2M>();
+    if ((pad + 2) * rowb >= (1ull << 32)) return hipErrorInvalidValue;  // refused by the API first
     const int bmax = (int)std::min<uint64_t>((uint64_t)B, (((1ull << 32) - 1) / rowb - pad) & ~1ull);
     for (int b0 = 0; b0 < B; b0 += bmax) {
         const size_t o = (size_t)b0 * H * N;
-        hipLaunchKernelGGL((k_fft_conv_mfma<LOG2M, IO, SPOL>), dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
-                           (const T *)u + o, f, D, (T *)y + o, std::min(bmax, B - b0), H, N);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch(k_fft_conv_mfma<LOG2M, IO, SPOL>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
+                                    (const T *)u + o, f, D, (T *)y + o, std::min(bmax, B - b0), H, N);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -189,9 +212,8 @@ template <int LOG2M, int IO>
 static hipError_t launch_fc(const void *u, const float *f, const float *D, void *y, int B, int H,
                             int N, hipStream_t s) {
     using T = typename io_elem<IO>::T;
-    hipLaunchKernelGGL((k_fft_conv<LOG2M, IO>), dim3(H), dim3(Plan<LOG2M>::NT), 0, s,
-                       (const T *)u, f, D, (T *)y, B, H, N);
-    return hipGetLastError();
+    return launch(k_fft_conv<LOG2M, IO>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T *)u, f, D, (T *)y, B, H,
+                  N);
 }
 
 template <int IO, int SPOL = mf::kNT>
@@ -238,9 +260,8 @@ static hipError_t launch_hm(const void *q, const void *k, const void *v, const f
                             const float *f, const float *D, void *out, int B, int N, int Dm, int L,
                             hipStream_t s) {
     using T = typename io_elem<IO>::T;
-    hipLaunchKernelGGL((k_h3_mix<LOG2M, IO>), dim3(Dm), dim3(Plan<LOG2M>::NT), 0, s, (const T *)q,
-                       (const T *)k, (const T *)v, w, f, D, (T *)out, B, N, Dm, L);
-    return hipGetLastError();
+    return launch(k_h3_mix<LOG2M, IO>, dim3(Dm), dim3(Plan<LOG2M>::NT), 0, s, (const T *)q, (const T *)k,
+                  (const T *)v, w, f, D, (T *)out, B, N, Dm, L);
 }
 
 template <int IO>
@@ -479,17 +500,15 @@ static hipError_t hm_16bit(const void *q, const void *k, const void *v, const fl
     const dim3 grid((Dm + HM_TD - 1) / HM_TD, (N + HM_TT - 1) / HM_TT, B);
     const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)ws;
     const int vec = (N % 8 == 0 && Dm % 8 == 0 && (al & 15) == 0 && (one & 15) == 0) ? 1 : 0;
-    hipLaunchKernelGGL((k_h3_gate_in<IO>), grid, dim3(256), 0, s, (const uint16_t *)k, (const uint16_t *)v, w, mT,
-                       N, Dm, L, vec);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch(k_h3_gate_in<IO>, grid, dim3(256), 0, s, (const uint16_t *)k, (const uint16_t *)v, w,
+                          mT, N, Dm, L, vec);
     if (e != hipSuccess) return e;
     // z_T is read back by the output gate right away: its stores keep the
     // default cache policy
     e = fc_dispatch<IO_BF16, 0>(fused_log2m(N), mT, f, D, zT, B, Dm, N, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_h3_gate_out<IO>), grid, dim3(256), 0, s, (const uint16_t *)q, (const uint16_t *)zT,
-                       (uint16_t *)out, N, Dm, vec);
-    return hipGetLastError();
+    return launch(k_h3_gate_out<IO>, grid, dim3(256), 0, s, (const uint16_t *)q, (const uint16_t *)zT,
+                  (uint16_t *)out, N, Dm, vec);
 }
 
 hipError_t launch_h3_mix(const void *q, const void *k, const void *v, const float *w,

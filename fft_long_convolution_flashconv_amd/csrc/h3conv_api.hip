@@ -43,6 +43,51 @@ h3conv_status device_check() {
 
 h3conv_status from_hip(hipError_t e) { return e == hipSuccess ? H3CONV_OK : H3CONV_ERR_HIP; }
 
+// Status meaning "arguments valid, sizes non-empty: run it" (never returned
+// to a caller; within the enum's value range, above every real status).
+constexpr h3conv_status SP_RUN = (h3conv_status)7;
+
+// Host-side validation shared by the state-passing entry points (everything
+// but the workspace).  Returns SP_RUN when the call has work to do; a
+// zero-length call (N == 0) with x_out is completed here (x_out = x_in or 0).
+h3conv_status sp_validate(const void *u, const float *A, const float *Bm, const float *C,
+                          const float *dt, const float *D, const float *x_in, float *x_out,
+                          void *y, int64_t B, int64_t H, int64_t N, int64_t S, int64_t T, int io,
+                          void *stream) {
+    if (B < 0 || H < 0 || N < 0 || S < 1 || T < 1 || !valid_io(io)) return H3CONV_ERR_INVALID_ARG;
+    if (B == 0 || H == 0) return H3CONV_OK;
+    if (N == 0) {
+        // no samples: the final state is the initial one (zero without x_in)
+        if (!x_out) return H3CONV_OK;
+        if (S > H3CONV_MAX_STATE || !mul_ok(B * H, S, INT64_MAX / 16)) return H3CONV_ERR_UNSUPPORTED;
+        if (!aligned16(x_out) || (x_in && !aligned16(x_in))) return H3CONV_ERR_INVALID_ARG;
+        const size_t nx = (size_t)(B * H * S) * 8;
+        if (overlap(x_out, nx, x_in, nx)) return H3CONV_ERR_INVALID_ARG;
+        h3conv_status st = device_check();
+        if (st != H3CONV_OK) return st;
+        return from_hip(h3c::launch_state_copy(x_in, x_out, B * H * S, (hipStream_t)stream));
+    }
+    if (S > H3CONV_MAX_STATE || T < 64 || T > H3CONV_MAX_FUSED_N || (T & (T - 1)) != 0 || N % T != 0)
+        return H3CONV_ERR_UNSUPPORTED;
+    if (!u || !A || !Bm || !C || !dt || !D || !y) return H3CONV_ERR_INVALID_ARG;
+    const void *ptrs[] = {u, A, Bm, C, dt, D, y, x_in, x_out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return H3CONV_ERR_INVALID_ARG;
+    if (B > 65535 || H > 65535 || N / T > INT32_MAX || !mul_ok(B * H, N, INT64_MAX / 4))
+        return H3CONV_ERR_UNSUPPORTED;
+    const size_t ny = (size_t)(B * H * N) * esize(io), np = (size_t)(H * S) * 8,
+                 nx = (size_t)(B * H * S) * 8, nh = (size_t)H * 4;
+    // outputs (y, x_out) must not overlap the inputs or each other
+    struct R { const void *p; size_t n; } ins[] = {{u, ny}, {A, np}, {Bm, np}, {C, np},
+                                                   {dt, nh}, {D, nh}, {x_in, nx}};
+    struct R outs[] = {{y, ny}, {x_out, nx}};
+    for (auto &o : outs)
+        for (auto &i : ins)
+            if (overlap(o.p, o.n, i.p, i.n)) return H3CONV_ERR_INVALID_ARG;
+    if (overlap(y, ny, x_out, nx)) return H3CONV_ERR_INVALID_ARG;
+    return SP_RUN;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +129,7 @@ h3conv_status h3conv_fft_conv(const void *u, const float *f, const float *D, voi
     if (!aligned16(u) || !aligned16(f) || !aligned16(D) || !aligned16(y)) return H3CONV_ERR_INVALID_ARG;
     if (N > H3CONV_MAX_FUSED_N) return H3CONV_ERR_UNSUPPORTED;
     if (!mul_ok(B, H, INT32_MAX) || !mul_ok(B * H, N, INT64_MAX / 4)) return H3CONV_ERR_UNSUPPORTED;
+    if (!h3c::fft_conv_rows_fit(H, N, io)) return H3CONV_ERR_UNSUPPORTED;
     const size_t ny = (size_t)(B * H * N) * esize(io);
     if (overlap(y, ny, u, ny) || overlap(y, ny, f, (size_t)(H * N) * 4) ||
         overlap(y, ny, D, (size_t)H * 4))
@@ -116,35 +162,48 @@ h3conv_status h3conv_state_pass(const void *u, const float *A, const float *Bm, 
                                 const float *dt, const float *D, const float *x_in, float *x_out,
                                 void *y, int64_t B, int64_t H, int64_t N, int64_t S, int64_t T,
                                 int io, void *ws, size_t ws_bytes, void *stream) {
-    if (B < 0 || H < 0 || N < 0 || S < 1 || T < 1 || !valid_io(io)) return H3CONV_ERR_INVALID_ARG;
-    if (B == 0 || H == 0) return H3CONV_OK;
-    if (S > H3CONV_MAX_STATE || T < 64 || T > H3CONV_MAX_FUSED_N || (T & (T - 1)) != 0 ||
-        N == 0 || N % T != 0)
-        return N == 0 ? H3CONV_OK : H3CONV_ERR_UNSUPPORTED;
-    if (!u || !A || !Bm || !C || !dt || !D || !y) return H3CONV_ERR_INVALID_ARG;
-    const void *ptrs[] = {u, A, Bm, C, dt, D, y, x_in, x_out, ws};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p)) return H3CONV_ERR_INVALID_ARG;
-    if (B > 65535 || H > 65535 || N / T > INT32_MAX || !mul_ok(B * H, N, INT64_MAX / 4))
-        return H3CONV_ERR_UNSUPPORTED;
+    h3conv_status st = sp_validate(u, A, Bm, C, dt, D, x_in, x_out, y, B, H, N, S, T, io, stream);
+    if (st != SP_RUN) return st;
+    const size_t need = h3c::state_pass_workspace_io(B, H, N, S, T, io);
+    if (!ws || ws_bytes < need) return H3CONV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return H3CONV_ERR_INVALID_ARG;
+    // the workspace must not overlap any input or output
     const size_t ny = (size_t)(B * H * N) * esize(io), np = (size_t)(H * S) * 8,
                  nx = (size_t)(B * H * S) * 8, nh = (size_t)H * 4;
-    const size_t need = h3c::state_pass_workspace(B, H, N, S, T);
-    if (!ws || ws_bytes < need) return H3CONV_ERR_WORKSPACE;
-    // outputs (y, x_out, ws) must not overlap inputs or each other
-    struct R { const void *p; size_t n; } ins[] = {{u, ny}, {A, np}, {Bm, np}, {C, np},
-                                                   {dt, nh}, {D, nh}, {x_in, nx}};
-    struct R outs[] = {{y, ny}, {x_out, nx}, {ws, need}};
-    for (auto &o : outs) {
-        for (auto &i : ins)
-            if (overlap(o.p, o.n, i.p, i.n)) return H3CONV_ERR_INVALID_ARG;
-    }
-    if (overlap(y, ny, x_out, nx) || overlap(y, ny, ws, need) || overlap(x_out, nx, ws, need))
-        return H3CONV_ERR_INVALID_ARG;
-    h3conv_status st = device_check();
+    struct R { const void *p; size_t n; } bufs[] = {{u, ny}, {A, np}, {Bm, np}, {C, np}, {dt, nh},
+                                                    {D, nh}, {x_in, nx}, {y, ny}, {x_out, nx}};
+    for (auto &b : bufs)
+        if (overlap(ws, need, b.p, b.n)) return H3CONV_ERR_INVALID_ARG;
+    st = device_check();
     if (st != H3CONV_OK) return st;
     return from_hip(h3c::launch_state_pass(u, A, Bm, C, dt, D, x_in, x_out, y, (int)B, (int)H, N,
                                            (int)S, (int)T, io, ws, (hipStream_t)stream));
+}
+
+h3conv_status h3conv_ssm_step(const void *u, const float *A, const float *Bm, const float *C,
+                              const float *dt, const float *D, float *x, void *y, int64_t B, int64_t H,
+                              int64_t K, int64_t S, int io, void *stream) {
+    if (B < 0 || H < 0 || K < 0 || S < 1 || !valid_io(io)) return H3CONV_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || K == 0) return H3CONV_OK;
+    if (S > H3CONV_MAX_STATE) return H3CONV_ERR_UNSUPPORTED;
+    if (!u || !A || !Bm || !C || !dt || !D || !x || !y) return H3CONV_ERR_INVALID_ARG;
+    const void *ptrs[] = {u, A, Bm, C, dt, D, x, y};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return H3CONV_ERR_INVALID_ARG;
+    if (H > INT32_MAX || !mul_ok(B, H, ((int64_t)UINT32_MAX) * 4) || !mul_ok(B * H, K, INT64_MAX / 4) ||
+        !mul_ok(B * H, S, INT64_MAX / 16))
+        return H3CONV_ERR_UNSUPPORTED;
+    const size_t ny = (size_t)(B * H * K) * esize(io), np = (size_t)(H * S) * 8,
+                 nx = (size_t)(B * H * S) * 8, nh = (size_t)H * 4;
+    // outputs (y, and x, read and written in place) must not overlap the
+    // inputs or each other
+    struct R { const void *p; size_t n; } ins[] = {{u, ny}, {A, np}, {Bm, np}, {C, np}, {dt, nh}, {D, nh}};
+    for (auto &i : ins)
+        if (overlap(y, ny, i.p, i.n) || overlap(x, nx, i.p, i.n)) return H3CONV_ERR_INVALID_ARG;
+    if (overlap(y, ny, x, nx)) return H3CONV_ERR_INVALID_ARG;
+    h3conv_status st = device_check();
+    if (st != H3CONV_OK) return st;
+    return from_hip(h3c::launch_ssm_step(u, A, Bm, C, dt, D, x, y, B, H, K, (int)S, io, (hipStream_t)stream));
 }
 
 h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const float *w,
@@ -158,6 +217,10 @@ h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const f
     for (const void *p : ptrs)
         if (!aligned16(p)) return H3CONV_ERR_INVALID_ARG;
     if (!mul_ok(B, Dm, INT32_MAX) || !mul_ok(B * Dm, N, INT64_MAX / 4)) return H3CONV_ERR_UNSUPPORTED;
+    // 16-bit path: one gate workgroup row per batch row (grid z <= 65535),
+    // and the channel-major convolution rows within 32-bit slice offsets
+    if (io != H3CONV_F32 && (B > 65535 || !h3c::fft_conv_rows_fit(Dm, N, H3CONV_BF16)))
+        return H3CONV_ERR_UNSUPPORTED;
     const size_t n = (size_t)(B * N * Dm) * esize(io);
     if (overlap(out, n, q, n) || overlap(out, n, k, n) || overlap(out, n, v, n) ||
         overlap(out, n, w, (size_t)(Dm * L) * 4) || overlap(out, n, f, (size_t)(Dm * N) * 4) ||

@@ -15,6 +15,9 @@
 //   x_c = Abar^T x_{c-1} + sum_k Abar^{T-1-k} Bbar u_{c,k}
 // The chunk convolutions run on the fused FFT engine; the two projections use
 // the same factored power tables.
+#include <algorithm>
+#include <atomic>
+
 #include "h3conv_device.h"
 #include "h3conv_internal.h"
 #include "mfma_engine.h"
@@ -200,19 +203,18 @@ __global__ __launch_bounds__(512) void k_ssm_filter(const float *__restrict__ A,
 
 hipError_t launch_ssm_filter(const float *A, const float *Bm, const float *C, const float *dt,
                              float *f, int H, int S, int64_t N, hipStream_t s) {
-    hipLaunchKernelGGL(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, (const float *)nullptr,
-                       f, S, N, N);
-    return hipGetLastError();
+    return launch(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, (const float *)nullptr, f, S, N, N);
 }
 
 // ---------------------------------------------------------------- state passing
 
-// Workspace layout (256-byte aligned blocks):
+// Workspace layout (256-byte aligned blocks), by path.  Both start with
 //   fT  [H, T]            chunk filter with D folded into tap 0            fp32
+// fp32 activations (vector-ALU projections) then hold
 //   E   [H, S, 65]        Abar^l, l = 0..64                                complex
 //   G   [H, S, T/64 + 1]  Abar^(64 i), i = 0..T/64                         complex
 //   sc  [B, H, C, 64]     per-chunk state contributions                    complex
-// and for the matrix-core projections (16-bit activations), modes padded to 64:
+// and 16-bit activations (matrix-core projections, modes padded to 64)
 //   Et  [H, 128, 64]      row 2j+p, column l: part p of Abar_j^(63-l)      fp16
 //   Rt  [H, 64, 128]      row l, column 2j+p: 2 Re / -2 Im of C_j Abar_j^(l+1)  fp16
 //   Pc  [H, 64, 8]        Bbar_j Abar_j^(1024 (NCT-1-ih))                  complex
@@ -221,33 +223,41 @@ hipError_t launch_ssm_filter(const float *A, const float *Bm, const float *C, co
 //   Qx  [H, 64, 16]       Abar_j^(64 il), zero for il >= TL                complex
 //   aT  [H, 64]           Abar_j^T                                         complex
 // with T2 = T/64 columns i = 16 ih + il, NCT = ceil(T2/16), TL = min(T2, 16).
+// The workspace size the API reports is the larger of the two.
 struct SpLayout {
     size_t fT, E, G, sc, Et, Rt, Pc, Qc, Px, Qx, aT, total;
 };
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static SpLayout sp_layout(int64_t B, int64_t H, int64_t N, int64_t S, int64_t T) {
-    SpLayout L;
+static SpLayout sp_layout(int64_t B, int64_t H, int64_t N, int64_t S, int64_t T, bool f32) {
+    SpLayout L{};
     const int64_t C = N / T, T2 = T / 64;
     size_t o = 0;
     L.fT = o; o += al256((size_t)H * T * 4);
-    L.E = o; o += al256((size_t)H * S * 65 * 8);
-    L.G = o; o += al256((size_t)H * S * (T2 + 1) * 8);
-    L.sc = o; o += al256((size_t)B * H * C * 64 * 8);
-    L.Et = o; o += al256((size_t)H * 128 * 64 * 2);
-    L.Rt = o; o += al256((size_t)H * 64 * 128 * 2);
-    L.Pc = o; o += al256((size_t)H * 64 * 8 * 8);
-    L.Qc = o; o += al256((size_t)H * 64 * 16 * 8);
-    L.Px = o; o += al256((size_t)H * 64 * 8 * 8);
-    L.Qx = o; o += al256((size_t)H * 64 * 16 * 8);
-    L.aT = o; o += al256((size_t)H * 64 * 8);
+    if (f32) {
+        L.E = o; o += al256((size_t)H * S * 65 * 8);
+        L.G = o; o += al256((size_t)H * S * (T2 + 1) * 8);
+        L.sc = o; o += al256((size_t)B * H * C * 64 * 8);
+    } else {
+        L.Et = o; o += al256((size_t)H * 128 * 64 * 2);
+        L.Rt = o; o += al256((size_t)H * 64 * 128 * 2);
+        L.Pc = o; o += al256((size_t)H * 64 * 8 * 8);
+        L.Qc = o; o += al256((size_t)H * 64 * 16 * 8);
+        L.Px = o; o += al256((size_t)H * 64 * 8 * 8);
+        L.Qx = o; o += al256((size_t)H * 64 * 16 * 8);
+        L.aT = o; o += al256((size_t)H * 64 * 8);
+    }
     L.total = o;
     return L;
 }
 
 size_t state_pass_workspace(int64_t B, int64_t H, int64_t N, int64_t S, int64_t T) {
-    return sp_layout(B, H, N, S, T).total;
+    return std::max(sp_layout(B, H, N, S, T, true).total, sp_layout(B, H, N, S, T, false).total);
+}
+
+size_t state_pass_workspace_io(int64_t B, int64_t H, int64_t N, int64_t S, int64_t T, int io) {
+    return sp_layout(B, H, N, S, T, io == IO_F32).total;
 }
 
 __global__ __launch_bounds__(256) void k_sp_tables(const float *__restrict__ A,
@@ -869,13 +879,45 @@ static hipError_t sp_conv(const void *u, const float *fT, void *y, int B, int H,
                           hipStream_t s) {
     using T_ = typename io_elem<IO>::T;
     if constexpr (IO != IO_F32 && LOG2M >= 9) {
-        hipLaunchKernelGGL((k_sp_chunk_conv_mfma<LOG2M, IO>), dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
-                           (const T_ *)u, fT, (T_ *)y, B, H, N, T);
+        return launch(k_sp_chunk_conv_mfma<LOG2M, IO>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s, (const T_ *)u,
+                      fT, (T_ *)y, B, H, N, T);
     } else {
-        hipLaunchKernelGGL((k_sp_chunk_conv<LOG2M, IO>), dim3(H), dim3(Plan<LOG2M>::NT), 0, s,
-                           (const T_ *)u, fT, (T_ *)y, B, H, N, T);
+        return launch(k_sp_chunk_conv<LOG2M, IO>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T_ *)u, fT,
+                      (T_ *)y, B, H, N, T);
     }
-    return hipGetLastError();
+}
+
+// Dynamic LDS limits of the fp32 projection kernels, set once per device
+// (for the largest chunk, T = 8192) with the status of the calls kept.
+template <int IO>
+static hipError_t sp_f32_attributes() {
+    constexpr int kDev = 64;
+    static std::atomic<int> state[kDev];  // 0 unset, 1 set, else -(hipError_t)
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDev) return hipErrorInvalidDevice;
+    const int st = state[dev].load(std::memory_order_acquire);
+    if (st == 1) return hipSuccess;
+    if (st < 0) return (hipError_t)(-st);
+    const int sm_c = 8192 * 4 + 64 * 64 * 8 + 4 * 64 * 8;
+    const int sm_x = 64 * 64 * 8 + 64 * (8192 / 64) * 8;
+    e = hipFuncSetAttribute((const void *)k_sp_contrib<IO>, hipFuncAttributeMaxDynamicSharedMemorySize, sm_c);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)k_sp_correct<IO>, hipFuncAttributeMaxDynamicSharedMemorySize, sm_x);
+    state[dev].store(e == hipSuccess ? 1 : -(int)e, std::memory_order_release);
+    return e;
+}
+
+__global__ __launch_bounds__(256) void k_state_copy(const float *__restrict__ x_in, float *__restrict__ x_out,
+                                                   int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n; i += (int64_t)gridDim.x * 256)
+        x_out[i] = x_in ? x_in[i] : 0.f;
+}
+
+hipError_t launch_state_copy(const float *x_in, float *x_out, int64_t n, hipStream_t s) {
+    const int64_t blocks = std::min<int64_t>((2 * n + 255) / 256, 65535);
+    return launch(k_state_copy, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, x_in, x_out, n);
 }
 
 template <int IO>
@@ -883,7 +925,7 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
                          const float *dt, const float *D, const float *x_in, float *x_out, void *y,
                          int B, int H, int64_t N, int S, int T, void *ws, hipStream_t s) {
     using T_ = typename io_elem<IO>::T;
-    const SpLayout L = sp_layout(B, H, N, S, T);
+    const SpLayout L = sp_layout(B, H, N, S, T, IO == IO_F32);
     char *w = (char *)ws;
     float *fT = (float *)(w + L.fT);
     cf *E = (cf *)(w + L.E);
@@ -893,16 +935,15 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
 
     hipError_t e;
     if constexpr (IO != IO_F32) {
-        hipLaunchKernelGGL(k_sp_params, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, (uint16_t *)(w + L.Et),
-                           (uint16_t *)(w + L.Rt), (cf *)(w + L.Pc), (cf *)(w + L.Qc), (cf *)(w + L.Px),
-                           (cf *)(w + L.Qx), (cf *)(w + L.aT), S, T);
+        e = launch(k_sp_params, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, (uint16_t *)(w + L.Et),
+                   (uint16_t *)(w + L.Rt), (cf *)(w + L.Pc), (cf *)(w + L.Qc), (cf *)(w + L.Px), (cf *)(w + L.Qx),
+                   (cf *)(w + L.aT), S, T);
     } else {
-        hipLaunchKernelGGL(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, S, (int64_t)T,
-                           (int64_t)T);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_sp_tables, dim3(H), dim3(256), 0, s, A, dt, E, G, S, T2);
+        e = launch(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, S, (int64_t)T, (int64_t)T);
+        if (e != hipSuccess) return e;
+        e = launch(k_sp_tables, dim3(H), dim3(256), 0, s, A, dt, E, G, S, T2);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
     switch (fused_log2m(T)) {
         case 7: e = sp_conv<7, IO>(u, fT, y, B, H, N, T, s); break;
         case 8: e = sp_conv<8, IO>(u, fT, y, B, H, N, T, s); break;
@@ -916,24 +957,21 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
     }
     if (e != hipSuccess) return e;
     if constexpr (IO != IO_F32) {
-        hipLaunchKernelGGL((k_sp_proj_mfma<IO>), dim3(H, B), dim3(512), 0, s, (const T_ *)u, (T_ *)y,
-                           (const uint16_t *)(w + L.Et), (const uint16_t *)(w + L.Rt), (const cf *)(w + L.Pc),
-                           (const cf *)(w + L.Qc), (const cf *)(w + L.Px), (const cf *)(w + L.Qx),
-                           (const cf *)(w + L.aT), x_in, x_out, H, N, S, T);
-        return hipGetLastError();
+        return launch(k_sp_proj_mfma<IO>, dim3(H, B), dim3(512), 0, s, (const T_ *)u, (T_ *)y,
+                      (const uint16_t *)(w + L.Et), (const uint16_t *)(w + L.Rt), (const cf *)(w + L.Pc),
+                      (const cf *)(w + L.Qc), (const cf *)(w + L.Px), (const cf *)(w + L.Qx),
+                      (const cf *)(w + L.aT), x_in, x_out, H, N, S, T);
     } else {
         const size_t sm_c = (size_t)T * 4 + 64 * 64 * 8 + 4 * 64 * 8;
         const size_t sm_x = 64 * 64 * 8 + (size_t)64 * T2 * 8;
-        (void)hipFuncSetAttribute((const void *)k_sp_contrib<IO>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sm_c);
-        (void)hipFuncSetAttribute((const void *)k_sp_correct<IO>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sm_x);
-        hipLaunchKernelGGL((k_sp_contrib<IO>), dim3(C_, H, B), dim3(256), sm_c, s, (const T_ *)u, Bm, dt,
-                           E, G, sc, B, H, N, S, T);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_sp_correct<IO>), dim3(C_, H, B), dim3(256), sm_x, s, (T_ *)y, C, E, G, sc,
-                           x_in, x_out, B, H, N, S, T);
-        return hipGetLastError();
+        // the dynamic LDS limits are set once per device, for the largest
+        // chunk length (T = 8192), and their status is checked
+        if ((e = sp_f32_attributes<IO>()) != hipSuccess) return e;
+        e = launch(k_sp_contrib<IO>, dim3(C_, H, B), dim3(256), sm_c, s, (const T_ *)u, Bm, dt, E, G, sc, B, H,
+                   N, S, T);
+        if (e != hipSuccess) return e;
+        return launch(k_sp_correct<IO>, dim3(C_, H, B), dim3(256), sm_x, s, (T_ *)y, C, E, G, sc, x_in, x_out,
+                      B, H, N, S, T);
     }
 }
 

@@ -69,7 +69,17 @@ typedef enum { H3CONV_OP_FFT_CONV = 0, H3CONV_OP_STATE_PASS = 1, H3CONV_OP_H3_MI
  *   D  [H]      fp32         residual weight
  *   y  [B,H,N]  io dtype     output (must not overlap u, f or D)
  * Supported: 1 <= N <= H3CONV_MAX_FUSED_N (any N; longer inputs use
- * h3conv_state_pass), B*H < 2^31.  Otherwise H3CONV_ERR_UNSUPPORTED.
+ * h3conv_state_pass), B*H < 2^31, and for 16-bit activations with N > 128
+ * (the matrix-core engine, whose row offsets within one launch are 32-bit)
+ * (2*SIG + 4) * 2*H*N < 2^32 bytes, SIG being the complex signals per round
+ * of that transform size: 8 for 2N = 512, 4 for 1024 and 2048, 2 for 4096,
+ * 1 for 8192 and 16384 (so at N = 8192, H <= 43690).  Larger batches B are
+ * split by the library.  Otherwise H3CONV_ERR_UNSUPPORTED, before any HIP call.
+ * Rows are transformed two at a time as one complex signal; each row has a
+ * scale of its own, so its error is set by its own magnitude, and a row of
+ * zeros gives exact zeros (16-bit activations).  With fp32 activations a
+ * row's rounding error also holds a part of about 2^-22 times its partner
+ * row's magnitude.
  */
 h3conv_status h3conv_fft_conv(const void *u, const float *f, const float *D, void *y,
                               int64_t B, int64_t H, int64_t N, int io, void *stream);
@@ -108,12 +118,41 @@ h3conv_status h3conv_ssm_filter(const float *A, const float *Bm, const float *C,
  *   y      [B,H,N]  io dtype      output (must not overlap any input)
  *   ws, ws_bytes    workspace of at least h3conv_workspace_size(H3CONV_OP_STATE_PASS, ...)
  * Supported: T a power of two, 64 <= T <= H3CONV_MAX_FUSED_N, N % T == 0,
- * 1 <= S <= H3CONV_MAX_STATE.
+ * 1 <= S <= H3CONV_MAX_STATE, B <= 65535, H <= 65535.  N == 0 writes x_in
+ * (or zeros) to x_out and nothing else.
+ * 16-bit activations require stable or neutral modes, |exp(dt A_j)| <= 1
+ * (Re(dt A_j) <= 0), as every SSM of the pages is: the powers of Abar that
+ * the projections use are then fp16 operands in [-1, 1].  Modes with
+ * |Abar| > 1 overflow them (the results are then undefined); fp32
+ * activations have no such limit.
  */
 h3conv_status h3conv_state_pass(const void *u, const float *A, const float *Bm, const float *C,
                                 const float *dt, const float *D, const float *x_in, float *x_out,
                                 void *y, int64_t B, int64_t H, int64_t N, int64_t S, int64_t T,
                                 int io, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Recurrent generation: K steps of the diagonal SSM per row from its current
+ * state, the state updated in place (the recurrent view of the blog's
+ * section "Background: What Are State Space Models?" and of the
+ * paperlayer.ai summary, section 2; cheap generation, summary section 5):
+ *     x_j <- Abar_j x_j + Bbar_j u_t,   y_t = 2 Re(sum_j C_j x_j) + D u_t
+ * for t = 0 .. K-1, Abar = exp(dt A), Bbar = dt B: the recurrence and state
+ * layout of h3conv_state_pass, so x_out of a state-passing prefix continues
+ * here token by token.
+ *
+ *   u      [B,H,K]  io dtype      the next K inputs of every row
+ *   A,Bm,C [H,S]    complex fp32  SSM parameters
+ *   dt, D  [H]      fp32
+ *   x      [B,H,S]  complex fp32  state: read, then overwritten with the
+ *                                 state after the K steps
+ *   y      [B,H,K]  io dtype      outputs (must not overlap any input or x)
+ * Supported: 1 <= S <= H3CONV_MAX_STATE, B*H <= 2^34.  The recurrence runs
+ * in fp32 (Abar from fp64 exponentials).
+ */
+h3conv_status h3conv_ssm_step(const void *u, const float *A, const float *Bm, const float *C,
+                              const float *dt, const float *D, float *x, void *y, int64_t B, int64_t H,
+                              int64_t K, int64_t S, int io, void *stream);
 
 /*
  * H3 mixing with head dimension 1 (the blog's section "The Solution, Part 1";
@@ -130,7 +169,9 @@ h3conv_status h3conv_state_pass(const void *u, const float *A, const float *Bm, 
  *             16-byte aligned, overlapping nothing else (m and z are staged
  *             there channel-major, as bf16); ignored for H3CONV_F32 (may be
  *             NULL).  Too small or NULL: H3CONV_ERR_WORKSPACE.
- * Supported: 1 <= N <= H3CONV_MAX_FUSED_N, 1 <= L <= 4, B*Dm < 2^31.
+ * Supported: 1 <= N <= H3CONV_MAX_FUSED_N, 1 <= L <= 4, B*Dm < 2^31; for
+ * 16-bit activations also B <= 65535 and the h3conv_fft_conv limit with
+ * H = Dm.  Otherwise H3CONV_ERR_UNSUPPORTED, before any HIP call.
  */
 h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const float *w,
                             const float *f, const float *D, void *out, int64_t B, int64_t N,

@@ -132,3 +132,98 @@ def test_valid_call_without_device_reports_no_device(lib):
     if torch.cuda.device_count() > 0:
         pytest.skip("a HIP device is present; this host-only path is exercised on CPU machines")
     assert _fc(lib) == pkg.ERR_NO_DEVICE
+
+
+def test_row_offset_limits_refused_before_any_hip_call(lib):
+    """The 16-bit engine keeps row byte offsets of one launch within 32 bits:
+    (2 SIG + 4) * 2 H N < 2^32 (SIG = 1 at N = 8192, so H <= 43690).  Larger
+    H is refused on the host (UNSUPPORTED, not NO_DEVICE on a GPU-less host)."""
+    assert _fc(lib, B=2, H=43691, N=8192, io=1) == pkg.ERR_UNSUPPORTED
+    assert _fc(lib, B=2, H=43691, N=8192, io=2) == pkg.ERR_UNSUPPORTED
+    # at N = 1024 (SIG = 4): 12 * 2 H * 1024 < 2^32  <=>  H <= 174762
+    assert _fc(lib, B=2, H=174763, N=1024, io=1) == pkg.ERR_UNSUPPORTED
+    # fp32 activations use 64-bit offsets
+    r = _fc(lib, u=1 << 40, f=2 << 40, D=3 << 40, y=4 << 40, B=2, H=43691, N=8192, io=0)
+    assert r in (pkg.ERR_NO_DEVICE, pkg.OK, pkg.ERR_HIP) and r != pkg.ERR_UNSUPPORTED
+    # the H3 mix: B <= 65535 and the same row limit with H = Dm (16-bit)
+    assert _hm(lib, B=65536, io=2) == pkg.ERR_UNSUPPORTED
+    assert _hm(lib, N=8192, Dm=43691, io=1) == pkg.ERR_UNSUPPORTED
+
+
+def test_state_pass_zero_length(lib):
+    """N == 0: only x_out is written (a copy of x_in, or zeros); it is
+    validated like any output."""
+    assert _sp(lib, N=0) == pkg.OK                                     # no x_out: nothing to do
+    assert _sp(lib, N=0, x_out=0x300008) == pkg.ERR_INVALID_ARG        # misaligned
+    assert _sp(lib, N=0, x_in=0x300000, x_out=0x300000) == pkg.ERR_INVALID_ARG  # overlap
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert _sp(lib, N=0, x_out=0x300000) == pkg.ERR_NO_DEVICE
+
+
+# ------------------------------------------------------------------ Python binding
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.float32)
+
+
+def test_binding_checks_every_shape():
+    """Every tensor's exact shape is checked before the C ABI is called (the
+    library cannot see buffer sizes); CPU tensors of the right shapes are
+    then refused for their device."""
+    import torch
+    h = torch.float16
+    u = _cpu(2, 3, 64, dtype=h)
+    with pytest.raises(ValueError, match="f must have shape"):
+        pkg.fft_conv(u, _cpu(3, 63), _cpu(3))
+    with pytest.raises(ValueError, match="D must have shape"):
+        pkg.fft_conv(u, _cpu(3, 64), _cpu(4))
+    with pytest.raises(ValueError, match="out must have shape"):
+        pkg.fft_conv(u, _cpu(3, 64), _cpu(3), out=_cpu(2, 3, 32, dtype=h))
+    with pytest.raises(ValueError, match="out must be"):
+        pkg.fft_conv(u, _cpu(3, 64), _cpu(3), out=_cpu(2, 3, 64))
+    with pytest.raises(ValueError, match="HIP device"):
+        pkg.fft_conv(u, _cpu(3, 64), _cpu(3))
+    A = _cpu(3, 8, 2)
+    with pytest.raises(ValueError, match="Bm must have shape"):
+        pkg.ssm_filter(A, _cpu(3, 7, 2), A.clone(), _cpu(3), 64)
+    with pytest.raises(ValueError, match="dt must have shape"):
+        pkg.ssm_filter(A, A.clone(), A.clone(), _cpu(4), 64)
+    with pytest.raises(ValueError, match="out must have shape"):
+        pkg.ssm_filter(A, A.clone(), A.clone(), _cpu(3), 64, out=_cpu(3, 65))
+    with pytest.raises(ValueError, match="A must be"):
+        pkg.state_pass(u, _cpu(4, 8, 2), A.clone(), A.clone(), _cpu(3), _cpu(3), 64)
+    with pytest.raises(ValueError, match="C must have shape"):
+        pkg.state_pass(u, A, A.clone(), _cpu(3, 8), _cpu(3), _cpu(3), 64)
+    with pytest.raises(ValueError, match="x_in must have shape"):
+        pkg.state_pass(u, A, A.clone(), A.clone(), _cpu(3), _cpu(3), 64, x_in=_cpu(2, 3, 7, 2))
+    with pytest.raises(ValueError, match="D must have shape"):
+        pkg.state_pass(u, A, A.clone(), A.clone(), _cpu(3), _cpu(2), 64)
+    q = _cpu(2, 64, 5, dtype=h)
+    with pytest.raises(ValueError, match="k must have shape"):
+        pkg.h3_mix(q, _cpu(2, 64, 4, dtype=h), q.clone(), _cpu(5, 4), _cpu(5, 64), _cpu(5))
+    with pytest.raises(ValueError, match="w must be"):
+        pkg.h3_mix(q, q.clone(), q.clone(), _cpu(4, 4), _cpu(5, 64), _cpu(5))
+    with pytest.raises(ValueError, match="f must have shape"):
+        pkg.h3_mix(q, q.clone(), q.clone(), _cpu(5, 4), _cpu(5, 63), _cpu(5))
+    with pytest.raises(ValueError, match="out must have shape"):
+        pkg.h3_mix(q, q.clone(), q.clone(), _cpu(5, 4), _cpu(5, 64), _cpu(5), out=_cpu(2, 64, 6, dtype=h))
+    with pytest.raises(ValueError, match="HIP device"):
+        pkg.h3_mix(q, q.clone(), q.clone(), _cpu(5, 4), _cpu(5, 64), _cpu(5))
+
+
+def test_ssm_step_validation(lib):
+    f = lib.h3conv_ssm_step
+
+    def call(u=0x100000, x=0x700000, y=0x800000, B=2, H=4, K=3, S=8, io=1):
+        return f(u, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, x, y, B, H, K, S, io, None)
+
+    assert call(S=0) == pkg.ERR_INVALID_ARG
+    assert call(S=65) == pkg.ERR_UNSUPPORTED
+    assert call(K=-1) == pkg.ERR_INVALID_ARG
+    assert call(u=None) == pkg.ERR_INVALID_ARG
+    assert call(x=0x700008) == pkg.ERR_INVALID_ARG          # misaligned
+    assert call(y=0x100000) == pkg.ERR_INVALID_ARG          # y aliases u
+    assert call(x=0x200000) == pkg.ERR_INVALID_ARG          # x aliases A
+    assert call(K=0, u=None, x=None, y=None) == pkg.OK      # empty: no-op

@@ -261,6 +261,43 @@ def test_state_pass_zero_state_equals_none(io):
     assert torch.equal(y0, y1) and torch.equal(x0, x1)
 
 
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_state_pass_neutral_modes(io):
+    """Modes on the unit circle (Re A = 0, |exp(dt A)| = 1, the edge of what
+    16-bit state passing supports): the powers of Abar stay in fp16 range and
+    the result is the full-length recurrence."""
+    dev = device()
+    B, H, N, S, T = 2, 3, 4096, 16, 1024
+    say("state_pass neutral modes io=%s B=%d H=%d N=%d S=%d T=%d" % (io, B, H, N, S, T))
+    u, p, D = _sp_inputs(B, H, N, S, io, seed=505)
+    p["A"][..., 0] = 0.0
+    d = {k: v.to(dev) for k, v in p.items()}
+    y, x = pkg.state_pass(u.to(dev), d["A"], d["Bm"], d["C"], d["dt"], D.to(dev), T, return_state=True)
+    torch.cuda.synchronize()
+    ref, xr = _sp_ref(u, p, D)
+    err, errx = rel_l2(to_np(y), ref), rel_l2(x.cpu().numpy().astype(np.complex128), xr)
+    say("  rel_l2=%.3e state=%.3e" % (err, errx))
+    assert np.isfinite(to_np(y)).all()
+    assert err <= TOL[io] and errx <= 1e-3
+
+
+def test_state_pass_zero_length_writes_state():
+    """No samples: x_out is x_in (or zero without x_in)."""
+    dev = device()
+    B, H, S = 2, 3, 8
+    say("state_pass N=0 B=%d H=%d S=%d" % (B, H, S))
+    u, p, D = _sp_inputs(B, H, 0, S, "f16", seed=9)
+    d = {k: v.to(dev) for k, v in p.items()}
+    xi = torch.randn(B, H, S, dtype=torch.complex64, device=dev)
+    y, x = pkg.state_pass(u.to(dev), d["A"], d["Bm"], d["C"], d["dt"], D.to(dev), 64, x_in=xi,
+                          return_state=True)
+    torch.cuda.synchronize()
+    assert y.shape == (B, H, 0) and torch.equal(x, xi)
+    y, x = pkg.state_pass(u.to(dev), d["A"], d["Bm"], d["C"], d["dt"], D.to(dev), 64, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(torch.view_as_real(x)) == 0
+
+
 # ------------------------------------------------------------------ H3 mix
 
 @pytest.mark.parametrize("io", ["f32", "f16", "bf16"])
