@@ -34,8 +34,9 @@ MAX_STATE = 64
 _IO = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
 
-EXPORTS = ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass",
+EXPORTS = ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
            "h3conv_ssm_step", "h3conv_h3_mix", "h3conv_workspace_size", "h3conv_status_string", "h3conv_version")
+NOALLOC_WORKSPACE_BYTES = 128 * 1024 * 1024
 
 
 class H3ConvError(RuntimeError):
@@ -57,6 +58,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.h3conv_fft_conv.argtypes = [P, P, P, P, I64, I64, I64, I, P]
     lib.h3conv_ssm_filter.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.h3conv_state_pass.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
+    lib.h3conv_state_pass_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P]
     lib.h3conv_ssm_step.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I, P]
     lib.h3conv_h3_mix.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.h3conv_workspace_size.argtypes = [I, I64, I64, I64, I64, I64]
@@ -64,7 +66,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.h3conv_status_string.argtypes = [I]
     lib.h3conv_status_string.restype = ctypes.c_char_p
     lib.h3conv_version.restype = I
-    for name in ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass",
+    for name in ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
                  "h3conv_ssm_step", "h3conv_h3_mix"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -220,6 +222,25 @@ def state_pass(u, A, Bm, C, dt, D, T: int, x_in=None, return_state: bool = False
     if return_state:
         return y, torch.view_as_complex(x_out)
     return y
+
+
+def state_pass_noalloc(u, A, Bm, C, dt, D, T: int, out, x_in=None, x_out=None):
+    """state_pass through h3conv_state_pass_noalloc: no workspace, no device
+    allocation in the library or here (``out``, and ``x_out`` [B,H,S,2]
+    float32 if the final state is wanted, are the caller's).  The library's
+    static scratch array of NOALLOC_WORKSPACE_BYTES per device is shared by
+    all such calls on a device: calls that overlap in time race."""
+    io, B, H, N, S, A, Bm, C, x_in = _sp_args(u, A, Bm, C, dt, D, x_in, out, None)
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    if x_out is not None:
+        x_out = _cplx_param(x_out, "x_out", (B, H, S))
+        _same_device(u=u, x_out=x_out)
+    _check(load().h3conv_state_pass_noalloc(_ptr(u), _ptr(A), _ptr(Bm), _ptr(C), _ptr(dt), _ptr(D),
+                                             _ptr(x_in), _ptr(x_out), _ptr(out), B, H, N, S, int(T), io,
+                                             _stream()),
+           "h3conv_state_pass_noalloc")
+    return out
 
 
 def ssm_step(u, A, Bm, C, dt, D, x, out=None):

@@ -3,6 +3,7 @@
 // for the contract of every entry point.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/h3conv.h"
 #include "h3conv_internal.h"
@@ -42,6 +43,33 @@ h3conv_status device_check() {
 }
 
 h3conv_status from_hip(hipError_t e) { return e == hipSuccess ? H3CONV_OK : H3CONV_ERR_HIP; }
+
+// Scratch memory of h3conv_state_pass_noalloc: one array per device, part of
+// the library's device code (allocated when the code is loaded on a device,
+// held until the process ends).  Host code never passes `scratch` itself to
+// a kernel (on the host it is only a stand-in for the symbol); the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+static __device__ __align__(256) unsigned char scratch[H3CONV_NOALLOC_WORKSPACE_BYTES];
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+h3conv_status scratch_ptr(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return H3CONV_ERR_NO_DEVICE;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_acquire);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) return H3CONV_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return H3CONV_OK;
+}
 
 // Status meaning "arguments valid, sizes non-empty: run it" (never returned
 // to a caller; within the enum's value range, above every real status).
@@ -175,6 +203,24 @@ h3conv_status h3conv_state_pass(const void *u, const float *A, const float *Bm, 
     for (auto &b : bufs)
         if (overlap(ws, need, b.p, b.n)) return H3CONV_ERR_INVALID_ARG;
     st = device_check();
+    if (st != H3CONV_OK) return st;
+    return from_hip(h3c::launch_state_pass(u, A, Bm, C, dt, D, x_in, x_out, y, (int)B, (int)H, N,
+                                           (int)S, (int)T, io, ws, (hipStream_t)stream));
+}
+
+h3conv_status h3conv_state_pass_noalloc(const void *u, const float *A, const float *Bm,
+                                        const float *C, const float *dt, const float *D,
+                                        const float *x_in, float *x_out, void *y, int64_t B,
+                                        int64_t H, int64_t N, int64_t S, int64_t T, int io,
+                                        void *stream) {
+    h3conv_status st = sp_validate(u, A, Bm, C, dt, D, x_in, x_out, y, B, H, N, S, T, io, stream);
+    if (st != SP_RUN) return st;
+    if (h3c::state_pass_workspace_io(B, H, N, S, T, io) > (size_t)H3CONV_NOALLOC_WORKSPACE_BYTES)
+        return H3CONV_ERR_WORKSPACE;
+    st = device_check();
+    if (st != H3CONV_OK) return st;
+    void *ws = nullptr;
+    st = scratch_ptr(&ws);
     if (st != H3CONV_OK) return st;
     return from_hip(h3c::launch_state_pass(u, A, Bm, C, dt, D, x_in, x_out, y, (int)B, (int)H, N,
                                            (int)S, (int)T, io, ws, (hipStream_t)stream));

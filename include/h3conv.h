@@ -132,6 +132,30 @@ h3conv_status h3conv_state_pass(const void *u, const float *A, const float *Bm, 
                                 int io, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * h3conv_state_pass without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same operation, arguments (less ws and
+ * ws_bytes), kernels and results as h3conv_state_pass; the workspace is the
+ * library's own static device array of H3CONV_NOALLOC_WORKSPACE_BYTES per
+ * device (part of its device code, held until the process ends).  No call
+ * allocates or frees anything.
+ * Sizes whose workspace, h3conv_workspace_size(H3CONV_OP_STATE_PASS, ...) for
+ * this activation type, exceeds the array return H3CONV_ERR_WORKSPACE before
+ * any HIP call (16-bit activations: about 90 KiB per channel at T = 8192,
+ * so up to about 1450 channels of chunk 8192).
+ * All calls on one device share that device's array: calls that overlap in
+ * time on one device (several streams, or several host threads) race and
+ * must be serialised by the caller, e.g. by issuing them on one stream.
+ * Nothing in the array needs to start zeroed; each call writes what it reads.
+ */
+#define H3CONV_NOALLOC_WORKSPACE_BYTES (128u * 1024u * 1024u)
+h3conv_status h3conv_state_pass_noalloc(const void *u, const float *A, const float *Bm,
+                                        const float *C, const float *dt, const float *D,
+                                        const float *x_in, float *x_out, void *y, int64_t B,
+                                        int64_t H, int64_t N, int64_t S, int64_t T, int io,
+                                        void *stream);
+
+/*
  * Recurrent generation: K steps of the diagonal SSM per row from its current
  * state, the state updated in place (the recurrent view of the blog's
  * section "Background: What Are State Space Models?" and of the
