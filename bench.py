@@ -13,11 +13,17 @@ the next of several independent input/output sets whose total exceeds 512 MB.
 Output: one JSON line with elements/s (B*H*N per second), the roofline of the
 dominant kernel against MI355X HBM3E (8 TB/s) measured with HIP events on the
 launch stream, and the fp64 CPU oracle timed on this host's cores.  The HBM
-traffic of the dominant kernel comes from the committed rocprofv3 counter
-summary (profiles/), and is reported only while the kernel sources still hash
-to the value recorded there.
+traffic and the matrix-core flops of the dominant kernel come from the
+committed rocprofv3 counter summary of the workload (profiles/), and are
+reported only while the kernel sources still hash to the value recorded
+there; the matrix-core utilisation is those flops over the live kernel time
+and the dense fp16 peak (2.5 PFLOP/s).  The other workloads, and a sweep of
+the sequence length (N = 256 ... 32K, fused up to 8K, state passing above)
+timed beside an unfused torch.fft FFT convolution on the same GPU (the
+analogue of the pages' cuFFT baseline), are reported under "secondary" and
+"sweep".
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-sweep]
     python bench.py --calib-copy    # plain 1 GiB device copy, for counter calibration
 """
 from __future__ import annotations
@@ -48,34 +54,47 @@ ESZ = {"f32": 4, "f16": 2, "bf16": 2}
 # scaling and the spectrum product are packed fp16; fp32 activations use the
 # fp32 vector engine
 COMPUTE_DTYPE = {"f16": "f16", "bf16": "f16", "f32": "f32"}
-# sources that define the dominant kernel, and the counter summary of it
-KERNEL_SOURCES = ("fft_long_convolution_flashconv_amd/csrc/mfma_engine.h",
-                  "fft_long_convolution_flashconv_amd/csrc/fftconv.hip",
-                  "fft_long_convolution_flashconv_amd/csrc/h3conv_device.h")
-PROFILE = "profiles/k_fft_conv_mfma_conv_1k.md"
+MFMA_PEAK_FLOPS = 2.5e15   # dense fp16 matrix-core peak of MI355X
+# the kernel sources whose hash a counter summary records
+KERNEL_SRC_DIR = "fft_long_convolution_flashconv_amd/csrc"
+# counter summary of the dominant kernel of each workload
+PROFILES = {"conv_1k": "profiles/k_fft_conv_mfma_conv_1k.md",
+            "conv_8k": "profiles/k_fft_conv_mfma_conv_8k.md",
+            "state_64k": "profiles/k_sp_chunk_conv_mfma_state_64k.md",
+            "h3_mix_2k": "profiles/k_fft_conv_mfma_h3_mix_2k.md"}
 
 
 def kernel_source_hash() -> str:
+    """sha256 (16 hex digits) over every source of the library's kernels."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
+    d = os.path.join(ROOT, KERNEL_SRC_DIR)
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(workload: str):
-    """HBM bytes per launch from the counter summary, if it covers this
-    workload and the current kernel sources (else None)."""
-    path = os.path.join(ROOT, PROFILE)
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
+def profiled(workload: str) -> dict:
+    """Per-launch HBM traffic (bytes) and matrix-core flops of the dominant
+    kernel from the counter summary, if it covers this workload and the
+    current kernel sources (else None values)."""
+    out = {"traffic": None, "mfma_flops": None, "kernel": None}
+    rel = PROFILES.get(workload)
+    if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
+        return out
+    text = open(os.path.join(ROOT, rel)).read()
     m_hash = re.search(r"kernel source hash: `([0-9a-f]+)`", text)
     m_wl = re.search(r"workload: `([a-z0-9_]+)`", text)
-    m_tr = re.search(r"traffic per launch(?: of `[^`]*`)?: ([0-9]+) bytes", text)
-    if not (m_hash and m_wl and m_tr) or m_wl.group(1) != workload or m_hash.group(1) != kernel_source_hash():
-        return None
-    return int(m_tr.group(1))
+    if not (m_hash and m_wl) or m_wl.group(1) != workload or m_hash.group(1) != kernel_source_hash():
+        return out
+    m_tr = re.search(r"traffic per launch of `([^`]*)`: ([0-9]+) bytes", text)
+    m_fl = re.search(r"matrix-core flops per launch of `[^`]*`: ([0-9]+)", text)
+    if m_tr:
+        out["kernel"], out["traffic"] = m_tr.group(1), int(m_tr.group(2))
+    if m_fl:
+        out["mfma_flops"] = int(m_fl.group(1))
+    return out
 
 
 def log(*a):
@@ -153,45 +172,122 @@ def time_case(case: Case, steps: int, warmup: int):
     return wall, e0.elapsed_time(e1) / steps
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w: wl.Workload, budget_s: float = 12.0) -> dict:
-    """fp64 oracle on this host's cores over a bounded sample of the workload."""
+    """fp64 oracle on this host's cores over a bounded sample of the workload,
+    then on one thread over a smaller sample (both scaled to elements/s)."""
     import numpy as np
 
     import oracle
 
+    if w.kind != "fft_conv":
+        raise ValueError(w.kind)
     inp = wl.make_inputs(w)
-    g = np.random.default_rng(0)
-    if w.kind == "fft_conv":
-        f = oracle.ssm_filter(inp["A"].double().numpy()[..., 0] + 1j * inp["A"].double().numpy()[..., 1],
-                              inp["Bm"].double().numpy()[..., 0] + 1j * inp["Bm"].double().numpy()[..., 1],
-                              inp["C"].double().numpy()[..., 0] + 1j * inp["C"].double().numpy()[..., 1],
-                              inp["dt"].double().numpy(), w.N) if "A" in inp else inp["f"].double().numpy()
-        u = inp["u"].double().numpy()
-        D = inp["D"].double().numpy()
-        # sample: whole batch rows of a growing number of channels, then the
-        # sample repeated, until about `budget_s` seconds of CPU work
-        H = w.H
-        hs = 16
-        while True:
-            sel = np.arange(min(hs, H))
-            ua, fa, Da = np.ascontiguousarray(u[:, sel]), np.ascontiguousarray(f[sel]), D[sel]
-            t0 = time.perf_counter()
-            oracle.causal_conv(ua, fa, Da)
-            t_one = time.perf_counter() - t0
-            if t_one > budget_s / 4 or hs >= H:
-                break
-            hs = min(H, hs * 4)
+    if "A" in inp:
+        cp = lambda t: t.double().numpy()[..., 0] + 1j * t.double().numpy()[..., 1]
+        f = oracle.ssm_filter(cp(inp["A"]), cp(inp["Bm"]), cp(inp["C"]), inp["dt"].double().numpy(), w.N)
+    else:
+        f = inp["f"].double().numpy()
+    u = inp["u"].double().numpy()
+    D = inp["D"].double().numpy()
+    H = w.H
+
+    def timed(ua, fa, Da, budget):
+        t0 = time.perf_counter()
+        oracle.causal_conv(ua, fa, Da)
+        t_one = time.perf_counter() - t0
         reps, total = 1, t_one
-        while total < budget_s:
+        while total < budget:
             t0 = time.perf_counter()
             oracle.causal_conv(ua, fa, Da)
             total += time.perf_counter() - t0
             reps += 1
-        n_el = w.B * len(sel) * w.N * reps
-        return {"value": n_el / total, "unit": "elements/s", "cores": oracle.max_threads(), "kind": "oracle",
-                "sample": "direct O(N^2) causal conv (fp64) of all %d batch rows x %d of %d channels, N=%d, "
-                          "%d repetition(s), %.1f s" % (w.B, len(sel), H, w.N, reps, total)}
-    raise ValueError(w.kind)
+        return reps, total, t_one
+
+    # all cores: whole batch rows of a growing number of channels, then the
+    # sample repeated, until about `budget_s` seconds of CPU work
+    hs = 16
+    while True:
+        sel = np.arange(min(hs, H))
+        ua, fa, Da = np.ascontiguousarray(u[:, sel]), np.ascontiguousarray(f[sel]), D[sel]
+        t0 = time.perf_counter()
+        oracle.causal_conv(ua, fa, Da)
+        if time.perf_counter() - t0 > budget_s / 4 or hs >= H:
+            break
+        hs = min(H, hs * 4)
+    reps, total, _ = timed(ua, fa, Da, budget_s)
+    cores = oracle.max_threads()
+    out = {"value": w.B * len(sel) * w.N * reps / total, "unit": "elements/s", "cores": cores,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": "direct O(N^2) causal conv (fp64) of all %d batch rows x %d of %d channels, N=%d, "
+                     "%d repetition(s), %.1f s" % (w.B, len(sel), H, w.N, reps, total)}
+    # one thread: one batch row of 8 channels
+    oracle.set_threads(1)
+    try:
+        u1, f1, D1 = np.ascontiguousarray(u[:1, :8]), np.ascontiguousarray(f[:8]), D[:8]
+        reps1, total1, _ = timed(u1, f1, D1, budget_s / 4)
+    finally:
+        oracle.set_threads(cores)
+    out["one_thread"] = {"value": 8 * w.N * reps1 / total1, "unit": "elements/s", "cores": 1,
+                         "sample": "1 batch row x 8 channels, N=%d, %d repetition(s), %.1f s"
+                                   % (w.N, reps1, total1)}
+    return out
+
+
+def torch_fftconv(u, f, D):
+    """Unfused FFT convolution with torch.fft (rocFFT): rfft of the
+    zero-padded input and filter, product, irfft, first N outputs, plus D*u;
+    in fp32.  Timing comparison only (the analogue of the pages' cuFFT
+    FFTConv baseline)."""
+    N = u.shape[-1]
+    uf = u.float()
+    y = torch.fft.irfft(torch.fft.rfft(uf, n=2 * N) * torch.fft.rfft(f, n=2 * N), n=2 * N)[..., :N]
+    return (y + uf * D[:, None]).to(u.dtype)
+
+
+def sweep(dev, steps: int, warmup: int) -> list:
+    """Sequence-length sweep at the H3-125M width (B=8, H=768, fp16, 64
+    modes): fused fft_conv for N <= 8192, state passing (T = 8192) above,
+    each timed beside torch_fftconv on the same inputs."""
+    out = []
+    for i, N in enumerate([256, 512, 1024, 2048, 4096, 8192, 16384, 32768]):
+        kind = "fft_conv" if N <= 8192 else "state_pass"
+        w = wl.Workload("sweep_%d" % N, kind, "f16", B=8, H=768, N=N, T=8192 if kind == "state_pass" else 0,
+                        seed=100 + i)
+        c = Case(w, dev)
+        _, m_ms = time_case(c, steps, warmup)
+        s0 = c.sets[0]
+        if "f" not in s0:
+            s0["f"] = pkg.ssm_filter(s0["A"], s0["Bm"], s0["C"], s0["dt"], N)
+        for _ in range(warmup):
+            torch_fftconv(s0["u"], s0["f"], s0["D"])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch_fftconv(s0["u"], s0["f"], s0["D"])
+        e1.record()
+        torch.cuda.synchronize()
+        t_ms = e0.elapsed_time(e1) / steps
+        nb = algorithmic_bytes(w)
+        out.append({"N": N, "path": kind, "us": m_ms * 1e3, "elements_per_s": w.elements / (m_ms * 1e-3),
+                    "frac_hbm": nb / (m_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "torch_fft_us": t_ms * 1e3,
+                    "speedup_vs_torch_fft": t_ms / m_ms})
+        log("bench: sweep N=%d %s %.1f us (%.1f%% of HBM) torch.fft %.1f us x%.2f"
+            % (N, kind, m_ms * 1e3, 100 * out[-1]["frac_hbm"], t_ms * 1e3, t_ms / m_ms))
+        del c, s0
+        torch.cuda.empty_cache()
+    return out
 
 
 def calib_copy():
@@ -214,6 +310,7 @@ def main():
     ap.add_argument("--workload", default="conv_1k", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the sequence-length sweep")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash and exit")
     a = ap.parse_args()
@@ -222,11 +319,11 @@ def main():
               "(channels shard with no communication; see the design notes). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
-    if a.calib_copy:
-        calib_copy()
-        return
     if a.source_hash:
         print(kernel_source_hash())
+        return
+    if a.calib_copy:
+        calib_copy()
         return
     dev = torch.device("cuda:0")
     pkg.load()
@@ -238,6 +335,8 @@ def main():
     ms_per_step = wall * 1e3 / a.steps
     nbytes = algorithmic_bytes(w)
     achieved = nbytes / (mean_ms * 1e-3) / 1e9
+    prof = profiled(w.name)
+    mfma_util = (prof["mfma_flops"] / (mean_ms * 1e-3) / MFMA_PEAK_FLOPS) if prof["mfma_flops"] else None
     out = {
         "metric": METRIC,
         "value": w.elements / (ms_per_step * 1e-3),
@@ -254,8 +353,10 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H or w.Dm, "N": w.N, "io_dtype": w.dtype,
                    "kind": w.kind, "input_sets_rotated": case.nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(w.name),
-                     "kernel_mean_us": mean_ms * 1e3, "algorithmic_bytes_per_launch": nbytes},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": prof["traffic"],
+                     "kernel_mean_us": mean_ms * 1e3, "algorithmic_bytes_per_launch": nbytes,
+                     "mfma_util": mfma_util, "mfma_flops_per_launch": prof["mfma_flops"],
+                     "mfma_peak_flops": MFMA_PEAK_FLOPS},
     }
     del case
     torch.cuda.empty_cache()
@@ -266,15 +367,19 @@ def main():
                 continue
             ww = wl.WORKLOADS[name]
             c = Case(ww, dev)
-            _, m_ms = time_case(c, max(5, a.steps // 5), 3)
+            _, m_ms = time_case(c, max(10, a.steps), max(3, a.warmup))
             nb = algorithmic_bytes(ww)
+            pr = profiled(name)
             sec[name] = {"elements_per_s": ww.elements / (m_ms * 1e-3), "mean_us": m_ms * 1e3,
                          "algorithmic_bytes": nb, "GB_s": nb / (m_ms * 1e-3) / 1e9,
-                         "frac_hbm": nb / (m_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "sets": c.nsets}
+                         "frac_hbm": nb / (m_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "sets": c.nsets,
+                         "traffic_per_step_kernel": pr["traffic"], "profiled_kernel": pr["kernel"]}
             log("bench: %s mean %.1f us  %.1f GB/s" % (name, m_ms * 1e3, sec[name]["GB_s"]))
             del c
             torch.cuda.empty_cache()
         out["secondary"] = sec
+    if not a.no_sweep:
+        out["sweep"] = sweep(dev, max(10, a.steps // 2), max(3, a.warmup // 2))
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

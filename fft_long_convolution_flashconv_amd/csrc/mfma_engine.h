@@ -362,7 +362,7 @@ struct Shape {
     // round, the per-signal input maxima (one slot per pass-0 tile, or per
     // wave when a round holds one signal) and the filter sums of the waves.
     static constexpr int NSLOT = SIG == 1 ? NW : T0;
-    static constexpr int RBK = (NSLOT + NW > 2 * NW) ? NSLOT + NW : 2 * NW;
+    static constexpr int RBK = ((NSLOT + NW > 2 * NW ? NSLOT + NW : 2 * NW) + 3) / 4 * 4;  // 16-byte banks
     static_assert(2 * RBK <= 64, "two reduction banks fit the 64 slots");
     // With several signals per round, the pass-0 tiles of one wave belong to
     // different signals (32 NW columns >= one signal's S0 columns).
@@ -730,13 +730,16 @@ struct Engine {
         return f2{sa, mb};
     }
 
-    // Per-signal, per-half maxima of the round's inputs: sm[s] holds max |re|
-    // (low half) and max |im| (high half) of signal s as 16-bit bit patterns
-    // (wave-uniform); with FILT, also the workgroup's sum of `fs` (the
-    // filter's |f|).  One barrier.  A signal's two halves are separate rows,
-    // so each gets a scale of its own from these.
+    // Input scales of a round, one per row: each signal's real and imaginary
+    // halves are different rows.  From the per-half maxima of the round's
+    // inputs (as 16-bit bit patterns), one barrier: kp[i] = scale exponents
+    // (real, imaginary half) of the signal of pass-0 tile i, kq[i] those of
+    // inverse pass-0 tile i (see scale_exp).  With FILT, also returns the
+    // workgroup's sum of `fs` (the filter's |f|).  The exponents are read
+    // from the slots right after the barrier, so the bank can be written
+    // again two reductions later.
     template <bool FILT>
-    __device__ float block_scales(uint32_t (&sm)[SIG], float fs) {
+    __device__ float block_scales(float fs, int hb, int (&kp)[T0W][2], int (&kq)[TIW][2]) {
         uint32_t tm[T0W];
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
@@ -763,14 +766,35 @@ struct Engine {
             if constexpr (FILT) ((float *)r)[NSLOT + w] = fs;
         }
         __syncthreads();
+        // lane l < SIG: the maximum of signal l over its slots and its two
+        // scale exponents (all signals at once), packed as two 16-bit fields;
+        // each tile then takes its signal's pair with one readlane
         constexpr int PER = NSLOT / SIG;
+        uint32_t m = 0;
+        {
+            const uint32_t *q = r + (lane < SIG ? lane : 0) * PER;
+            if constexpr (PER % 4 == 0) {
 #pragma unroll
-        for (int sg = 0; sg < SIG; ++sg) {
-            uint32_t m = 0;
+                for (int k = 0; k < PER; k += 4) {
+                    const u32x4 v = *(const u32x4 *)(q + k);
+                    const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+                    m = pkmax_u16(m, pkmax_u16(pkmax_u16(v0, v1), pkmax_u16(v2, v3)));
+                }
+            } else {
 #pragma unroll
-            for (int k = 0; k < PER; ++k) m = pkmax_u16(m, r[sg * PER + k]);
-            sm[sg] = (uint32_t)__builtin_amdgcn_readfirstlane((int)m);
+                for (int k = 0; k < PER; ++k) m = pkmax_u16(m, q[k]);
+            }
         }
+        const uint32_t kpk = ((uint32_t)scale_exp(m & 0xffffu, hb) & 0xffffu) | ((uint32_t)scale_exp(m >> 16, hb) << 16);
+        auto get = [&](int (&k)[2], int sg) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpk, sg);
+            k[0] = (int)(int16_t)(uint16_t)(v & 0xffffu);
+            k[1] = (int)v >> 16;
+        };
+#pragma unroll
+        for (int i = 0; i < T0W; ++i) get(kp[i], SIG == 1 ? 0 : tile_sig(i));
+#pragma unroll
+        for (int i = 0; i < TIW; ++i) get(kq[i], SIG == 1 ? 0 : (16 * (w + i * NW)) / S0);
         float sa = 0.f;
         if constexpr (FILT) {
 #pragma unroll
@@ -779,23 +803,38 @@ struct Engine {
         return sa;
     }
 
-    // the magnitude whose 16-bit pattern is the low (H = 0) or high half of v
-    template <int H>
-    __device__ __forceinline__ static float half_mag(uint32_t v) {
-        const uint32_t b = H ? (v >> 16) : (v & 0xffffu);
-        if constexpr (KIND == IN_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-        else return __uint_as_float(b << 16);
+    // Scale exponents.  For a 16-bit magnitude pattern m > 0 of the input
+    // type, mag_exp(m) = e with 2^(e-1) <= |x| < 2^e (normal and subnormal
+    // fp16 / bf16; an inf or NaN pattern counts as 2^129).  The input scale of
+    // a row is 2^k with k = 8 - e - hb (the old float form of this was
+    // pow2_scale), limited to the fp16 range for fp16 inputs (which are
+    // scaled in fp16) and to the normal fp32 range otherwise; an all-zero row
+    // gets kZero, which the output stage writes as zeros.  All of it is
+    // integer arithmetic on wave-uniform values.
+    static constexpr int kZero = 0x4000;  // (fits a signed 16-bit field)
+    __device__ __forceinline__ static int mag_exp(uint32_t m) {
+        if constexpr (KIND == IN_F16) {
+            const int E = (int)(m >> 10);
+            return E ? E - 14 : (32 - __builtin_clz(m)) - 24;
+        } else {
+            const int E = (int)(m >> 7);
+            return E ? E - 126 : (32 - __builtin_clz(m)) - 133;
+        }
     }
-    // entry s of a per-signal array for a wave-uniform signal index
-    template <class V>
-    __device__ __forceinline__ static V pick(const V (&a)[SIG], int s) {
-        V r = a[0];
-#pragma unroll
-        for (int k = 1; k < SIG; ++k)
-            if (s == k) r = a[k];
-        return r;
+    __device__ __forceinline__ static int scale_exp(uint32_t m, int hb) {
+        const int k = 8 - mag_exp(m | (m == 0 ? 1u : 0u)) - hb;
+        const int kc = (KIND == IN_F16) ? min(max(k, -24), 14) : min(max(k, -126), 127);
+        return m ? kc : kZero;
     }
-
+    // 2^k as fp32 bits (k in [-126, 127]; kZero gives 1, the scale is unused)
+    __device__ __forceinline__ static float exp2i(int k) {
+        return __uint_as_float((uint32_t)((k == kZero ? 0 : k) + 127) << 23);
+    }
+    // 2^k as fp16 bits, k in [-24, 15] (kZero gives 1)
+    __device__ __forceinline__ static uint32_t exp2h(int k) {
+        if (k == kZero) return 0x3c00u;
+        return k >= -14 ? (uint32_t)(k + 15) << 10 : 1u << (k + 24);
+    }
     // LDS access by byte address.  Addresses are built as a per-lane base,
     // laundered once per pass (so the compiler does not keep one register per
     // tile and slot alive across the whole kernel), XORed with compile-time or
@@ -882,7 +921,7 @@ struct Engine {
     // the activation type; st(s, n, m, v) stores the packed pair v (row 2s
     // in the low half, row 2s + 1 in the high half) of output m = 2g, 2g+1.
     template <class ST>
-    __device__ void pass0_inv(const ST &st, const f2 (&osg)[SIG]) {
+    __device__ void pass0_inv(const ST &st, const int (&kq)[TIW][2], float ob) {
         const int lb = opaque((j ^ phys<LOG2M>(2 * g * S0)) << 2);
         // All twiddles and products first, then all stores: loads and stores
         // retire in order, so a table load behind a store would wait for it.
@@ -899,11 +938,12 @@ struct Engine {
         constexpr int BI = TIW < SH::BD / 4 ? TIW : SH::BD / 4;
         static_assert(TIW % BI == 0, "inverse pass-0 tiles split into equal batches");
         uint32_t ov[TIW][2];
-        // output scale of each tile's signal: real half (row 2s), imaginary
-        // half (row 2s + 1)
+        // output scale of each tile's signal, ob 2^-k: real half (row 2s),
+        // imaginary half (row 2s + 1); zero for a row of zeros
         f2 os[TIW];
 #pragma unroll
-        for (int i = 0; i < TIW; ++i) os[i] = pick(osg, (16 * (w + i * NW)) / S0);
+        for (int i = 0; i < TIW; ++i)
+            os[i] = f2{kq[i][0] == kZero ? 0.f : ldexpf(ob, -kq[i][0]), kq[i][1] == kZero ? 0.f : ldexpf(ob, -kq[i][1])};
         auto cv = [&](float re, float im, f2 o) -> uint32_t {
             const f2 v = {re * o.x, im * o.y};
             if constexpr (KIND == IN_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
@@ -1236,26 +1276,18 @@ struct Engine {
         // Every row gets a scale of its own: a signal's real and imaginary
         // halves are different rows, and one scale for both would leave a
         // small row with rounding errors of the size of its partner's values.
-        uint32_t sm[SIG];
+        int kp[T0W][2], kq[TIW][2];
         float sf = 0.f;
         {
-            const float fa = block_scales<FILT>(sm, FILT ? filter_asum(fin) : 0.f);
+            const float fa = block_scales<FILT>(FILT ? filter_asum(fin) : 0.f, hb, kp, kq);
             if constexpr (FILT) sf = filter_scale(fa);
         }
-        // fp16 inputs are scaled in fp16, so a scale must be an fp16 power of two
-        auto in_scale = [&](float am) -> float {
-            const float s0 = pow2_scale(am, hb);
-            return (KIND == IN_F16) ? fminf(s0, 16384.0f) : s0;
-        };
-        f2 su[SIG];
-#pragma unroll
-        for (int sg = 0; sg < SIG; ++sg) su[sg] = f2{in_scale(half_mag<0>(sm[sg])), in_scale(half_mag<1>(sm[sg]))};
-        f2 sut[T0W];
-        uint32_t suh[T0W];
+        f2 sut[T0W] = {};
+        uint32_t suh[T0W] = {};
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
-            sut[i] = pick(su, tile_sig(i));
-            suh[i] = pk(sut[i].x, sut[i].y);
+            if constexpr (KIND == IN_F16) suh[i] = exp2h(kp[i][0]) | (exp2h(kp[i][1]) << 16);
+            else sut[i] = f2{exp2i(kp[i][0]), exp2i(kp[i][1])};
         }
         pass0<SIG, FILT>([&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], sut[i], suh[i]); },
                          [&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); });
@@ -1300,13 +1332,9 @@ struct Engine {
         if (vm > 0.f) (void)frexpf(vm, &ev);
         const float sy = fminf(fmaxf(ldexpf(1.f, 14 - ev - (LOG2M - SH::LR)), 1.0f / 16384.0f), 32768.0f);
         inv_middle<K>(pk(sy, sy));
-        // output scales; a row whose inputs are all zero is written as zeros
-        const float ob = (float)R / ((float)M * sy * cF);
-        f2 osg[SIG];
-#pragma unroll
-        for (int sg = 0; sg < SIG; ++sg)
-            osg[sg] = f2{(sm[sg] & 0xffffu) ? ob / su[sg].x : 0.f, (sm[sg] >> 16) ? ob / su[sg].y : 0.f};
-        pass0_inv(out, osg);
+        // output scales R / (M su sy cF), su = 2^k per row (rows of zeros
+        // are written as zeros)
+        pass0_inv(out, kq, (float)R / ((float)M * sy * cF));
     }
 
     // A whole channel of 16-bit activations: the filter spectrum, then
