@@ -49,12 +49,13 @@ def _load():
         P = ctypes.c_void_p
         I = ctypes.c_int64
         lib.oracle_causal_conv.argtypes = [P, P, P, P, I, I, I]
+        lib.oracle_causal_conv_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I]
         lib.oracle_ssm_filter.argtypes = [P, P, P, P, P, I, I, I]
         lib.oracle_ssm_recurrence.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I]
         lib.oracle_h3_mix.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
-        for fn in (lib.oracle_causal_conv, lib.oracle_ssm_filter,
+        for fn in (lib.oracle_causal_conv, lib.oracle_causal_conv_bwd, lib.oracle_ssm_filter,
                    lib.oracle_ssm_recurrence, lib.oracle_h3_mix):
             fn.restype = None
         _lib = lib
@@ -106,6 +107,27 @@ def causal_conv(u, f, D) -> np.ndarray:
     y = np.empty_like(u)
     _load().oracle_causal_conv(_ptr(u), _ptr(f), _ptr(D), _ptr(y), B, H, N)
     return y
+
+
+def causal_conv_bwd(u, f, D, dy):
+    """Gradients (du, df, dD) of y = causal_conv(u, f, D) for upstream dy (fp64):
+
+      du[b,h,k] = sum_{t>=k} f[h,t-k] dy[b,h,t] + D[h] dy[b,h,k]
+      df[h,s]   = sum_b sum_{t>=s} dy[b,h,t] u[b,h,t-s]
+      dD[h]     = sum_b sum_t dy[b,h,t] u[b,h,t]
+
+    u, dy: [B,H,N]; f: [H,N]; D: [H].  The backward pass of the summary
+    page's Appendix C.1: correlations with the filter and with the input,
+    D*dy entering du.
+    """
+    u = _f64(u); f = _f64(f); D = _f64(D); dy = _f64(dy)
+    B, H, N = u.shape
+    assert dy.shape == u.shape and f.shape == (H, N) and D.shape == (H,)
+    du = np.empty_like(u)
+    df = np.empty((H, N), dtype=np.float64)
+    dD = np.empty(H, dtype=np.float64)
+    _load().oracle_causal_conv_bwd(_ptr(u), _ptr(f), _ptr(D), _ptr(dy), _ptr(du), _ptr(df), _ptr(dD), B, H, N)
+    return du, df, dD
 
 
 def ssm_filter(A, Bm, C, dt, N: int) -> np.ndarray:

@@ -99,6 +99,60 @@ void oracle_causal_conv(const double *u, const double *f, const double *D,
 }
 
 /*
+ * Gradients (reverse mode) of the causal convolution with residual above,
+ * for an upstream gradient dy of y:
+ *   du[b,h,k] = sum_{t=k..N-1} f[h,t-k] * dy[b,h,t]  +  D[h] * dy[b,h,k]
+ *   df[h,s]   = sum_b sum_{t=s..N-1} dy[b,h,t] * u[b,h,t-s]
+ *   dD[h]     = sum_b sum_t dy[b,h,t] * u[b,h,t]
+ * u, dy, du: [B,H,N]; f, df: [H,N]; D, dD: [H].  O(N^2) per row.
+ * Source: summary page Appendix C.1 "Backward Pass": the gradients of u, f
+ * and D are the transposed (correlation) convolutions of the forward one,
+ * with D*dy entering du, derived from the Toeplitz form of the causal
+ * convolution (signals padded to 2L, the first N entries kept).  Each sum
+ * runs in the order written (b outer, t inner).
+ */
+void oracle_causal_conv_bwd(const double *u, const double *f, const double *D,
+                            const double *dy, double *du, double *df,
+                            double *dD, int64_t B, int64_t H, int64_t N)
+{
+    int64_t rows = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t h = r % H;
+        const double *dyr = dy + r * N;
+        const double *fh = f + h * N;
+        double *dur = du + r * N;
+        for (int64_t k = 0; k < N; ++k) {
+            double acc = 0.0;
+            for (int64_t t = k; t < N; ++t)
+                acc += fh[t - k] * dyr[t];
+            dur[k] = acc + D[h] * dyr[k];
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t h = 0; h < H; ++h) {
+        for (int64_t s = 0; s < N; ++s) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                const double *ur = u + (b * H + h) * N;
+                const double *dyr = dy + (b * H + h) * N;
+                for (int64_t t = s; t < N; ++t)
+                    acc += dyr[t] * ur[t - s];
+            }
+            df[h * N + s] = acc;
+        }
+        double d = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            const double *ur = u + (b * H + h) * N;
+            const double *dyr = dy + (b * H + h) * N;
+            for (int64_t t = 0; t < N; ++t)
+                d += dyr[t] * ur[t];
+        }
+        dD[h] = d;
+    }
+}
+
+/*
  * Filter of a diagonal complex SSM (S modes per channel):
  *   f[h,k] = 2 Re( sum_j C[h,j] * exp(dt[h] * A[h,j] * k) * dt[h] * B[h,j] )
  * Complex arrays are interleaved (re, im) pairs: A, Bm, C are [H,S,2].

@@ -293,3 +293,84 @@ def test_h3_mix_shift_delay():
     out = oracle.h3_mix(q, k, v, w, np.zeros_like(f), np.ones(q.shape[2]))
     s = np.zeros_like(k); s[:, 1:, :] = k[:, :-1, :]
     assert np.array_equal(out, q * (s * v))
+
+
+# ---------------------------------------------------------------- backward pass
+
+def test_golden_causal_conv_bwd():
+    g = _read_golden("causal_conv_bwd_hand.txt")
+    f = g["f"][None, :]
+    D = g["D"]
+    # row 0 alone
+    du, df, dD = oracle.causal_conv_bwd(g["u0"][None, None, :], f, D, g["dy0"][None, None, :])
+    assert np.array_equal(du[0, 0], g["du0"])
+    assert np.array_equal(df[0], g["df_row0"]) and np.array_equal(dD, g["dD_row0"])
+    # both rows: du per row, df and dD summed over the batch
+    u = np.stack([g["u0"], g["u1"]])[:, None, :]
+    dy = np.stack([g["dy0"], g["dy1"]])[:, None, :]
+    du, df, dD = oracle.causal_conv_bwd(u, f, D, dy)
+    assert np.array_equal(du[0, 0], g["du0"]) and np.array_equal(du[1, 0], g["du1"])
+    assert np.array_equal(df[0], g["df"]) and np.array_equal(dD, g["dD"])
+
+
+@pytest.mark.parametrize("N", [1, 2, 7, 33, 64])
+def test_causal_conv_bwd_bruteforce_exact(N):
+    """Small integers: fp64 is exact, so compare bitwise with the transposed
+    Jacobians built in integers (J_u = Toeplitz(f) + D I, J_f[t][s] = u[t-s])."""
+    rng = np.random.default_rng(100 + N)
+    B, H = 3, 2
+    u = rng.integers(-6, 7, size=(B, H, N))
+    dy = rng.integers(-6, 7, size=(B, H, N))
+    f = rng.integers(-6, 7, size=(H, N))
+    D = rng.integers(-3, 4, size=H)
+    du, df, dD = oracle.causal_conv_bwd(u.astype(float), f.astype(float), D.astype(float), dy.astype(float))
+    for h in range(H):
+        fh, Dh = [int(x) for x in f[h]], int(D[h])
+        df_ref = [0] * N
+        dD_ref = 0
+        for b in range(B):
+            ub, dyb = [int(x) for x in u[b, h]], [int(x) for x in dy[b, h]]
+            Ju = [[(fh[t - k] if k <= t else 0) + (Dh if k == t else 0) for k in range(N)] for t in range(N)]
+            du_ref = [sum(Ju[t][k] * dyb[t] for t in range(N)) for k in range(N)]
+            assert du[b, h].tolist() == [float(x) for x in du_ref]
+            Jf = [[ub[t - s] if s <= t else 0 for s in range(N)] for t in range(N)]
+            for s in range(N):
+                df_ref[s] += sum(Jf[t][s] * dyb[t] for t in range(N))
+            dD_ref += sum(dyb[t] * ub[t] for t in range(N))
+        assert df[h].tolist() == [float(x) for x in df_ref]
+        assert dD[h] == float(dD_ref)
+
+
+def test_causal_conv_bwd_vs_numpy_convolve():
+    """Library cross-check: du from a convolution of the reversed dy with f,
+    df from a convolution of the reversed u with dy."""
+    rng = np.random.default_rng(7)
+    B, H, N = 2, 3, 257
+    u, dy = rng.standard_normal((2, B, H, N))
+    f = rng.standard_normal((H, N)); D = rng.standard_normal(H)
+    du, df, dD = oracle.causal_conv_bwd(u, f, D, dy)
+    for h in range(H):
+        dfr = np.zeros(N)
+        for b in range(B):
+            ref = np.convolve(dy[b, h][::-1], f[h])[:N][::-1] + D[h] * dy[b, h]
+            assert _rel(du[b, h], ref) < 1e-13
+            dfr += np.convolve(u[b, h][::-1], dy[b, h])[N - 1:2 * N - 1]
+        assert _rel(df[h], dfr) < 1e-13
+        assert abs(dD[h] - np.sum(dy[:, h] * u[:, h])) < 1e-12 * np.sum(np.abs(dy[:, h] * u[:, h]))
+
+
+def test_causal_conv_bwd_adjoint_of_the_forward():
+    """The gradients are the adjoint of the oracle's own forward map:
+    <dy, y(v, f, D)> = <du, v>,  <dy, y(u, g, 0)> = <df, g>,  and the D term."""
+    rng = np.random.default_rng(8)
+    B, H, N = 3, 2, 300
+    u, dy, v = rng.standard_normal((3, B, H, N))
+    f, g = rng.standard_normal((2, H, N))
+    D, E = rng.standard_normal((2, H))
+    du, df, dD = oracle.causal_conv_bwd(u, f, D, dy)
+    lhs = np.sum(dy * oracle.causal_conv(v, f, D))
+    assert abs(lhs - np.sum(du * v)) < 1e-11 * np.sum(np.abs(dy * oracle.causal_conv(v, f, D)))
+    lhs = np.sum(dy * oracle.causal_conv(u, g, np.zeros(H)))
+    assert abs(lhs - np.sum(df * g)) < 1e-11 * max(1.0, abs(lhs))
+    lhs = np.sum(dy * oracle.causal_conv(u, np.zeros((H, N)), E))
+    assert abs(lhs - np.sum(dD * E)) < 1e-11 * max(1.0, abs(lhs))
