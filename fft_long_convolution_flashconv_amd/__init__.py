@@ -34,7 +34,7 @@ MAX_STATE = 64
 _IO = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
 
-EXPORTS = ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
+EXPORTS = ("h3conv_fft_conv", "h3conv_fft_conv_bwd", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
            "h3conv_ssm_step", "h3conv_h3_mix", "h3conv_workspace_size", "h3conv_status_string", "h3conv_version")
 NOALLOC_WORKSPACE_BYTES = 128 * 1024 * 1024
 
@@ -56,6 +56,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.h3conv_fft_conv.argtypes = [P, P, P, P, I64, I64, I64, I, P]
+    lib.h3conv_fft_conv_bwd.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, P]
     lib.h3conv_ssm_filter.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.h3conv_state_pass.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
     lib.h3conv_state_pass_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P]
@@ -66,7 +67,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.h3conv_status_string.argtypes = [I]
     lib.h3conv_status_string.restype = ctypes.c_char_p
     lib.h3conv_version.restype = I
-    for name in ("h3conv_fft_conv", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
+    for name in ("h3conv_fft_conv", "h3conv_fft_conv_bwd", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
                  "h3conv_ssm_step", "h3conv_h3_mix"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -160,6 +161,34 @@ def fft_conv(u: torch.Tensor, f: torch.Tensor, D: torch.Tensor, out: torch.Tenso
     _check(load().h3conv_fft_conv(_ptr(u), _ptr(f), _ptr(D), _ptr(y), B, H, N, io, _stream()),
            "h3conv_fft_conv")
     return y
+
+
+def fft_conv_bwd(u: torch.Tensor, f: torch.Tensor, D: torch.Tensor, dy: torch.Tensor, du=None, df=None, dD=None):
+    """Gradients of y = fft_conv(u, f, D) for an upstream gradient dy.
+
+    Returns (du [B,H,N] like u, df [H,N] f32, dD [H] f32); df and dD are
+    summed over the batch."""
+    _need(u, "u")
+    io = _io(u, "u")
+    if u.dim() != 3:
+        raise ValueError("u must be [B,H,N], got %s" % (tuple(u.shape),))
+    B, H, N = u.shape
+    _need(f, "f", torch.float32, (H, N)); _need(D, "D", torch.float32, (H,))
+    _need(dy, "dy", u.dtype, (B, H, N))
+    if du is not None:
+        _need(du, "du", u.dtype, (B, H, N))
+    if df is not None:
+        _need(df, "df", torch.float32, (H, N))
+    if dD is not None:
+        _need(dD, "dD", torch.float32, (H,))
+    _same_device(u=u, f=f, D=D, dy=dy, du=du, df=df, dD=dD)
+    du = torch.empty_like(u) if du is None else du
+    df = torch.empty(H, N, device=u.device, dtype=torch.float32) if df is None else df
+    dD = torch.empty(H, device=u.device, dtype=torch.float32) if dD is None else dD
+    _check(load().h3conv_fft_conv_bwd(_ptr(u), _ptr(f), _ptr(D), _ptr(dy), _ptr(du), _ptr(df), _ptr(dD),
+                                       B, H, N, io, _stream()),
+           "h3conv_fft_conv_bwd")
+    return du, df, dD
 
 
 def ssm_filter(A: torch.Tensor, Bm: torch.Tensor, C: torch.Tensor, dt: torch.Tensor, N: int,

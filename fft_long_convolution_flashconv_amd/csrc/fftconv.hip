@@ -26,7 +26,9 @@ int fused_log2m(int64_t N) {
     return l + 1;
 }
 
-template <int LOG2M, int IO>
+// CORR: correlation with the filter instead of convolution (the conjugated
+// filter spectrum; the backward pass's du).
+template <int LOG2M, int IO, bool CORR>
 __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_fft_conv(
     const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f,
     const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
@@ -44,6 +46,12 @@ __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_fft_conv(
         return mk(v, 0.f);
     };
     filter_spectrum<LOG2M>(lds, tid, ldf, F);
+    if constexpr (CORR) {
+#pragma unroll
+        for (int i = 0; i < FiltReg<LOG2M>::NBT; ++i)
+#pragma unroll
+            for (int k = 0; k < FiltReg<LOG2M>::R; ++k) F.v[i][k].y = -F.v[i][k].y;
+    }
 
     const int nsig = (B + 1) / 2;
     for (int s = 0; s < nsig; ++s) {
@@ -126,13 +134,101 @@ __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_h3_mix(
 }
 
 
+// Backward pass of the causal convolution with residual (the paperlayer.ai
+// summary of "Hungry Hungry Hippos", Appendix C.1: the gradients of u, f and
+// D are correlations computed through the same zero-padded transforms, D dy
+// entering du).  Two kernels per call:
+//   du[b] = IDFT(DY_b conj(F))[:N] with F = DFT(f + D delta): the forward
+//           convolution kernels with the conjugated filter spectrum (CORR),
+//           the correlation of dy with the filter, D dy included by tap 0;
+//   df    = Re IDFT(sum_pairs conj(Z_u) Z_dy)[:N], Z = row 2s + i row 2s+1:
+//           the real part of the correlation of the complex pair signals is
+//           the sum of the two rows' correlations of u with dy (k_fft_corr_df
+//           below, one workgroup per channel, fp32 transforms, the spectrum
+//           summed over the batch and inverted once);
+//   dD    = df[0] (the gradient of tap 0, which D shares).
+// The zero padding to 2N keeps every correlation lag in [0, N) free of wrap.
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(Plan<LOG2M>::NT) void k_fft_corr_df(
+    const typename io_elem<IO>::T *__restrict__ u, const typename io_elem<IO>::T *__restrict__ dy,
+    float *__restrict__ df, float *__restrict__ dD, int B, int H, int N) {
+    using T = typename io_elem<IO>::T;
+    using FR = FiltReg<LOG2M>;
+    __shared__ cf lds[Plan<LOG2M>::LDS_ELEMS];
+    const int tid = threadIdx.x;
+    const int h = blockIdx.x;
+    FR acc;
+#pragma unroll
+    for (int i = 0; i < FR::NBT; ++i)
+#pragma unroll
+        for (int k = 0; k < FR::R; ++k) acc.v[i][k] = mk(0.f, 0.f);
+    const int nsig = (B + 1) / 2;
+    for (int s = 0; s < nsig; ++s) {
+        const int b0 = 2 * s;
+        const bool has1 = (b0 + 1) < B;
+        const size_t o0 = ((size_t)b0 * H + h) * N, o1 = o0 + (size_t)H * N;
+        auto ldp = [&](const T *x) {
+            return [=](int pos) -> cf {
+                if (pos >= N) return mk(0.f, 0.f);
+                return mk(ld_io<IO>(x + o0 + pos), has1 ? ld_io<IO>(x + o1 + pos) : 0.f);
+            };
+        };
+        FR Sd, Su;
+        spectrum<LOG2M>(lds, tid, ldp(dy), Sd, 1.f);
+        spectrum<LOG2M>(lds, tid, ldp(u), Su, 1.f);
+#pragma unroll
+        for (int i = 0; i < FR::NBT; ++i)
+#pragma unroll
+            for (int k = 0; k < FR::R; ++k) {
+                const cf a = Su.v[i][k], d = Sd.v[i][k];  // += conj(a) d
+                acc.v[i][k] = cadd(acc.v[i][k], mk(fmaf(a.x, d.x, a.y * d.y), fmaf(a.x, d.y, -a.y * d.x)));
+            }
+    }
+    constexpr float SC = 1.0f / (float)Plan<LOG2M>::M;
+#pragma unroll
+    for (int i = 0; i < FR::NBT; ++i)
+#pragma unroll
+        for (int k = 0; k < FR::R; ++k) acc.v[i][k] = cscale(acc.v[i][k], SC);
+    inverse_regs<LOG2M>(lds, tid, acc, [&](int pos, cf v) {
+        if (pos < N) {
+            df[(size_t)h * N + pos] = v.x;
+            if (pos == 0) dD[h] = v.x;
+        }
+    });
+}
+
+template <int LOG2M, int IO>
+static hipError_t launch_df(const void *u, const void *dy, float *df, float *dD, int B, int H, int N,
+                            hipStream_t s) {
+    using T = typename io_elem<IO>::T;
+    return launch(k_fft_corr_df<LOG2M, IO>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T *)u, (const T *)dy, df,
+                  dD, B, H, N);
+}
+
+template <int IO>
+static hipError_t df_dispatch(int log2m, const void *u, const void *dy, float *df, float *dD, int B, int H, int N,
+                              hipStream_t s) {
+    switch (log2m) {
+        case 6: return launch_df<6, IO>(u, dy, df, dD, B, H, N, s);
+        case 7: return launch_df<7, IO>(u, dy, df, dD, B, H, N, s);
+        case 8: return launch_df<8, IO>(u, dy, df, dD, B, H, N, s);
+        case 9: return launch_df<9, IO>(u, dy, df, dD, B, H, N, s);
+        case 10: return launch_df<10, IO>(u, dy, df, dD, B, H, N, s);
+        case 11: return launch_df<11, IO>(u, dy, df, dD, B, H, N, s);
+        case 12: return launch_df<12, IO>(u, dy, df, dD, B, H, N, s);
+        case 13: return launch_df<13, IO>(u, dy, df, dD, B, H, N, s);
+        case 14: return launch_df<14, IO>(u, dy, df, dD, B, H, N, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // ---------------------------------------------------------------- MFMA block-FFT variants
 // fp16 / bf16 activations, 2N >= 256: same per-channel structure, transforms on
 // the matrix cores (see mfma_engine.h).
 
 // SPOL: cache policy of the output stores (non-temporal unless the output
 // is read again right away)
-template <int LOG2M, int IO, int SPOL>
+template <int LOG2M, int IO, int SPOL, bool CORR = false>
 __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M>::WPE))) void k_fft_conv_mfma(
     const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f,
     const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
@@ -161,7 +257,7 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
         return {mf::row_rsrc(uh + o, nb0), mf::row_rsrc(uh + o + rsb, nb1), mf::row_rsrc(yh + o, nb0),
                 mf::row_rsrc(yh + o + rsb, nb1)};
     };
-    E.template run_raw<SPOL>(mf::row_rsrc(fh, 4 * N), dh, rows, (B + 1) / 2, hb);
+    E.template run_raw<SPOL, CORR>(mf::row_rsrc(fh, 4 * N), dh, rows, (B + 1) / 2, hb);
 }
 
 // Row byte offsets inside one launch of the 16-bit engine are 32-bit,
@@ -191,7 +287,7 @@ bool fft_conv_rows_fit(int64_t H, int64_t N, int io) {
     return (pad + 2) * rowb < (1ull << 32);
 }
 
-template <int LOG2M, int IO, int SPOL>
+template <int LOG2M, int IO, int SPOL, bool CORR>
 static hipError_t launch_fc_mfma(const void *u, const float *f, const float *D, void *y, int B,
                                  int H, int N, hipStream_t s) {
     using T = typename io_elem<IO>::T;
@@ -201,45 +297,45 @@ static hipError_t launch_fc_mfma(const void *u, const float *f, const float *D, 
     const int bmax = (int)std::min<uint64_t>((uint64_t)B, (((1ull << 32) - 1) / rowb - pad) & ~1ull);
     for (int b0 = 0; b0 < B; b0 += bmax) {
         const size_t o = (size_t)b0 * H * N;
-        const hipError_t e = launch(k_fft_conv_mfma<LOG2M, IO, SPOL>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
+        const hipError_t e = launch(k_fft_conv_mfma<LOG2M, IO, SPOL, CORR>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
                                     (const T *)u + o, f, D, (T *)y + o, std::min(bmax, B - b0), H, N);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-template <int LOG2M, int IO>
+template <int LOG2M, int IO, bool CORR>
 static hipError_t launch_fc(const void *u, const float *f, const float *D, void *y, int B, int H,
                             int N, hipStream_t s) {
     using T = typename io_elem<IO>::T;
-    return launch(k_fft_conv<LOG2M, IO>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T *)u, f, D, (T *)y, B, H,
-                  N);
+    return launch(k_fft_conv<LOG2M, IO, CORR>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T *)u, f, D, (T *)y,
+                  B, H, N);
 }
 
-template <int IO, int SPOL = mf::kNT>
+template <int IO, int SPOL = mf::kNT, bool CORR = false>
 static hipError_t fc_dispatch(int log2m, const void *u, const float *f, const float *D, void *y,
                               int B, int H, int N, hipStream_t s) {
     if constexpr (IO != IO_F32) {
         switch (log2m) {
-            case 9: return launch_fc_mfma<9, IO, SPOL>(u, f, D, y, B, H, N, s);
-            case 10: return launch_fc_mfma<10, IO, SPOL>(u, f, D, y, B, H, N, s);
-            case 11: return launch_fc_mfma<11, IO, SPOL>(u, f, D, y, B, H, N, s);
-            case 12: return launch_fc_mfma<12, IO, SPOL>(u, f, D, y, B, H, N, s);
-            case 13: return launch_fc_mfma<13, IO, SPOL>(u, f, D, y, B, H, N, s);
-            case 14: return launch_fc_mfma<14, IO, SPOL>(u, f, D, y, B, H, N, s);
+            case 9: return launch_fc_mfma<9, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
+            case 10: return launch_fc_mfma<10, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
+            case 11: return launch_fc_mfma<11, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
+            case 12: return launch_fc_mfma<12, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
+            case 13: return launch_fc_mfma<13, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
+            case 14: return launch_fc_mfma<14, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
             default: break;
         }
     }
     switch (log2m) {
-        case 6: return launch_fc<6, IO>(u, f, D, y, B, H, N, s);
-        case 7: return launch_fc<7, IO>(u, f, D, y, B, H, N, s);
-        case 8: return launch_fc<8, IO>(u, f, D, y, B, H, N, s);
-        case 9: return launch_fc<9, IO>(u, f, D, y, B, H, N, s);
-        case 10: return launch_fc<10, IO>(u, f, D, y, B, H, N, s);
-        case 11: return launch_fc<11, IO>(u, f, D, y, B, H, N, s);
-        case 12: return launch_fc<12, IO>(u, f, D, y, B, H, N, s);
-        case 13: return launch_fc<13, IO>(u, f, D, y, B, H, N, s);
-        case 14: return launch_fc<14, IO>(u, f, D, y, B, H, N, s);
+        case 6: return launch_fc<6, IO, CORR>(u, f, D, y, B, H, N, s);
+        case 7: return launch_fc<7, IO, CORR>(u, f, D, y, B, H, N, s);
+        case 8: return launch_fc<8, IO, CORR>(u, f, D, y, B, H, N, s);
+        case 9: return launch_fc<9, IO, CORR>(u, f, D, y, B, H, N, s);
+        case 10: return launch_fc<10, IO, CORR>(u, f, D, y, B, H, N, s);
+        case 11: return launch_fc<11, IO, CORR>(u, f, D, y, B, H, N, s);
+        case 12: return launch_fc<12, IO, CORR>(u, f, D, y, B, H, N, s);
+        case 13: return launch_fc<13, IO, CORR>(u, f, D, y, B, H, N, s);
+        case 14: return launch_fc<14, IO, CORR>(u, f, D, y, B, H, N, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -251,6 +347,24 @@ hipError_t launch_fft_conv(const void *u, const float *f, const float *D, void *
         case IO_F32: return fc_dispatch<IO_F32>(l, u, f, D, y, B, H, N, s);
         case IO_F16: return fc_dispatch<IO_F16>(l, u, f, D, y, B, H, N, s);
         case IO_BF16: return fc_dispatch<IO_BF16>(l, u, f, D, y, B, H, N, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fft_conv_bwd(const void *u, const float *f, const float *D, const void *dy, void *du,
+                               float *df, float *dD, int B, int H, int N, int io, hipStream_t s) {
+    const int l = fused_log2m(N);
+    hipError_t e;
+    switch (io) {
+        case IO_F32:
+            e = fc_dispatch<IO_F32, mf::kNT, true>(l, dy, f, D, du, B, H, N, s);
+            return e != hipSuccess ? e : df_dispatch<IO_F32>(l, u, dy, df, dD, B, H, N, s);
+        case IO_F16:
+            e = fc_dispatch<IO_F16, mf::kNT, true>(l, dy, f, D, du, B, H, N, s);
+            return e != hipSuccess ? e : df_dispatch<IO_F16>(l, u, dy, df, dD, B, H, N, s);
+        case IO_BF16:
+            e = fc_dispatch<IO_BF16, mf::kNT, true>(l, dy, f, D, du, B, H, N, s);
+            return e != hipSuccess ? e : df_dispatch<IO_BF16>(l, u, dy, df, dD, B, H, N, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -168,6 +168,33 @@ h3conv_status h3conv_fft_conv(const void *u, const float *f, const float *D, voi
                                          (hipStream_t)stream));
 }
 
+h3conv_status h3conv_fft_conv_bwd(const void *u, const float *f, const float *D, const void *dy,
+                                  void *du, float *df, float *dD, int64_t B, int64_t H, int64_t N,
+                                  int io, void *stream) {
+    if (B < 0 || H < 0 || N < 0 || !valid_io(io)) return H3CONV_ERR_INVALID_ARG;
+    if (H == 0 || N == 0) return H3CONV_OK;
+    if (!f || !D || !df || !dD || (B > 0 && (!u || !dy || !du))) return H3CONV_ERR_INVALID_ARG;
+    const void *ptrs[] = {u, f, D, dy, du, df, dD};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return H3CONV_ERR_INVALID_ARG;
+    if (N > H3CONV_MAX_FUSED_N) return H3CONV_ERR_UNSUPPORTED;
+    if (!mul_ok(B, H, INT32_MAX) || !mul_ok(B * H, N, INT64_MAX / 4) || H > INT32_MAX)
+        return H3CONV_ERR_UNSUPPORTED;
+    if (!h3c::fft_conv_rows_fit(H, N, io)) return H3CONV_ERR_UNSUPPORTED;
+    const size_t na = (size_t)(B * H * N) * esize(io), nf = (size_t)(H * N) * 4, nh = (size_t)H * 4;
+    struct R { const void *p; size_t n; } ins[] = {{u, na}, {f, nf}, {D, nh}, {dy, na}};
+    struct R outs[] = {{du, na}, {df, nf}, {dD, nh}};
+    for (auto &o : outs)
+        for (auto &i : ins)
+            if (overlap(o.p, o.n, i.p, i.n)) return H3CONV_ERR_INVALID_ARG;
+    if (overlap(du, na, df, nf) || overlap(du, na, dD, nh) || overlap(df, nf, dD, nh))
+        return H3CONV_ERR_INVALID_ARG;
+    h3conv_status st = device_check();
+    if (st != H3CONV_OK) return st;
+    return from_hip(h3c::launch_fft_conv_bwd(u, f, D, dy, du, df, dD, (int)B, (int)H, (int)N, io,
+                                             (hipStream_t)stream));
+}
+
 h3conv_status h3conv_ssm_filter(const float *A, const float *Bm, const float *C, const float *dt,
                                 float *f, int64_t H, int64_t S, int64_t N, void *stream) {
     if (H < 0 || N < 0 || S < 1) return H3CONV_ERR_INVALID_ARG;

@@ -272,16 +272,16 @@ __device__ __forceinline__ void final_pass(cf *lds, int tid, const ST &st) {
     }
 }
 
-// Spectrum of a zero-padded real filter into registers: F = DFT_M(f || 0)/M,
-// digit-reversed, at the positions the last pass of this thread covers.
+// Spectrum of a zero-padded signal (positions < M/2 loaded by `ld`) into
+// registers: S = DFT_M(x || 0) * sc, digit-reversed, at the positions the
+// last pass of this thread covers.
 template <int LOG2M, class LD>
-__device__ __forceinline__ void filter_spectrum(cf *lds, int tid, const LD &ld, FiltReg<LOG2M> &F) {
+__device__ __forceinline__ void spectrum(cf *lds, int tid, const LD &ld, FiltReg<LOG2M> &S, float sc) {
     using PL = Plan<LOG2M>;
     using FR = FiltReg<LOG2M>;
     constexpr int R = FR::R, NB = PL::M / R;
     first_pass<LOG2M>(lds, tid, ld);
     dif_middle<LOG2M, 1>(lds, tid);
-    constexpr float SC = 1.0f / (float)PL::M;
 #pragma unroll
     for (int i = 0; i < FR::NBT; ++i) {
         const int beta = tid + i * PL::NT;
@@ -291,10 +291,42 @@ __device__ __forceinline__ void filter_spectrum(cf *lds, int tid, const LD &ld, 
             for (int m = 0; m < R; ++m) x[m] = lds[pad(beta * R + m)];
             dft<R, false>(x);
 #pragma unroll
-            for (int k = 0; k < R; ++k) F.v[i][k] = cscale(x[k], SC);
+            for (int k = 0; k < R; ++k) S.v[i][k] = cscale(x[k], sc);
         }
     }
     __syncthreads();
+}
+
+// Spectrum of a zero-padded real filter into registers: F = DFT_M(f || 0)/M.
+template <int LOG2M, class LD>
+__device__ __forceinline__ void filter_spectrum(cf *lds, int tid, const LD &ld, FiltReg<LOG2M> &F) {
+    spectrum<LOG2M>(lds, tid, ld, F, 1.0f / (float)Plan<LOG2M>::M);
+}
+
+// Inverse transform (unnormalised) of a spectrum held in registers in the
+// FiltReg layout: the inverse last-pass DFT into LDS, the inverse DIT
+// passes, and st(pos, value) for the first M/2 positions.
+template <int LOG2M, class ST>
+__device__ __forceinline__ void inverse_regs(cf *lds, int tid, const FiltReg<LOG2M> &Y, const ST &st) {
+    using PL = Plan<LOG2M>;
+    using FR = FiltReg<LOG2M>;
+    constexpr int R = FR::R, NB = PL::M / R;
+#pragma unroll
+    for (int i = 0; i < FR::NBT; ++i) {
+        const int beta = tid + i * PL::NT;
+        if (beta < NB) {
+            cf x[R];
+#pragma unroll
+            for (int k = 0; k < R; ++k) x[k] = Y.v[i][k];
+            dft<R, true>(x);
+#pragma unroll
+            for (int m = 0; m < R; ++m) lds[pad(beta * R + m)] = x[m];
+        }
+    }
+    __syncthreads();
+    dit_middle<LOG2M, PL::NPASS - 2>(lds, tid);
+    final_pass<LOG2M>(lds, tid, st);
+    __syncthreads();  // LDS is reused by the next transform
 }
 
 // Full fused convolution of one complex signal with the filter spectrum:

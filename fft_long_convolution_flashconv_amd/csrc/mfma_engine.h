@@ -1241,10 +1241,13 @@ struct Engine {
         cF = ldexpf(1.f, -ef);
         return ldexpf(1.f, 14 - ef);
     }
-    // last pass of the filter transform (signal slot `s`): the spectrum into F
+    // last pass of the filter transform (signal slot `s`): the spectrum into
+    // F, conjugated (the products take conj(X) conj(F) = conj(X F)), or as
+    // it is with CORR (conj(X) F = conj(X conj(F)): correlation)
+    template <bool CORR>
     __device__ __forceinline__ void filter_last(int s) {
         constexpr float c = 1.0f / (16384.0f * R);
-        const uint32_t ch = pk(c, -c);  // conjugate
+        const uint32_t ch = CORR ? pk(c, c) : pk(c, -c);
         const int lb = opaque(lbase());
 #pragma unroll
         for (int slot = 0; slot < NLS; ++slot) {
@@ -1257,19 +1260,20 @@ struct Engine {
         }
     }
     // the filter on its own, in signal slot 0
+    template <bool CORR>
     __device__ void filter(const float (&fin)[T0W][4]) {
         const float sf = filter_scale(block_reduce<true>(filter_asum(fin)));
         auto fop = [&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); };
         pass0<1>(fop, fop);
         fwd_middle<1, 1>();
-        filter_last(0);
+        filter_last<CORR>(0);
     }
 
     // ---------------------------------------------------------- conv round
     // One round of SIG signals from pin.  FILT: the filter (fin) is
     // transformed alongside, in slot SIG, and its spectrum taken into F
     // before the products.  prefetch() is called once pin has been consumed.
-    template <bool FILT, class OUT, class PF>
+    template <bool FILT, bool CORR, class OUT, class PF>
     __device__ void conv_round(const OUT &out, int hb, const float (&fin)[T0W][4], const PF &prefetch) {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         __builtin_amdgcn_s_setprio(kPrioLoad);
@@ -1294,7 +1298,7 @@ struct Engine {
         prefetch();
         __builtin_amdgcn_s_setprio(kPrioWork);
         fwd_middle<1, SIG + (FILT ? 1 : 0)>();
-        if constexpr (FILT) filter_last(SIG);
+        if constexpr (FILT) filter_last<CORR>(SIG);
         // Last pass, in place: forward DFT-R, product with the filter spectrum
         // (stored as conj(F) cF / R, so no product can overflow the inverse
         // DFT-R), inverse DFT-R on conjugated values.  The maximum of what it
@@ -1344,7 +1348,9 @@ struct Engine {
     // round always transforms SIG signals).  The inputs of each round are
     // fetched while the previous round (or the filter) is being transformed.
     // SPOL: cache policy of the output stores.
-    template <int SPOL = kNT, class RB>
+    // CORR: correlation with the filter (its conjugated spectrum) instead of
+    // convolution.
+    template <int SPOL = kNT, bool CORR = false, class RB>
     __device__ void run_raw(__amdgpu_buffer_rsrc_t frs, float d0, const RB &rows, int nsig, int hb) {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         float fin[T0W][4];
@@ -1365,17 +1371,17 @@ struct Engine {
         int r1 = 0;
         if constexpr (SH::FUSEF) {
             // first round with the filter alongside
-            conv_round<true>([&](int s, int n, int m, uint32_t hv) { store(0, s, n, m, hv); }, hb, fin,
-                             [&]() { prefetch(0); });
+            conv_round<true, CORR>([&](int s, int n, int m, uint32_t hv) { store(0, s, n, m, hv); }, hb, fin,
+                                   [&]() { prefetch(0); });
             r1 = SIG;
         } else {
-            filter(fin);
+            filter<CORR>(fin);
         }
         for (int r0 = r1; r0 < nsig; r0 += SIG) {
             __builtin_amdgcn_s_setprio(kPrioLoad);
             if (!PREFETCH && (!SH::FUSEF || r0 > 0)) fetch_raw(rows, r0, pin);
-            conv_round<false>([&](int s, int n, int m, uint32_t hv) { store(r0, s, n, m, hv); }, hb, fin,
-                              [&]() { prefetch(r0); });
+            conv_round<false, CORR>([&](int s, int n, int m, uint32_t hv) { store(r0, s, n, m, hv); }, hb, fin,
+                                    [&]() { prefetch(r0); });
         }
     }
 };

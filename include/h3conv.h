@@ -85,6 +85,28 @@ h3conv_status h3conv_fft_conv(const void *u, const float *f, const float *D, voi
                               int64_t B, int64_t H, int64_t N, int io, void *stream);
 
 /*
+ * Backward pass of h3conv_fft_conv: for an upstream gradient dy of y,
+ *     du[b,h,k] = sum_{t=k..N-1} f[h,t-k] dy[b,h,t] + D[h] dy[b,h,k]
+ *     df[h,s]   = sum_b sum_{t=s..N-1} dy[b,h,t] u[b,h,t-s]
+ *     dD[h]     = sum_b sum_t dy[b,h,t] u[b,h,t]
+ * i.e. the correlations of dy with the filter and with the input, computed
+ * through the same zero-padded 2N-point transforms (the paperlayer.ai
+ * summary, Appendix C.1 "Backward Pass": gradients of u, f and D through
+ * (inverse) FFTs of the conjugated spectra, D dy entering du).
+ *
+ *   u, dy   [B,H,N]  io dtype   forward input and upstream gradient
+ *   f [H,N], D [H]   fp32       forward filter and residual weight
+ *   du      [B,H,N]  io dtype   output
+ *   df [H,N], dD [H] fp32       outputs, summed over the batch (written, not
+ *                               accumulated into)
+ * Outputs must not overlap any input or each other.  B == 0 writes zeros
+ * to df and dD.  Supported sizes: those of h3conv_fft_conv.
+ */
+h3conv_status h3conv_fft_conv_bwd(const void *u, const float *f, const float *D, const void *dy,
+                                  void *du, float *df, float *dD, int64_t B, int64_t H, int64_t N,
+                                  int io, void *stream);
+
+/*
  * Filter of a diagonal complex SSM with S modes per channel:
  *     f[h,k] = 2 Re( sum_j C[h,j] * exp(dt[h] * A[h,j] * k) * dt[h] * Bm[h,j] ),  k < N
  * i.e. f = [C Bbar, C Abar Bbar, C Abar^2 Bbar, ...] with Abar = exp(dt A),

@@ -227,3 +227,20 @@ def test_ssm_step_validation(lib):
     assert call(y=0x100000) == pkg.ERR_INVALID_ARG          # y aliases u
     assert call(x=0x200000) == pkg.ERR_INVALID_ARG          # x aliases A
     assert call(K=0, u=None, x=None, y=None) == pkg.OK      # empty: no-op
+
+
+def test_fft_conv_bwd_validation(lib):
+    f = lib.h3conv_fft_conv_bwd
+
+    def call(u=0x100000, dy=0x200000, du=0x300000, df=0x400000, dD=0x500000, B=2, H=4, N=64, io=1):
+        return f(u, 0x600000, 0x700000, dy, du, df, dD, B, H, N, io, None)
+
+    assert call(io=9) == pkg.ERR_INVALID_ARG
+    assert call(dy=None) == pkg.ERR_INVALID_ARG
+    assert call(df=None) == pkg.ERR_INVALID_ARG
+    assert call(du=0x300008) == pkg.ERR_INVALID_ARG        # misaligned
+    assert call(du=0x200000) == pkg.ERR_INVALID_ARG        # du aliases dy
+    assert call(dD=0x400000) == pkg.ERR_INVALID_ARG        # dD inside df
+    assert call(N=8193) == pkg.ERR_UNSUPPORTED
+    assert call(H=43691, N=8192, u=1 << 40, dy=2 << 40, du=3 << 40, df=4 << 40, dD=5 << 40) == pkg.ERR_UNSUPPORTED
+    assert call(H=0) == pkg.OK
