@@ -110,6 +110,10 @@ def algorithmic_bytes(w: wl.Workload) -> int:
         return 2 * w.B * w.H * w.N * e + w.H * (3 * w.S * 8 + 8)
     if w.kind == "h3_mix":
         return 4 * w.B * w.N * w.Dm * e + w.Dm * (w.L * 4 + w.N * 4 + 4)
+    if w.kind == "fft_conv_bwd":  # read u, dy, f, D; write du, df, dD
+        return 3 * w.B * w.H * w.N * e + 2 * w.H * w.N * 4 + 2 * w.H * 4
+    if w.kind == "ssm_step":      # read u, x, parameters; write y, x
+        return w.B * w.H * (2 * w.N * e + 2 * w.S * 8) + w.H * (3 * w.S * 8 + 8)
     raise ValueError(w.kind)
 
 
@@ -125,9 +129,15 @@ class Case:
         self.sets = []
         for i in range(self.nsets):
             s = {k: (v if i == 0 else v.clone()) for k, v in d.items()}
-            if w.kind in ("fft_conv", "h3_mix") and "A" in s:
+            if w.kind in ("fft_conv", "h3_mix", "fft_conv_bwd") and "A" in s:
                 s["f"] = pkg.ssm_filter(s["A"], s["Bm"], s["C"], s["dt"], w.N)
             if w.kind == "fft_conv":
+                s["y"] = torch.empty_like(s["u"])
+            elif w.kind == "fft_conv_bwd":
+                s["du"] = torch.empty_like(s["u"])
+                s["df"] = torch.empty(w.H, w.N, device=dev, dtype=torch.float32)
+                s["dD"] = torch.empty(w.H, device=dev, dtype=torch.float32)
+            elif w.kind == "ssm_step":
                 s["y"] = torch.empty_like(s["u"])
             elif w.kind == "state_pass":
                 s["y"] = torch.empty_like(s["u"])
@@ -145,6 +155,10 @@ class Case:
         w = self.w
         if w.kind == "fft_conv":
             pkg.fft_conv(s["u"], s["f"], s["D"], out=s["y"])
+        elif w.kind == "fft_conv_bwd":
+            pkg.fft_conv_bwd(s["u"], s["f"], s["D"], s["dy"], du=s["du"], df=s["df"], dD=s["dD"])
+        elif w.kind == "ssm_step":
+            pkg.ssm_step(s["u"], s["A"], s["Bm"], s["C"], s["dt"], s["D"], s["x"], out=s["y"])
         elif w.kind == "state_pass":
             pkg.state_pass(s["u"], s["A"], s["Bm"], s["C"], s["dt"], s["D"], w.T, out=s["y"],
                            workspace=s["ws"])
@@ -362,7 +376,7 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_secondary:
         sec = {}
-        for name in ("conv_8k", "state_64k", "h3_mix_2k"):
+        for name in ("conv_8k", "state_64k", "h3_mix_2k", "conv_1k_bwd", "decode_125m"):
             if name == w.name:
                 continue
             ww = wl.WORKLOADS[name]

@@ -17,6 +17,15 @@ length 1024 of the 125M model, width 2560 and length 2048 of the 2.7B model,
   state_64k    fp16  B=2  H=1024 N=65536  chunk T=8192, 64 modes
   h3_mix_2k    bf16  B=4  N=2048 Dm=2560  shift taps L=4, 64 modes
 
+and two more for the backward pass and generation (not among the five
+parity configurations, timed beside them):
+
+  conv_1k_bwd  fp16  B=8  H=768  N=1024   conv_1k with an upstream gradient
+                                          dy ~ N(0, 1)
+  decode_125m  fp16  B=64 H=768  K=1      one generated token per row from a
+                                          state x ~ CN(0, 1), 64 modes (batch
+                                          64 as in the pages' generation runs)
+
 Diagonal-SSM parameters: A_j = -0.5 + i*pi*j (j = 0..S-1), B_j = 1,
 C_j ~ CN(0, 0.5) (real and imaginary parts independent N(0, 0.25)),
 dt = exp(U(log 1e-3, log 1e-1)) per channel, D ~ N(0, 1) per channel.
@@ -34,7 +43,7 @@ DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "fft_conv" | "state_pass" | "h3_mix"
+    kind: str            # "fft_conv" | "state_pass" | "h3_mix" | "fft_conv_bwd" | "ssm_step"
     dtype: str           # I/O dtype: "f32" | "f16" | "bf16"
     B: int
     N: int
@@ -57,6 +66,8 @@ WORKLOADS = {
     "conv_8k": Workload("conv_8k", "fft_conv", "f16", B=4, H=768, N=8192, seed=2),
     "state_64k": Workload("state_64k", "state_pass", "f16", B=2, H=1024, N=65536, T=8192, seed=3),
     "h3_mix_2k": Workload("h3_mix_2k", "h3_mix", "bf16", B=4, N=2048, Dm=2560, seed=4),
+    "conv_1k_bwd": Workload("conv_1k_bwd", "fft_conv_bwd", "f16", B=8, H=768, N=1024, seed=5),
+    "decode_125m": Workload("decode_125m", "ssm_step", "f16", B=64, H=768, N=1, seed=6),
 }
 
 
@@ -118,6 +129,20 @@ def make_inputs(w: Workload, *, B: int | None = None, H: int | None = None,
         else:
             out.update(diag_ssm_params(H, w.S, g))
         out["D"] = normal((H,), g, dtype=torch.float32)
+        return out
+    if w.kind == "fft_conv_bwd":
+        H = w.H if H is None else H
+        out = {"u": normal((B, H, N), g, dtype=io)}
+        out.update(diag_ssm_params(H, w.S, g))
+        out["D"] = normal((H,), g, dtype=torch.float32)
+        out["dy"] = normal((B, H, N), g, dtype=io)
+        return out
+    if w.kind == "ssm_step":
+        H = w.H if H is None else H
+        out = {"u": normal((B, H, N), g, dtype=io)}
+        out.update(diag_ssm_params(H, w.S, g))
+        out["D"] = normal((H,), g, dtype=torch.float32)
+        out["x"] = normal((B, H, w.S, 2), g, std=math.sqrt(0.5), dtype=torch.float32)
         return out
     if w.kind == "state_pass":
         H = w.H if H is None else H
