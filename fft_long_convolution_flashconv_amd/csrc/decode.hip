@@ -38,15 +38,21 @@ __global__ __launch_bounds__(256) void k_ssm_step(const typename io_elem<IO>::T 
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;  // (the whole wave)
     const int h = (int)(r % H);
-    // this lane's mode: Abar = exp(dt A) from fp64 exponentials, Bbar = dt B
+    // this lane's mode: Abar = exp(dt A), Bbar = dt B.  The phase dt Im A
+    // (up to ~1e2 rad) is formed exactly in fp64 and reduced by whole turns
+    // there; the fp32 sine, cosine and exponential of the reduced values are
+    // then accurate to about one ulp.
     cf ab = mk(0.f, 0.f), bb = mk(0.f, 0.f), cc = mk(0.f, 0.f), xs = mk(0.f, 0.f);
     if (lane < S) {
         const size_t o = ((size_t)h * S + lane) * 2;
         const double dth = (double)dt[h];
-        const double m = exp(dth * (double)A[o]);
-        double sn, cs;
-        sincos(dth * (double)A[o + 1], &sn, &cs);
-        ab = mk((float)(m * cs), (float)(m * sn));
+        constexpr double kTwoPi = 6.283185307179586232;
+        const double ph = dth * (double)A[o + 1];
+        const float r = (float)fma(-rint(ph * (1.0 / kTwoPi)), kTwoPi, ph);
+        float sn, cs;
+        sincosf(r, &sn, &cs);
+        const float m = expf((float)(dth * (double)A[o]));
+        ab = mk(m * cs, m * sn);
         bb = mk((float)(dth * (double)Bm[o]), (float)(dth * (double)Bm[o + 1]));
         cc = mk(C[o], C[o + 1]);
         xs = mk(x[((size_t)r * S + lane) * 2], x[((size_t)r * S + lane) * 2 + 1]);

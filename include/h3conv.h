@@ -194,7 +194,7 @@ h3conv_status h3conv_state_pass_noalloc(const void *u, const float *A, const flo
  *                                 state after the K steps
  *   y      [B,H,K]  io dtype      outputs (must not overlap any input or x)
  * Supported: 1 <= S <= H3CONV_MAX_STATE, B*H <= 2^34.  The recurrence runs
- * in fp32 (Abar from fp64 exponentials).
+ * in fp32.
  */
 h3conv_status h3conv_ssm_step(const void *u, const float *A, const float *Bm, const float *C,
                               const float *dt, const float *D, float *x, void *y, int64_t B, int64_t H,

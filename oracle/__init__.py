@@ -50,12 +50,13 @@ def _load():
         I = ctypes.c_int64
         lib.oracle_causal_conv.argtypes = [P, P, P, P, I, I, I]
         lib.oracle_causal_conv_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I]
+        lib.oracle_bidir_conv.argtypes = [P, P, P, P, P, I, I, I]
         lib.oracle_ssm_filter.argtypes = [P, P, P, P, P, I, I, I]
         lib.oracle_ssm_recurrence.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I]
         lib.oracle_h3_mix.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
-        for fn in (lib.oracle_causal_conv, lib.oracle_causal_conv_bwd, lib.oracle_ssm_filter,
+        for fn in (lib.oracle_causal_conv, lib.oracle_causal_conv_bwd, lib.oracle_bidir_conv, lib.oracle_ssm_filter,
                    lib.oracle_ssm_recurrence, lib.oracle_h3_mix):
             fn.restype = None
         _lib = lib
@@ -106,6 +107,21 @@ def causal_conv(u, f, D) -> np.ndarray:
     assert f.shape == (H, N) and D.shape == (H,)
     y = np.empty_like(u)
     _load().oracle_causal_conv(_ptr(u), _ptr(f), _ptr(D), _ptr(y), B, H, N)
+    return y
+
+
+def bidir_conv(u, f, g, D) -> np.ndarray:
+    """y[b,h,t] = sum_{k<=t} f[h,t-k] u[b,h,k] + sum_{k>=t} g[h,k-t] u[b,h,k] + D[h] u[b,h,t] (fp64).
+
+    u: [B,H,N]; f, g: [H,N]; D: [H].  The layer as bidirectional copies (the
+    summary page, E.4): a causal and an anti-causal convolution, summed, with
+    one residual.
+    """
+    u = _f64(u); f = _f64(f); g = _f64(g); D = _f64(D)
+    B, H, N = u.shape
+    assert f.shape == (H, N) and g.shape == (H, N) and D.shape == (H,)
+    y = np.empty_like(u)
+    _load().oracle_bidir_conv(_ptr(u), _ptr(f), _ptr(g), _ptr(D), _ptr(y), B, H, N)
     return y
 
 

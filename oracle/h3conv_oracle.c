@@ -99,6 +99,40 @@ void oracle_causal_conv(const double *u, const double *f, const double *D,
 }
 
 /*
+ * Bidirectional long convolution with residual: a causal copy with filter f
+ * and an anti-causal copy with filter g over the same input, summed,
+ *   y[b,h,t] = sum_{k=0..t} f[h,t-k] u[b,h,k] + sum_{k=t..N-1} g[h,k-t] u[b,h,k]
+ *              + D[h] u[b,h,t]
+ * u, y: [B,H,N]; f, g: [H,N]; D: [H].  O(N^2) per row.
+ * Source: summary page, E.4 "LRA evaluation" (the layer used as bidirectional
+ * copies) with the convolution of section 2; the anti-causal copy is the
+ * causal convolution of the time-reversed input, reversed back.  Reading:
+ * the two copies' outputs are summed and share one residual D u.
+ */
+void oracle_bidir_conv(const double *u, const double *f, const double *g,
+                       const double *D, double *y, int64_t B, int64_t H,
+                       int64_t N)
+{
+    int64_t rows = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t h = r % H;
+        const double *ur = u + r * N;
+        const double *fh = f + h * N;
+        const double *gh = g + h * N;
+        double *yr = y + r * N;
+        for (int64_t t = 0; t < N; ++t) {
+            double acc = 0.0;
+            for (int64_t k = 0; k <= t; ++k)
+                acc += fh[t - k] * ur[k];
+            for (int64_t k = t; k < N; ++k)
+                acc += gh[k - t] * ur[k];
+            yr[t] = acc + D[h] * ur[t];
+        }
+    }
+}
+
+/*
  * Gradients (reverse mode) of the causal convolution with residual above,
  * for an upstream gradient dy of y:
  *   du[b,h,k] = sum_{t=k..N-1} f[h,t-k] * dy[b,h,t]  +  D[h] * dy[b,h,k]

@@ -374,3 +374,40 @@ def test_causal_conv_bwd_adjoint_of_the_forward():
     assert abs(lhs - np.sum(df * g)) < 1e-11 * max(1.0, abs(lhs))
     lhs = np.sum(dy * oracle.causal_conv(u, np.zeros((H, N)), E))
     assert abs(lhs - np.sum(dD * E)) < 1e-11 * max(1.0, abs(lhs))
+
+
+# ---------------------------------------------------------------- bidirectional copies
+
+def test_golden_bidir_conv():
+    g = _read_golden("causal_conv_hand.txt")
+    y = oracle.bidir_conv(g["bidir_u"][None, None, :], g["bidir_f"][None, :], g["bidir_g"][None, :], g["bidir_D"])
+    assert np.array_equal(y[0, 0], g["bidir_y"])
+
+
+@pytest.mark.parametrize("N", [1, 3, 16, 50])
+def test_bidir_conv_bruteforce_exact(N):
+    """Small integers, exact in fp64: the full (upper + lower triangular)
+    Toeplitz matrix built in integers."""
+    rng = np.random.default_rng(300 + N)
+    B, H = 2, 2
+    u = rng.integers(-5, 6, size=(B, H, N)); f = rng.integers(-5, 6, size=(H, N))
+    g = rng.integers(-5, 6, size=(H, N)); D = rng.integers(-3, 4, size=H)
+    y = oracle.bidir_conv(u.astype(float), f.astype(float), g.astype(float), D.astype(float))
+    for b in range(B):
+        for h in range(H):
+            T = [[(int(f[h, t - k]) if k <= t else 0) + (int(g[h, k - t]) if k >= t else 0) + (int(D[h]) if k == t else 0)
+                  for k in range(N)] for t in range(N)]
+            ref = [sum(T[t][k] * int(u[b, h, k]) for k in range(N)) for t in range(N)]
+            assert y[b, h].tolist() == [float(x) for x in ref]
+
+
+def test_bidir_conv_reductions():
+    """g = 0 is the causal convolution; f = 0 is the causal convolution of the
+    reversed input with g, reversed back (the anti-causal copy)."""
+    rng = np.random.default_rng(31)
+    B, H, N = 2, 3, 200
+    u = rng.standard_normal((B, H, N)); f, g = rng.standard_normal((2, H, N)); D = rng.standard_normal(H)
+    z = np.zeros((H, N))
+    assert _rel(oracle.bidir_conv(u, f, z, D), oracle.causal_conv(u, f, D)) < 1e-14
+    rev = oracle.causal_conv(u[..., ::-1].copy(), g, D)[..., ::-1]
+    assert _rel(oracle.bidir_conv(u, z, g, D), rev) < 1e-13
