@@ -34,7 +34,7 @@ MAX_STATE = 64
 _IO = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
 
-EXPORTS = ("h3conv_fft_conv", "h3conv_fft_conv_bwd", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
+EXPORTS = ("h3conv_fft_conv", "h3conv_fft_conv_bidir", "h3conv_fft_conv_bwd", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
            "h3conv_ssm_step", "h3conv_h3_mix", "h3conv_workspace_size", "h3conv_status_string", "h3conv_version")
 NOALLOC_WORKSPACE_BYTES = 128 * 1024 * 1024
 
@@ -56,6 +56,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.h3conv_fft_conv.argtypes = [P, P, P, P, I64, I64, I64, I, P]
+    lib.h3conv_fft_conv_bidir.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
     lib.h3conv_fft_conv_bwd.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, P]
     lib.h3conv_ssm_filter.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.h3conv_state_pass.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
@@ -67,7 +68,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.h3conv_status_string.argtypes = [I]
     lib.h3conv_status_string.restype = ctypes.c_char_p
     lib.h3conv_version.restype = I
-    for name in ("h3conv_fft_conv", "h3conv_fft_conv_bwd", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
+    for name in ("h3conv_fft_conv", "h3conv_fft_conv_bidir", "h3conv_fft_conv_bwd", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
                  "h3conv_ssm_step", "h3conv_h3_mix"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -160,6 +161,25 @@ def fft_conv(u: torch.Tensor, f: torch.Tensor, D: torch.Tensor, out: torch.Tenso
     y = torch.empty_like(u) if out is None else out
     _check(load().h3conv_fft_conv(_ptr(u), _ptr(f), _ptr(D), _ptr(y), B, H, N, io, _stream()),
            "h3conv_fft_conv")
+    return y
+
+
+def fft_conv_bidir(u: torch.Tensor, f: torch.Tensor, g: torch.Tensor, D: torch.Tensor,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Bidirectional copies: y = causal (f * u) + anti-causal (g * u) + D u;
+    u [B,H,N] f32/f16/bf16, f, g [H,N] f32, D [H] f32."""
+    _need(u, "u")
+    io = _io(u, "u")
+    if u.dim() != 3:
+        raise ValueError("u must be [B,H,N], got %s" % (tuple(u.shape),))
+    B, H, N = u.shape
+    _need(f, "f", torch.float32, (H, N)); _need(g, "g", torch.float32, (H, N)); _need(D, "D", torch.float32, (H,))
+    if out is not None:
+        _need(out, "out", u.dtype, (B, H, N))
+    _same_device(u=u, f=f, g=g, D=D, out=out)
+    y = torch.empty_like(u) if out is None else out
+    _check(load().h3conv_fft_conv_bidir(_ptr(u), _ptr(f), _ptr(g), _ptr(D), _ptr(y), B, H, N, io, _stream()),
+           "h3conv_fft_conv_bidir")
     return y
 
 

@@ -26,7 +26,7 @@ FLAGS = [
     # no packed fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", CSRC, "-I", INCLUDE,
-    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    "-Wall", "-Wshadow", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
 

@@ -48,9 +48,9 @@ __global__ __launch_bounds__(256) void k_ssm_step(const typename io_elem<IO>::T 
         const double dth = (double)dt[h];
         constexpr double kTwoPi = 6.283185307179586232;
         const double ph = dth * (double)A[o + 1];
-        const float r = (float)fma(-rint(ph * (1.0 / kTwoPi)), kTwoPi, ph);
+        const float phr = (float)fma(-rint(ph * (1.0 / kTwoPi)), kTwoPi, ph);
         float sn, cs;
-        sincosf(r, &sn, &cs);
+        sincosf(phr, &sn, &cs);
         const float m = expf((float)(dth * (double)A[o]));
         ab = mk(m * cs, m * sn);
         bb = mk((float)(dth * (double)Bm[o]), (float)(dth * (double)Bm[o + 1]));

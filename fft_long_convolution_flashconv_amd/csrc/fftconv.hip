@@ -260,6 +260,79 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
     E.template run_raw<SPOL, CORR>(mf::row_rsrc(fh, 4 * N), dh, rows, (B + 1) / 2, hb);
 }
 
+// Bidirectional copies of the layer (the paperlayer.ai summary, E.4 "LRA
+// evaluation"): y = causal (f * u) + anti-causal (g * u) + D u, one
+// transform per row pair with the spectrum F + conj(G) of the two-sided
+// filter (g's taps sit at negative lags, which the zero padding to 2N keeps
+// apart from f's).
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(Plan<LOG2M>::NT) void k_fft_bidir(
+    const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f, const float *__restrict__ g,
+    const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
+    using T = typename io_elem<IO>::T;
+    using FR = FiltReg<LOG2M>;
+    __shared__ cf lds[Plan<LOG2M>::LDS_ELEMS];
+    const int tid = threadIdx.x;
+    const int h = blockIdx.x;
+    const float *fh = f + (size_t)h * N, *gh = g + (size_t)h * N;
+    const float dh = D[h];
+    FR F, G;
+    filter_spectrum<LOG2M>(lds, tid, [&](int pos) -> cf {
+        float v = (pos < N) ? fh[pos] : 0.f;
+        if (pos == 0) v += dh;
+        return mk(v, 0.f);
+    }, F);
+    filter_spectrum<LOG2M>(lds, tid, [&](int pos) -> cf { return mk(pos < N ? gh[pos] : 0.f, 0.f); }, G);
+#pragma unroll
+    for (int i = 0; i < FR::NBT; ++i)
+#pragma unroll
+        for (int k = 0; k < FR::R; ++k) F.v[i][k] = mk(F.v[i][k].x + G.v[i][k].x, F.v[i][k].y - G.v[i][k].y);
+    const int nsig = (B + 1) / 2;
+    for (int s = 0; s < nsig; ++s) {
+        const int b0 = 2 * s;
+        const bool has1 = (b0 + 1) < B;
+        const T *u0 = u + ((size_t)b0 * H + h) * N;
+        const T *u1 = u0 + (size_t)H * N;
+        T *y0 = y + ((size_t)b0 * H + h) * N;
+        T *y1 = y0 + (size_t)H * N;
+        auto ld = [&](int pos) -> cf {
+            if (pos >= N) return mk(0.f, 0.f);
+            return mk(ld_io<IO>(u0 + pos), has1 ? ld_io<IO>(u1 + pos) : 0.f);
+        };
+        auto st = [&](int pos, cf v) {
+            if (pos < N) {
+                st_io<IO>(y0 + pos, v.x);
+                if (has1) st_io<IO>(y1 + pos, v.y);
+            }
+        };
+        conv_signal<LOG2M>(lds, tid, F, ld, st);
+    }
+}
+
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M>::WPE))) void k_fft_bidir_mfma(
+    const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f, const float *__restrict__ g,
+    const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
+    using SH = mf::Shape<LOG2M>;
+    constexpr int KIND = IO == IO_F16 ? mf::IN_F16 : mf::IN_BF16;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[SH::LDS_DWORDS];
+    mf::Engine<LOG2M, KIND> E(smem);
+    E.init();
+    const int h = blockIdx.x;
+    const uint32_t rsb = mf::opaque_u32(2u * (uint32_t)H * (uint32_t)N);
+    const char *uh = (const char *)(u + (size_t)h * N);
+    char *yh = (char *)(y + (size_t)h * N);
+    auto rows = [&](int sig) -> mf::RowBufs {
+        const uint32_t o = (uint32_t)(2 * sig) * rsb;
+        const int nb0 = (2 * sig < B) ? 2 * N : 0;
+        const int nb1 = (2 * sig + 1 < B) ? 2 * N : 0;
+        return {mf::row_rsrc(uh + o, nb0), mf::row_rsrc(uh + o + rsb, nb1), mf::row_rsrc(yh + o, nb0),
+                mf::row_rsrc(yh + o + rsb, nb1)};
+    };
+    E.run_raw_bidir(mf::row_rsrc(f + (size_t)h * N, 4 * N), D[h], mf::row_rsrc(g + (size_t)h * N, 4 * N), rows,
+                    (B + 1) / 2, mf::half_bits(N));
+}
+
 // Row byte offsets inside one launch of the 16-bit engine are 32-bit,
 // including the empty rows a last partial round addresses (up to 2 SIG + 2
 // past the batch): larger batches go in slices of an even number of rows,
@@ -347,6 +420,56 @@ hipError_t launch_fft_conv(const void *u, const float *f, const float *D, void *
         case IO_F32: return fc_dispatch<IO_F32>(l, u, f, D, y, B, H, N, s);
         case IO_F16: return fc_dispatch<IO_F16>(l, u, f, D, y, B, H, N, s);
         case IO_BF16: return fc_dispatch<IO_BF16>(l, u, f, D, y, B, H, N, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int LOG2M, int IO>
+static hipError_t launch_bidir(const void *u, const float *f, const float *g, const float *D, void *y, int B, int H,
+                               int N, hipStream_t s) {
+    using T = typename io_elem<IO>::T;
+    if constexpr (IO != IO_F32 && LOG2M >= 9) {
+        const uint64_t rowb = 2ull * (uint64_t)H * (uint64_t)N;
+        const uint64_t pad = fc_row_pad<LOG2M>();
+        if ((pad + 2) * rowb >= (1ull << 32)) return hipErrorInvalidValue;  // refused by the API first
+        const int bmax = (int)std::min<uint64_t>((uint64_t)B, (((1ull << 32) - 1) / rowb - pad) & ~1ull);
+        for (int b0 = 0; b0 < B; b0 += bmax) {
+            const size_t o = (size_t)b0 * H * N;
+            const hipError_t e = launch(k_fft_bidir_mfma<LOG2M, IO>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,
+                                        (const T *)u + o, f, g, D, (T *)y + o, std::min(bmax, B - b0), H, N);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    } else {
+        return launch(k_fft_bidir<LOG2M, IO>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T *)u, f, g, D, (T *)y, B,
+                      H, N);
+    }
+}
+
+template <int IO>
+static hipError_t bidir_dispatch(int log2m, const void *u, const float *f, const float *g, const float *D, void *y,
+                                 int B, int H, int N, hipStream_t s) {
+    switch (log2m) {
+        case 6: return launch_bidir<6, IO>(u, f, g, D, y, B, H, N, s);
+        case 7: return launch_bidir<7, IO>(u, f, g, D, y, B, H, N, s);
+        case 8: return launch_bidir<8, IO>(u, f, g, D, y, B, H, N, s);
+        case 9: return launch_bidir<9, IO>(u, f, g, D, y, B, H, N, s);
+        case 10: return launch_bidir<10, IO>(u, f, g, D, y, B, H, N, s);
+        case 11: return launch_bidir<11, IO>(u, f, g, D, y, B, H, N, s);
+        case 12: return launch_bidir<12, IO>(u, f, g, D, y, B, H, N, s);
+        case 13: return launch_bidir<13, IO>(u, f, g, D, y, B, H, N, s);
+        case 14: return launch_bidir<14, IO>(u, f, g, D, y, B, H, N, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fft_bidir(const void *u, const float *f, const float *g, const float *D, void *y, int B, int H,
+                            int N, int io, hipStream_t s) {
+    const int l = fused_log2m(N);
+    switch (io) {
+        case IO_F32: return bidir_dispatch<IO_F32>(l, u, f, g, D, y, B, H, N, s);
+        case IO_F16: return bidir_dispatch<IO_F16>(l, u, f, g, D, y, B, H, N, s);
+        case IO_BF16: return bidir_dispatch<IO_BF16>(l, u, f, g, D, y, B, H, N, s);
         default: return hipErrorInvalidValue;
     }
 }

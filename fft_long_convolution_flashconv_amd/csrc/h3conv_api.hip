@@ -168,6 +168,25 @@ h3conv_status h3conv_fft_conv(const void *u, const float *f, const float *D, voi
                                          (hipStream_t)stream));
 }
 
+h3conv_status h3conv_fft_conv_bidir(const void *u, const float *f, const float *g, const float *D,
+                                    void *y, int64_t B, int64_t H, int64_t N, int io, void *stream) {
+    if (B < 0 || H < 0 || N < 0 || !valid_io(io)) return H3CONV_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || N == 0) return H3CONV_OK;
+    if (!u || !f || !g || !D || !y) return H3CONV_ERR_INVALID_ARG;
+    if (!aligned16(u) || !aligned16(f) || !aligned16(g) || !aligned16(D) || !aligned16(y))
+        return H3CONV_ERR_INVALID_ARG;
+    if (N > H3CONV_MAX_FUSED_N) return H3CONV_ERR_UNSUPPORTED;
+    if (!mul_ok(B, H, INT32_MAX) || !mul_ok(B * H, N, INT64_MAX / 4)) return H3CONV_ERR_UNSUPPORTED;
+    if (!h3c::fft_conv_rows_fit(H, N, io)) return H3CONV_ERR_UNSUPPORTED;
+    const size_t ny = (size_t)(B * H * N) * esize(io), nf = (size_t)(H * N) * 4;
+    if (overlap(y, ny, u, ny) || overlap(y, ny, f, nf) || overlap(y, ny, g, nf) ||
+        overlap(y, ny, D, (size_t)H * 4))
+        return H3CONV_ERR_INVALID_ARG;
+    h3conv_status st = device_check();
+    if (st != H3CONV_OK) return st;
+    return from_hip(h3c::launch_fft_bidir(u, f, g, D, y, (int)B, (int)H, (int)N, io, (hipStream_t)stream));
+}
+
 h3conv_status h3conv_fft_conv_bwd(const void *u, const float *f, const float *D, const void *dy,
                                   void *du, float *df, float *dD, int64_t B, int64_t H, int64_t N,
                                   int io, void *stream) {

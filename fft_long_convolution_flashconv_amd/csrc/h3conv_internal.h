@@ -41,6 +41,10 @@ int fused_log2m(int64_t N);
 hipError_t launch_fft_conv(const void *u, const float *f, const float *D, void *y, int B, int H,
                            int N, int io, hipStream_t s);
 
+// Bidirectional copies: causal convolution with f plus anti-causal with g.
+hipError_t launch_fft_bidir(const void *u, const float *f, const float *g, const float *D, void *y, int B, int H,
+                            int N, int io, hipStream_t s);
+
 // Gradients du, df, dD of the causal convolution for an upstream dy.
 hipError_t launch_fft_conv_bwd(const void *u, const float *f, const float *D, const void *dy, void *du,
                                float *df, float *dD, int B, int H, int N, int io, hipStream_t s);

@@ -1244,7 +1244,8 @@ struct Engine {
     // last pass of the filter transform (signal slot `s`): the spectrum into
     // F, conjugated (the products take conj(X) conj(F) = conj(X F)), or as
     // it is with CORR (conj(X) F = conj(X conj(F)): correlation)
-    template <bool CORR>
+    // ACC: added to the spectrum already in F (both at the same scale).
+    template <bool CORR, bool ACC = false>
     __device__ __forceinline__ void filter_last(int s) {
         constexpr float c = 1.0f / (16384.0f * R);
         const uint32_t ch = CORR ? pk(c, c) : pk(c, -c);
@@ -1255,7 +1256,12 @@ struct Engine {
                 uint32_t y[NV];
                 last_fwd((lb ^ lpos(slot)) + s * SB, y);
 #pragma unroll
-                for (int q = 0; q < NV; ++q) F[fslot(slot) + q] = pkmul(y[q], ch);
+                for (int q = 0; q < NV; ++q) {
+                    const uint32_t v = pkmul(y[q], ch);
+                    F[fslot(slot) + q] = ACC ? __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, F[fslot(slot) + q]) +
+                                                                               __builtin_bit_cast(h2, v))
+                                             : v;
+                }
             }
         }
     }
@@ -1348,6 +1354,51 @@ struct Engine {
     // round always transforms SIG signals).  The inputs of each round are
     // fetched while the previous round (or the filter) is being transformed.
     // SPOL: cache policy of the output stores.
+    // Bidirectional copies: the convolution with the two-sided filter whose
+    // causal taps are f (with d0 added to tap 0, the residual) and whose
+    // anti-causal taps are g, i.e. the spectrum F + conj(G): both filters are
+    // transformed on their own (f, then g, in signal slot 0) with one input
+    // scale from sum |f| + sum |g|, which bounds every partial sum of either
+    // transform and of the combined spectrum; the stored conjugate is
+    // conj(F) + G.  Then the rounds, as in run_raw.
+    template <int SPOL = kNT, class RB>
+    __device__ void run_raw_bidir(__amdgpu_buffer_rsrc_t frs, float d0, __amdgpu_buffer_rsrc_t grs, const RB &rows,
+                                  int nsig, int hb) {
+        static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
+        float fin[T0W][4];
+        __builtin_amdgcn_s_setprio(kPrioLoad);
+        {
+            float gin[T0W][4];
+            filter_fetch(frs, d0, fin);
+            filter_fetch(grs, 0.f, gin);
+            if constexpr (PREFETCH) fetch_raw(rows, 0, pin);
+            const float sf = filter_scale(block_reduce<true>(filter_asum(fin) + filter_asum(gin)));
+            auto fop = [&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); };
+            pass0<1>(fop, fop);
+            fwd_middle<1, 1>();
+            filter_last<false>(0);
+            __syncthreads();  // slot 0 has been read; the second transform writes it
+            auto gop = [&](int i, int e) -> uint32_t { return pk(gin[i][e] * sf, 0.f); };
+            pass0<1>(gop, gop);
+            fwd_middle<1, 1>();
+            filter_last<true, true>(0);
+        }
+        auto store = [&](int r0, int s, int n, int m, uint32_t hv) {
+            const RowBufs rb = rows(r0 + s);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, SPOL);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, SPOL);
+        };
+        auto prefetch = [&](int r0) {
+            if (PREFETCH && r0 + SIG < nsig) fetch_raw(rows, r0 + SIG, pin);
+        };
+        for (int r0 = 0; r0 < nsig; r0 += SIG) {
+            __builtin_amdgcn_s_setprio(kPrioLoad);
+            if (!PREFETCH) fetch_raw(rows, r0, pin);
+            conv_round<false, false>([&](int s, int n, int m, uint32_t hv) { store(r0, s, n, m, hv); }, hb, fin,
+                                     [&]() { prefetch(r0); });
+        }
+    }
+
     // CORR: correlation with the filter (its conjugated spectrum) instead of
     // convolution.
     template <int SPOL = kNT, bool CORR = false, class RB>

@@ -85,6 +85,21 @@ h3conv_status h3conv_fft_conv(const void *u, const float *f, const float *D, voi
                               int64_t B, int64_t H, int64_t N, int io, void *stream);
 
 /*
+ * Bidirectional copies of the convolution (the paperlayer.ai summary, E.4
+ * "LRA evaluation": the layer used as bidirectional copies), one residual:
+ *     y[b,h,t] = sum_{k<=t} f[h,t-k] u[b,h,k] + sum_{k>=t} g[h,k-t] u[b,h,k]
+ *                + D[h] u[b,h,t]
+ * i.e. a causal copy with filter f and an anti-causal copy with filter g
+ * (the causal convolution of the time-reversed input, reversed back),
+ * computed as one fused transform per row pair with the two-sided filter.
+ *
+ *   u, y [B,H,N] io dtype;  f, g [H,N] fp32;  D [H] fp32
+ * Supported sizes and errors: as h3conv_fft_conv.
+ */
+h3conv_status h3conv_fft_conv_bidir(const void *u, const float *f, const float *g, const float *D,
+                                    void *y, int64_t B, int64_t H, int64_t N, int io, void *stream);
+
+/*
  * Backward pass of h3conv_fft_conv: for an upstream gradient dy of y,
  *     du[b,h,k] = sum_{t=k..N-1} f[h,t-k] dy[b,h,t] + D[h] dy[b,h,k]
  *     df[h,s]   = sum_b sum_{t=s..N-1} dy[b,h,t] u[b,h,t-s]
