@@ -51,12 +51,14 @@ def _load():
         lib.oracle_causal_conv.argtypes = [P, P, P, P, I, I, I]
         lib.oracle_causal_conv_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I]
         lib.oracle_bidir_conv.argtypes = [P, P, P, P, P, I, I, I]
+        lib.oracle_h3_mix_mh.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
         lib.oracle_ssm_filter.argtypes = [P, P, P, P, P, I, I, I]
         lib.oracle_ssm_recurrence.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I]
         lib.oracle_h3_mix.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
-        for fn in (lib.oracle_causal_conv, lib.oracle_causal_conv_bwd, lib.oracle_bidir_conv, lib.oracle_ssm_filter,
+        for fn in (lib.oracle_causal_conv, lib.oracle_causal_conv_bwd, lib.oracle_bidir_conv, lib.oracle_h3_mix_mh,
+                   lib.oracle_ssm_filter,
                    lib.oracle_ssm_recurrence, lib.oracle_h3_mix):
             fn.restype = None
         _lib = lib
@@ -199,4 +201,23 @@ def h3_mix(q, k, v, w, f, D) -> np.ndarray:
     scratch = np.empty(2 * N * max(1, max_threads()), dtype=np.float64)
     _load().oracle_h3_mix(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(f), _ptr(D),
                           _ptr(out), B, N, Dm, L, _ptr(scratch))
+    return out
+
+
+def h3_mix_mh(q, k, v, w, f, D, dh: int) -> np.ndarray:
+    """Multi-head H3 mixing with head dimension dh (fp64): per head, the
+    outer product of shift(k) and v, a long convolution of every entry
+    (i, j) with its own filter f[(h*dh+i)*dh+j] and D, then out_j = sum_i
+    q_i z_ij.  q, k, v: [B,N,Dm]; w: [Dm,L]; f: [Dm*dh,N]; D: [Dm*dh].  The
+    summary page's section 3 and Appendix C (keys in separate heads); dh = 1
+    is h3_mix.
+    """
+    q = _f64(q); k = _f64(k); v = _f64(v); w = _f64(w); f = _f64(f); D = _f64(D)
+    B, N, Dm = q.shape
+    L = w.shape[1]
+    assert Dm % dh == 0 and f.shape == (Dm * dh, N) and D.shape == (Dm * dh,) and w.shape[0] == Dm
+    out = np.empty_like(q)
+    scratch = np.empty((2 * dh * dh + dh) * N * max(1, max_threads()), dtype=np.float64)
+    _load().oracle_h3_mix_mh(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(f), _ptr(D), _ptr(out),
+                             B, N, Dm, int(dh), L, _ptr(scratch))
     return out

@@ -99,6 +99,75 @@ void oracle_causal_conv(const double *u, const double *f, const double *D,
 }
 
 /*
+ * Multi-head H3 mixing, head dimension dh, channel-last [B,N,Dm], Dm = heads*dh.
+ * For head h (model channels h*dh .. h*dh+dh-1), step t:
+ *   s[t,i]   = sum_{l<L, l<=t} w[h*dh+i, l] k[t-l, h*dh+i]    shift SSM on each key channel
+ *   m[t,i,j] = s[t,i] * v[t, h*dh+j]                          outer product of key and value
+ *   z[t,i,j] = sum_{tau<=t} f[c, t-tau] m[tau,i,j] + D[c] m[t,i,j],  c = (h*dh+i)*dh + j
+ *   out[t, h*dh+j] = sum_i q[t, h*dh+i] z[t,i,j]
+ * q, k, v, out: [B,N,Dm]; w: [Dm,L]; f: [Dm*dh,N]; D: [Dm*dh].
+ * Source: summary page section 3 (cost O(d^2 N + d N log N) when the head
+ * dimension is O(1)) and Appendix C "H3 Model to Solve Lambda" (keys in
+ * separate heads); blog "The Solution, Part 1" (Q gate on the diagonal SSM
+ * of shift(K) gate V).  Readings: the gates become the outer product
+ * shift(K)^T V per head and the contraction with Q, one long filter and one
+ * D per state entry (i, j); dh = 1 is oracle_h3_mix.
+ * `scratch` must hold (2*dh*dh + dh) * N doubles per OpenMP thread.
+ */
+void oracle_h3_mix_mh(const double *q, const double *k, const double *v,
+                      const double *w, const double *f, const double *D,
+                      double *out, int64_t B, int64_t N, int64_t Dm,
+                      int64_t dh, int64_t L, double *scratch)
+{
+    int64_t heads = Dm / dh;
+    int64_t items = B * heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t it = 0; it < items; ++it) {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        double *m = scratch + (int64_t)tid * (2 * dh * dh + dh) * N; /* [dh*dh][N] */
+        double *z = m + dh * dh * N;                                  /* [dh*dh][N] */
+        double *sk = z + dh * dh * N;                                 /* [dh][N] */
+        int64_t b = it / heads, h = it % heads;
+        const int64_t base = b * N * Dm; /* element (t, d) at base + t*Dm + d */
+        for (int64_t i = 0; i < dh; ++i) {
+            int64_t d = h * dh + i;
+            for (int64_t t = 0; t < N; ++t) {
+                double s = 0.0;
+                for (int64_t l = 0; l < L && l <= t; ++l)
+                    s += w[d * L + l] * k[base + (t - l) * Dm + d];
+                sk[i * N + t] = s;
+            }
+        }
+        for (int64_t i = 0; i < dh; ++i)
+            for (int64_t j = 0; j < dh; ++j)
+                for (int64_t t = 0; t < N; ++t)
+                    m[(i * dh + j) * N + t] = sk[i * N + t] * v[base + t * Dm + h * dh + j];
+        for (int64_t i = 0; i < dh; ++i)
+            for (int64_t j = 0; j < dh; ++j) {
+                int64_t c = (h * dh + i) * dh + j;
+                const double *mr = m + (i * dh + j) * N;
+                double *zr = z + (i * dh + j) * N;
+                for (int64_t t = 0; t < N; ++t) {
+                    double acc = 0.0;
+                    for (int64_t tau = 0; tau <= t; ++tau)
+                        acc += f[c * N + t - tau] * mr[tau];
+                    zr[t] = acc + D[c] * mr[t];
+                }
+            }
+        for (int64_t j = 0; j < dh; ++j)
+            for (int64_t t = 0; t < N; ++t) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dh; ++i)
+                    acc += q[base + t * Dm + h * dh + i] * z[(i * dh + j) * N + t];
+                out[base + t * Dm + h * dh + j] = acc;
+            }
+    }
+}
+
+/*
  * Bidirectional long convolution with residual: a causal copy with filter f
  * and an anti-causal copy with filter g over the same input, summed,
  *   y[b,h,t] = sum_{k=0..t} f[h,t-k] u[b,h,k] + sum_{k=t..N-1} g[h,k-t] u[b,h,k]

@@ -411,3 +411,53 @@ def test_bidir_conv_reductions():
     assert _rel(oracle.bidir_conv(u, f, z, D), oracle.causal_conv(u, f, D)) < 1e-14
     rev = oracle.causal_conv(u[..., ::-1].copy(), g, D)[..., ::-1]
     assert _rel(oracle.bidir_conv(u, z, g, D), rev) < 1e-13
+
+
+# ---------------------------------------------------------------- multi-head H3
+
+def test_golden_h3_mix_mh():
+    g = _read_golden("h3_mix_hand.txt")
+    q, k, v = (g["mh_" + x].reshape(1, 2, 2) for x in ("q", "k", "v"))
+    w = g["mh_w"].reshape(2, 1)
+    f = g["mh_f"].reshape(4, 2)
+    out = oracle.h3_mix_mh(q, k, v, w, f, np.zeros(4), 2)
+    assert np.array_equal(out.reshape(-1), g["mh_out"])
+
+
+def test_h3_mix_mh_head_dim_one_is_h3_mix():
+    rng = np.random.default_rng(41)
+    B, N, Dm, L = 2, 90, 5, 3
+    q, k, v = rng.standard_normal((3, B, N, Dm))
+    w = rng.standard_normal((Dm, L)); f = rng.standard_normal((Dm, N)); D = rng.standard_normal(Dm)
+    assert _rel(oracle.h3_mix_mh(q, k, v, w, f, D, 1), oracle.h3_mix(q, k, v, w, f, D)) < 1e-14
+
+
+def test_h3_mix_mh_gates_only_closed_form():
+    """f = 0, D = 1: out_j = (sum_i q_i s_i) v_j per head, s = shift(k)."""
+    rng = np.random.default_rng(42)
+    B, N, dh, heads, L = 2, 40, 4, 3, 2
+    Dm = dh * heads
+    q, k, v = rng.standard_normal((3, B, N, Dm))
+    w = rng.standard_normal((Dm, L))
+    out = oracle.h3_mix_mh(q, k, v, w, np.zeros((Dm * dh, N)), np.ones(Dm * dh), dh)
+    s = w[None, None, :, 0] * k
+    s[:, 1:, :] += w[None, None, :, 1] * k[:, :-1, :]
+    qs = (q * s).reshape(B, N, heads, dh).sum(-1)                 # [B, N, heads]
+    ref = (qs[..., None] * v.reshape(B, N, heads, dh)).reshape(B, N, Dm)
+    assert _rel(out, ref) < 1e-13
+
+
+def test_h3_mix_mh_entry_filters_are_separate():
+    """A delta filter on one state entry (i, j) and zeros elsewhere routes
+    exactly q_i s_i v_j to output channel j (catches swapped i, j)."""
+    rng = np.random.default_rng(43)
+    B, N, dh = 1, 30, 3
+    q, k, v = rng.standard_normal((3, B, N, dh))
+    w = np.ones((dh, 1))
+    for i in range(dh):
+        for j in range(dh):
+            f = np.zeros((dh * dh, N)); f[i * dh + j, 0] = 1.0
+            out = oracle.h3_mix_mh(q, k, v, w, f, np.zeros(dh * dh), dh)
+            ref = np.zeros_like(out)
+            ref[0, :, j] = q[0, :, i] * k[0, :, i] * v[0, :, j]
+            assert _rel(out, ref) < 1e-15
