@@ -110,6 +110,8 @@ def algorithmic_bytes(w: wl.Workload) -> int:
         return 2 * w.B * w.H * w.N * e + w.H * (3 * w.S * 8 + 8)
     if w.kind == "h3_mix":
         return 4 * w.B * w.N * w.Dm * e + w.Dm * (w.L * 4 + w.N * 4 + 4)
+    if w.kind == "h3_mix_mh":     # read q, k, v, w, f, D; write out
+        return 4 * w.B * w.N * w.Dm * e + w.Dm * w.L * 4 + w.Dm * w.dh * (w.N * 4 + 4)
     if w.kind == "fft_conv_bwd":  # read u, dy, f, D; write du, df, dD
         return 3 * w.B * w.H * w.N * e + 2 * w.H * w.N * 4 + 2 * w.H * 4
     if w.kind == "ssm_step":      # read u, x, parameters; write y, x
@@ -129,7 +131,7 @@ class Case:
         self.sets = []
         for i in range(self.nsets):
             s = {k: (v if i == 0 else v.clone()) for k, v in d.items()}
-            if w.kind in ("fft_conv", "h3_mix", "fft_conv_bwd") and "A" in s:
+            if w.kind in ("fft_conv", "h3_mix", "fft_conv_bwd", "h3_mix_mh") and "A" in s:
                 s["f"] = pkg.ssm_filter(s["A"], s["Bm"], s["C"], s["dt"], w.N)
             if w.kind == "fft_conv":
                 s["y"] = torch.empty_like(s["u"])
@@ -139,6 +141,10 @@ class Case:
                 s["dD"] = torch.empty(w.H, device=dev, dtype=torch.float32)
             elif w.kind == "ssm_step":
                 s["y"] = torch.empty_like(s["u"])
+            elif w.kind == "h3_mix_mh":
+                s["y"] = torch.empty_like(s["q"])
+                s["ws"] = torch.empty(pkg.workspace_size(pkg.OP_H3_MIX_MH, w.B, w.Dm, w.N, w.dh), device=dev,
+                                      dtype=torch.uint8)
             elif w.kind == "state_pass":
                 s["y"] = torch.empty_like(s["u"])
                 s["ws"] = torch.empty(pkg.workspace_size(pkg.OP_STATE_PASS, w.B, w.H, w.N, w.S, w.T),
@@ -159,6 +165,8 @@ class Case:
             pkg.fft_conv_bwd(s["u"], s["f"], s["D"], s["dy"], du=s["du"], df=s["df"], dD=s["dD"])
         elif w.kind == "ssm_step":
             pkg.ssm_step(s["u"], s["A"], s["Bm"], s["C"], s["dt"], s["D"], s["x"], out=s["y"])
+        elif w.kind == "h3_mix_mh":
+            pkg.h3_mix_mh(s["q"], s["k"], s["v"], s["w"], s["f"], s["D"], w.dh, out=s["y"], workspace=s["ws"])
         elif w.kind == "state_pass":
             pkg.state_pass(s["u"], s["A"], s["Bm"], s["C"], s["dt"], s["D"], w.T, out=s["y"],
                            workspace=s["ws"])
@@ -376,7 +384,7 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_secondary:
         sec = {}
-        for name in ("conv_8k", "state_64k", "h3_mix_2k", "conv_1k_bwd", "decode_125m"):
+        for name in ("conv_8k", "state_64k", "h3_mix_2k", "conv_1k_bwd", "decode_125m", "h3_mix_mh_1k"):
             if name == w.name:
                 continue
             ww = wl.WORKLOADS[name]

@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(HERE, "libh3conv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_HIP, ERR_WORKSPACE = range(6)
 F32, F16, BF16 = 0, 1, 2
-OP_FFT_CONV, OP_STATE_PASS, OP_H3_MIX = 0, 1, 2
+OP_FFT_CONV, OP_STATE_PASS, OP_H3_MIX, OP_H3_MIX_MH = 0, 1, 2, 3
 MAX_FUSED_N = 8192
 MAX_STATE = 64
 
@@ -35,7 +35,7 @@ _IO = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
 
 EXPORTS = ("h3conv_fft_conv", "h3conv_fft_conv_bidir", "h3conv_fft_conv_bwd", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
-           "h3conv_ssm_step", "h3conv_h3_mix", "h3conv_workspace_size", "h3conv_status_string", "h3conv_version")
+           "h3conv_ssm_step", "h3conv_h3_mix", "h3conv_h3_mix_mh", "h3conv_workspace_size", "h3conv_status_string", "h3conv_version")
 NOALLOC_WORKSPACE_BYTES = 128 * 1024 * 1024
 
 
@@ -63,13 +63,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.h3conv_state_pass_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P]
     lib.h3conv_ssm_step.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I, P]
     lib.h3conv_h3_mix.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.h3conv_h3_mix_mh.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]
     lib.h3conv_workspace_size.argtypes = [I, I64, I64, I64, I64, I64]
     lib.h3conv_workspace_size.restype = SZ
     lib.h3conv_status_string.argtypes = [I]
     lib.h3conv_status_string.restype = ctypes.c_char_p
     lib.h3conv_version.restype = I
     for name in ("h3conv_fft_conv", "h3conv_fft_conv_bidir", "h3conv_fft_conv_bwd", "h3conv_ssm_filter", "h3conv_state_pass", "h3conv_state_pass_noalloc",
-                 "h3conv_ssm_step", "h3conv_h3_mix"):
+                 "h3conv_ssm_step", "h3conv_h3_mix", "h3conv_h3_mix_mh"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -349,4 +350,38 @@ def h3_mix(q, k, v, w, f, D, out=None, workspace=None):
     _check(load().h3conv_h3_mix(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(f), _ptr(D), _ptr(o), B, N, Dm, L,
                                 io, _ptr(ws) if ws is not None else None, nws, _stream()),
            "h3conv_h3_mix")
+    return o
+
+
+def h3_mix_mh(q, k, v, w, f, D, dh: int, out=None, workspace=None):
+    """Multi-head H3 mixing, head dimension dh: per head, m = shift(k)^T v
+    (outer product), z = (f * m)[:N] + D m per state entry, out_j = sum_i q_i z_ij.
+    q, k, v [B,N,Dm]; w [Dm,L]; f [Dm*dh, N]; D [Dm*dh].  The workspace (two
+    channel-major stagings of the B x Dm*dh state rows) is allocated here
+    when not given."""
+    _need(q, "q")
+    io = _io(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [B,N,Dm], got %s" % (tuple(q.shape),))
+    B, N, Dm = q.shape
+    dh = int(dh)
+    if dh < 1 or Dm % dh != 0:
+        raise ValueError("dh must divide Dm = %d" % Dm)
+    _need(k, "k", q.dtype, (B, N, Dm)); _need(v, "v", q.dtype, (B, N, Dm))
+    _need(w, "w", torch.float32)
+    if w.dim() != 2 or w.shape[0] != Dm:
+        raise ValueError("w must be [Dm,L] with Dm = %d, got %s" % (Dm, tuple(w.shape)))
+    L = w.shape[1]
+    _need(f, "f", torch.float32, (Dm * dh, N)); _need(D, "D", torch.float32, (Dm * dh,))
+    if out is not None:
+        _need(out, "out", q.dtype, (B, N, Dm))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _same_device(q=q, k=k, v=v, w=w, f=f, D=D, out=out, workspace=workspace)
+    o = torch.empty_like(q) if out is None else out
+    need = workspace_size(OP_H3_MIX_MH, B, Dm, N, dh) * (2 if io == F32 else 1)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(load().h3conv_h3_mix_mh(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(f), _ptr(D), _ptr(o), B, N, Dm, dh, L,
+                                   io, _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+           "h3conv_h3_mix_mh")
     return o

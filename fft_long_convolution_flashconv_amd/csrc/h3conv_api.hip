@@ -140,6 +140,11 @@ size_t h3conv_workspace_size(int op, int64_t B, int64_t H, int64_t N, int64_t S,
         case H3CONV_OP_H3_MIX:
             if (B < 0 || H < 0 || N < 0) return (size_t)-1;
             return h3c::h3_mix_workspace(B, N, H);
+        case H3CONV_OP_H3_MIX_MH:
+            // H = Dm, S = head dimension; the 16-bit activation path (bf16
+            // intermediates); fp32 activations need twice this
+            if (B < 0 || H < 0 || N < 0 || S < 1 || H % S != 0) return (size_t)-1;
+            return h3c::h3_mix_mh_workspace(B, N, H, S, H3CONV_BF16);
         case H3CONV_OP_STATE_PASS:
             if (B < 0 || H < 0 || N < 0 || S < 1 || S > H3CONV_MAX_STATE || T < 64 ||
                 T > H3CONV_MAX_FUSED_N || (T & (T - 1)) != 0 || N % T != 0)
@@ -296,6 +301,38 @@ h3conv_status h3conv_ssm_step(const void *u, const float *A, const float *Bm, co
     h3conv_status st = device_check();
     if (st != H3CONV_OK) return st;
     return from_hip(h3c::launch_ssm_step(u, A, Bm, C, dt, D, x, y, B, H, K, (int)S, io, (hipStream_t)stream));
+}
+
+h3conv_status h3conv_h3_mix_mh(const void *q, const void *k, const void *v, const float *w,
+                               const float *f, const float *D, void *out, int64_t B, int64_t N,
+                               int64_t Dm, int64_t dh, int64_t L, int io, void *ws, size_t ws_bytes,
+                               void *stream) {
+    if (B < 0 || N < 0 || Dm < 0 || dh < 1 || L < 1 || !valid_io(io)) return H3CONV_ERR_INVALID_ARG;
+    if (B == 0 || N == 0 || Dm == 0) return H3CONV_OK;
+    if (L > 4 || N > H3CONV_MAX_FUSED_N || dh > 256 || (dh & (dh - 1)) != 0 || Dm % dh != 0)
+        return H3CONV_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !w || !f || !D || !out || !ws) return !ws ? H3CONV_ERR_WORKSPACE : H3CONV_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, w, f, D, out, ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return H3CONV_ERR_INVALID_ARG;
+    if (B > 65535 || !mul_ok(B, Dm * dh, INT32_MAX) || !mul_ok(B * Dm * dh, N, INT64_MAX / 8) ||
+        (N + 31) / 32 > 65535)
+        return H3CONV_ERR_UNSUPPORTED;
+    // the convolution over the state rows: its row-offset limit with H = Dm dh
+    if (!h3c::fft_conv_rows_fit(Dm * dh, N, io == H3CONV_F32 ? H3CONV_F32 : H3CONV_BF16))
+        return H3CONV_ERR_UNSUPPORTED;
+    const size_t need = h3c::h3_mix_mh_workspace(B, N, Dm, dh, io);
+    if (ws_bytes < need) return H3CONV_ERR_WORKSPACE;
+    const size_t n = (size_t)(B * N * Dm) * esize(io), nf = (size_t)(Dm * dh * N) * 4;
+    struct R { const void *p; size_t n; } ins[] = {{q, n}, {k, n}, {v, n}, {w, (size_t)(Dm * L) * 4}, {f, nf},
+                                                   {D, (size_t)(Dm * dh) * 4}};
+    for (auto &i : ins)
+        if (overlap(out, n, i.p, i.n) || overlap(ws, need, i.p, i.n)) return H3CONV_ERR_INVALID_ARG;
+    if (overlap(out, n, ws, need)) return H3CONV_ERR_INVALID_ARG;
+    h3conv_status st = device_check();
+    if (st != H3CONV_OK) return st;
+    return from_hip(h3c::launch_h3_mix_mh(q, k, v, w, f, D, out, (int)B, (int)N, (int)Dm, (int)dh, (int)L, io,
+                                          ws, (hipStream_t)stream));
 }
 
 h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const float *w,

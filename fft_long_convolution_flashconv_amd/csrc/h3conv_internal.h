@@ -41,6 +41,12 @@ int fused_log2m(int64_t N);
 hipError_t launch_fft_conv(const void *u, const float *f, const float *D, void *y, int B, int H,
                            int N, int io, hipStream_t s);
 
+// Multi-head H3 mixing (head dimension dh); workspace bytes for io.
+hipError_t launch_h3_mix_mh(const void *q, const void *k, const void *v, const float *w, const float *f,
+                            const float *D, void *out, int B, int N, int Dm, int dh, int L, int io, void *ws,
+                            hipStream_t s);
+size_t h3_mix_mh_workspace(int64_t B, int64_t N, int64_t Dm, int64_t dh, int io);
+
 // Bidirectional copies: causal convolution with f plus anti-causal with g.
 hipError_t launch_fft_bidir(const void *u, const float *f, const float *g, const float *D, void *y, int B, int H,
                             int N, int io, hipStream_t s);

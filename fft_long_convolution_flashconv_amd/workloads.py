@@ -25,6 +25,9 @@ parity configurations, timed beside them):
   decode_125m  fp16  B=64 H=768  K=1      one generated token per row from a
                                           state x ~ CN(0, 1), 64 modes (batch
                                           64 as in the pages' generation runs)
+  h3_mix_mh_1k fp16  B=4  N=1024 Dm=768 dh=4  multi-head H3 mixing, heads of
+                                          dimension 4, one diagonal-SSM filter
+                                          per state entry
 
 Diagonal-SSM parameters: A_j = -0.5 + i*pi*j (j = 0..S-1), B_j = 1,
 C_j ~ CN(0, 0.5) (real and imaginary parts independent N(0, 0.25)),
@@ -54,6 +57,7 @@ class Workload:
     L: int = 4           # shift-SSM taps (h3_mix)
     filt: str = "ssm"    # "ssm" | "random_env"
     seed: int = 0
+    dh: int = 1          # head dimension (multi-head H3 mixing)
 
     @property
     def elements(self) -> int:
@@ -68,6 +72,7 @@ WORKLOADS = {
     "h3_mix_2k": Workload("h3_mix_2k", "h3_mix", "bf16", B=4, N=2048, Dm=2560, seed=4),
     "conv_1k_bwd": Workload("conv_1k_bwd", "fft_conv_bwd", "f16", B=8, H=768, N=1024, seed=5),
     "decode_125m": Workload("decode_125m", "ssm_step", "f16", B=64, H=768, N=1, seed=6),
+    "h3_mix_mh_1k": Workload("h3_mix_mh_1k", "h3_mix_mh", "f16", B=4, N=1024, Dm=768, dh=4, seed=7),
 }
 
 
@@ -149,6 +154,17 @@ def make_inputs(w: Workload, *, B: int | None = None, H: int | None = None,
         out = {"u": normal((B, H, N), g, dtype=io)}
         out.update(diag_ssm_params(H, w.S, g))
         out["D"] = normal((H,), g, dtype=torch.float32)
+        return out
+    if w.kind == "h3_mix_mh":
+        Dm = w.Dm if H is None else H
+        out = {
+            "q": normal((B, N, Dm), g, dtype=io),
+            "k": normal((B, N, Dm), g, dtype=io),
+            "v": normal((B, N, Dm), g, dtype=io),
+            "w": normal((Dm, w.L), g, std=0.5, dtype=torch.float32),
+        }
+        out.update(diag_ssm_params(Dm * w.dh, w.S, g))
+        out["D"] = normal((Dm * w.dh,), g, dtype=torch.float32)
         return out
     if w.kind == "h3_mix":
         Dm = w.Dm if H is None else H

@@ -47,7 +47,12 @@ typedef enum {
 
 typedef enum { H3CONV_F32 = 0, H3CONV_F16 = 1, H3CONV_BF16 = 2 } h3conv_dtype;
 
-typedef enum { H3CONV_OP_FFT_CONV = 0, H3CONV_OP_STATE_PASS = 1, H3CONV_OP_H3_MIX = 2 } h3conv_op;
+typedef enum {
+    H3CONV_OP_FFT_CONV = 0,
+    H3CONV_OP_STATE_PASS = 1,
+    H3CONV_OP_H3_MIX = 2,
+    H3CONV_OP_H3_MIX_MH = 3
+} h3conv_op;
 
 /* Largest sequence length handled by one fused FFT block (2N <= 16384 points). */
 #define H3CONV_MAX_FUSED_N 8192
@@ -240,10 +245,41 @@ h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const f
                             void *stream);
 
 /*
+ * Multi-head H3 mixing, head dimension dh (model width Dm = heads * dh),
+ * channel-last layout.  The summary page's section 3 (cost O(d^2 N + d N
+ * log N) for an O(1) head dimension) and Appendix C "H3 Model to Solve
+ * Lambda" (keys in separate heads), with the blog's "The Solution, Part 1";
+ * the readings (the gates as an outer product and a contraction, one filter
+ * per state entry) are this library's.  For head h, channels h*dh + (0..dh-1):
+ *     s[t,i]   = sum_{l<L, l<=t} w[h*dh+i, l] k[t-l, h*dh+i]   shift SSM on keys
+ *     m[t,i,j] = s[t,i] v[t, h*dh+j]                          outer product
+ *     z[.,i,j] = (f[c] * m[.,i,j])[:N] + D[c] m[.,i,j],  c = (h*dh+i)*dh + j
+ *     out[t, h*dh+j] = sum_i q[t, h*dh+i] z[t,i,j]
+ * dh = 1 is h3conv_h3_mix.
+ *
+ *   q, k, v, out [B,N,Dm] io dtype;  w [Dm,L] fp32;  f [Dm*dh, N] fp32;
+ *   D [Dm*dh] fp32
+ *   ws, ws_bytes  workspace: the state entries staged channel-major twice,
+ *                 2 * B*N*Dm*dh elements of bf16 (16-bit activations; this
+ *                 is h3conv_workspace_size(H3CONV_OP_H3_MIX_MH, B, Dm, N, dh,
+ *                 0)) or fp32 (fp32 activations, twice that), 16-byte
+ *                 aligned, overlapping nothing else.
+ * Supported: dh a power of two <= 256 dividing Dm, 1 <= L <= 4,
+ * 1 <= N <= H3CONV_MAX_FUSED_N, B <= 65535, and the h3conv_fft_conv limits
+ * for B x (Dm*dh) rows.
+ */
+h3conv_status h3conv_h3_mix_mh(const void *q, const void *k, const void *v, const float *w,
+                               const float *f, const float *D, void *out, int64_t B, int64_t N,
+                               int64_t Dm, int64_t dh, int64_t L, int io, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/*
  * Workspace bytes an operation needs for the given sizes (0 if none).
  * `op` is an h3conv_op; unused size arguments are ignored.  For
  * H3CONV_OP_H3_MIX, H is the model width Dm and the size is that of the
- * 16-bit activation path (the fp32 path needs none).  Returns (size_t)-1 for
+ * 16-bit activation path (the fp32 path needs none).  For
+ * H3CONV_OP_H3_MIX_MH, H is Dm and S the head dimension dh; the size is that
+ * of the 16-bit activation path (fp32 activations need twice as much).  Returns (size_t)-1 for
  * sizes the operation does not support.
  */
 size_t h3conv_workspace_size(int op, int64_t B, int64_t H, int64_t N, int64_t S, int64_t T);

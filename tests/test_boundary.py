@@ -244,3 +244,21 @@ def test_fft_conv_bwd_validation(lib):
     assert call(N=8193) == pkg.ERR_UNSUPPORTED
     assert call(H=43691, N=8192, u=1 << 40, dy=2 << 40, du=3 << 40, df=4 << 40, dD=5 << 40) == pkg.ERR_UNSUPPORTED
     assert call(H=0) == pkg.OK
+
+
+def test_h3_mix_mh_validation(lib):
+    f = lib.h3conv_h3_mix_mh
+
+    def call(out=0x900000, B=2, N=64, Dm=8, dh=2, L=4, io=2, ws=0xa00000, nws=1 << 20):
+        return f(0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, out, B, N, Dm, dh, L, io, ws, nws,
+                 None)
+
+    assert call(dh=0) == pkg.ERR_INVALID_ARG
+    assert call(dh=3, Dm=9) == pkg.ERR_UNSUPPORTED      # not a power of two
+    assert call(dh=4, Dm=6) == pkg.ERR_UNSUPPORTED      # does not divide Dm
+    assert call(L=5) == pkg.ERR_UNSUPPORTED
+    assert call(ws=None) == pkg.ERR_WORKSPACE
+    assert call(nws=16) == pkg.ERR_WORKSPACE
+    assert call(out=0x100000) == pkg.ERR_INVALID_ARG    # out aliases q
+    assert call(B=0) == pkg.OK
+    assert pkg.workspace_size(pkg.OP_H3_MIX_MH, 2, 8, 64, 2) == 2 * (2 * 64 * 8 * 2 * 2)

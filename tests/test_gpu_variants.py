@@ -75,3 +75,66 @@ def test_bidir_workload_shape_every_row():
     err = rel_l2(got, ref)
     say("  rel_l2=%.3e max_row=%.3e" % (err, rows.max()))
     assert err <= TOL["f16"] and rows.max() <= TOL["f16"]
+
+
+# ------------------------------------------------------------------ multi-head H3
+
+def _mh_inputs(B, N, Dm, dh, L, io, seed):
+    gen = wl.gen(seed)
+    q, k, v = (wl.normal((B, N, Dm), gen, dtype=DT[io]) for _ in range(3))
+    w = wl.normal((Dm, L), gen, std=0.5)
+    f = wl.random_env_filter(Dm * dh, N, gen)
+    D = wl.normal((Dm * dh,), gen)
+    return q, k, v, w, f, D
+
+
+@pytest.mark.parametrize("io", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dh,Dm", [(1, 9), (2, 6), (4, 40), (8, 48)])
+@pytest.mark.parametrize("N", [77, 1000])
+def test_h3_mix_mh_shapes(io, dh, Dm, N):
+    dev = device()
+    B, L = 2, 4
+    label = "h3_mix_mh io=%s B=%d N=%d Dm=%d dh=%d L=%d" % (io, B, N, Dm, dh, L)
+    say(label)
+    q, k, v, w, f, D = _mh_inputs(B, N, Dm, dh, L, io, seed=N + 10 * dh + Dm)
+    out = pkg.h3_mix_mh(*(t.to(dev) for t in (q, k, v, w, f, D)), dh)
+    torch.cuda.synchronize()
+    ref = oracle.h3_mix_mh(q, k, v, w, f, D, dh)
+    err = rel_l2(to_np(out), ref)
+    say("  rel_l2=%.3e" % err)
+    assert np.isfinite(to_np(out)).all() and err <= TOL[io], (label, err)
+
+
+def test_h3_mix_mh_head_dim_one_matches_h3_mix():
+    dev = device()
+    B, N, Dm, L = 2, 600, 136, 4
+    say("h3_mix_mh dh=1 vs h3_mix bf16 B=%d N=%d Dm=%d" % (B, N, Dm))
+    q, k, v, w, f, D = _mh_inputs(B, N, Dm, 1, L, "bf16", seed=5)
+    a = pkg.h3_mix_mh(*(t.to(dev) for t in (q, k, v, w, f, D)), 1)
+    b = pkg.h3_mix(*(t.to(dev) for t in (q, k, v, w, f, D)))
+    torch.cuda.synchronize()
+    ref = oracle.h3_mix(q, k, v, w, f, D)
+    assert rel_l2(to_np(a), ref) <= TOL["bf16"] and rel_l2(to_np(b), ref) <= TOL["bf16"]
+
+
+def test_h3_mix_mh_125m_width():
+    """The H3-125M width (768) in heads of dimension 4, fp16, diagonal-SSM
+    filters (one per state entry): every (batch, channel) sequence checked."""
+    dev = device()
+    B, N, Dm, dh, L = 2, 1024, 768, 4, 4
+    say("h3_mix_mh 125M width f16 B=%d N=%d Dm=%d dh=%d" % (B, N, Dm, dh))
+    gen = wl.gen(2024)
+    q, k, v = (wl.normal((B, N, Dm), gen, dtype=torch.float16) for _ in range(3))
+    w = wl.normal((Dm, L), gen, std=0.5)
+    p = wl.diag_ssm_params(Dm * dh, 64, gen)
+    D = wl.normal((Dm * dh,), gen)
+    pd = {kk: vv.to(dev) for kk, vv in p.items()}
+    f = pkg.ssm_filter(pd["A"], pd["Bm"], pd["C"], pd["dt"], N)
+    out = pkg.h3_mix_mh(q.to(dev), k.to(dev), v.to(dev), w.to(dev), f, D.to(dev), dh)
+    torch.cuda.synchronize()
+    ref = oracle.h3_mix_mh(q, k, v, w, to_np(f), D, dh)
+    got = to_np(out)
+    rows = row_rel_l2(got.transpose(0, 2, 1).reshape(-1, N), ref.transpose(0, 2, 1).reshape(-1, N))
+    err = rel_l2(got, ref)
+    say("  rel_l2=%.3e max_row=%.3e" % (err, rows.max()))
+    assert err <= TOL["f16"] and rows.max() <= TOL["f16"]
