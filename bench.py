@@ -279,11 +279,12 @@ def torch_fftconv(u, f, D):
 
 def sweep(dev, steps: int, warmup: int) -> list:
     """Sequence-length sweep at the H3-125M width (B=8, H=768, fp16, 64
-    modes): fused fft_conv for N <= 8192, state passing (T = 8192) above,
-    each timed beside torch_fftconv on the same inputs."""
+    modes): fused fft_conv for N <= 16384, state passing (T = 8192) at 16384
+    and above, each timed beside torch_fftconv on the same inputs."""
     out = []
-    for i, N in enumerate([256, 512, 1024, 2048, 4096, 8192, 16384, 32768]):
-        kind = "fft_conv" if N <= 8192 else "state_pass"
+    pts = [(N, "fft_conv") for N in (256, 512, 1024, 2048, 4096, 8192, 16384)] + \
+          [(16384, "state_pass"), (32768, "state_pass")]
+    for i, (N, kind) in enumerate(pts):
         w = wl.Workload("sweep_%d" % N, kind, "f16", B=8, H=768, N=N, T=8192 if kind == "state_pass" else 0,
                         seed=100 + i)
         c = Case(w, dev)

@@ -29,6 +29,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_HIP, ERR_WORKSPACE = ra
 F32, F16, BF16 = 0, 1, 2
 OP_FFT_CONV, OP_STATE_PASS, OP_H3_MIX, OP_H3_MIX_MH = 0, 1, 2, 3
 MAX_FUSED_N = 8192
+MAX_FUSED_N_16BIT = 16384
 MAX_STATE = 64
 
 _IO = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}

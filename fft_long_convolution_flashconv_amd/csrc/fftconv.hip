@@ -348,6 +348,7 @@ static uint64_t fc_pad_for(int log2m) {
         case 12: return fc_row_pad<12>();
         case 13: return fc_row_pad<13>();
         case 14: return fc_row_pad<14>();
+        case 15: return fc_row_pad<15>();
         default: return 0;  // fp32 engine: 64-bit offsets
     }
 }
@@ -396,6 +397,7 @@ static hipError_t fc_dispatch(int log2m, const void *u, const float *f, const fl
             case 12: return launch_fc_mfma<12, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
             case 13: return launch_fc_mfma<13, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
             case 14: return launch_fc_mfma<14, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
+            case 15: return launch_fc_mfma<15, IO, SPOL, CORR>(u, f, D, y, B, H, N, s);
             default: break;
         }
     }
@@ -440,9 +442,11 @@ static hipError_t launch_bidir(const void *u, const float *f, const float *g, co
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
-    } else {
+    } else if constexpr (LOG2M <= 14) {
         return launch(k_fft_bidir<LOG2M, IO>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T *)u, f, g, D, (T *)y, B,
                       H, N);
+    } else {
+        return hipErrorInvalidValue;  // fp32 activations: up to 2N = 16384 (refused by the API first)
     }
 }
 
@@ -459,6 +463,7 @@ static hipError_t bidir_dispatch(int log2m, const void *u, const float *f, const
         case 12: return launch_bidir<12, IO>(u, f, g, D, y, B, H, N, s);
         case 13: return launch_bidir<13, IO>(u, f, g, D, y, B, H, N, s);
         case 14: return launch_bidir<14, IO>(u, f, g, D, y, B, H, N, s);
+        case 15: return launch_bidir<15, IO>(u, f, g, D, y, B, H, N, s);
         default: return hipErrorInvalidValue;
     }
 }

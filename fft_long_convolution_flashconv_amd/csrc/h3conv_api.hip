@@ -160,7 +160,7 @@ h3conv_status h3conv_fft_conv(const void *u, const float *f, const float *D, voi
     if (B == 0 || H == 0 || N == 0) return H3CONV_OK;
     if (!u || !f || !D || !y) return H3CONV_ERR_INVALID_ARG;
     if (!aligned16(u) || !aligned16(f) || !aligned16(D) || !aligned16(y)) return H3CONV_ERR_INVALID_ARG;
-    if (N > H3CONV_MAX_FUSED_N) return H3CONV_ERR_UNSUPPORTED;
+    if (N > (io == H3CONV_F32 ? H3CONV_MAX_FUSED_N : H3CONV_MAX_FUSED_N_16BIT)) return H3CONV_ERR_UNSUPPORTED;
     if (!mul_ok(B, H, INT32_MAX) || !mul_ok(B * H, N, INT64_MAX / 4)) return H3CONV_ERR_UNSUPPORTED;
     if (!h3c::fft_conv_rows_fit(H, N, io)) return H3CONV_ERR_UNSUPPORTED;
     const size_t ny = (size_t)(B * H * N) * esize(io);
@@ -180,7 +180,7 @@ h3conv_status h3conv_fft_conv_bidir(const void *u, const float *f, const float *
     if (!u || !f || !g || !D || !y) return H3CONV_ERR_INVALID_ARG;
     if (!aligned16(u) || !aligned16(f) || !aligned16(g) || !aligned16(D) || !aligned16(y))
         return H3CONV_ERR_INVALID_ARG;
-    if (N > H3CONV_MAX_FUSED_N) return H3CONV_ERR_UNSUPPORTED;
+    if (N > (io == H3CONV_F32 ? H3CONV_MAX_FUSED_N : H3CONV_MAX_FUSED_N_16BIT)) return H3CONV_ERR_UNSUPPORTED;
     if (!mul_ok(B, H, INT32_MAX) || !mul_ok(B * H, N, INT64_MAX / 4)) return H3CONV_ERR_UNSUPPORTED;
     if (!h3c::fft_conv_rows_fit(H, N, io)) return H3CONV_ERR_UNSUPPORTED;
     const size_t ny = (size_t)(B * H * N) * esize(io), nf = (size_t)(H * N) * 4;

@@ -62,8 +62,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 namespace tab {
 
 constexpr double kPi = 3.14159265358979323846;
-constexpr int kBaseLog = 14;
-constexpr int kBaseM = 1 << kBaseLog;  // finest root of unity: exp(-2 pi i / 16384)
+constexpr int kBaseLog = 15;
+constexpr int kBaseM = 1 << kBaseLog;  // finest root of unity: exp(-2 pi i / 32768)
 
 // cos x and sin x for 0 <= x <= pi/4 (Taylor terms up to x^29)
 constexpr void cos_sin_small(double x, double &c, double &s) {
@@ -301,7 +301,7 @@ __device__ __forceinline__ float habs_max(uint32_t v) {
 // themselves: a lane's column within a 32-column tile is used as is.  The map is linear over XOR, so
 // phys(a ^ b) = phys(a) ^ phys(b); addresses are split that way into
 // per-lane and compile-time parts.
-constexpr int kSwz[15][8] = {
+constexpr int kSwz[16][9] = {
     {}, {}, {}, {}, {}, {}, {}, {}, {},
     {48, 18, 16},                        // 9
     {4, 48, 16, 32},                     // 10
@@ -309,8 +309,9 @@ constexpr int kSwz[15][8] = {
     {24, 4, 16, 48, 16, 32},             // 12
     {16, 34, 16, 32, 48, 32, 16},        // 13
     {4, 48, 16, 32, 16, 48, 16, 32},     // 14
+    {4, 48, 16, 32, 16, 48, 16, 32, 48}, // 15 (the 2^14 pattern, one bit more)
 };
-constexpr int kSwz5[15] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 8, 0, 0, 16, 8, 0};
+constexpr int kSwz5[16] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 8, 0, 0, 16, 8, 0, 0};
 template <int LOG2M>
 __host__ __device__ constexpr int phys(int i) {
     int r = (i >> 5) & 1 ? i ^ kSwz5[LOG2M] : i;
@@ -329,6 +330,9 @@ template <> struct Cfg<11> { static constexpr int SIG = 4, NW = 8, OCC = 3, BD =
 template <> struct Cfg<12> { static constexpr int SIG = 2, NW = 8, OCC = 2, BD = 16; };
 template <> struct Cfg<13> { static constexpr int SIG = 1, NW = 8, OCC = 2, BD = 16; };
 template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8, OCC = 2, BD = 16; };
+// 2N = 32768 (sequences up to 16K in one fused block): one signal of 128 KiB
+// in LDS per workgroup, one workgroup per compute unit
+template <> struct Cfg<15> { static constexpr int SIG = 1, NW = 8, OCC = 1, BD = 16; };
 
 template <int LOG2M>
 struct Shape {

@@ -54,8 +54,13 @@ typedef enum {
     H3CONV_OP_H3_MIX_MH = 3
 } h3conv_op;
 
-/* Largest sequence length handled by one fused FFT block (2N <= 16384 points). */
+/* Largest sequence length handled by one fused FFT block (2N <= 16384 points),
+ * for every activation type and operation. */
 #define H3CONV_MAX_FUSED_N 8192
+/* Largest for h3conv_fft_conv and h3conv_fft_conv_bidir with 16-bit
+ * activations (2N = 32768 points: one 128 KiB signal in a compute unit's
+ * LDS). */
+#define H3CONV_MAX_FUSED_N_16BIT 16384
 /* Largest number of diagonal-SSM modes per channel. */
 #define H3CONV_MAX_STATE 64
 
@@ -73,12 +78,13 @@ typedef enum {
  *   f  [H,N]    fp32         filter
  *   D  [H]      fp32         residual weight
  *   y  [B,H,N]  io dtype     output (must not overlap u, f or D)
- * Supported: 1 <= N <= H3CONV_MAX_FUSED_N (any N; longer inputs use
+ * Supported: 1 <= N <= H3CONV_MAX_FUSED_N for fp32 activations and
+ * N <= H3CONV_MAX_FUSED_N_16BIT for fp16 / bf16 (any N; longer inputs use
  * h3conv_state_pass), B*H < 2^31, and for 16-bit activations with N > 128
  * (the matrix-core engine, whose row offsets within one launch are 32-bit)
  * (2*SIG + 4) * 2*H*N < 2^32 bytes, SIG being the complex signals per round
  * of that transform size: 8 for 2N = 512, 4 for 1024 and 2048, 2 for 4096,
- * 1 for 8192 and 16384 (so at N = 8192, H <= 43690).  Larger batches B are
+ * 1 for 8192, 16384 and 32768 (so at N = 8192, H <= 43690).  Larger batches B are
  * split by the library.  Otherwise H3CONV_ERR_UNSUPPORTED, before any HIP call.
  * Rows are transformed two at a time as one complex signal; each row has a
  * scale of its own, so its error is set by its own magnitude, and a row of
@@ -99,7 +105,8 @@ h3conv_status h3conv_fft_conv(const void *u, const float *f, const float *D, voi
  * computed as one fused transform per row pair with the two-sided filter.
  *
  *   u, y [B,H,N] io dtype;  f, g [H,N] fp32;  D [H] fp32
- * Supported sizes and errors: as h3conv_fft_conv.
+ * Supported sizes and errors: as h3conv_fft_conv (N up to
+ * H3CONV_MAX_FUSED_N_16BIT for 16-bit activations).
  */
 h3conv_status h3conv_fft_conv_bidir(const void *u, const float *f, const float *g, const float *D,
                                     void *y, int64_t B, int64_t H, int64_t N, int io, void *stream);
@@ -120,7 +127,8 @@ h3conv_status h3conv_fft_conv_bidir(const void *u, const float *f, const float *
  *   df [H,N], dD [H] fp32       outputs, summed over the batch (written, not
  *                               accumulated into)
  * Outputs must not overlap any input or each other.  B == 0 writes zeros
- * to df and dD.  Supported sizes: those of h3conv_fft_conv.
+ * to df and dD.  Supported sizes: those of h3conv_fft_conv with
+ * N <= H3CONV_MAX_FUSED_N.
  */
 h3conv_status h3conv_fft_conv_bwd(const void *u, const float *f, const float *D, const void *dy,
                                   void *du, float *df, float *dD, int64_t B, int64_t H, int64_t N,

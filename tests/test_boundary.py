@@ -69,7 +69,8 @@ def test_fft_conv_validation(lib):
     assert _fc(lib, u=None) == pkg.ERR_INVALID_ARG
     assert _fc(lib, y=None) == pkg.ERR_INVALID_ARG
     assert _fc(lib, u=MIS) == pkg.ERR_INVALID_ARG
-    assert _fc(lib, N=8193) == pkg.ERR_UNSUPPORTED
+    assert _fc(lib, N=8193, io=0) == pkg.ERR_UNSUPPORTED      # fp32: 2N <= 16384
+    assert _fc(lib, N=16385, io=1) == pkg.ERR_UNSUPPORTED     # 16-bit: 2N <= 32768
     # y overlapping u / f / D
     assert _fc(lib, y=A16 + 64) == pkg.ERR_INVALID_ARG
     assert _fc(lib, y=A16b) == pkg.ERR_INVALID_ARG

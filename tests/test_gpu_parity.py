@@ -337,3 +337,27 @@ def test_h3_mix_vector_ragged_tiles(io):
     err = rel_l2(to_np(out), ref)
     say("  rel_l2=%.3e" % err)
     assert err <= TOL[io]
+
+
+# ------------------------------------------------------------------ 16K fused block
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("N", [8193, 12000, 16384])
+def test_fft_conv_16k_fused_block(io, N):
+    """Sequences up to 16K in one fused block (2N = 32768 points) with 16-bit
+    activations: odd batch (a partial round), ragged N; also the bidirectional
+    copies at that size."""
+    dev = device()
+    B, H = 3, 2
+    label = "fft_conv 16K block io=%s B=%d H=%d N=%d" % (io, B, H, N)
+    say(label)
+    u, f, D = _conv_inputs(B, H, N, io, seed=N + 1)
+    y = pkg.fft_conv(u.to(dev), f.to(dev), D.to(dev))
+    torch.cuda.synchronize()
+    _check_conv(u, f, D, y, io, label)
+    g = wl.random_env_filter(H, N, wl.gen(N + 2))
+    yb = pkg.fft_conv_bidir(u.to(dev), f.to(dev), g.to(dev), D.to(dev))
+    torch.cuda.synchronize()
+    err = rel_l2(to_np(yb), oracle.bidir_conv(u, f, g, D))
+    say("  bidir rel_l2=%.3e" % err)
+    assert err <= TOL[io]

@@ -142,3 +142,25 @@ def test_h3_mix_2k_workload_every_channel():
     r_r = np.ascontiguousarray(ref.transpose(0, 2, 1))
     _assert_rows(g_r, r_r, None, w.dtype, w.name)
     clk.lap("done")
+
+
+def test_fft_conv_16k_block_every_row():
+    """The 16K fused block at the conv_8k width (B=4, H=768, N=16384, fp16,
+    diagonal-SSM filters): every row against the oracle, run twice bitwise."""
+    dev = device()
+    B, H, N = 4, 768, 16384
+    say("fft_conv 16K block B=%d H=%d N=%d f16: every row" % (B, H, N))
+    clk = _Clock("conv_16k")
+    w = wl.Workload("conv_16k", "fft_conv", "f16", B=B, H=H, N=N, seed=12)
+    inp = wl.make_inputs(w)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    f = pkg.ssm_filter(d["A"], d["Bm"], d["C"], d["dt"], N)
+    y1 = pkg.fft_conv(d["u"], f, d["D"])
+    y2 = pkg.fft_conv(d["u"], f, d["D"])
+    torch.cuda.synchronize()
+    clk.lap("gpu")
+    assert torch.equal(y1, y2), "second run differs"
+    ref = oracle.causal_conv(inp["u"], to_np(f), inp["D"])
+    clk.lap("oracle")
+    du = to_np(inp["D"])[None, :, None] * to_np(inp["u"])
+    _assert_rows(to_np(y1), ref, du, "f16", "conv_16k")
