@@ -23,7 +23,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libh3conv.so")
+# H3CONV_LIB selects another build of the library (e.g. libh3conv_san.so,
+# host code under AddressSanitizer, for host-only checks)
+LIB_PATH = os.environ.get("H3CONV_LIB") or os.path.join(HERE, "libh3conv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_HIP, ERR_WORKSPACE = range(6)
 F32, F16, BF16 = 0, 1, 2

@@ -24,7 +24,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "h3conv_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# H3CONV_ORACLE_SANITIZE=1 builds and loads a copy instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer (the process must preload
+# gcc's libasan, e.g. LD_PRELOAD=$(gcc -print-file-name=libasan.so)).
+_SANITIZE = os.environ.get("H3CONV_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 _lib = None
 
 MAX_STATE = 256  # per-row state buffer size of oracle_ssm_recurrence
@@ -36,6 +40,9 @@ def build(force: bool = False) -> str:
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
                "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        if _SANITIZE:
+            cmd[1:1] = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=undefined"]
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB)
     return _LIB
