@@ -287,7 +287,7 @@ h3conv_status h3conv_ssm_step(const void *u, const float *A, const float *Bm, co
     const void *ptrs[] = {u, A, Bm, C, dt, D, x, y};
     for (const void *p : ptrs)
         if (!aligned16(p)) return H3CONV_ERR_INVALID_ARG;
-    if (H > INT32_MAX || !mul_ok(B, H, ((int64_t)UINT32_MAX) * 4) || !mul_ok(B * H, K, INT64_MAX / 4) ||
+    if (H > INT32_MAX || !h3c::ssm_step_fits(B, H) || !mul_ok(B * H, K, INT64_MAX / 4) ||
         !mul_ok(B * H, S, INT64_MAX / 16))
         return H3CONV_ERR_UNSUPPORTED;
     const size_t ny = (size_t)(B * H * K) * esize(io), np = (size_t)(H * S) * 8,
@@ -309,7 +309,7 @@ h3conv_status h3conv_h3_mix_mh(const void *q, const void *k, const void *v, cons
                                void *stream) {
     if (B < 0 || N < 0 || Dm < 0 || dh < 1 || L < 1 || !valid_io(io)) return H3CONV_ERR_INVALID_ARG;
     if (B == 0 || N == 0 || Dm == 0) return H3CONV_OK;
-    if (L > 4 || N > H3CONV_MAX_FUSED_N || dh > 256 || (dh & (dh - 1)) != 0 || Dm % dh != 0)
+    if (L > 4 || N > H3CONV_MAX_FUSED_N || dh > 32 || (dh & (dh - 1)) != 0 || Dm % dh != 0)
         return H3CONV_ERR_UNSUPPORTED;
     if (!q || !k || !v || !w || !f || !D || !out || !ws) return !ws ? H3CONV_ERR_WORKSPACE : H3CONV_ERR_INVALID_ARG;
     const void *ptrs[] = {q, k, v, w, f, D, out, ws};

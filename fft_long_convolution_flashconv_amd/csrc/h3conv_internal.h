@@ -78,6 +78,8 @@ hipError_t launch_state_pass(const void *u, const float *A, const float *Bm, con
                              hipStream_t s);
 
 // K steps of the recurrence per row from the state x (updated in place).
+// Whether the generation step's grid for B x H rows fits one dispatch.
+bool ssm_step_fits(int64_t B, int64_t H);
 hipError_t launch_ssm_step(const void *u, const float *A, const float *Bm, const float *C, const float *dt,
                            const float *D, float *x, void *y, int64_t B, int64_t H, int64_t K, int S, int io,
                            hipStream_t s);

@@ -221,8 +221,9 @@ h3conv_status h3conv_state_pass_noalloc(const void *u, const float *A, const flo
  *   x      [B,H,S]  complex fp32  state: read, then overwritten with the
  *                                 state after the K steps
  *   y      [B,H,K]  io dtype      outputs (must not overlap any input or x)
- * Supported: 1 <= S <= H3CONV_MAX_STATE, B*H <= 2^34.  The recurrence runs
- * in fp32.
+ * Supported: 1 <= S <= H3CONV_MAX_STATE, H * ceil(B/4) < 2^26 (one wave
+ * per channel and four batch rows; about 2^28 rows), else
+ * H3CONV_ERR_UNSUPPORTED.  The recurrence runs in fp32.
  */
 h3conv_status h3conv_ssm_step(const void *u, const float *A, const float *Bm, const float *C,
                               const float *dt, const float *D, float *x, void *y, int64_t B, int64_t H,
@@ -272,7 +273,7 @@ h3conv_status h3conv_h3_mix(const void *q, const void *k, const void *v, const f
  *                 is h3conv_workspace_size(H3CONV_OP_H3_MIX_MH, B, Dm, N, dh,
  *                 0)) or fp32 (fp32 activations, twice that), 16-byte
  *                 aligned, overlapping nothing else.
- * Supported: dh a power of two <= 256 dividing Dm, 1 <= L <= 4,
+ * Supported: dh a power of two <= 32 dividing Dm, 1 <= L <= 4,
  * 1 <= N <= H3CONV_MAX_FUSED_N, B <= 65535, and the h3conv_fft_conv limits
  * for B x (Dm*dh) rows.
  */

@@ -227,6 +227,8 @@ def test_ssm_step_validation(lib):
     assert call(x=0x700008) == pkg.ERR_INVALID_ARG          # misaligned
     assert call(y=0x100000) == pkg.ERR_INVALID_ARG          # y aliases u
     assert call(x=0x200000) == pkg.ERR_INVALID_ARG          # x aliases A
+    assert call(B=4, H=1 << 26) == pkg.ERR_UNSUPPORTED      # grid past 2^32 work-items
+    assert call(B=(1 << 28) + 4, H=1) == pkg.ERR_UNSUPPORTED
     assert call(K=0, u=None, x=None, y=None) == pkg.OK      # empty: no-op
 
 
@@ -256,6 +258,7 @@ def test_h3_mix_mh_validation(lib):
 
     assert call(dh=0) == pkg.ERR_INVALID_ARG
     assert call(dh=3, Dm=9) == pkg.ERR_UNSUPPORTED      # not a power of two
+    assert call(dh=64, Dm=64) == pkg.ERR_UNSUPPORTED    # above 32
     assert call(dh=4, Dm=6) == pkg.ERR_UNSUPPORTED      # does not divide Dm
     assert call(L=5) == pkg.ERR_UNSUPPORTED
     assert call(ws=None) == pkg.ERR_WORKSPACE
