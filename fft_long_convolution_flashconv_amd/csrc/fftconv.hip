@@ -205,9 +205,68 @@ static hipError_t launch_df(const void *u, const void *dy, float *df, float *dD,
                   dD, B, H, N);
 }
 
+// The same gradient on the matrix-core engine for 16-bit activations (2N >=
+// 512): see Engine::run_df.  One workgroup per channel; rounds alternate
+// between SIG row pairs of u and the same pairs of dy.  Rows are addressed
+// with 64-bit offsets, so no batch is split (the sum runs over all of it).
+// Waves per SIMD the gradient kernel's registers are set for: it holds a
+// round of last-pass values and the fp32 sum besides the transform's own,
+// so it runs fewer workgroups per compute unit than the convolution.
+template <int LOG2M> struct DfOcc { static constexpr int WPE = 4; };
+
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(DfOcc<LOG2M>::WPE))) void k_fft_df_mfma(
+    const typename io_elem<IO>::T *__restrict__ u, const typename io_elem<IO>::T *__restrict__ dy,
+    float *__restrict__ df, float *__restrict__ dD, int B, int H, int N) {
+    using SH = mf::Shape<LOG2M>;
+    constexpr int KIND = IO == IO_F16 ? mf::IN_F16 : mf::IN_BF16;
+    constexpr int SIG = SH::SIG;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[SH::LDS_DWORDS];
+    mf::Engine<LOG2M, KIND> E(smem);
+    E.init();
+    const int h = blockIdx.x;
+    const size_t rowb = (size_t)H * (size_t)N * 2;
+    const char *uh = (const char *)(u + (size_t)h * N);
+    const char *dh = (const char *)(dy + (size_t)h * N);
+    const int np = (B + 1) / 2;
+    const int nround = 2 * ((np + SIG - 1) / SIG);
+    // virtual signal v = round * SIG + s: pair (round / 2) * SIG + s of u
+    // (even rounds) or dy (odd rounds); rows past B get empty resources
+    auto rows = [&](int v) -> mf::RowBufs {
+        const int r = v / SIG, p = (r >> 1) * SIG + v % SIG;
+        const char *p0 = ((r & 1) ? dh : uh) + (size_t)(2 * p) * rowb;
+        const int nb0 = (2 * p < B) ? 2 * N : 0;
+        const int nb1 = (2 * p + 1 < B) ? 2 * N : 0;
+        return {mf::row_rsrc(p0, nb0), mf::row_rsrc(p0 + rowb, nb1), mf::row_rsrc(p0, 0), mf::row_rsrc(p0, 0)};
+    };
+    const __amdgpu_buffer_rsrc_t drs = mf::row_rsrc(df + (size_t)h * N, 4 * N);
+    float *dDh = dD + h;
+    E.run_df(rows, nround, mf::half_bits(N), [&](int pos, float v) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), drs, 4 * pos, 0, 0);
+        if (pos == 0) *dDh = v;
+    });
+}
+
+template <int LOG2M, int IO>
+static hipError_t launch_df_mfma(const void *u, const void *dy, float *df, float *dD, int B, int H, int N,
+                                 hipStream_t s) {
+    using T = typename io_elem<IO>::T;
+    return launch(k_fft_df_mfma<LOG2M, IO>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s, (const T *)u, (const T *)dy,
+                  df, dD, B, H, N);
+}
+
 template <int IO>
 static hipError_t df_dispatch(int log2m, const void *u, const void *dy, float *df, float *dD, int B, int H, int N,
                               hipStream_t s) {
+    if constexpr (IO != IO_F32) {
+        switch (log2m) {
+            case 10: return launch_df_mfma<10, IO>(u, dy, df, dD, B, H, N, s);
+            case 11: return launch_df_mfma<11, IO>(u, dy, df, dD, B, H, N, s);
+            case 12: return launch_df_mfma<12, IO>(u, dy, df, dD, B, H, N, s);
+            case 13: return launch_df_mfma<13, IO>(u, dy, df, dD, B, H, N, s);
+            default: break;  // 2N = 16384: the fp32 engine (the sum would not fit the registers)
+        }
+    }
     switch (log2m) {
         case 6: return launch_df<6, IO>(u, dy, df, dD, B, H, N, s);
         case 7: return launch_df<7, IO>(u, dy, df, dD, B, H, N, s);

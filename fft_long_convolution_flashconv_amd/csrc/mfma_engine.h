@@ -744,6 +744,26 @@ struct Engine {
     // again two reductions later.
     template <bool FILT>
     __device__ float block_scales(float fs, int hb, int (&kp)[T0W][2], int (&kq)[TIW][2]) {
+        const uint32_t kpk = round_exps<FILT>(fs, hb);
+        auto get = [&](int (&k)[2], int sg) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpk, sg);
+            k[0] = lo16(v);
+            k[1] = hi16(v);
+        };
+#pragma unroll
+        for (int i = 0; i < T0W; ++i) get(kp[i], SIG == 1 ? 0 : tile_sig(i));
+#pragma unroll
+        for (int i = 0; i < TIW; ++i) get(kq[i], SIG == 1 ? 0 : (16 * (w + i * NW)) / S0);
+        return fs;
+    }
+    __device__ __forceinline__ static int lo16(uint32_t v) { return (int)(int16_t)(uint16_t)(v & 0xffffu); }
+    __device__ __forceinline__ static int hi16(uint32_t v) { return (int)v >> 16; }
+
+    // The reduction behind block_scales: returns, in lane l < SIG, the two
+    // scale exponents of signal l (real half in the low 16 bits, imaginary
+    // half in the high 16 bits); with FILT, fs becomes the workgroup's sum.
+    template <bool FILT>
+    __device__ uint32_t round_exps(float &fs, int hb) {
         uint32_t tm[T0W];
 #pragma unroll
         for (int i = 0; i < T0W; ++i) {
@@ -790,21 +810,13 @@ struct Engine {
             }
         }
         const uint32_t kpk = ((uint32_t)scale_exp(m & 0xffffu, hb) & 0xffffu) | ((uint32_t)scale_exp(m >> 16, hb) << 16);
-        auto get = [&](int (&k)[2], int sg) {
-            const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpk, sg);
-            k[0] = (int)(int16_t)(uint16_t)(v & 0xffffu);
-            k[1] = (int)v >> 16;
-        };
-#pragma unroll
-        for (int i = 0; i < T0W; ++i) get(kp[i], SIG == 1 ? 0 : tile_sig(i));
-#pragma unroll
-        for (int i = 0; i < TIW; ++i) get(kq[i], SIG == 1 ? 0 : (16 * (w + i * NW)) / S0);
-        float sa = 0.f;
         if constexpr (FILT) {
+            float sa = 0.f;
 #pragma unroll
             for (int k = 0; k < NW; ++k) sa += ((const float *)r)[NSLOT + k];
+            fs = sa;
         }
-        return sa;
+        return kpk;
     }
 
     // Scale exponents.  For a 16-bit magnitude pattern m > 0 of the input
@@ -1070,11 +1082,11 @@ struct Engine {
             fwd_middle<P + 1, NS>();
         }
     }
-    template <int P>
+    template <int P, int NS = SIG>
     __device__ void inv_middle(uint32_t pre) {
         if constexpr (P >= 1) {
-            mid_pass<P, true, SIG>(pre);
-            inv_middle<P - 1>(pre);
+            mid_pass<P, true, NS>(pre);
+            inv_middle<P - 1, NS>(pre);
         }
     }
 
@@ -1438,6 +1450,188 @@ struct Engine {
             conv_round<false, CORR>([&](int s, int n, int m, uint32_t hv) { store(r0, s, n, m, hv); }, hb, fin,
                                     [&]() { prefetch(r0); });
         }
+    }
+
+    // ---------------------------------------------------------- filter gradient
+    // Inverse of pass 0 for signal 0 alone, real part only, in fp32:
+    // st(p, v) receives output point p = n + m S0 (m < 8) times ob.
+    template <class ST>
+    __device__ void pass0_inv_real(const ST &st, float ob) {
+        constexpr int TI0 = S0 / 16;  // signal 0's inverse pass-0 tiles
+        static_assert(TI0 % NW == 0, "signal 0's inverse tiles split evenly over the waves");
+        constexpr int TW0 = TI0 / NW;
+        const int lb = opaque((j ^ phys<LOG2M>(2 * g * S0)) << 2);
+#pragma unroll
+        for (int i = 0; i < TW0; ++i) {
+            const int n0 = 16 * (w + i * NW);
+            const int pn = lb ^ (phys<LOG2M>(n0) << 2);
+            uint32_t x[4], tu[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[t] = lds(pn ^ (phys<LOG2M>(tab::kChain[t] * S0) << 2));
+            get_tu0(i % NDI, tu);
+            cmulh_n(x, tu);
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
+            const f4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(C0, as_half8(x[0], x[1], x[2], x[3]), z, 0, 0, 0);
+            st(n0 + j + 2 * g * S0, r[0] * ob);
+            st(n0 + j + (2 * g + 1) * S0, r[2] * ob);
+        }
+    }
+
+    // Gradient of the filter of a causal convolution: Re IDFT(sum_p conj(U_p)
+    // DY_p)[:M/2] with U_p = DFT(u_2p + i u_2p+1) and DY_p the same of dy;
+    // the real part is the sum over the rows of the correlations of u with
+    // dy (the cross terms of a pair are imaginary).  Rounds come in twos over
+    // the same SIG row pairs: the u round keeps its last-pass values in
+    // registers, the dy round multiplies its own into them and adds the
+    // products, in fp32, to this lane's points of the sum.  Row x of a pair
+    // enters with scales 2^ku_x (u, its own) and 2^(K - ku_x) (dy), with K =
+    // min over the rows of ku_x + kd_x (kd_x = dy row x's own exponent), so
+    // both rows' products carry the same factor 2^K, removed exactly; a row
+    // scaled below its own exponent holds a product at most 2^(K - ku_x -
+    // kd_x) of the largest one's.  After the last round the sum is scaled to
+    // the fp16 range, inverted once (signal 0 alone) and stored through
+    // st(p, v).  rows(v): the buffers of virtual signal v = round * SIG + s
+    // (u rows in even rounds, dy rows in odd ones).
+    template <class RB, class ST>
+    __device__ void run_df(const RB &rows, int nround, int hb, const ST &st) {
+        static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
+        constexpr int kDrop = -0x4000;  // input exponent of a row left out (ldexp to zero)
+        float acc[FN][2];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) acc[i][0] = acc[i][1] = 0.f;
+        uint32_t yu[NU][NV];
+        __builtin_amdgcn_s_setprio(kPrioLoad);
+        fetch_raw(rows, 0, pin);
+        constexpr int UB = NU * NVD <= SH::BD ? NU : SH::BD / NVD;
+        static_assert(NU % UB == 0, "last-pass units split into equal batches");
+        for (int r = 0; r < nround; r += 2) {
+            // ---- u round: per-row scales, as in a convolution round
+            uint32_t kpu;
+            {
+                __builtin_amdgcn_s_setprio(kPrioLoad);
+                if (!PREFETCH && r > 0) fetch_raw(rows, r * SIG, pin);
+                float fs = 0.f;
+                kpu = round_exps<false>(fs, hb);
+                f2 sut[T0W] = {};
+                uint32_t suh[T0W] = {};
+#pragma unroll
+                for (int i = 0; i < T0W; ++i) {
+                    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpu, SIG == 1 ? 0 : tile_sig(i));
+                    if constexpr (KIND == IN_F16) suh[i] = exp2h(lo16(v)) | (exp2h(hi16(v)) << 16);
+                    else sut[i] = f2{exp2i(lo16(v)), exp2i(hi16(v))};
+                }
+                auto op = [&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], sut[i], suh[i]); };
+                pass0<SIG>(op, op);
+                if (PREFETCH) fetch_raw(rows, (r + 1) * SIG, pin);
+                __builtin_amdgcn_s_setprio(kPrioWork);
+                fwd_middle<1, SIG>();
+                const int lb = opaque(lbase());
+#pragma unroll
+                for (int u0 = 0; u0 < NU; u0 += UB) {
+                    uint32_t vb[UB][NVD];
+#pragma unroll
+                    for (int k = 0; k < UB; ++k) last_load((lb ^ lpos(u0 + k)) + lsig(u0 + k) * SB, vb[k]);
+#pragma unroll
+                    for (int k = 0; k < UB; ++k) last_fwd(vb[k], yu[u0 + k]);
+                }
+            }
+            // ---- dy round: scales tied to the u round's, products summed
+            {
+                __builtin_amdgcn_s_setprio(kPrioLoad);
+                if (!PREFETCH) fetch_raw(rows, (r + 1) * SIG, pin);
+                float fs = 0.f;
+                const uint32_t kpd = round_exps<false>(fs, hb);
+                // lane s < SIG: signal s's dy exponents and product exponent K
+                const int ka = lo16(kpu), kb = hi16(kpu), da = lo16(kpd), db = hi16(kpd);
+                const bool va = ka != kZero && da != kZero, vb = kb != kZero && db != kZero;
+                int kk = va ? ka + da : (vb ? kb + db : 0);
+                if (va && vb) kk = min(kk, kb + db);
+                const int ea = va ? kk - ka : kDrop, eb = vb ? kk - kb : kDrop;
+                const uint32_t kpe = ((uint32_t)ea & 0xffffu) | ((uint32_t)eb << 16);
+                int eda[T0W], edb[T0W];
+#pragma unroll
+                for (int i = 0; i < T0W; ++i) {
+                    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpe, SIG == 1 ? 0 : tile_sig(i));
+                    eda[i] = lo16(v);
+                    edb[i] = hi16(v);
+                }
+                auto op = [&](int i, int e) -> uint32_t {
+                    const uint32_t x = pin[i][e];
+                    float a, b;
+                    if constexpr (KIND == IN_F16) {
+                        const h2 hv = __builtin_bit_cast(h2, x);
+                        a = (float)hv.x;
+                        b = (float)hv.y;
+                    } else {
+                        a = __uint_as_float(x << 16);
+                        b = __uint_as_float(x & 0xffff0000u);
+                    }
+                    return pk(ldexpf(a, eda[i]), ldexpf(b, edb[i]));
+                };
+                pass0<SIG>(op, op);
+                if (PREFETCH && r + 2 < nround) fetch_raw(rows, (r + 2) * SIG, pin);
+                __builtin_amdgcn_s_setprio(kPrioWork);
+                fwd_middle<1, SIG>();
+                int nk[SIG];
+#pragma unroll
+                for (int sg = 0; sg < SIG; ++sg) nk[sg] = -__builtin_amdgcn_readlane(kk, sg);
+                const int lb = opaque(lbase());
+#pragma unroll
+                for (int u0 = 0; u0 < NU; u0 += UB) {
+                    uint32_t vb2[UB][NVD];
+#pragma unroll
+                    for (int k = 0; k < UB; ++k) last_load((lb ^ lpos(u0 + k)) + lsig(u0 + k) * SB, vb2[k]);
+#pragma unroll
+                    for (int k = 0; k < UB; ++k) {
+                        const int u = u0 + k;
+                        uint32_t y[NV];
+                        last_fwd(vb2[k], y);
+#pragma unroll
+                        for (int q = 0; q < NV; ++q) {
+                            // acc += conj(Yu) Ydy 2^-K
+                            const h2 a = __builtin_bit_cast(h2, yu[u][q]), d = __builtin_bit_cast(h2, y[q]);
+                            const float ar = (float)a.x, ai = (float)a.y, dr = (float)d.x, di = (float)d.y;
+                            const float re = fmaf(ar, dr, ai * di), im = fmaf(ar, di, -ai * dr);
+                            const int ix = fslot(u % NLS) + q;
+                            acc[ix][0] += ldexpf(re, nk[lsig(u)]);
+                            acc[ix][1] += ldexpf(im, nk[lsig(u)]);
+                        }
+                    }
+                }
+            }
+        }
+        // Scale the sum so that |values| < 2^(14 - LR): its DFT-R (the first
+        // inverse step) then stays below 2^14.  Inverse on conjugated values,
+        // as in a convolution round, for signal 0 only.
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) am = fmaxf(am, fmaxf(fabsf(acc[i][0]), fabsf(acc[i][1])));
+        const float vm0 = block_reduce<false>(am);
+        int ea0 = 0;
+        if (vm0 > 0.f) (void)frexpf(vm0, &ea0);
+        const int ec = 14 - SH::LR - ea0;
+        float vmax = 0.f;
+        {
+            const int lb = opaque(lbase());
+            constexpr int NU0 = R >= 8 ? NLS : NSL;  // signal 0's units
+#pragma unroll
+            for (int u = 0; u < NU0; ++u) {
+                uint32_t y[NV];
+#pragma unroll
+                for (int q = 0; q < NV; ++q) {
+                    const int ix = fslot(u % NLS) + q;
+                    y[q] = pk(ldexpf(acc[ix][0], ec), -ldexpf(acc[ix][1], ec));
+                }
+                vmax = fmaxf(vmax, last_inv(lb ^ lpos(u), y));
+            }
+        }
+        const float vm = block_reduce<false>(vmax);
+        int ev = 0;
+        if (vm > 0.f) (void)frexpf(vm, &ev);
+        const float sy = fminf(fmaxf(ldexpf(1.f, 14 - ev - (LOG2M - SH::LR)), 1.0f / 16384.0f), 32768.0f);
+        inv_middle<K, 1>(pk(sy, sy));
+        // the output chain multiplied the sum by M sy 2^ec
+        pass0_inv_real(st, ldexpf(1.0f / ((float)M * sy), -ec));
     }
 };
 

@@ -85,3 +85,26 @@ def test_fft_conv_bwd_empty_batch():
     torch.cuda.synchronize()
     assert du.shape == (0, H, N)
     assert torch.count_nonzero(df) == 0 and torch.count_nonzero(dD) == 0
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("N", [500, 1000, 2000, 3000])
+def test_fft_conv_bwd_mixed_row_magnitudes(io, N):
+    """Rows of u and dy of very different magnitudes, crossed so that every
+    row's correlation is of the same size (each pair's two rows must keep
+    their own weight in the summed filter gradient), and a pair whose
+    products are far below the others'."""
+    dev = device()
+    B, H = 6, 3
+    label = "fft_conv_bwd mixed magnitudes io=%s B=%d H=%d N=%d" % (io, B, H, N)
+    say(label)
+    g = wl.gen(7000 + N)
+    su = torch.tensor([1e2, 1e-2, 1.0, 1e-3, 1e-2, 1e-2], dtype=torch.float64).view(B, 1, 1)
+    sd = torch.tensor([1e-2, 1e2, 1e-3, 1.0, 1e-2, 1e-2], dtype=torch.float64).view(B, 1, 1)
+    u = (wl.normal((B, H, N), g) * su).to(DT[io])
+    dy = (wl.normal((B, H, N), g) * sd).to(DT[io])
+    f = wl.random_env_filter(H, N, g)
+    D = wl.normal((H,), g)
+    got = pkg.fft_conv_bwd(u.to(dev), f.to(dev), D.to(dev), dy.to(dev))
+    torch.cuda.synchronize()
+    _check(u, f, D, dy, got, io, label)
