@@ -247,6 +247,57 @@ __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_p
     });
 }
 
+// The whole backward pass in one kernel (Engine::run_bwd): du, df and dD
+// from one read of u and dy.  One workgroup per channel; rounds alternate
+// between SIG row pairs of dy (with du as output) and the same pairs of u.
+template <int LOG2M, int IO>
+__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(DfOcc<LOG2M>::WPE))) void k_fft_bwd_mfma(
+    const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f, const float *__restrict__ D,
+    const typename io_elem<IO>::T *__restrict__ dy, typename io_elem<IO>::T *__restrict__ du,
+    float *__restrict__ df, float *__restrict__ dD, int B, int H, int N) {
+    using SH = mf::Shape<LOG2M>;
+    constexpr int KIND = IO == IO_F16 ? mf::IN_F16 : mf::IN_BF16;
+    constexpr int SIG = SH::SIG;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[SH::LDS_DWORDS];
+    mf::Engine<LOG2M, KIND> E(smem);
+    E.init();
+    const int h = blockIdx.x;
+    const size_t rowb = (size_t)H * (size_t)N * 2;
+    const char *uh = (const char *)(u + (size_t)h * N);
+    const char *dyh = (const char *)(dy + (size_t)h * N);
+    char *duh = (char *)(du + (size_t)h * N);
+    const int np = (B + 1) / 2;
+    const int nround = 2 * ((np + SIG - 1) / SIG);
+    // virtual signal v = round * SIG + s: pair (round / 2) * SIG + s of dy
+    // with du as output (even rounds) or of u (odd rounds); rows past B get
+    // empty resources
+    auto rows = [&](int v) -> mf::RowBufs {
+        const int r = v / SIG, p = (r >> 1) * SIG + v % SIG;
+        const size_t o = (size_t)(2 * p) * rowb;
+        const int nb0 = (2 * p < B) ? 2 * N : 0;
+        const int nb1 = (2 * p + 1 < B) ? 2 * N : 0;
+        if (r & 1)
+            return {mf::row_rsrc(uh + o, nb0), mf::row_rsrc(uh + o + rowb, nb1), mf::row_rsrc(uh, 0), mf::row_rsrc(uh, 0)};
+        return {mf::row_rsrc(dyh + o, nb0), mf::row_rsrc(dyh + o + rowb, nb1), mf::row_rsrc(duh + o, nb0),
+                mf::row_rsrc(duh + o + rowb, nb1)};
+    };
+    const __amdgpu_buffer_rsrc_t drs = mf::row_rsrc(df + (size_t)h * N, 4 * N);
+    float *dDh = dD + h;
+    E.template run_bwd<mf::kNT>(mf::row_rsrc(f + (size_t)h * N, 4 * N), D[h], rows, nround, mf::half_bits(N),
+                                [&](int pos, float v) {
+                                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), drs, 4 * pos, 0, 0);
+                                    if (pos == 0) *dDh = v;
+                                });
+}
+
+template <int LOG2M, int IO>
+static hipError_t launch_bwd_mfma(const void *u, const float *f, const float *D, const void *dy, void *du, float *df,
+                                  float *dD, int B, int H, int N, hipStream_t s) {
+    using T = typename io_elem<IO>::T;
+    return launch(k_fft_bwd_mfma<LOG2M, IO>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s, (const T *)u, f, D,
+                  (const T *)dy, (T *)du, df, dD, B, H, N);
+}
+
 template <int LOG2M, int IO>
 static hipError_t launch_df_mfma(const void *u, const void *dy, float *df, float *dD, int B, int H, int N,
                                  hipStream_t s) {
@@ -538,10 +589,29 @@ hipError_t launch_fft_bidir(const void *u, const float *f, const float *g, const
     }
 }
 
+template <int IO>
+static hipError_t bwd_fused(int log2m, const void *u, const float *f, const float *D, const void *dy, void *du,
+                            float *df, float *dD, int B, int H, int N, hipStream_t s, bool *done) {
+    *done = true;
+    switch (log2m) {
+        case 10: return launch_bwd_mfma<10, IO>(u, f, D, dy, du, df, dD, B, H, N, s);
+        case 11: return launch_bwd_mfma<11, IO>(u, f, D, dy, du, df, dD, B, H, N, s);
+        // (2N = 4096, 8192: the registers of the fused kernel would spill at
+        //  two workgroups per compute unit; two kernels instead)
+        default: *done = false; return hipSuccess;
+    }
+}
+
 hipError_t launch_fft_conv_bwd(const void *u, const float *f, const float *D, const void *dy, void *du,
                                float *df, float *dD, int B, int H, int N, int io, hipStream_t s) {
     const int l = fused_log2m(N);
     hipError_t e;
+    bool done = false;
+    // 16-bit activations with 2N = 1024, 2048: one kernel for all three
+    // gradients; otherwise the correlation kernel for du, then df and dD
+    if (io == IO_F16) e = bwd_fused<IO_F16>(l, u, f, D, dy, du, df, dD, B, H, N, s, &done);
+    else if (io == IO_BF16) e = bwd_fused<IO_BF16>(l, u, f, D, dy, du, df, dD, B, H, N, s, &done);
+    if (done) return e;
     switch (io) {
         case IO_F32:
             e = fc_dispatch<IO_F32, mf::kNT, true>(l, dy, f, D, du, B, H, N, s);

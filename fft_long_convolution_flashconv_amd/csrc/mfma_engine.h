@@ -735,16 +735,12 @@ struct Engine {
     }
 
     // Input scales of a round, one per row: each signal's real and imaginary
-    // halves are different rows.  From the per-half maxima of the round's
-    // inputs (as 16-bit bit patterns), one barrier: kp[i] = scale exponents
-    // (real, imaginary half) of the signal of pass-0 tile i, kq[i] those of
-    // inverse pass-0 tile i (see scale_exp).  With FILT, also returns the
-    // workgroup's sum of `fs` (the filter's |f|).  The exponents are read
-    // from the slots right after the barrier, so the bank can be written
-    // again two reductions later.
-    template <bool FILT>
-    __device__ float block_scales(float fs, int hb, int (&kp)[T0W][2], int (&kq)[TIW][2]) {
-        const uint32_t kpk = round_exps<FILT>(fs, hb);
+    // halves are different rows.  round_exps (below) reduces the per-half
+    // maxima of the round's inputs (as 16-bit bit patterns) with one barrier;
+    // exps_of then gives kp[i] = scale exponents (real, imaginary half) of
+    // the signal of pass-0 tile i and kq[i] those of inverse pass-0 tile i
+    // (see scale_exp).
+    __device__ __forceinline__ void exps_of(uint32_t kpk, int (&kp)[T0W][2], int (&kq)[TIW][2]) {
         auto get = [&](int (&k)[2], int sg) {
             const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpk, sg);
             k[0] = lo16(v);
@@ -754,14 +750,16 @@ struct Engine {
         for (int i = 0; i < T0W; ++i) get(kp[i], SIG == 1 ? 0 : tile_sig(i));
 #pragma unroll
         for (int i = 0; i < TIW; ++i) get(kq[i], SIG == 1 ? 0 : (16 * (w + i * NW)) / S0);
-        return fs;
     }
     __device__ __forceinline__ static int lo16(uint32_t v) { return (int)(int16_t)(uint16_t)(v & 0xffffu); }
     __device__ __forceinline__ static int hi16(uint32_t v) { return (int)v >> 16; }
 
-    // The reduction behind block_scales: returns, in lane l < SIG, the two
+    // The reduction behind the round scales: returns, in lane l < SIG, the two
     // scale exponents of signal l (real half in the low 16 bits, imaginary
-    // half in the high 16 bits); with FILT, fs becomes the workgroup's sum.
+    // half in the high 16 bits); with FILT, fs (the filter's |f| of this
+    // thread) becomes the workgroup's sum.  The exponents are read from the
+    // slots right after the barrier, so the bank can be written again two
+    // reductions later.
     template <bool FILT>
     __device__ uint32_t round_exps(float &fs, int hb) {
         uint32_t tm[T0W];
@@ -1297,6 +1295,14 @@ struct Engine {
     // before the products.  prefetch() is called once pin has been consumed.
     template <bool FILT, bool CORR, class OUT, class PF>
     __device__ void conv_round(const OUT &out, int hb, const float (&fin)[T0W][4], const PF &prefetch) {
+        conv_round<FILT, CORR>(out, hb, fin, prefetch, [](uint32_t) {}, [](int, const uint32_t(&)[NV]) {});
+    }
+    // With hooks: onexp(e) receives the round's row exponents (lane s <
+    // SIG: signal s's pair, as round_exps returns them), onfwd(u, y) the
+    // forward last-pass values of unit u before the product.
+    template <bool FILT, bool CORR, class OUT, class PF, class OE, class OF>
+    __device__ void conv_round(const OUT &out, int hb, const float (&fin)[T0W][4], const PF &prefetch,
+                               const OE &onexp, const OF &onfwd) {
         static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
         __builtin_amdgcn_s_setprio(kPrioLoad);
         // Every row gets a scale of its own: a signal's real and imaginary
@@ -1305,7 +1311,10 @@ struct Engine {
         int kp[T0W][2], kq[TIW][2];
         float sf = 0.f;
         {
-            const float fa = block_scales<FILT>(FILT ? filter_asum(fin) : 0.f, hb, kp, kq);
+            float fa = FILT ? filter_asum(fin) : 0.f;
+            const uint32_t kpk = round_exps<FILT>(fa, hb);
+            onexp(kpk);
+            exps_of(kpk, kp, kq);
             if constexpr (FILT) sf = filter_scale(fa);
         }
         f2 sut[T0W] = {};
@@ -1345,6 +1354,7 @@ struct Engine {
                 const int pb = (lb ^ lpos(u)) + lsig(u) * SB;
                 uint32_t y[NV], fr[NV];
                 last_fwd(vb[k], y);
+                onfwd(u, y);
 #pragma unroll
                 for (int q = 0; q < NV; ++q) fr[q] = Fr[fslot(slot) + q];
                 cmulh_cx_n(y, fr);  // conj(Y) = conj(X) conj(F)
@@ -1477,132 +1487,132 @@ struct Engine {
         }
     }
 
-    // Gradient of the filter of a causal convolution: Re IDFT(sum_p conj(U_p)
+    // Filter gradient of a causal convolution: Re IDFT(sum_p conj(U_p)
     // DY_p)[:M/2] with U_p = DFT(u_2p + i u_2p+1) and DY_p the same of dy;
     // the real part is the sum over the rows of the correlations of u with
-    // dy (the cross terms of a pair are imaginary).  Rounds come in twos over
-    // the same SIG row pairs: the u round keeps its last-pass values in
-    // registers, the dy round multiplies its own into them and adds the
-    // products, in fp32, to this lane's points of the sum.  Row x of a pair
-    // enters with scales 2^ku_x (u, its own) and 2^(K - ku_x) (dy), with K =
-    // min over the rows of ku_x + kd_x (kd_x = dy row x's own exponent), so
-    // both rows' products carry the same factor 2^K, removed exactly; a row
-    // scaled below its own exponent holds a product at most 2^(K - ku_x -
-    // kd_x) of the largest one's.  After the last round the sum is scaled to
-    // the fp16 range, inverted once (signal 0 alone) and stored through
-    // st(p, v).  rows(v): the buffers of virtual signal v = round * SIG + s
-    // (u rows in even rounds, dy rows in odd ones).
-    template <class RB, class ST>
-    __device__ void run_df(const RB &rows, int nround, int hb, const ST &st) {
-        static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
-        constexpr int kDrop = -0x4000;  // input exponent of a row left out (ldexp to zero)
-        float acc[FN][2];
-#pragma unroll
-        for (int i = 0; i < FN; ++i) acc[i][0] = acc[i][1] = 0.f;
-        uint32_t yu[NU][NV];
+    // dy (the cross terms of a pair are imaginary).  Rounds come in twos
+    // over the same SIG row pairs: the first keeps its forward last-pass
+    // values in registers, with each row at its own scale 2^k_x; the second
+    // ("tied") scales row x of the other tensor by 2^(K - k_x), K = min over
+    // the pair's rows of k_x + k'_x (k'_x = that row's own exponent), so both
+    // rows' products carry the one factor 2^K, removed exactly as they are
+    // added, in fp32, to this lane's points of the sum.  A row scaled below
+    // its own exponent holds a product at most 2^(K - k_x - k'_x) of the
+    // pair's largest.  Rows of zeros take no part.
+    static constexpr int kDrop = -0x4000;  // input exponent of a row left out (ldexp to zero)
+    static constexpr int UBL = NU * NVD <= SH::BD ? NU : SH::BD / NVD;  // last-pass units per batch of reads
+    static_assert(NU % UBL == 0, "last-pass units split into equal batches");
+
+    // The kept round of a pair (run_df: u rows at their own scales): forward
+    // passes, last-pass values into yk; returns the row exponents.
+    template <class RB>
+    __device__ __forceinline__ uint32_t keep_round(const RB &rows, int r, int nround, int hb,
+                                                   uint32_t (&yk)[NU][NV]) {
         __builtin_amdgcn_s_setprio(kPrioLoad);
-        fetch_raw(rows, 0, pin);
-        constexpr int UB = NU * NVD <= SH::BD ? NU : SH::BD / NVD;
-        static_assert(NU % UB == 0, "last-pass units split into equal batches");
-        for (int r = 0; r < nround; r += 2) {
-            // ---- u round: per-row scales, as in a convolution round
-            uint32_t kpu;
-            {
-                __builtin_amdgcn_s_setprio(kPrioLoad);
-                if (!PREFETCH && r > 0) fetch_raw(rows, r * SIG, pin);
-                float fs = 0.f;
-                kpu = round_exps<false>(fs, hb);
-                f2 sut[T0W] = {};
-                uint32_t suh[T0W] = {};
+        if (!PREFETCH && r > 0) fetch_raw(rows, r * SIG, pin);
+        float fs = 0.f;
+        const uint32_t kpk = round_exps<false>(fs, hb);
+        f2 sut[T0W] = {};
+        uint32_t suh[T0W] = {};
 #pragma unroll
-                for (int i = 0; i < T0W; ++i) {
-                    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpu, SIG == 1 ? 0 : tile_sig(i));
-                    if constexpr (KIND == IN_F16) suh[i] = exp2h(lo16(v)) | (exp2h(hi16(v)) << 16);
-                    else sut[i] = f2{exp2i(lo16(v)), exp2i(hi16(v))};
-                }
-                auto op = [&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], sut[i], suh[i]); };
-                pass0<SIG>(op, op);
-                if (PREFETCH) fetch_raw(rows, (r + 1) * SIG, pin);
-                __builtin_amdgcn_s_setprio(kPrioWork);
-                fwd_middle<1, SIG>();
-                const int lb = opaque(lbase());
+        for (int i = 0; i < T0W; ++i) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpk, SIG == 1 ? 0 : tile_sig(i));
+            if constexpr (KIND == IN_F16) suh[i] = exp2h(lo16(v)) | (exp2h(hi16(v)) << 16);
+            else sut[i] = f2{exp2i(lo16(v)), exp2i(hi16(v))};
+        }
+        auto op = [&](int i, int e) -> uint32_t { return in_scaled<KIND>(pin[i][e], sut[i], suh[i]); };
+        pass0<SIG>(op, op);
+        if (PREFETCH && r + 1 < nround) fetch_raw(rows, (r + 1) * SIG, pin);
+        __builtin_amdgcn_s_setprio(kPrioWork);
+        fwd_middle<1, SIG>();
+        const int lb = opaque(lbase());
 #pragma unroll
-                for (int u0 = 0; u0 < NU; u0 += UB) {
-                    uint32_t vb[UB][NVD];
+        for (int u0 = 0; u0 < NU; u0 += UBL) {
+            uint32_t vb[UBL][NVD];
 #pragma unroll
-                    for (int k = 0; k < UB; ++k) last_load((lb ^ lpos(u0 + k)) + lsig(u0 + k) * SB, vb[k]);
+            for (int k = 0; k < UBL; ++k) last_load((lb ^ lpos(u0 + k)) + lsig(u0 + k) * SB, vb[k]);
 #pragma unroll
-                    for (int k = 0; k < UB; ++k) last_fwd(vb[k], yu[u0 + k]);
-                }
+            for (int k = 0; k < UBL; ++k) last_fwd(vb[k], yk[u0 + k]);
+        }
+        return kpk;
+    }
+
+    // The tied round of a pair: scales tied to the kept round's exponents
+    // kpk, products with the kept values yk added to acc.  CONJ_CUR: the
+    // sum takes conj(this round's values) (u in this round), else conj(yk).
+    template <bool CONJ_CUR, class RB>
+    __device__ __forceinline__ void tied_round(const RB &rows, int r, int nround, int hb, uint32_t kpk,
+                                               const uint32_t (&yk)[NU][NV], float (&acc)[FN][2]) {
+        __builtin_amdgcn_s_setprio(kPrioLoad);
+        if (!PREFETCH) fetch_raw(rows, r * SIG, pin);
+        float fs = 0.f;
+        const uint32_t kpo = round_exps<false>(fs, hb);
+        // lane s < SIG: this round's input exponents for signal s, and K
+        const int ka = lo16(kpk), kb = hi16(kpk), oa = lo16(kpo), ob = hi16(kpo);
+        const bool va = ka != kZero && oa != kZero, vb = kb != kZero && ob != kZero;
+        int kk = va ? ka + oa : (vb ? kb + ob : 0);
+        if (va && vb) kk = min(kk, kb + ob);
+        const int ea = va ? kk - ka : kDrop, eb = vb ? kk - kb : kDrop;
+        const uint32_t kpe = ((uint32_t)ea & 0xffffu) | ((uint32_t)eb << 16);
+        int eia[T0W], eib[T0W];
+#pragma unroll
+        for (int i = 0; i < T0W; ++i) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpe, SIG == 1 ? 0 : tile_sig(i));
+            eia[i] = lo16(v);
+            eib[i] = hi16(v);
+        }
+        auto op = [&](int i, int e) -> uint32_t {
+            const uint32_t x = pin[i][e];
+            float a, b;
+            if constexpr (KIND == IN_F16) {
+                const h2 hv = __builtin_bit_cast(h2, x);
+                a = (float)hv.x;
+                b = (float)hv.y;
+            } else {
+                a = __uint_as_float(x << 16);
+                b = __uint_as_float(x & 0xffff0000u);
             }
-            // ---- dy round: scales tied to the u round's, products summed
-            {
-                __builtin_amdgcn_s_setprio(kPrioLoad);
-                if (!PREFETCH) fetch_raw(rows, (r + 1) * SIG, pin);
-                float fs = 0.f;
-                const uint32_t kpd = round_exps<false>(fs, hb);
-                // lane s < SIG: signal s's dy exponents and product exponent K
-                const int ka = lo16(kpu), kb = hi16(kpu), da = lo16(kpd), db = hi16(kpd);
-                const bool va = ka != kZero && da != kZero, vb = kb != kZero && db != kZero;
-                int kk = va ? ka + da : (vb ? kb + db : 0);
-                if (va && vb) kk = min(kk, kb + db);
-                const int ea = va ? kk - ka : kDrop, eb = vb ? kk - kb : kDrop;
-                const uint32_t kpe = ((uint32_t)ea & 0xffffu) | ((uint32_t)eb << 16);
-                int eda[T0W], edb[T0W];
+            return pk(ldexpf(a, eia[i]), ldexpf(b, eib[i]));
+        };
+        pass0<SIG>(op, op);
+        if (PREFETCH && r + 1 < nround) fetch_raw(rows, (r + 1) * SIG, pin);
+        __builtin_amdgcn_s_setprio(kPrioWork);
+        fwd_middle<1, SIG>();
+        int nk[SIG];
 #pragma unroll
-                for (int i = 0; i < T0W; ++i) {
-                    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)kpe, SIG == 1 ? 0 : tile_sig(i));
-                    eda[i] = lo16(v);
-                    edb[i] = hi16(v);
-                }
-                auto op = [&](int i, int e) -> uint32_t {
-                    const uint32_t x = pin[i][e];
-                    float a, b;
-                    if constexpr (KIND == IN_F16) {
-                        const h2 hv = __builtin_bit_cast(h2, x);
-                        a = (float)hv.x;
-                        b = (float)hv.y;
-                    } else {
-                        a = __uint_as_float(x << 16);
-                        b = __uint_as_float(x & 0xffff0000u);
-                    }
-                    return pk(ldexpf(a, eda[i]), ldexpf(b, edb[i]));
-                };
-                pass0<SIG>(op, op);
-                if (PREFETCH && r + 2 < nround) fetch_raw(rows, (r + 2) * SIG, pin);
-                __builtin_amdgcn_s_setprio(kPrioWork);
-                fwd_middle<1, SIG>();
-                int nk[SIG];
+        for (int sg = 0; sg < SIG; ++sg) nk[sg] = -__builtin_amdgcn_readlane(kk, sg);
+        const int lb = opaque(lbase());
 #pragma unroll
-                for (int sg = 0; sg < SIG; ++sg) nk[sg] = -__builtin_amdgcn_readlane(kk, sg);
-                const int lb = opaque(lbase());
+        for (int u0 = 0; u0 < NU; u0 += UBL) {
+            uint32_t vb2[UBL][NVD];
 #pragma unroll
-                for (int u0 = 0; u0 < NU; u0 += UB) {
-                    uint32_t vb2[UB][NVD];
+            for (int k = 0; k < UBL; ++k) last_load((lb ^ lpos(u0 + k)) + lsig(u0 + k) * SB, vb2[k]);
 #pragma unroll
-                    for (int k = 0; k < UB; ++k) last_load((lb ^ lpos(u0 + k)) + lsig(u0 + k) * SB, vb2[k]);
+            for (int k = 0; k < UBL; ++k) {
+                const int u = u0 + k;
+                uint32_t y[NV];
+                last_fwd(vb2[k], y);
 #pragma unroll
-                    for (int k = 0; k < UB; ++k) {
-                        const int u = u0 + k;
-                        uint32_t y[NV];
-                        last_fwd(vb2[k], y);
-#pragma unroll
-                        for (int q = 0; q < NV; ++q) {
-                            // acc += conj(Yu) Ydy 2^-K
-                            const h2 a = __builtin_bit_cast(h2, yu[u][q]), d = __builtin_bit_cast(h2, y[q]);
-                            const float ar = (float)a.x, ai = (float)a.y, dr = (float)d.x, di = (float)d.y;
-                            const float re = fmaf(ar, dr, ai * di), im = fmaf(ar, di, -ai * dr);
-                            const int ix = fslot(u % NLS) + q;
-                            acc[ix][0] += ldexpf(re, nk[lsig(u)]);
-                            acc[ix][1] += ldexpf(im, nk[lsig(u)]);
-                        }
-                    }
+                for (int q = 0; q < NV; ++q) {
+                    // acc += conj(a) d 2^-K
+                    const h2 a = __builtin_bit_cast(h2, CONJ_CUR ? y[q] : yk[u][q]);
+                    const h2 d = __builtin_bit_cast(h2, CONJ_CUR ? yk[u][q] : y[q]);
+                    const float ar = (float)a.x, ai = (float)a.y, dr = (float)d.x, di = (float)d.y;
+                    const float re = fmaf(ar, dr, ai * di), im = fmaf(ar, di, -ai * dr);
+                    const int ix = fslot(u % NLS) + q;
+                    acc[ix][0] += ldexpf(re, nk[lsig(u)]);
+                    acc[ix][1] += ldexpf(im, nk[lsig(u)]);
                 }
             }
         }
-        // Scale the sum so that |values| < 2^(14 - LR): its DFT-R (the first
-        // inverse step) then stays below 2^14.  Inverse on conjugated values,
-        // as in a convolution round, for signal 0 only.
+    }
+
+    // After the last pair: the sum scaled so that |values| < 2^(14 - LR)
+    // (its DFT-R, the first inverse step, then stays below 2^14), inverted
+    // as in a convolution round (on conjugated values) for signal 0 alone,
+    // real part stored through st(p, v).
+    template <class ST>
+    __device__ __forceinline__ void df_finish(const float (&acc)[FN][2], const ST &st) {
         float am = 0.f;
 #pragma unroll
         for (int i = 0; i < FN; ++i) am = fmaxf(am, fmaxf(fabsf(acc[i][0]), fabsf(acc[i][1])));
@@ -1632,6 +1642,83 @@ struct Engine {
         inv_middle<K, 1>(pk(sy, sy));
         // the output chain multiplied the sum by M sy 2^ec
         pass0_inv_real(st, ldexpf(1.0f / ((float)M * sy), -ec));
+    }
+
+    // The filter gradient alone.  rows(v): the buffers of virtual signal v =
+    // round * SIG + s (u rows in even rounds, dy rows in odd ones).
+    template <class RB, class ST>
+    __device__ void run_df(const RB &rows, int nround, int hb, const ST &st) {
+        static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
+        float acc[FN][2];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) acc[i][0] = acc[i][1] = 0.f;
+        uint32_t yk[NU][NV];
+        __builtin_amdgcn_s_setprio(kPrioLoad);
+        fetch_raw(rows, 0, pin);
+        for (int r = 0; r < nround; r += 2) {
+            const uint32_t kpk = keep_round(rows, r, nround, hb, yk);
+            tied_round<false>(rows, r + 1, nround, hb, kpk, yk, acc);
+        }
+        df_finish(acc, st);
+    }
+
+    // The whole backward pass of a causal convolution with residual, one
+    // read of u and dy: in each pair of rounds, the dy round is a
+    // correlation round (CORR: du = the correlation of dy with the filter,
+    // D dy by tap 0, dy rows at their own scales) whose forward last-pass
+    // values are kept; the u round that follows (the same row pairs) is
+    // tied to dy's exponents and adds conj(U) DY to the sum; df_finish then
+    // gives df.  rows(v): dy rows (du as output) in even rounds, u rows in
+    // odd ones.  `frs` covers the filter's taps, d0 is added to tap 0.
+    template <int SPOL, class RB, class ST>
+    __device__ void run_bwd(__amdgpu_buffer_rsrc_t frs, float d0, const RB &rows, int nround, int hb, const ST &st) {
+        static_assert(KIND == IN_F16 || KIND == IN_BF16, "16-bit activations");
+        float acc[FN][2];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) acc[i][0] = acc[i][1] = 0.f;
+        uint32_t yk[NU][NV];
+        uint32_t kpd = 0;
+        float fin[T0W][4];
+        __builtin_amdgcn_s_setprio(kPrioLoad);
+        filter_fetch(frs, d0, fin);
+        fetch_raw(rows, 0, pin);
+        auto store = [&](int r0, int s, int n, int m, uint32_t hv) {
+            const RowBufs rb = rows(r0 + s);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, rb.out0, 2 * (n + m * S0), 0, SPOL);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), rb.out1, 2 * (n + m * S0), 0, SPOL);
+        };
+        auto onexp = [&](uint32_t e) { kpd = e; };
+        auto onfwd = [&](int u, const uint32_t (&y)[NV]) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q) yk[u][q] = y[q];
+        };
+        // (with B = 0 the first pair still runs, on empty rows: no stores,
+        //  a zero sum)
+        int r = 0;
+        if constexpr (SH::FUSEF) {
+            // the first dy round with the filter alongside
+            auto pf = [&]() {
+                if (PREFETCH) fetch_raw(rows, SIG, pin);
+            };
+            conv_round<true, true>([&](int s, int n, int m, uint32_t hv) { store(0, s, n, m, hv); }, hb, fin, pf,
+                                   onexp, onfwd);
+            tied_round<true>(rows, 1, nround, hb, kpd, yk, acc);
+            r = 2;
+        } else {
+            filter<true>(fin);
+        }
+        for (; r < nround; r += 2) {
+            const int r0 = r * SIG;
+            auto pf = [&]() {
+                if (PREFETCH) fetch_raw(rows, r0 + SIG, pin);
+            };
+            __builtin_amdgcn_s_setprio(kPrioLoad);
+            if (!PREFETCH && r > 0) fetch_raw(rows, r0, pin);
+            conv_round<false, true>([&](int s, int n, int m, uint32_t hv) { store(r0, s, n, m, hv); }, hb, fin, pf,
+                                    onexp, onfwd);
+            tied_round<true>(rows, r + 1, nround, hb, kpd, yk, acc);
+        }
+        df_finish(acc, st);
     }
 };
 
