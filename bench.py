@@ -61,7 +61,11 @@ KERNEL_SRC_DIR = "fft_long_convolution_flashconv_amd/csrc"
 PROFILES = {"conv_1k": "profiles/k_fft_conv_mfma_conv_1k.md",
             "conv_8k": "profiles/k_fft_conv_mfma_conv_8k.md",
             "state_64k": "profiles/k_sp_chunk_conv_mfma_state_64k.md",
-            "h3_mix_2k": "profiles/k_fft_conv_mfma_h3_mix_2k.md"}
+            "h3_mix_2k": "profiles/k_fft_conv_mfma_h3_mix_2k.md",
+            "conv_1k_bwd": "profiles/k_fft_bwd_mfma_conv_1k_bwd.md",
+            "decode_125m": "profiles/k_ssm_step_decode_125m.md",
+            "h3_mix_mh_1k": "profiles/k_fft_conv_mfma_h3_mix_mh_1k.md",
+            "bidir_1k": "profiles/k_fft_bidir_mfma_bidir_1k.md"}
 
 
 def kernel_source_hash() -> str:
@@ -114,6 +118,8 @@ def algorithmic_bytes(w: wl.Workload) -> int:
         return 4 * w.B * w.N * w.Dm * e + w.Dm * w.L * 4 + w.Dm * w.dh * (w.N * 4 + 4)
     if w.kind == "fft_conv_bwd":  # read u, dy, f, D; write du, df, dD
         return 3 * w.B * w.H * w.N * e + 2 * w.H * w.N * 4 + 2 * w.H * 4
+    if w.kind == "fft_conv_bidir":  # read u, f, g, D; write y
+        return 2 * w.B * w.H * w.N * e + 2 * w.H * w.N * 4 + w.H * 4
     if w.kind == "ssm_step":      # read u, x, parameters; write y, x
         return w.B * w.H * (2 * w.N * e + 2 * w.S * 8) + w.H * (3 * w.S * 8 + 8)
     raise ValueError(w.kind)
@@ -131,9 +137,12 @@ class Case:
         self.sets = []
         for i in range(self.nsets):
             s = {k: (v if i == 0 else v.clone()) for k, v in d.items()}
-            if w.kind in ("fft_conv", "h3_mix", "fft_conv_bwd", "h3_mix_mh") and "A" in s:
+            if w.kind in ("fft_conv", "h3_mix", "fft_conv_bwd", "h3_mix_mh", "fft_conv_bidir") and "A" in s:
                 s["f"] = pkg.ssm_filter(s["A"], s["Bm"], s["C"], s["dt"], w.N)
-            if w.kind == "fft_conv":
+            if w.kind == "fft_conv_bidir":
+                s["g"] = pkg.ssm_filter(s["gA"], s["gBm"], s["gC"], s["gdt"], w.N)
+                s["y"] = torch.empty_like(s["u"])
+            elif w.kind == "fft_conv":
                 s["y"] = torch.empty_like(s["u"])
             elif w.kind == "fft_conv_bwd":
                 s["du"] = torch.empty_like(s["u"])
@@ -161,6 +170,8 @@ class Case:
         w = self.w
         if w.kind == "fft_conv":
             pkg.fft_conv(s["u"], s["f"], s["D"], out=s["y"])
+        elif w.kind == "fft_conv_bidir":
+            pkg.fft_conv_bidir(s["u"], s["f"], s["g"], s["D"], out=s["y"])
         elif w.kind == "fft_conv_bwd":
             pkg.fft_conv_bwd(s["u"], s["f"], s["D"], s["dy"], du=s["du"], df=s["df"], dD=s["dD"])
         elif w.kind == "ssm_step":
@@ -385,7 +396,7 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_secondary:
         sec = {}
-        for name in ("conv_8k", "state_64k", "h3_mix_2k", "conv_1k_bwd", "decode_125m", "h3_mix_mh_1k"):
+        for name in ("conv_8k", "state_64k", "h3_mix_2k", "conv_1k_bwd", "decode_125m", "h3_mix_mh_1k", "bidir_1k"):
             if name == w.name:
                 continue
             ww = wl.WORKLOADS[name]
@@ -396,7 +407,8 @@ def main():
             sec[name] = {"elements_per_s": ww.elements / (m_ms * 1e-3), "mean_us": m_ms * 1e3,
                          "algorithmic_bytes": nb, "GB_s": nb / (m_ms * 1e-3) / 1e9,
                          "frac_hbm": nb / (m_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "sets": c.nsets,
-                         "traffic_per_step_kernel": pr["traffic"], "profiled_kernel": pr["kernel"]}
+                         "traffic_per_step_kernel": pr["traffic"], "profiled_kernel": pr["kernel"],
+                         "mfma_util": (pr["mfma_flops"] / (m_ms * 1e-3) / MFMA_PEAK_FLOPS) if pr["mfma_flops"] else None}
             log("bench: %s mean %.1f us  %.1f GB/s" % (name, m_ms * 1e3, sec[name]["GB_s"]))
             del c
             torch.cuda.empty_cache()

@@ -28,6 +28,9 @@ parity configurations, timed beside them):
   h3_mix_mh_1k fp16  B=4  N=1024 Dm=768 dh=4  multi-head H3 mixing, heads of
                                           dimension 4, one diagonal-SSM filter
                                           per state entry
+  bidir_1k     fp16  B=8  H=768  N=1024   bidirectional copies: a causal and
+                                          an anti-causal diagonal-SSM filter
+                                          per channel (two parameter draws)
 
 Diagonal-SSM parameters: A_j = -0.5 + i*pi*j (j = 0..S-1), B_j = 1,
 C_j ~ CN(0, 0.5) (real and imaginary parts independent N(0, 0.25)),
@@ -46,7 +49,8 @@ DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "fft_conv" | "state_pass" | "h3_mix" | "fft_conv_bwd" | "ssm_step"
+    kind: str            # "fft_conv" | "state_pass" | "h3_mix" | "fft_conv_bwd" | "ssm_step" |
+                         # "h3_mix_mh" | "fft_conv_bidir"
     dtype: str           # I/O dtype: "f32" | "f16" | "bf16"
     B: int
     N: int
@@ -73,6 +77,7 @@ WORKLOADS = {
     "conv_1k_bwd": Workload("conv_1k_bwd", "fft_conv_bwd", "f16", B=8, H=768, N=1024, seed=5),
     "decode_125m": Workload("decode_125m", "ssm_step", "f16", B=64, H=768, N=1, seed=6),
     "h3_mix_mh_1k": Workload("h3_mix_mh_1k", "h3_mix_mh", "f16", B=4, N=1024, Dm=768, dh=4, seed=7),
+    "bidir_1k": Workload("bidir_1k", "fft_conv_bidir", "f16", B=8, H=768, N=1024, seed=8),
 }
 
 
@@ -133,6 +138,14 @@ def make_inputs(w: Workload, *, B: int | None = None, H: int | None = None,
             out["f"] = random_env_filter(H, N, g)
         else:
             out.update(diag_ssm_params(H, w.S, g))
+        out["D"] = normal((H,), g, dtype=torch.float32)
+        return out
+    if w.kind == "fft_conv_bidir":
+        # causal filter from (A, Bm, C, dt), anti-causal from (gA, gBm, gC, gdt)
+        H = w.H if H is None else H
+        out = {"u": normal((B, H, N), g, dtype=io)}
+        out.update(diag_ssm_params(H, w.S, g))
+        out.update({"g" + k: v for k, v in diag_ssm_params(H, w.S, g).items()})
         out["D"] = normal((H,), g, dtype=torch.float32)
         return out
     if w.kind == "fft_conv_bwd":

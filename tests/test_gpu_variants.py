@@ -55,20 +55,21 @@ def test_bidir_reduces_to_causal_and_reversed():
 
 
 def test_bidir_workload_shape_every_row():
-    """The H3-125M convolution shape (B=8, H=768, N=1024, fp16) with both
-    filters from diagonal-SSM parameters (the anti-causal copy has its own);
-    every row checked."""
-    w = wl.WORKLOADS["conv_1k"]
+    """The bidirectional workload (the H3-125M convolution shape B=8, H=768,
+    N=1024, fp16) with both filters from diagonal-SSM parameters (the
+    anti-causal copy has its own draw); every row checked, and a second run
+    bitwise equal."""
+    w = wl.WORKLOADS["bidir_1k"]
     dev = device()
-    say("fft_conv_bidir B=%d H=%d N=%d f16: every row" % (w.B, w.H, w.N))
+    say("fft_conv_bidir workload %s B=%d H=%d N=%d f16: every row" % (w.name, w.B, w.H, w.N))
     inp = wl.make_inputs(w)
-    p2 = wl.diag_ssm_params(w.H, w.S, wl.gen(555))
     d = {k: v.to(dev) for k, v in inp.items()}
-    d2 = {k: v.to(dev) for k, v in p2.items()}
     f = pkg.ssm_filter(d["A"], d["Bm"], d["C"], d["dt"], w.N)
-    g = pkg.ssm_filter(d2["A"], d2["Bm"], d2["C"], d2["dt"], w.N)
+    g = pkg.ssm_filter(d["gA"], d["gBm"], d["gC"], d["gdt"], w.N)
     y = pkg.fft_conv_bidir(d["u"], f, g, d["D"])
+    again = pkg.fft_conv_bidir(d["u"], f, g, d["D"])
     torch.cuda.synchronize()
+    assert torch.equal(y, again), "second run differs"
     ref = oracle.bidir_conv(inp["u"], to_np(f), to_np(g), inp["D"])
     got = to_np(y)
     rows = row_rel_l2(got.reshape(-1, w.N), ref.reshape(-1, w.N))
