@@ -337,16 +337,17 @@ static hipError_t df_dispatch(int log2m, const void *u, const void *dy, float *d
 // the matrix cores (see mfma_engine.h).
 
 // SPOL: cache policy of the output stores (non-temporal unless the output
-// is read again right away)
-template <int LOG2M, int IO, int SPOL, bool CORR = false>
-__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M>::WPE))) void k_fft_conv_mfma(
+// is read again right away); V: the engine's shape variant (1: half the
+// signals per round, for batches that fill at most half a round)
+template <int LOG2M, int IO, int SPOL, bool CORR = false, int V = 0>
+__global__ __launch_bounds__((mf::Shape<LOG2M, V>::NT)) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M, V>::WPE))) void k_fft_conv_mfma(
     const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ f,
     const float *__restrict__ D, typename io_elem<IO>::T *__restrict__ y, int B, int H, int N) {
     using T = typename io_elem<IO>::T;
-    using SH = mf::Shape<LOG2M>;
+    using SH = mf::Shape<LOG2M, V>;
     constexpr int KIND = IO == IO_F16 ? mf::IN_F16 : mf::IN_BF16;
     __shared__ __attribute__((aligned(16))) uint32_t smem[SH::LDS_DWORDS];
-    mf::Engine<LOG2M, KIND> E(smem);
+    mf::Engine<LOG2M, KIND, V> E(smem);
     E.init();
     const int h = blockIdx.x;
     const float *fh = f + (size_t)h * N;
@@ -479,6 +480,11 @@ static hipError_t launch_fc_mfma(const void *u, const float *f, const float *D, 
     const uint64_t pad = fc_row_pad<LOG2M>();
     if ((pad + 2) * rowb >= (1ull << 32)) return hipErrorInvalidValue;  // refused by the API first
     const int bmax = (int)std::min<uint64_t>((uint64_t)B, (((1ull << 32) - 1) / rowb - pad) & ~1ull);
+    // batches of at most half a round's signals: the half shape (2N <= 4096)
+    constexpr bool HALF = LOG2M <= 12;
+    if (HALF && (B + 1) / 2 <= mf::Shape<LOG2M>::SIG / 2)
+        return launch(k_fft_conv_mfma<LOG2M, IO, SPOL, CORR, HALF ? 1 : 0>, dim3(H), dim3(mf::Shape<LOG2M, HALF ? 1 : 0>::NT),
+                      0, s, (const T *)u, f, D, (T *)y, B, H, N);
     for (int b0 = 0; b0 < B; b0 += bmax) {
         const size_t o = (size_t)b0 * H * N;
         const hipError_t e = launch(k_fft_conv_mfma<LOG2M, IO, SPOL, CORR>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s,

@@ -334,15 +334,29 @@ template <> struct Cfg<14> { static constexpr int SIG = 1, NW = 8, OCC = 2, BD =
 // in LDS per workgroup, one workgroup per compute unit
 template <> struct Cfg<15> { static constexpr int SIG = 1, NW = 8, OCC = 1, BD = 16; };
 
-template <int LOG2M>
+// Shape variant V = 1 (2N <= 4096): half the signals per round with half the
+// waves, about twice the workgroups per compute unit (the same work per
+// wave), for batches that fill at most half a round.  At 2N = 2048 a wave
+// of the half shape holds 8 more registers (its share of the filter
+// spectrum and of the inverse twiddles doubles), so it is set for 5
+// workgroups (20 waves) rather than 6.
+template <int LOG2M, int V> struct CfgV {
+    static_assert(V == 0 || (Cfg<LOG2M>::SIG >= 2 && Cfg<LOG2M>::NW >= 2), "no half shape for this size");
+    static constexpr int SIG = V ? Cfg<LOG2M>::SIG / 2 : Cfg<LOG2M>::SIG;
+    static constexpr int NW = V ? Cfg<LOG2M>::NW / 2 : Cfg<LOG2M>::NW;
+    static constexpr int OCC = V ? (LOG2M == 11 ? 5 : 2 * Cfg<LOG2M>::OCC) : Cfg<LOG2M>::OCC;
+    static constexpr int BD = Cfg<LOG2M>::BD;
+};
+
+template <int LOG2M, int V = 0>
 struct Shape {
     static constexpr int M = 1 << LOG2M;
     static constexpr int K = (LOG2M - 5) / 4;          // middle radix-16 passes
     static constexpr int LR = LOG2M - 4 - 4 * K;       // log2 of the last radix
     static constexpr int R = 1 << LR;
     static constexpr int S0 = M / 16;                  // pass-0 columns per signal
-    static constexpr int SIG = Cfg<LOG2M>::SIG, NW = Cfg<LOG2M>::NW, NT = 64 * NW, OCC = Cfg<LOG2M>::OCC;
-    static constexpr int BD = Cfg<LOG2M>::BD;
+    static constexpr int SIG = CfgV<LOG2M, V>::SIG, NW = CfgV<LOG2M, V>::NW, NT = 64 * NW, OCC = CfgV<LOG2M, V>::OCC;
+    static constexpr int BD = CfgV<LOG2M, V>::BD;
     static constexpr int WPE = (OCC * NW + 3) / 4;     // waves per SIMD at that occupancy
     static constexpr int T0 = SIG * S0 / 32;           // pass-0 tiles (32 columns) per round
     static constexpr int T0W = T0 / NW;
@@ -395,14 +409,14 @@ namespace tab {
 //   2d, 2d+1   pass 0, offset d: w_M^(n q) for this lane's 8 outputs q = q32(v, h)
 //   Q_TU + d   inverse pass 0, offset d: w_M^(n k), k = chain(g, 0..3)
 //   Q_MID + p  middle pass p+1 (length L, stride S = L/16): w_L^(n k), k = chain(g, 0..3)
-template <int LOG2M>
+template <int LOG2M, int V>
 struct TwTab {
-    uint32_t q[Shape<LOG2M>::NQ][Shape<LOG2M>::NT][4];
+    uint32_t q[Shape<LOG2M, V>::NQ][Shape<LOG2M, V>::NT][4];
 };
-template <int LOG2M>
-constexpr TwTab<LOG2M> make_tw() {
-    using SH = Shape<LOG2M>;
-    TwTab<LOG2M> t{};
+template <int LOG2M, int V>
+constexpr TwTab<LOG2M, V> make_tw() {
+    using SH = Shape<LOG2M, V>;
+    TwTab<LOG2M, V> t{};
     for (int tid = 0; tid < SH::NT; ++tid) {
         const int w = tid >> 6, lane = tid & 63, j = lane & 15, g = lane >> 4;
         for (int d = 0; d < SH::ND0; ++d) {
@@ -422,8 +436,8 @@ constexpr TwTab<LOG2M> make_tw() {
     }
     return t;
 }
-template <int LOG2M>
-__device__ const TwTab<LOG2M> kTw = make_tw<LOG2M>();
+template <int LOG2M, int V = 0>
+__device__ const TwTab<LOG2M, V> kTw = make_tw<LOG2M, V>();
 }  // namespace tab
 
 // ================================================================ helpers
@@ -573,9 +587,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *p, int by
 
 // ================================================================ engine
 
-template <int LOG2M, int KIND>
+template <int LOG2M, int KIND, int VAR = 0>
 struct Engine {
-    using SH = Shape<LOG2M>;
+    using SH = Shape<LOG2M, VAR>;
     using IT = typename InT<KIND>::T;
     static constexpr int M = SH::M, K = SH::K, R = SH::R, S0 = SH::S0, SIG = SH::SIG, NW = SH::NW,
                          NT = SH::NT, T0W = SH::T0W, TIW = SH::TIW, TPW = SH::TPW, T8W = SH::T8W,
@@ -641,7 +655,7 @@ struct Engine {
             const uint32_t a0 = a.x, a1 = a.y;
             A8 = as_half4(a0, a1);
         }
-        twr = row_rsrc(&tab::kTw<LOG2M>.q[0][0][0], (int)sizeof(tab::TwTab<LOG2M>));
+        twr = row_rsrc(&tab::kTw<LOG2M, VAR>.q[0][0][0], (int)sizeof(tab::TwTab<LOG2M, VAR>));
         two = tid * 16;
         if constexpr (TWREG) {
 #pragma unroll

@@ -13,7 +13,7 @@ import torch
 import fft_long_convolution_flashconv_amd as pkg
 from fft_long_convolution_flashconv_amd import workloads as wl
 import oracle
-from parity_util import TOL, cplx, device, rel_l2, say, to_np
+from parity_util import TOL, cplx, device, rel_l2, row_rel_l2, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,25 @@ def test_fft_conv_shapes(io, N):
         y = pkg.fft_conv(u.to(dev), f.to(dev), D.to(dev))
         torch.cuda.synchronize()
         _check_conv(u, f, D, y, io, label)
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("N", [200, 256, 500, 1000, 2000])
+def test_fft_conv_batch_sizes(io, N):
+    """Batches on both sides of half a round of signals (the 16-bit engine
+    takes a half-width workgroup shape for batches that fill at most half a
+    round at 2N <= 4096), each with every row checked."""
+    dev = device()
+    H = 3
+    for B in (1, 2, 3, 4, 5, 8, 9, 16, 17):
+        label = "fft_conv io=%s B=%d H=%d N=%d" % (io, B, H, N)
+        say(label)
+        u, f, D = _conv_inputs(B, H, N, io, seed=N * 13 + B)
+        y = pkg.fft_conv(u.to(dev), f.to(dev), D.to(dev))
+        torch.cuda.synchronize()
+        got, ref = to_np(y), oracle.causal_conv(u, f, D)
+        rows = row_rel_l2(got.reshape(-1, N), ref.reshape(-1, N))
+        assert rows.max() <= TOL[io], (label, rows.max())
 
 
 @pytest.mark.parametrize("io", ["f32", "f16"])
