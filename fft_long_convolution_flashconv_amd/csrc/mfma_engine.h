@@ -1408,18 +1408,27 @@ struct Engine {
         float fin[T0W][4];
         __builtin_amdgcn_s_setprio(kPrioLoad);
         {
-            float gin[T0W][4];
-            filter_fetch(frs, d0, fin);
-            filter_fetch(grs, 0.f, gin);
-            if constexpr (PREFETCH) fetch_raw(rows, 0, pin);
-            const float sf = filter_scale(block_reduce<true>(filter_asum(fin) + filter_asum(gin)));
+            // g is loaded twice: for its sum |g| now, and for its transform
+            // after f's (kept in registers through f's transform, it would
+            // spill)
+            float gs;
+            {
+                float gin[T0W][4];
+                filter_fetch(frs, d0, fin);
+                filter_fetch(grs, 0.f, gin);
+                gs = filter_asum(gin);
+            }
+            const float sf = filter_scale(block_reduce<true>(filter_asum(fin) + gs));
             auto fop = [&](int i, int e) -> uint32_t { return pk(fin[i][e] * sf, 0.f); };
             pass0<1>(fop, fop);
+            float gin[T0W][4];
+            filter_fetch(grs, 0.f, gin);
             fwd_middle<1, 1>();
             filter_last<false>(0);
             __syncthreads();  // slot 0 has been read; the second transform writes it
             auto gop = [&](int i, int e) -> uint32_t { return pk(gin[i][e] * sf, 0.f); };
             pass0<1>(gop, gop);
+            if constexpr (PREFETCH) fetch_raw(rows, 0, pin);
             fwd_middle<1, 1>();
             filter_last<true, true>(0);
         }
