@@ -129,6 +129,11 @@ h3conv_status h3conv_fft_conv_bidir(const void *u, const float *f, const float *
  * Outputs must not overlap any input or each other.  B == 0 writes zeros
  * to df and dD.  Supported sizes: those of h3conv_fft_conv with
  * N <= H3CONV_MAX_FUSED_N.
+ * Precision with fp16 / bf16 activations: the transforms run in fp16 on the
+ * matrix cores; du scales every row on its own (as h3conv_fft_conv); df
+ * sums fp16 spectrum products in fp32, the two rows of a row pair sharing
+ * one exact power-of-two weight, so a row whose u-dy product is far below
+ * its partner's is carried to about 2^-11 of the partner's (not of its own).
  */
 h3conv_status h3conv_fft_conv_bwd(const void *u, const float *f, const float *D, const void *dy,
                                   void *du, float *df, float *dD, int64_t B, int64_t H, int64_t N,
