@@ -13,10 +13,11 @@
 // over those rows with one filter per row, and gate-out contracts them with
 // the queries back to channel-last [B, N, Dm].  The intermediates are bf16
 // for 16-bit activations (fp32 range, so no product overflows them) and fp32
-// for fp32 activations.  A tile covers one 128-byte line of steps of the
-// state rows of mh_td(dh) model channels (whole heads, at least 8 channels:
-// one 16-byte access); the gates' LDS is sized per launch for those
-// channels, and the shift of each key channel is computed once per tile.  Head dimension 1 runs the H3 mix kernels (the
+// for fp32 activations.  A tile covers the state rows of mh_td(dh) model
+// channels (whole heads, at least 8 channels: one 16-byte access) over one
+// 128-byte line of steps (fewer steps past 256 state rows); the gates' LDS
+// is sized per launch for those channels, and the shift of each key channel
+// is computed once per tile.  Head dimension 1 runs the H3 mix kernels (the
 // same formula).
 #include <hip/hip_runtime.h>
 
@@ -28,7 +29,9 @@ namespace h3c {
 // Model channels per gate tile: whole heads, 128 state rows (or 8 channels,
 // one 16-byte access, when the heads are wider), so that several
 // workgroups share a compute unit while their tiles load.
-__host__ __device__ constexpr int mh_td(int dh) { return 128 / dh > 8 ? 128 / dh : 8; }
+__host__ __device__ constexpr int mh_td(int dh) {
+    return dh > (128 / dh > 8 ? 128 / dh : 8) ? dh : (128 / dh > 8 ? 128 / dh : 8);
+}
 
 template <class MT>
 __device__ __forceinline__ MT mh_put(float x) {
@@ -44,20 +47,24 @@ __device__ __forceinline__ float mh_get(MT x) {
 // Steps per gate tile: one 128-byte line of a state row of the
 // intermediate (64 bf16 or 32 fp32 values), so every state-row access of
 // the gates moves whole lines.
+// (Tiles of more than 256 state rows, wide heads, take proportionally fewer
+// steps, so that the output gate's z tile stays within 64 KiB of LDS.)
 template <class MT>
-constexpr int mh_tt() { return 128 / (int)sizeof(MT); }
+__host__ __device__ constexpr int mh_tt(int dh) {
+    return mh_td(dh) * dh <= 256 ? 128 / (int)sizeof(MT) : 128 / (int)sizeof(MT) * 256 / (mh_td(dh) * dh);
+}
 
 // LDS of the gates, sized per launch for the tile's TD = mh_td(dh) model
 // channels (rows padded by one element against bank conflicts); activation
 // tiles are kept in the activation type.
 template <int IO, class MT>
 static size_t mh_in_lds(int dh) {
-    const int TD = mh_td(dh), TT = mh_tt<MT>();
+    const int TD = mh_td(dh), TT = mh_tt<MT>(dh);
     return (size_t)(2 * TT + 3) * (TD + 1) * sizeof(typename io_elem<IO>::T);
 }
 template <int IO, class MT>
 static size_t mh_out_lds(int dh) {
-    const int TD = mh_td(dh), TT = mh_tt<MT>();
+    const int TD = mh_td(dh), TT = mh_tt<MT>(dh);
     return (((size_t)TD * dh * (TT + 2) * sizeof(MT) + 15) & ~(size_t)15) +
            (size_t)TT * (TD + 1) * sizeof(typename io_elem<IO>::T);
 }
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(256) void k_h3mh_gate_in(const typename io_elem<IO>
                                                      const float *__restrict__ w, MT *__restrict__ mT, int N,
                                                      int Dm, int dh, int L, int vec) {
     using T = typename io_elem<IO>::T;
-    constexpr int TT = mh_tt<MT>();
+    const int TT = mh_tt<MT>(dh);
     const int TD = mh_td(dh);  // model channels of the tile (whole heads)
     const int P = TD + 1;
     extern __shared__ __attribute__((aligned(16))) unsigned char mh_lds[];
@@ -161,8 +168,8 @@ __global__ __launch_bounds__(256) void k_h3mh_gate_out(const typename io_elem<IO
                                                       typename io_elem<IO>::T *__restrict__ out, int N, int Dm,
                                                       int dh, int vec) {
     using T = typename io_elem<IO>::T;
-    constexpr int TT = mh_tt<MT>();
-    constexpr int PZ = TT + 2;  // (even, so a row of 16-bit values stays 4-byte aligned)
+    const int TT = mh_tt<MT>(dh);
+    const int PZ = TT + 2;  // (even, so a row of 16-bit values stays 4-byte aligned)
     const int TD = mh_td(dh), ROWS = TD * dh;
     const int PQ = TD + 1;
     extern __shared__ __attribute__((aligned(16))) unsigned char mh_lds[];
@@ -246,7 +253,7 @@ static hipError_t mh_run(const void *q, const void *k, const void *v, const floa
     const size_t one = h3_mix_mh_workspace(B, N, Dm, dh, IO) / 2;
     MT *mT = (MT *)ws;
     MT *zT = (MT *)((char *)ws + one);
-    const int TD = mh_td(dh), TT = mh_tt<MT>();
+    const int TD = mh_td(dh), TT = mh_tt<MT>(dh);
     const dim3 grid((Dm + TD - 1) / TD, (N + TT - 1) / TT, B);
     // 16-byte accesses along the contiguous dimension when sizes and
     // pointers allow (else element by element)

@@ -33,7 +33,7 @@ def _check(u, f, D, dy, got, io, label, rows=False):
 
 
 @pytest.mark.parametrize("io", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("N", [1, 7, 64, 100, 256, 1000, 2048, 3000, 8192])
+@pytest.mark.parametrize("N", [1, 7, 64, 100, 256, 500, 1000, 2048, 3000, 8192])
 def test_fft_conv_bwd_shapes(io, N):
     dev = device()
     for B in (1, 3):
@@ -108,3 +108,24 @@ def test_fft_conv_bwd_mixed_row_magnitudes(io, N):
     got = pkg.fft_conv_bwd(u.to(dev), f.to(dev), D.to(dev), dy.to(dev))
     torch.cuda.synchronize()
     _check(u, f, D, dy, got, io, label)
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("N", [500, 1000, 2000, 4000])
+def test_fft_conv_bwd_batch_sizes(io, N):
+    """Batches of one to several pairs of rounds of the 16-bit backward
+    kernels (u and dy rounds over the same row pairs, the sum carried from
+    pair to pair), odd and even."""
+    dev = device()
+    H = 2
+    for B in (2, 8, 9, 16, 17):
+        label = "fft_conv_bwd io=%s B=%d H=%d N=%d" % (io, B, H, N)
+        say(label)
+        g = wl.gen(9000 + 17 * N + B)
+        u = wl.normal((B, H, N), g, dtype=DT[io])
+        dy = wl.normal((B, H, N), g, dtype=DT[io])
+        f = wl.random_env_filter(H, N, g)
+        D = wl.normal((H,), g)
+        got = pkg.fft_conv_bwd(u.to(dev), f.to(dev), D.to(dev), dy.to(dev))
+        torch.cuda.synchronize()
+        _check(u, f, D, dy, got, io, label, rows=True)

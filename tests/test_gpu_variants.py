@@ -90,7 +90,7 @@ def _mh_inputs(B, N, Dm, dh, L, io, seed):
 
 
 @pytest.mark.parametrize("io", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("dh,Dm", [(1, 9), (2, 6), (4, 40), (8, 48)])
+@pytest.mark.parametrize("dh,Dm", [(1, 9), (2, 6), (4, 40), (8, 48), (16, 32), (32, 64)])
 @pytest.mark.parametrize("N", [77, 1000])
 def test_h3_mix_mh_shapes(io, dh, Dm, N):
     dev = device()
