@@ -26,11 +26,12 @@
 
 namespace h3c {
 
-// Model channels per gate tile: whole heads, 128 state rows (or 8 channels,
-// one 16-byte access, when the heads are wider), so that several
-// workgroups share a compute unit while their tiles load.
+// Model channels per gate tile: 128 state rows (at least 8 channels, one
+// 16-byte access, and at least one whole head), so that several workgroups
+// share a compute unit while their tiles load.
 __host__ __device__ constexpr int mh_td(int dh) {
-    return dh > (128 / dh > 8 ? 128 / dh : 8) ? dh : (128 / dh > 8 ? 128 / dh : 8);
+    const int c = 128 / dh > 8 ? 128 / dh : 8;  // 128 state rows, at least 8 channels
+    return c > dh ? c : dh;                      // and at least one whole head
 }
 
 template <class MT>
