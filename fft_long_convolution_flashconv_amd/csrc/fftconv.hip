@@ -205,8 +205,9 @@ static hipError_t launch_df(const void *u, const void *dy, float *df, float *dD,
                   dD, B, H, N);
 }
 
-// The same gradient on the matrix-core engine for 16-bit activations (2N >=
-// 512): see Engine::run_df.  One workgroup per channel; rounds alternate
+// The same gradient on the matrix-core engine for 16-bit activations (2N =
+// 4096, 8192; smaller sizes take the fused backward kernel): see
+// Engine::run_df.  One workgroup per channel; rounds alternate
 // between SIG row pairs of u and the same pairs of dy.  Rows are addressed
 // with 64-bit offsets, so no batch is split (the sum runs over all of it).
 // Waves per SIMD the gradient kernel's registers are set for: it holds a
@@ -310,12 +311,12 @@ template <int IO>
 static hipError_t df_dispatch(int log2m, const void *u, const void *dy, float *df, float *dD, int B, int H, int N,
                               hipStream_t s) {
     if constexpr (IO != IO_F32) {
+        // (2N = 1024, 2048: the fused backward kernel; 2N = 16384: the fp32
+        //  engine, the sum would not fit the registers)
         switch (log2m) {
-            case 10: return launch_df_mfma<10, IO>(u, dy, df, dD, B, H, N, s);
-            case 11: return launch_df_mfma<11, IO>(u, dy, df, dD, B, H, N, s);
             case 12: return launch_df_mfma<12, IO>(u, dy, df, dD, B, H, N, s);
             case 13: return launch_df_mfma<13, IO>(u, dy, df, dD, B, H, N, s);
-            default: break;  // 2N = 16384: the fp32 engine (the sum would not fit the registers)
+            default: break;
         }
     }
     switch (log2m) {
