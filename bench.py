@@ -394,6 +394,15 @@ def main():
     }
     del case
     torch.cuda.empty_cache()
+    # side note: the same call with one input set, which stays resident in
+    # the 256 MB Infinity Cache and L2 between calls (the line's value and
+    # roofline are the rotated, cache-flushed figures above)
+    warm = Case(w, dev, rotate=False)
+    _, warm_ms = time_case(warm, a.steps, a.warmup)
+    out["warm"] = {"kernel_mean_us": warm_ms * 1e3, "GB_s": nbytes / (warm_ms * 1e-3) / 1e9,
+                   "note": "one input set, resident in the Infinity Cache / L2 between calls"}
+    del warm
+    torch.cuda.empty_cache()
     if not a.no_secondary:
         sec = {}
         for name in ("conv_8k", "state_64k", "h3_mix_2k", "conv_1k_bwd", "decode_125m", "h3_mix_mh_1k", "bidir_1k"):
