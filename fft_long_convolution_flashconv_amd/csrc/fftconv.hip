@@ -137,17 +137,20 @@ __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_h3_mix(
 // Backward pass of the causal convolution with residual (the paperlayer.ai
 // summary of "Hungry Hungry Hippos", Appendix C.1: the gradients of u, f and
 // D are correlations computed through the same zero-padded transforms, D dy
-// entering du).  Two kernels per call:
-//   du[b] = IDFT(DY_b conj(F))[:N] with F = DFT(f + D delta): the forward
-//           convolution kernels with the conjugated filter spectrum (CORR),
-//           the correlation of dy with the filter, D dy included by tap 0;
+// entering du):
+//   du[b] = IDFT(DY_b conj(F))[:N] with F = DFT(f + D delta): the correlation
+//           of dy with the filter, D dy included by tap 0;
 //   df    = Re IDFT(sum_pairs conj(Z_u) Z_dy)[:N], Z = row 2s + i row 2s+1:
 //           the real part of the correlation of the complex pair signals is
-//           the sum of the two rows' correlations of u with dy (k_fft_corr_df
-//           below, one workgroup per channel, fp32 transforms, the spectrum
+//           the sum of the two rows' correlations of u with dy (the spectrum
 //           summed over the batch and inverted once);
 //   dD    = df[0] (the gradient of tap 0, which D shares).
 // The zero padding to 2N keeps every correlation lag in [0, N) free of wrap.
+// Kernels: 16-bit activations at 2N = 1024, 2048 run all three in one
+// (k_fft_bwd_mfma); at 2N = 4096, 8192 du runs as the convolution kernel
+// with the conjugated filter spectrum (CORR) and df, dD as k_fft_df_mfma;
+// fp32 activations and the remaining sizes take CORR and k_fft_corr_df
+// below (one workgroup per channel, fp32 transforms).
 template <int LOG2M, int IO>
 __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_fft_corr_df(
     const typename io_elem<IO>::T *__restrict__ u, const typename io_elem<IO>::T *__restrict__ dy,
