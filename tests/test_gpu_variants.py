@@ -106,6 +106,23 @@ def test_h3_mix_mh_shapes(io, dh, Dm, N):
     assert np.isfinite(to_np(out)).all() and err <= TOL[io], (label, err)
 
 
+@pytest.mark.parametrize("io", ["f32", "f16"])
+@pytest.mark.parametrize("L", [1, 2, 3])
+def test_h3_mix_mh_shift_taps(io, L):
+    """Shift filters of 1 to 3 taps (the other tests use 4)."""
+    dev = device()
+    B, N, Dm, dh = 2, 300, 16, 4
+    label = "h3_mix_mh io=%s B=%d N=%d Dm=%d dh=%d L=%d" % (io, B, N, Dm, dh, L)
+    say(label)
+    q, k, v, w, f, D = _mh_inputs(B, N, Dm, dh, L, io, seed=400 + L)
+    out = pkg.h3_mix_mh(*(t.to(dev) for t in (q, k, v, w, f, D)), dh)
+    torch.cuda.synchronize()
+    ref = oracle.h3_mix_mh(q, k, v, w, f, D, dh)
+    err = rel_l2(to_np(out), ref)
+    say("  rel_l2=%.3e" % err)
+    assert np.isfinite(to_np(out)).all() and err <= TOL[io], (label, err)
+
+
 def test_h3_mix_mh_head_dim_one_matches_h3_mix():
     dev = device()
     B, N, Dm, L = 2, 600, 136, 4
