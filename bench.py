@@ -29,6 +29,7 @@ analogue of the pages' cuFFT baseline), are reported under "secondary" and
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -190,19 +191,55 @@ def time_case(case: Case, steps: int, warmup: int):
     stream bracket the whole timed region (launches queue back to back, so
     their elapsed time over `steps` is the average launch duration); the wall
     clock is bracketed by device synchronisations."""
-    for i in range(warmup):
-        case.step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
-        case.step(warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # no garbage-collection pause of the launching thread inside the timed
+    # steps (it would show as the GPU idling between launches); collected
+    # before the warm-up, so that no idle gap lets the clocks drop between the
+    # warm-up and the timed steps
+    gc.collect()
+    gc.disable()
+    try:
+        for i in range(warmup):
+            case.step(i)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            case.step(warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        gc.enable()
     return wall, e0.elapsed_time(e1) / steps
+
+
+def time_case_batches(case: Case, steps: int, warmup: int, nb: int = 5):
+    """`steps` steps in nb batches, each bracketed by HIP events on the launch
+    stream: the mean launch duration of every batch (a one-off stall of the
+    box shows in one batch, not in the median)."""
+    gc.collect()
+    gc.disable()
+    try:
+        for i in range(warmup):
+            case.step(i)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        per = max(1, steps // nb)
+        out, k = [], warmup
+        for _ in range(nb):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(per):
+                case.step(k)
+                k += 1
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / per)
+    finally:
+        gc.enable()
+    return out
 
 
 def cpu_model() -> str:
@@ -288,13 +325,28 @@ def torch_fftconv(u, f, D):
     return (y + uf * D[:, None]).to(u.dtype)
 
 
+def torch_fftconv_bwd(u, f, D, dy):
+    """Unfused backward of torch_fftconv with torch.fft: du = IDFT(DY conj(F))
+    [:N] + D dy, df = IDFT(sum_b conj(U_b) DY_b)[:N], dD = df[..., 0]; in
+    fp32.  Timing comparison only."""
+    N = u.shape[-1]
+    U = torch.fft.rfft(u.float(), n=2 * N)
+    DY = torch.fft.rfft(dy.float(), n=2 * N)
+    F = torch.fft.rfft(f, n=2 * N)
+    du = torch.fft.irfft(DY * F.conj(), n=2 * N)[..., :N] + dy.float() * D[:, None]
+    df = torch.fft.irfft((U.conj() * DY).sum(0), n=2 * N)[..., :N]
+    return du.to(u.dtype), df, df[..., 0]
+
+
 def sweep(dev, steps: int, warmup: int) -> list:
     """Sequence-length sweep at the H3-125M width (B=8, H=768, fp16, 64
     modes): fused fft_conv for N <= 16384, state passing (T = 8192) at 16384
-    and above, each timed beside torch_fftconv on the same inputs."""
+    and above, and the backward pass (fft_conv_bwd) for N <= 8192, each
+    timed beside its unfused torch.fft counterpart on the same inputs."""
     out = []
     pts = [(N, "fft_conv") for N in (256, 512, 1024, 2048, 4096, 8192, 16384)] + \
-          [(16384, "state_pass"), (32768, "state_pass")]
+          [(16384, "state_pass"), (32768, "state_pass")] + \
+          [(N, "fft_conv_bwd") for N in (256, 512, 1024, 2048, 4096, 8192)]
     for i, (N, kind) in enumerate(pts):
         w = wl.Workload("sweep_%d" % N, kind, "f16", B=8, H=768, N=N, T=8192 if kind == "state_pass" else 0,
                         seed=100 + i)
@@ -303,15 +355,24 @@ def sweep(dev, steps: int, warmup: int) -> list:
         s0 = c.sets[0]
         if "f" not in s0:
             s0["f"] = pkg.ssm_filter(s0["A"], s0["Bm"], s0["C"], s0["dt"], N)
-        for _ in range(warmup):
-            torch_fftconv(s0["u"], s0["f"], s0["D"])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            torch_fftconv(s0["u"], s0["f"], s0["D"])
-        e1.record()
-        torch.cuda.synchronize()
+        if kind == "fft_conv_bwd":
+            ref = lambda: torch_fftconv_bwd(s0["u"], s0["f"], s0["D"], s0["dy"])
+        else:
+            ref = lambda: torch_fftconv(s0["u"], s0["f"], s0["D"])
+        gc.collect()
+        gc.disable()
+        try:
+            for _ in range(warmup):
+                ref()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                ref()
+            e1.record()
+            torch.cuda.synchronize()
+        finally:
+            gc.enable()
         t_ms = e0.elapsed_time(e1) / steps
         nb = algorithmic_bytes(w)
         out.append({"N": N, "path": kind, "us": m_ms * 1e3, "elements_per_s": w.elements / (m_ms * 1e-3),
@@ -410,10 +471,12 @@ def main():
                 continue
             ww = wl.WORKLOADS[name]
             c = Case(ww, dev)
-            _, m_ms = time_case(c, max(10, a.steps), max(3, a.warmup))
+            batches = time_case_batches(c, max(10, a.steps), max(3, a.warmup))
+            m_ms = sorted(batches)[len(batches) // 2]
             nb = algorithmic_bytes(ww)
             pr = profiled(name)
             sec[name] = {"elements_per_s": ww.elements / (m_ms * 1e-3), "mean_us": m_ms * 1e3,
+                         "batches_us": [x * 1e3 for x in batches],
                          "algorithmic_bytes": nb, "GB_s": nb / (m_ms * 1e-3) / 1e9,
                          "frac_hbm": nb / (m_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "sets": c.nsets,
                          "traffic_per_step_kernel": pr["traffic"], "profiled_kernel": pr["kernel"],
