@@ -146,9 +146,10 @@ __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_h3_mix(
 //           summed over the batch and inverted once);
 //   dD    = df[0] (the gradient of tap 0, which D shares).
 // The zero padding to 2N keeps every correlation lag in [0, N) free of wrap.
-// Kernels: 16-bit activations at 2N = 1024, 2048 run all three in one
-// (k_fft_bwd_mfma); at 2N = 4096, 8192 du runs as the convolution kernel
-// with the conjugated filter spectrum (CORR) and df, dD as k_fft_df_mfma;
+// Kernels: 16-bit activations at 2N = 512, 1024, 2048 run all three in one
+// (k_fft_bwd_mfma); at 2N = 4096, 8192, 16384 du runs as the convolution
+// kernel with the conjugated filter spectrum (CORR) and df, dD as
+// k_fft_df_mfma;
 // fp32 activations and the remaining sizes take CORR and k_fft_corr_df
 // below (one workgroup per channel, fp32 transforms).
 template <int LOG2M, int IO>
@@ -217,6 +218,14 @@ static hipError_t launch_df(const void *u, const void *dy, float *df, float *dD,
 // round of last-pass values and the fp32 sum besides the transform's own,
 // so it runs fewer workgroups per compute unit than the convolution.
 template <int LOG2M> struct DfOcc { static constexpr int WPE = 4; };
+// 2N = 512: a two-wave workgroup carries eight signals a round, so each lane
+// holds twice the values of the larger sizes (166 registers, no spills at
+// three waves per SIMD; 64 spilled at four)
+template <> struct DfOcc<9> { static constexpr int WPE = 3; };
+// 2N = 16384: the sum alone is 64 registers a lane; at two waves per SIMD
+// (one workgroup per compute unit) the kernel holds 196 without spilling,
+// where four waves per SIMD would spill 68
+template <> struct DfOcc<14> { static constexpr int WPE = 2; };
 
 template <int LOG2M, int IO>
 __global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(DfOcc<LOG2M>::WPE))) void k_fft_df_mfma(
@@ -314,11 +323,11 @@ template <int IO>
 static hipError_t df_dispatch(int log2m, const void *u, const void *dy, float *df, float *dD, int B, int H, int N,
                               hipStream_t s) {
     if constexpr (IO != IO_F32) {
-        // (2N = 1024, 2048: the fused backward kernel; 2N = 16384: the fp32
-        //  engine, the sum would not fit the registers)
+        // (2N = 512, 1024, 2048: the fused backward kernel)
         switch (log2m) {
             case 12: return launch_df_mfma<12, IO>(u, dy, df, dD, B, H, N, s);
             case 13: return launch_df_mfma<13, IO>(u, dy, df, dD, B, H, N, s);
+            case 14: return launch_df_mfma<14, IO>(u, dy, df, dD, B, H, N, s);
             default: break;
         }
     }
@@ -604,6 +613,7 @@ static hipError_t bwd_fused(int log2m, const void *u, const float *f, const floa
                             float *df, float *dD, int B, int H, int N, hipStream_t s, bool *done) {
     *done = true;
     switch (log2m) {
+        case 9: return launch_bwd_mfma<9, IO>(u, f, D, dy, du, df, dD, B, H, N, s);
         case 10: return launch_bwd_mfma<10, IO>(u, f, D, dy, du, df, dD, B, H, N, s);
         case 11: return launch_bwd_mfma<11, IO>(u, f, D, dy, du, df, dD, B, H, N, s);
         // (2N = 4096, 8192: the registers of the fused kernel would spill at
@@ -617,7 +627,7 @@ hipError_t launch_fft_conv_bwd(const void *u, const float *f, const float *D, co
     const int l = fused_log2m(N);
     hipError_t e;
     bool done = false;
-    // 16-bit activations with 2N = 1024, 2048: one kernel for all three
+    // 16-bit activations with 2N = 512, 1024, 2048: one kernel for all three
     // gradients; otherwise the correlation kernel for du, then df and dD
     if (io == IO_F16) e = bwd_fused<IO_F16>(l, u, f, D, dy, du, df, dD, B, H, N, s, &done);
     else if (io == IO_BF16) e = bwd_fused<IO_BF16>(l, u, f, D, dy, du, df, dD, B, H, N, s, &done);

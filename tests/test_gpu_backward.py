@@ -88,7 +88,7 @@ def test_fft_conv_bwd_empty_batch():
 
 
 @pytest.mark.parametrize("io", ["f16", "bf16"])
-@pytest.mark.parametrize("N", [500, 1000, 2000, 3000])
+@pytest.mark.parametrize("N", [200, 500, 1000, 2000, 3000])
 def test_fft_conv_bwd_mixed_row_magnitudes(io, N):
     """Rows of u and dy of very different magnitudes, crossed so that every
     row's correlation is of the same size (each pair's two rows must keep
@@ -111,7 +111,7 @@ def test_fft_conv_bwd_mixed_row_magnitudes(io, N):
 
 
 @pytest.mark.parametrize("io", ["f16", "bf16"])
-@pytest.mark.parametrize("N", [500, 1000, 2000, 4000])
+@pytest.mark.parametrize("N", [200, 500, 1000, 2000, 4000, 8000])
 def test_fft_conv_bwd_batch_sizes(io, N):
     """Batches of one to several pairs of rounds of the 16-bit backward
     kernels (u and dy rounds over the same row pairs, the sum carried from
