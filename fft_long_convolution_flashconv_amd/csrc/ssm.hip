@@ -208,24 +208,17 @@ hipError_t launch_ssm_filter(const float *A, const float *Bm, const float *C, co
 
 // ---------------------------------------------------------------- state passing
 
-// Workspace layout (256-byte aligned blocks), by path.  Both start with
+// Workspace layout (256-byte aligned blocks), by path.  fp32 activations
+// (FFT chunk convolutions, vector-ALU projections):
 //   fT  [H, T]            chunk filter with D folded into tap 0            fp32
-// fp32 activations (vector-ALU projections) then hold
 //   E   [H, S, 65]        Abar^l, l = 0..64                                complex
 //   G   [H, S, T/64 + 1]  Abar^(64 i), i = 0..T/64                         complex
 //   sc  [B, H, C, 64]     per-chunk state contributions                    complex
-// and 16-bit activations (matrix-core projections, modes padded to 64)
-//   Et  [H, 128, 64]      row 2j+p, column l: part p of Abar_j^(63-l)      fp16
-//   Rt  [H, 64, 128]      row l, column 2j+p: 2 Re / -2 Im of C_j Abar_j^(l+1)  fp16
-//   Pc  [H, 64, 8]        Bbar_j Abar_j^(1024 (NCT-1-ih))                  complex
-//   Qc  [H, 64, 16]       Abar_j^(64 (TL-1-il)), zero for il >= TL         complex
-//   Px  [H, 64, 8]        Abar_j^(1024 ih)                                 complex
-//   Qx  [H, 64, 16]       Abar_j^(64 il), zero for il >= TL                complex
-//   aT  [H, 64]           Abar_j^T                                         complex
-// with T2 = T/64 columns i = 16 ih + il, NCT = ceil(T2/16), TL = min(T2, 16).
-// The workspace size the API reports is the larger of the two.
+// 16-bit activations (block state passing): fb, Eb, Rb, ab, ak, sb as
+// described above k_spb_params.  The workspace size the API reports is the
+// larger of the two.
 struct SpLayout {
-    size_t fT, E, G, sc, Et, Rt, Pc, Qc, Px, Qx, aT, total;
+    size_t fT, E, G, sc, fb, Eb, Rb, ab, ak, sb, total;
 };
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -234,19 +227,18 @@ static SpLayout sp_layout(int64_t B, int64_t H, int64_t N, int64_t S, int64_t T,
     SpLayout L{};
     const int64_t C = N / T, T2 = T / 64;
     size_t o = 0;
-    L.fT = o; o += al256((size_t)H * T * 4);
     if (f32) {
+        L.fT = o; o += al256((size_t)H * T * 4);
         L.E = o; o += al256((size_t)H * S * 65 * 8);
         L.G = o; o += al256((size_t)H * S * (T2 + 1) * 8);
         L.sc = o; o += al256((size_t)B * H * C * 64 * 8);
     } else {
-        L.Et = o; o += al256((size_t)H * 128 * 64 * 2);
-        L.Rt = o; o += al256((size_t)H * 64 * 128 * 2);
-        L.Pc = o; o += al256((size_t)H * 64 * 8 * 8);
-        L.Qc = o; o += al256((size_t)H * 64 * 16 * 8);
-        L.Px = o; o += al256((size_t)H * 64 * 8 * 8);
-        L.Qx = o; o += al256((size_t)H * 64 * 16 * 8);
-        L.aT = o; o += al256((size_t)H * 64 * 8);
+        L.fb = o; o += al256((size_t)H * 64 * 4);
+        L.Eb = o; o += al256((size_t)H * 128 * 64 * 2);
+        L.Rb = o; o += al256((size_t)H * 64 * 128 * 2);
+        L.ab = o; o += al256((size_t)H * 64 * 8);
+        L.ak = o; o += al256((size_t)H * 64 * 8);
+        L.sb = o; o += al256((size_t)H * 2 * 4);
     }
     L.total = o;
     return L;
@@ -448,443 +440,354 @@ __device__ __forceinline__ uint16_t f16bits(double x) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// The tables of channel h from its powers pw (ssm_powers), by the workgroup's
-// NT threads: eight runs of powers per mode (the modes past S are written as
-// zeros):
-//   runs 0..3  Abar^p, p = 16 q .. 16 q + 15 -> Et (l = 63 - p), Rt (l = p - 1)
-//   run 4      Abar^64                      -> Rt (l = 63)
-//   run 5      Abar^(64 k), k < 16         -> Qx[k], Qc[TL - 1 - k]
-//   run 6      Abar^(1024 k), k < 8        -> Px[k], Pc[NCT - 1 - k] (times Bbar)
-//   run 7      Abar^T                      -> aT
-constexpr int SP_EST = 66;                                // Et row stride in LDS (16-bit units)
-constexpr int SP_TAB_LDS = 128 * SP_EST * 2 + 64 * 128 * 2;  // bytes: Et, then Rt
+// ---------------------------------------------------------------- block state passing (16-bit)
+//
+// The state is passed at every block of Q = 64 samples, a refinement of any
+// chunk grid T (64 <= T, T | N) the caller names, so output and final state
+// are those of the chunked form for every such T.  For block c of a row (the
+// 0-based offset t < 64 inside it),
+//   y[64 c + t] = sum_{k <= t} f_{t-k} u[64 c + k] + D u[64 c + t]
+//               + 2 Re sum_j C_j Abar_j^(t+1) x_{c-1,j}
+//   x_c = Abar^64 x_{c-1} + s_c,   s_{c,j} = sum_k Abar_j^(63-k) Bbar_j u[64 c + k]
+// i.e. the pages' state passing with chunks of 64: the chunk's own
+// convolution is a 64 x 64 lower-triangular Toeplitz product (f_0 .. f_63,
+// D folded into f_0), the contribution is M_ux u_c and the correction the
+// projection of the carried state; the three are dense products on the
+// matrix cores (16x16x32, fp32 accumulate) over the 16 blocks a wave holds at
+// once, and only the state recurrence itself, x_c = Abar^64 x_{c-1} + s_c,
+// runs on the vector ALUs in fp32.
+//
+// Workspace of 16-bit activations (per channel h):
+//   fb  [H, 64]       taps f_0 .. f_63, D folded into f_0                       fp32
+//   Eb  [H, 128, 64]  row 2j+p, column k: part p of Abar_j^(63-k) Bbar_j / sB  fp16
+//   Rb  [H, 64, 128]  row t, columns 2j, 2j+1: 2 Re, -2 Im of C_j Abar_j^(t+1) / sC   fp16
+//   ab  [H, 64]       Abar_j^64                                                 complex
+//   ak  [H, 64]       Abar_j^1024                                               complex
+//   sb  [H, 2]        sB, sC: powers of two with |Bbar_j| < sB and 2 |C_j| < sC fp32
+// (modes j >= S are zero in every table).
 
-template <int NT>
-__device__ __forceinline__ void sp_tables_body(const float *__restrict__ Bm, const float *__restrict__ Cc, double dth,
-                               uint16_t *__restrict__ Et, uint16_t *__restrict__ Rt, cf *__restrict__ Pc,
-                               cf *__restrict__ Qc, cf *__restrict__ Px, cf *__restrict__ Qx, cf *__restrict__ aT,
-                               int S, int T, int h, const double2 (*pw)[64], uint16_t *lds) {
-    const int T2 = T / 64, NCT = (T2 + 15) / 16, TL = T2 < 16 ? T2 : 16;
-    // Et and Rt are built in LDS and written out with 16-byte stores.  The
-    // lanes of a wave take 64 modes of one run, so the runs' different code
-    // paths never diverge within a wave; Et rows are padded to 66 entries so
-    // those lanes' writes spread over the banks.
-    constexpr int EST = SP_EST;
-    uint16_t *const Eh = lds, *const Rh = lds + 128 * EST;
-    // cnt powers st^k times p, k < cnt
-    auto run_ = [&](double2 p, double2 st, int cnt, auto &&emit) {
-        for (int k = 0; k < cnt; ++k) {
-            emit(k, p.x, p.y);
-            p = dmul(p, st);
-        }
-    };
-    for (int e = threadIdx.x; e < 64 * 8; e += NT) {
-        const int j = e & 63, run = e >> 6;
+// The tables of one channel per workgroup of 8 waves.
+__global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A, const float *__restrict__ Bm,
+                                                   const float *__restrict__ Cc, const float *__restrict__ dt,
+                                                   const float *__restrict__ D, float *__restrict__ fb,
+                                                   uint16_t *__restrict__ Eb, uint16_t *__restrict__ Rb,
+                                                   cf *__restrict__ ab, cf *__restrict__ ak, float *__restrict__ sb,
+                                                   int S) {
+    static_assert(2 * 128 * 64 * 2 <= FILT_LDS * 4, "the tables fit the filter's LDS");
+    __shared__ __attribute__((aligned(16))) float lds[FILT_LDS];
+    __shared__ double2 pw[4][64];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const double dth = (double)dt[h];
+    ssm_powers(A, dth, S, h, pw);
+    __syncthreads();
+    ssm_filter_body(Bm, Cc, dth, D, fb, S, 64, 64, h, pw, lds);
+    __syncthreads();  // (the filter's operands have been read)
+    // scales, the same in every thread
+    double mb = 0.0, mc = 0.0;
+    for (int j = 0; j < S; ++j) {
+        const float *bj = Bm + ((size_t)h * S + j) * 2, *cj = Cc + ((size_t)h * S + j) * 2;
+        mb = fmax(mb, fabs(dth) * sqrt((double)bj[0] * bj[0] + (double)bj[1] * bj[1]));
+        mc = fmax(mc, 2.0 * sqrt((double)cj[0] * cj[0] + (double)cj[1] * cj[1]));
+    }
+    int eb = 0, ec = 0;
+    if (mb > 0.0) (void)frexp(mb, &eb);
+    if (mc > 0.0) (void)frexp(mc, &ec);
+    const double sB = ldexp(1.0, eb), sC = ldexp(1.0, ec);
+    uint16_t *const Eh = (uint16_t *)lds, *const Rh = Eh + 128 * 64;
+    // runs of 16 powers per (mode, quarter): Abar^(16 q + k); q = 4 is Abar^64
+    for (int e = tid; e < 64 * 5; e += 512) {
+        const int j = e & 63, q = e >> 6;
         const bool on = j < S;
         double br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
         if (on) {
             const size_t o = ((size_t)h * S + j) * 2;
-            br = dth * (double)Bm[o];
-            bi = dth * (double)Bm[o + 1];
-            cr = (double)Cc[o];
-            ci = (double)Cc[o + 1];
+            br = dth * (double)Bm[o] / sB;
+            bi = dth * (double)Bm[o + 1] / sB;
+            cr = (double)Cc[o] / sC;
+            ci = (double)Cc[o + 1] / sC;
         }
-        // modes past S: all-zero tables (the power run is evaluated and masked)
-        const double on_d = on ? 1.0 : 0.0;
-        auto et_rt = [&](int p, double pr, double pi) {
-            pr *= on_d;
-            pi *= on_d;
-            if (p <= 63) {
-                Eh[(2 * j) * EST + (63 - p)] = f16bits(pr);
-                Eh[(2 * j + 1) * EST + (63 - p)] = f16bits(pi);
+        double2 p = double2{1.0, 0.0};
+        for (int r = 0; r < q; ++r) p = dmul(p, pw[1][j]);
+        const int cnt = q < 4 ? 16 : 1;
+        for (int k = 0; k < cnt; ++k) {
+            const int pp = 16 * q + k;
+            const double pr = on ? p.x : 0.0, pi = on ? p.y : 0.0;
+            if (pp <= 63) {
+                const double zr = pr * br - pi * bi, zi = pr * bi + pi * br;
+                Eh[(2 * j) * 64 + 63 - pp] = f16bits(zr);
+                Eh[(2 * j + 1) * 64 + 63 - pp] = f16bits(zi);
             }
-            if (p >= 1) {
-                const int l = p - 1;
+            if (pp >= 1) {
                 const double zr = cr * pr - ci * pi, zi = cr * pi + ci * pr;
-                Rh[l * 128 + 2 * j] = f16bits(2.0 * zr);
-                Rh[l * 128 + 2 * j + 1] = f16bits(-2.0 * zi);
+                Rh[(pp - 1) * 128 + 2 * j] = f16bits(2.0 * zr);
+                Rh[(pp - 1) * 128 + 2 * j + 1] = f16bits(-2.0 * zi);
             }
-        };
-        const double2 one = double2{1.0, 0.0};
-        if (run < 4) {
-            double2 p = one;
-            for (int r = 0; r < run; ++r) p = dmul(p, pw[1][j]);
-            run_(p, pw[0][j], 16, [&](int k, double pr, double pi) { et_rt(16 * run + k, pr, pi); });
-        } else if (run == 4) {
-            et_rt(64, pw[2][j].x, pw[2][j].y);
-        } else if (run == 5) {
-            run_(one, pw[2][j], 16, [&](int k, double pr, double pi) {
-                const bool ok = on && k < TL;
-                const cf v = ok ? mk((float)pr, (float)pi) : mk(0.f, 0.f);
-                Qx[((size_t)h * 64 + j) * 16 + k] = v;
-                Qc[((size_t)h * 64 + j) * 16 + (k < TL ? TL - 1 - k : k)] = v;
-            });
-        } else if (run == 6) {
-            run_(one, pw[3][j], 8, [&](int k, double pr, double pi) {
-                const bool ok = on && k < NCT;
-                Px[((size_t)h * 64 + j) * 8 + k] = ok ? mk((float)pr, (float)pi) : mk(0.f, 0.f);
-                Pc[((size_t)h * 64 + j) * 8 + (k < NCT ? NCT - 1 - k : k)] =
-                    ok ? mk((float)(br * pr - bi * pi), (float)(br * pi + bi * pr)) : mk(0.f, 0.f);
-            });
-        } else {
-            // Abar^T, T = 64 2^m: squarings of Abar^64
-            double2 p = pw[2][j];
-            for (int t = 64; t < T; t <<= 1) p = dmul(p, p);
-            aT[(size_t)h * 64 + j] = on ? mk((float)p.x, (float)p.y) : mk(0.f, 0.f);
+            if (pp == 64) ab[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
+            p = dmul(p, pw[0][j]);
         }
+    }
+    if (tid < 64) ak[(size_t)h * 64 + tid] = tid < S ? mk((float)pw[3][tid].x, (float)pw[3][tid].y) : mk(0.f, 0.f);
+    if (tid == 0) {
+        sb[2 * h] = (float)sB;
+        sb[2 * h + 1] = (float)sC;
     }
     __syncthreads();
     using u32x4 = mf::u32x4;
-    u32x4 *eo = (u32x4 *)(Et + (size_t)h * 128 * 64), *ro = (u32x4 *)(Rt + (size_t)h * 64 * 128);
-    for (int e = threadIdx.x; e < 128 * 64 / 8; e += NT) {
-        const uint32_t *er = (const uint32_t *)(Eh + (e >> 3) * EST + 8 * (e & 7));
-        eo[e] = u32x4{er[0], er[1], er[2], er[3]};
+    u32x4 *eo = (u32x4 *)(Eb + (size_t)h * 8192), *ro = (u32x4 *)(Rb + (size_t)h * 8192);
+    for (int e = tid; e < 1024; e += 512) {
+        eo[e] = ((const u32x4 *)Eh)[e];
         ro[e] = ((const u32x4 *)Rh)[e];
     }
 }
 
-// The per-channel parameters of the 16-bit state passing in one launch, one
-// workgroup of 8 waves per channel: the powers, the chunk filter (with D
-// folded into tap 0) and then, in the same LDS, the projection tables.
-__global__ __launch_bounds__(512) void k_sp_params(const float *__restrict__ A, const float *__restrict__ Bm,
-                                                  const float *__restrict__ Cc, const float *__restrict__ dt,
-                                                  const float *__restrict__ D, float *__restrict__ fT,
-                                                  uint16_t *__restrict__ Et, uint16_t *__restrict__ Rt,
-                                                  cf *__restrict__ Pc, cf *__restrict__ Qc, cf *__restrict__ Px,
-                                                  cf *__restrict__ Qx, cf *__restrict__ aT, int S, int T) {
-    static_assert(SP_TAB_LDS <= FILT_LDS * 4, "the tables fit the filter's LDS");
-    __shared__ __attribute__((aligned(16))) float lds[FILT_LDS];
-    __shared__ double2 pw[4][64];
-    const int h = blockIdx.x;
-    const double dth = (double)dt[h];
-    ssm_powers(A, dth, S, h, pw);
-    __syncthreads();
-    ssm_filter_body(Bm, Cc, dth, D, fT, S, (int64_t)T, (int64_t)T, h, pw, lds);
-    __syncthreads();  // (the filter's operands have been read)
-    sp_tables_body<512>(Bm, Cc, dth, Et, Rt, Pc, Qc, Px, Qx, aT, S, T, h, pw, (uint16_t *)lds);
+__device__ __forceinline__ mf::f4 mfma16(mf::half8 a, mf::half8 b, mf::f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-
-__device__ __forceinline__ float sp_wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-// Both projections of one (batch row b, channel h), walking its chunks in
-// order; every wave carries its own copy of the state (lane l: mode l), so
-// the state update needs no barrier of its own.  Eight waves; for each chunk
-// c (the correction goes first, so that its stores are issued before the
-// next chunk's loads and are long complete when those are waited for):
-//   1. the chunk's activations are staged in LDS as fp16 (bf16 inputs scaled
-//      by a power of two into fp16 range);
-//   2. contribution: wave w owns modes 8w .. 8w+7 (Et row tile w) and all
-//      column tiles, so its Et operands stay in registers;
-//   3. correction with the state carried into the chunk,
-//        y[64 i + l] += 2 Re sum_j (C_j Abar_j^(l+1) x_j) Abar_j^(64 i):
-//      the power table G = Abar^(64 i) is the B operand, built once in LDS;
-//      wave w owns output rows l = 16 (w % 4) .. +15 and column tiles
-//      4 (w / 4) .. +3, scales its Rt operands (in registers) by the state,
-//      and updates y in place;
-//   4. x <- Abar^T x + s, in every wave at the top of the next chunk (the
-//      contributions s are complete at the chunk's last barrier).
-// Two barriers per chunk: after staging, and after the contribution.  The
-// next chunk's activations are loaded while the current one is used.
-constexpr int SP_USTR = 72;   // staged chunk: 64 samples per row i, padded (bank spread)
-constexpr int SP_XSTR = 136;  // G operand: 128 (mode, part) entries per column i, padded
-
+// two outputs rounded to the activation type (nearest even), packed
 template <int IO>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_sp_proj_mfma(const typename io_elem<IO>::T *__restrict__ u,
-                                                     typename io_elem<IO>::T *__restrict__ y,
-                                                     const uint16_t *__restrict__ Et,
-                                                     const uint16_t *__restrict__ Rt,
-                                                     const cf *__restrict__ Pc, const cf *__restrict__ Qc,
-                                                     const cf *__restrict__ Px, const cf *__restrict__ Qx,
-                                                     const cf *__restrict__ aT, const float *__restrict__ x_in,
-                                                     float *__restrict__ x_out, int H, int64_t N, int S, int T) {
+__device__ __forceinline__ uint32_t spb_pk(float a, float b) {
+    if constexpr (IO == IO_BF16) {
+        const mf::f2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, mf::bf2));
+    } else {
+        return mf::pk(a, b);
+    }
+}
+// orders this lane's LDS writes before the reads of the other lanes of its
+// wave that follow (LDS requests of one wave complete in order)
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int SPB_ES = 72;   // Eb rows in LDS (16-bit units; 144 bytes apart spreads a tile's 16 rows over the banks)
+constexpr int SPB_SS = 66;   // contributions of one block in LDS (complex; 64 modes + pad)
+constexpr int SPB_XS = 136;  // states entering one block in LDS (fp16; 128 + pad)
+
+// One workgroup of four waves per (batch row b, channel h).  A step takes 64
+// blocks (4096 samples); wave w holds blocks 16 w .. 16 w + 15 of it, the
+// 16 columns of its matrix-core products (the B operand, read straight from
+// HBM: lane (n, g) loads samples 32 ks + 8 g .. + 7 of block n).  Per step:
+//   1. contributions S[(j, part)][n] = Eb . U (8 row tiles) -> LDS, and the
+//      blocks' own convolutions Y = L . U (the Toeplitz tiles depend only on
+//      the tile's distance from the diagonal: 4 distinct tiles, 6 products);
+//   2. lane = mode: the wave's blocks scanned from a zero state (end state
+//      L_w, and P_w = Abar^(64 n_w) for its n_w valid blocks) -> LDS;
+//   3. one barrier; every wave folds the four (P_w, L_w) in order into the
+//      state carried between steps (the same in every wave), and takes the
+//      state entering its own first block;
+//   4. the scan again from that state gives the state entering each block,
+//      scaled by a power of two into fp16 range -> LDS (transposed to the
+//      B-operand layout), and Y += Rb . X (the correction);
+//   5. y stored once, rounded once.
+template <int IO>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_sp_block(
+    const typename io_elem<IO>::T *__restrict__ u, typename io_elem<IO>::T *__restrict__ y,
+    const float *__restrict__ fb, const uint16_t *__restrict__ Eb, const uint16_t *__restrict__ Rb,
+    const cf *__restrict__ ab, const cf *__restrict__ ak, const float *__restrict__ sb,
+    const float *__restrict__ x_in, float *__restrict__ x_out, int H, int64_t N, int S) {
     using namespace mf;
     using T_ = typename io_elem<IO>::T;
-    constexpr int NWV = 8;
     const int h = blockIdx.x, b = blockIdx.y;
-    const int C = (int)(N / T), T2 = T >> 6, NCT = (T2 + 15) >> 4;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, il = lane & 15, g = lane >> 4;
-    const int lr = w & 3, ch = w >> 2;  // correction rows 16 lr .., column tiles 4 ch ..
-    __shared__ __attribute__((aligned(16))) uint16_t us[128 * SP_USTR];
-    __shared__ __attribute__((aligned(16))) uint16_t xs[128 * SP_XSTR];
-    __shared__ cf pcs[64 * 8], pxs[64 * 8], qxs[64 * 16];
-    __shared__ cf xw[NWV][64], sst[64];
-    __shared__ float red[NWV], rmax[NWV];
-    const size_t orow = (size_t)b * H + h;
-    // tables and the initial state
-    for (int e = tid; e < 64 * 8; e += 512) {
-        pcs[e] = Pc[(size_t)h * 512 + e];
-        pxs[e] = Px[(size_t)h * 512 + e];
-    }
-    for (int e = tid; e < 64 * 16; e += 512) qxs[e] = Qx[(size_t)h * 1024 + e];
-    // rows i >= T2 of both operands stay zero, so the column-tile loops need
-    // no tests (the tables are zero past the chunk's tiles as well)
-    for (int e = tid; e < 128 * SP_USTR / 8; e += 512) ((u32x4 *)us)[e] = u32x4{0u, 0u, 0u, 0u};
-    for (int e = tid; e < 128 * SP_XSTR / 8; e += 512) ((u32x4 *)xs)[e] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    // G[(j, part)][i] = Abar_j^(64 i) as fp16 (|G| <= 1 for stable modes)
-    for (int e = tid; e < 64 * T2; e += 512) {
-        const int j = e & 63, i = e >> 6;
-        const cf X = cmul(pxs[j * 8 + (i >> 4)], qxs[j * 16 + (i & 15)]);
-        *(uint32_t *)(xs + i * SP_XSTR + 2 * j) = pk(X.x, X.y);
-    }
-    // every wave carries its own copy of the state: lane l holds mode l
-    cf xl = mk(0.f, 0.f);
-    if (x_in && lane < S) xl = mk(x_in[(orow * S + lane) * 2], x_in[(orow * S + lane) * 2 + 1]);
-    // matrix operands in registers
-    const uint16_t *Eh = Et + (size_t)h * 128 * 64, *Rh = Rt + (size_t)h * 64 * 128;
-    half8 Ea[2], Ra[4];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-        Ea[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Eh + (16 * w + il) * 64 + 32 * ks + 8 * g));
-    const int j0 = 8 * w + 2 * g;  // modes of this lane's accumulator pairs: j0, j0 + 1
-    const cf qc0 = Qc[((size_t)h * 64 + j0) * 16 + il], qc1 = Qc[((size_t)h * 64 + j0 + 1) * 16 + il];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        Ra[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Rh + (16 * lr + il) * 128 + 32 * ks + 8 * g));
-    const cf aTl = aT[(size_t)h * 64 + lane];
-    // max |Rt entry| < 2^er over the workgroup (sets the state scale below)
-    int er = 0;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
+    __shared__ __attribute__((aligned(16))) uint16_t Es[128 * SPB_ES];
+    __shared__ __attribute__((aligned(16))) cf Ss[4][16 * SPB_SS];
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[4][16 * SPB_XS];
+    __shared__ cf Lsh[2][4][64], Psh[2][4][64];
+    const size_t row = (size_t)b * H + h;
     {
-        float m = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)Ra[ks][e]));
-        m = sp_wave_max(m);
-        if (lane == 0) rmax[w] = m;
-        __syncthreads();
-        m = 0.f;
-#pragma unroll
-        for (int k = 0; k < NWV; ++k) m = fmaxf(m, rmax[k]);
-        if (m > 0.f) (void)frexpf(m, &er);
+        const u32x4 *eh = (const u32x4 *)(Eb + (size_t)h * 8192);
+        for (int e = tid; e < 1024; e += 256) *(u32x4 *)(Es + (e >> 3) * SPB_ES + 8 * (e & 7)) = eh[e];
     }
-    // chunk loads: T / 8 groups of 8 activations (at most 2 per thread), and
-    // the 4 outputs per column tile this lane corrects (read-modify-write).
-    const int nq = T >> 3;
-    u32x4 pre[2];
-    u32x2 ypre[4];
-    // Loads go through buffer resources: a chunk past the last (the loads
-    // issued during the last chunk) or outputs that no correction will use
-    // (chunk 0 without x_in) get an empty resource, whose loads read zero and
-    // touch no memory, with no branch around them.
-    auto load_chunk = [&](int c, bool uv, bool yv) {
-        const __amdgpu_buffer_rsrc_t ur = row_rsrc(u + orow * N + (size_t)c * T, uv ? 2 * T : 0);
+    // correction operands (A): rows t = 16 rt + col, columns 32 ks + 8 g ..
+    half8 Ra[4][4];
+    {
+        const uint16_t *rh = Rb + (size_t)h * 8192;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int q = tid + 512 * k;
-            if (q < nq) pre[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ur, 16 * q, 0, 0));
-        }
-        const __amdgpu_buffer_rsrc_t yrs = row_rsrc(y + orow * N + (size_t)c * T, yv ? 2 * T : 0);
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const int ct = 4 * ch + c4, i = 16 * ct + il;
-            if (ct < NCT && i < T2)
-                ypre[c4] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yrs, 2 * (64 * i + 16 * lr + 4 * g), 0, 0));
-        }
+            for (int ks = 0; ks < 4; ++ks)
+                Ra[rt][ks] = __builtin_bit_cast(half8, *(const u32x4 *)(rh + (16 * rt + col) * 128 + 32 * ks + 8 * g));
+    }
+    // Toeplitz tiles (A): tile d holds f[16 d + col - 8 g - e] (zero below index 0)
+    half8 La[4];
+    {
+        const float *fh = fb + (size_t)h * 64;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = 16 * d + col - 8 * g - e;
+                const float v = fh[i < 0 ? 0 : i];
+                La[d][e] = (_Float16)(i < 0 ? 0.f : v);
+            }
+    }
+    const cf a = ab[(size_t)h * 64 + lane], a16 = ak[(size_t)h * 64 + lane];
+    const float sB = sb[2 * h], sC = sb[2 * h + 1];
+    // state carried into the step (lane = mode), in units of sB
+    cf X = mk(0.f, 0.f);
+    if (x_in && lane < S) {
+        const float r = 1.f / sB;
+        X = mk(x_in[(row * S + lane) * 2] * r, x_in[(row * S + lane) * 2 + 1] * r);
+    }
+    const int64_t nch = N / 64;
+    const int nst = (int)((nch + 63) / 64);
+    const T_ *urow = u + row * N;
+    T_ *yrow = y + row * N;
+    // the step's window of the row as a buffer resource (empty past the end:
+    // its loads return zeros and its stores are dropped)
+    auto window = [&](const void *base, int st) -> __amdgpu_buffer_rsrc_t {
+        const int64_t s0 = (int64_t)st * 4096, rem = N - s0;
+        const int bytes = rem <= 0 ? 0 : (int)(2 * (rem < 4096 ? rem : 4096));
+        return row_rsrc((const char *)base + 2 * (rem > 0 ? s0 : 0), bytes);
     };
-    load_chunk(0, true, x_in != nullptr);
-    __syncthreads();
-    for (int c = 0; c < C; ++c) {
-        // 1. stage (fp16, scaled for bf16 inputs)
-        float su = 1.f;
+    const int uoff = (16 * w + col) * 128 + 16 * g;
+    auto load = [&](int st, u32x4 (&v)[2]) {
+        const __amdgpu_buffer_rsrc_t rs = window(urow, st);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            v[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, uoff + 64 * ks, 0, 0));
+    };
+    __syncthreads();  // Es
+    u32x4 cur[2], nxt[2];
+    load(0, cur);
+    cf *const Sw = Ss[w];
+    uint16_t *const Xw = Xs[w];
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < nst; ++st) {
+        load(st + 1, nxt);
+        // B operands in fp16: bf16 activations are scaled by a power of two
+        // into fp16 range (largest magnitude of the wave's 1024 samples
+        // below 2^14), then converted exactly but for fp16's subnormals
+        half8 U0, U1;
+        float isu = 1.f;
         if constexpr (IO == IO_BF16) {
-            float m = 0.f;
+            uint32_t mx = 0;
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-                if (tid + 512 * k < nq) {
-                    const uint32_t d4[4] = {pre[k].x, pre[k].y, pre[k].z, pre[k].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(d4[e] << 16)), fabsf(__uint_as_float(d4[e] & 0xffff0000u))));
-                }
-            m = sp_wave_max(m);
-            if (lane == 0) red[w] = m;
-            __syncthreads();
-            m = 0.f;
-#pragma unroll
-            for (int k = 0; k < NWV; ++k) m = fmaxf(m, red[k]);
-            int ex = 0;
-            if (m > 0.f) (void)frexpf(m, &ex);
-            su = ldexpf(1.f, 14 - ex);
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int q = tid + 512 * k;
-            if (q < nq) {
-                u32x4 v = pre[k];
-                if constexpr (IO == IO_BF16) {
-                    const uint32_t d4[4] = {v.x, v.y, v.z, v.w};
-                    uint32_t o4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o4[e] = pk(__uint_as_float(d4[e] << 16) * su, __uint_as_float(d4[e] & 0xffff0000u) * su);
-                    v = u32x4{o4[0], o4[1], o4[2], o4[3]};
-                }
-                *(u32x4 *)(us + (q >> 3) * SP_USTR + 8 * (q & 7)) = v;
+            for (int ks = 0; ks < 2; ++ks) {
+                mx = pkmax_u16(mx, cur[ks].x & 0x7fff7fffu);
+                mx = pkmax_u16(mx, cur[ks].y & 0x7fff7fffu);
+                mx = pkmax_u16(mx, cur[ks].z & 0x7fff7fffu);
+                mx = pkmax_u16(mx, cur[ks].w & 0x7fff7fffu);
             }
-        }
-        // (taken into registers of their own here, at the top of the pass,
-        //  so that no later use waits behind the stores issued meanwhile)
-        u32x2 ycur[4];
+            const uint32_t mh = (mx & 0xffffu) > (mx >> 16) ? (mx & 0xffffu) : (mx >> 16);
+            const float mu = wave_max(__uint_as_float(mh << 16));
+            int eu = 0;
+            if (mu > 0.f) (void)frexpf(mu, &eu);
+            eu = eu < -100 ? -100 : eu;
+            const float su = ldexpf(1.f, 14 - eu);
+            isu = ldexpf(1.f, eu - 14);
+            uint32_t o8[2][4];
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            ycur[c4] = ypre[c4];
-            asm volatile("" : "+v"(ycur[c4]));
-        }
-        // correction operand: this wave's Rt rows times the state carried in,
-        // (2 Re R, -2 Im R) (x) -> (2 Re (R x), -2 Im (R x)), with x scaled by
-        // sx = 2^(14 - e - er), max |x| < 2^e, so every product stays below 2^14
-        // 4. (for the previous chunk) x <- Abar^T x + s, in every wave; the
-        //    contributions s were completed at the previous chunk's last barrier
-        if (c > 0) xl = cadd(cmul(aTl, xl), sst[lane]);
-        const float xm = sp_wave_max(fmaxf(fabsf(xl.x), fabsf(xl.y)));
-        xw[w][lane] = xl;
-        const bool corr = xm > 0.f;
-        float sx = 1.f;
-        half8 Rx[4];
-        if (corr) {
-            int ex = 0;
-            (void)frexpf(xm, &ex);
-            sx = ldexpf(1.f, 14 - ex - er);
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint32_t d4[4] = {cur[ks].x, cur[ks].y, cur[ks].z, cur[ks].w};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const u32x4 r4 = __builtin_bit_cast(u32x4, Ra[ks]);
-                uint32_t o4[4] = {r4.x, r4.y, r4.z, r4.w}, xc[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const cf x = xw[w][16 * ks + 4 * g + q];  // mode of slot pair q
-                    xc[q] = pk(x.x * sx, -x.y * sx);
-                }
-                // (a + i b) conj(x sx) with (a, b) = (2 Re R, -2 Im R); the
-                // results are matrix-core operands (the helper ends with the
-                // wait states that needs)
-                cmulh_n(o4, xc);
-                Rx[ks] = __builtin_bit_cast(half8, u32x4{o4[0], o4[1], o4[2], o4[3]});
+                for (int q = 0; q < 4; ++q)
+                    o8[ks][q] = pk(__uint_as_float(d4[q] << 16) * su, __uint_as_float(d4[q] & 0xffff0000u) * su);
             }
+            U0 = __builtin_bit_cast(half8, u32x4{o8[0][0], o8[0][1], o8[0][2], o8[0][3]});
+            U1 = __builtin_bit_cast(half8, u32x4{o8[1][0], o8[1][1], o8[1][2], o8[1][3]});
+        } else {
+            U0 = __builtin_bit_cast(half8, cur[0]);
+            U1 = __builtin_bit_cast(half8, cur[1]);
         }
+        const int par = st & 1;
+        // 1. contributions: rows 16 rt + 4 g + v of tile rt are (mode 8 rt + 2 g + v / 2, part v % 2)
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const half8 e0 = __builtin_bit_cast(half8, *(const u32x4 *)(Es + (16 * rt + col) * SPB_ES + 8 * g));
+            const half8 e1 = __builtin_bit_cast(half8, *(const u32x4 *)(Es + (16 * rt + col) * SPB_ES + 32 + 8 * g));
+            f4 s = mfma16(e0, U0, z4);
+            s = mfma16(e1, U1, s);
+            *(f4 *)(Sw + col * SPB_SS + 8 * rt + 2 * g) = s;
+        }
+        //    and the blocks' own convolutions (tiles on and below the diagonal)
+        f4 Y[4];
+        Y[0] = mfma16(La[0], U0, z4);
+        Y[1] = mfma16(La[1], U0, z4);
+        Y[2] = mfma16(La[0], U1, mfma16(La[2], U0, z4));
+        Y[3] = mfma16(La[1], U1, mfma16(La[3], U0, z4));
+        wave_lds_sync();
+        // 2. lane = mode j: this wave's blocks from a zero state
+        cf s[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) s[c] = cscale(Sw[c * SPB_SS + lane], isu);
+        const int64_t cb = (int64_t)st * 64 + 16 * w;
+        const int nv = (int)(nch - cb >= 16 ? 16 : (nch - cb > 0 ? nch - cb : 0));
+        cf L = mk(0.f, 0.f), P = a16;
+        if (nv == 16) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) L = cadd(cmul(a, L), s[c]);
+        } else {
+            P = mk(1.f, 0.f);
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                if (c < nv) {
+                    L = cadd(cmul(a, L), s[c]);
+                    P = cmul(a, P);
+                }
+        }
+        Lsh[par][w][lane] = L;
+        Psh[par][w][lane] = P;
         __syncthreads();
-        // 3. correction: y += 2 Re(C Abar^(t+1) x), rows l = 16 lr + 4 g + v
-        if (corr) {
-            const float inv = 1.0f / sx;
-            T_ *yr = y + orow * N + (size_t)c * T;
+        // 3. the carried state through the four waves' blocks
+        cf X0 = X;
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const int ct = 4 * ch + c4, i = 16 * ct + il;
-                {
-                    f4 d = {0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < 4; ++v) {
+            if (v == w) X0 = X;
+            X = cadd(cmul(Psh[par][v][lane], X), Lsh[par][v][lane]);
+        }
+        // 4. states entering the wave's blocks
+        cf xin[16];
+        float m = 0.f;
+        {
+            cf x = X0;
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            Rx[ks], __builtin_bit_cast(half8, *(const u32x4 *)(xs + i * SP_XSTR + 32 * ks + 8 * g)), d, 0, 0, 0);
-                    if (i < T2) {
-                        T_ *p = yr + 64 * i + 16 * lr + 4 * g;
-                        const uint32_t y01 = ycur[c4].x, y23 = ycur[c4].y;
-                        const T_ *yv = (const T_ *)&y01;
-                        const T_ *yw = (const T_ *)&y23;
-                        T_ o[4];
-                        o[0] = yv[0]; o[1] = yv[1]; o[2] = yw[0]; o[3] = yw[1];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) st_io<IO>(o + v, ld_io<IO>(o + v) + d[v] * inv);
-                        const uint32_t a = *(const uint32_t *)&o[0], bb = *(const uint32_t *)&o[2];
-                        *(u32x2 *)p = u32x2{a, bb};
-                    }
-                }
+            for (int c = 0; c < 16; ++c) {
+                xin[c] = x;
+                m = fmaxf(m, fmaxf(fabsf(x.x), fabsf(x.y)));
+                x = cadd(cmul(a, x), s[c]);
             }
         }
-        // next chunk's loads (issued on every pass, with empty resources on
-        // the last: in a branch of their own they end up after the barrier)
-        load_chunk(c + 1 < C ? c + 1 : c, c + 1 < C, c + 1 < C);
-        // 2. contribution (column tiles unrolled, so their reads and products
-        //    overlap; the per-lane factor qc is applied once at the end)
-        cf acc0 = mk(0.f, 0.f), acc1 = mk(0.f, 0.f);
+        m = wave_max(m);
+        int ex = 0;
+        if (m > 0.f) (void)frexpf(m, &ex);
+        ex = ex < -100 ? -100 : ex;
+        const float sx = ldexpf(1.f, 14 - ex);  // |x sx| < 2^14
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int i = 16 * ct + il;
-            half8 Bop[2];
+        for (int c = 0; c < 16; ++c) *(uint32_t *)(Xw + c * SPB_XS + 2 * lane) = pk(xin[c].x * sx, xin[c].y * sx);
+        wave_lds_sync();
+        half8 Xo[4];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                Bop[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(us + i * SP_USTR + 32 * ks + 8 * g));
-            const f4 z = {0.f, 0.f, 0.f, 0.f};
-            f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ea[0], Bop[0], z, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ea[1], Bop[1], d, 0, 0, 0);
-            acc0 = cadd(acc0, cmul(pcs[j0 * 8 + ct], mk(d[0], d[1])));
-            acc1 = cadd(acc1, cmul(pcs[(j0 + 1) * 8 + ct], mk(d[2], d[3])));
-        }
-        acc0 = cmul(qc0, acc0);
-        acc1 = cmul(qc1, acc1);
+        for (int ks = 0; ks < 4; ++ks) Xo[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Xw + col * SPB_XS + 32 * ks + 8 * g));
+        const float inv = sB * sC / sx;
+        const __amdgpu_buffer_rsrc_t yrs = window(yrow, st);
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            acc0.x += __shfl_xor(acc0.x, o, 64);
-            acc0.y += __shfl_xor(acc0.y, o, 64);
-            acc1.x += __shfl_xor(acc1.x, o, 64);
-            acc1.y += __shfl_xor(acc1.y, o, 64);
+        for (int rt = 0; rt < 4; ++rt) {
+            f4 cc = z4;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) cc = mfma16(Ra[rt][ks], Xo[ks], cc);
+            const f4 o = Y[rt] * isu + cc * inv;
+            // 5. rows t = 16 rt + 4 g .. + 3 of block 16 w + col
+            const u32x2 v2 = {spb_pk<IO>(o[0], o[1]), spb_pk<IO>(o[2], o[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v2), yrs, (16 * w + col) * 128 + 2 * (16 * rt + 4 * g), 0, 0);
         }
-        if (il == 0) {
-            const float inv = 1.0f / su;
-            sst[j0] = cscale(acc0, inv);
-            sst[j0 + 1] = cscale(acc1, inv);
-        }
-        __syncthreads();
+        cur[0] = nxt[0];
+        cur[1] = nxt[1];
     }
-    if (x_out && w == 0) {
-        xl = cadd(cmul(aTl, xl), sst[lane]);
-        if (lane < S) {
-            x_out[(orow * S + lane) * 2] = xl.x;
-            x_out[(orow * S + lane) * 2 + 1] = xl.y;
-        }
+    if (x_out && w == 0 && lane < S) {
+        x_out[(row * S + lane) * 2] = X.x * sB;
+        x_out[(row * S + lane) * 2 + 1] = X.y * sB;
     }
-}
-
-// Same chunk convolution on the MFMA block-FFT engine (fp16 / bf16 I/O).
-template <int LOG2M, int IO>
-__global__ __launch_bounds__(mf::Shape<LOG2M>::NT) __attribute__((amdgpu_waves_per_eu(mf::Shape<LOG2M>::WPE))) void k_sp_chunk_conv_mfma(
-    const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ fT,
-    typename io_elem<IO>::T *__restrict__ y, int B, int H, int64_t N, int T) {
-    using SH = mf::Shape<LOG2M>;
-    constexpr int KIND = IO == IO_F16 ? mf::IN_F16 : mf::IN_BF16;
-    __shared__ __attribute__((aligned(16))) uint32_t smem[SH::LDS_DWORDS];
-    mf::Engine<LOG2M, KIND> E(smem);
-    E.init();
-    const int h = blockIdx.x;
-    const int C = (int)(N / T);
-    const float *fh = fT + (size_t)h * T;
-    const int hb = mf::half_bits(T);
-    const int rows = B * C;
-    auto off = [&](int r) -> size_t {
-        const int b = r / C, c = r % C;
-        return ((size_t)b * H + h) * N + (size_t)c * T;
-    };
-    // complex signal `sig` = row chunks 2 sig (real part), 2 sig + 1
-    // (imaginary); chunks past the last get empty resources
-    auto rowp = [&](int sig) -> mf::RowBufs {
-        const int r = 2 * sig;
-        const int nb0 = (r < rows) ? 2 * T : 0;
-        const int nb1 = (r + 1 < rows) ? 2 * T : 0;
-        const uint16_t *ub = (const uint16_t *)u;
-        uint16_t *yb = (uint16_t *)y;
-        const size_t o0 = (r < rows) ? off(r) : 0;
-        const size_t o1 = (r + 1 < rows) ? off(r + 1) : o0;
-        return {mf::row_rsrc(ub + o0, nb0), mf::row_rsrc(ub + o1, nb1), mf::row_rsrc(yb + o0, nb0),
-                mf::row_rsrc(yb + o1, nb1)};
-    };
-    E.run_raw(mf::row_rsrc(fh, 4 * T), 0.f, rowp, (rows + 1) / 2, hb);
 }
 
 template <int LOG2M, int IO>
 static hipError_t sp_conv(const void *u, const float *fT, void *y, int B, int H, int64_t N, int T,
                           hipStream_t s) {
     using T_ = typename io_elem<IO>::T;
-    if constexpr (IO != IO_F32 && LOG2M >= 9) {
-        return launch(k_sp_chunk_conv_mfma<LOG2M, IO>, dim3(H), dim3(mf::Shape<LOG2M>::NT), 0, s, (const T_ *)u,
-                      fT, (T_ *)y, B, H, N, T);
-    } else {
-        return launch(k_sp_chunk_conv<LOG2M, IO>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T_ *)u, fT,
-                      (T_ *)y, B, H, N, T);
-    }
+    return launch(k_sp_chunk_conv<LOG2M, IO>, dim3(H), dim3(Plan<LOG2M>::NT), 0, s, (const T_ *)u, fT, (T_ *)y,
+                  B, H, N, T);
 }
 
 // Dynamic LDS limits of the fp32 projection kernels, set once per device
@@ -920,12 +823,14 @@ hipError_t launch_state_copy(const float *x_in, float *x_out, int64_t n, hipStre
     return launch(k_state_copy, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, x_in, x_out, n);
 }
 
-template <int IO>
-static hipError_t sp_run(const void *u, const float *A, const float *Bm, const float *C,
-                         const float *dt, const float *D, const float *x_in, float *x_out, void *y,
-                         int B, int H, int64_t N, int S, int T, void *ws, hipStream_t s) {
-    using T_ = typename io_elem<IO>::T;
-    const SpLayout L = sp_layout(B, H, N, S, T, IO == IO_F32);
+// fp32 activations: chunk filter and power tables, FFT chunk convolutions,
+// then the contributions and corrections of every chunk.
+static hipError_t sp_run_f32(const void *u, const float *A, const float *Bm, const float *C,
+                             const float *dt, const float *D, const float *x_in, float *x_out, void *y,
+                             int B, int H, int64_t N, int S, int T, void *ws, hipStream_t s) {
+    constexpr int IO = IO_F32;
+    using T_ = float;
+    const SpLayout L = sp_layout(B, H, N, S, T, true);
     char *w = (char *)ws;
     float *fT = (float *)(w + L.fT);
     cf *E = (cf *)(w + L.E);
@@ -933,16 +838,9 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
     cf *sc = (cf *)(w + L.sc);
     const int C_ = (int)(N / T), T2 = T / 64;
 
-    hipError_t e;
-    if constexpr (IO != IO_F32) {
-        e = launch(k_sp_params, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, (uint16_t *)(w + L.Et),
-                   (uint16_t *)(w + L.Rt), (cf *)(w + L.Pc), (cf *)(w + L.Qc), (cf *)(w + L.Px), (cf *)(w + L.Qx),
-                   (cf *)(w + L.aT), S, T);
-    } else {
-        e = launch(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, S, (int64_t)T, (int64_t)T);
-        if (e != hipSuccess) return e;
-        e = launch(k_sp_tables, dim3(H), dim3(256), 0, s, A, dt, E, G, S, T2);
-    }
+    hipError_t e = launch(k_ssm_filter, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, fT, S, (int64_t)T, (int64_t)T);
+    if (e != hipSuccess) return e;
+    e = launch(k_sp_tables, dim3(H), dim3(256), 0, s, A, dt, E, G, S, T2);
     if (e != hipSuccess) return e;
     switch (fused_log2m(T)) {
         case 7: e = sp_conv<7, IO>(u, fT, y, B, H, N, T, s); break;
@@ -956,23 +854,34 @@ static hipError_t sp_run(const void *u, const float *A, const float *Bm, const f
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    if constexpr (IO != IO_F32) {
-        return launch(k_sp_proj_mfma<IO>, dim3(H, B), dim3(512), 0, s, (const T_ *)u, (T_ *)y,
-                      (const uint16_t *)(w + L.Et), (const uint16_t *)(w + L.Rt), (const cf *)(w + L.Pc),
-                      (const cf *)(w + L.Qc), (const cf *)(w + L.Px), (const cf *)(w + L.Qx),
-                      (const cf *)(w + L.aT), x_in, x_out, H, N, S, T);
-    } else {
-        const size_t sm_c = (size_t)T * 4 + 64 * 64 * 8 + 4 * 64 * 8;
-        const size_t sm_x = 64 * 64 * 8 + (size_t)64 * T2 * 8;
-        // the dynamic LDS limits are set once per device, for the largest
-        // chunk length (T = 8192), and their status is checked
-        if ((e = sp_f32_attributes<IO>()) != hipSuccess) return e;
-        e = launch(k_sp_contrib<IO>, dim3(C_, H, B), dim3(256), sm_c, s, (const T_ *)u, Bm, dt, E, G, sc, B, H,
-                   N, S, T);
-        if (e != hipSuccess) return e;
-        return launch(k_sp_correct<IO>, dim3(C_, H, B), dim3(256), sm_x, s, (T_ *)y, C, E, G, sc, x_in, x_out,
-                      B, H, N, S, T);
-    }
+    const size_t sm_c = (size_t)T * 4 + 64 * 64 * 8 + 4 * 64 * 8;
+    const size_t sm_x = 64 * 64 * 8 + (size_t)64 * T2 * 8;
+    // the dynamic LDS limits are set once per device, for the largest
+    // chunk length (T = 8192), and their status is checked
+    if ((e = sp_f32_attributes<IO>()) != hipSuccess) return e;
+    e = launch(k_sp_contrib<IO>, dim3(C_, H, B), dim3(256), sm_c, s, (const T_ *)u, Bm, dt, E, G, sc, B, H, N,
+               S, T);
+    if (e != hipSuccess) return e;
+    return launch(k_sp_correct<IO>, dim3(C_, H, B), dim3(256), sm_x, s, (T_ *)y, C, E, G, sc, x_in, x_out, B,
+                  H, N, S, T);
+}
+
+// 16-bit activations: the channel tables, then one pass of the block state
+// passing over every row (the result does not depend on T).
+template <int IO>
+static hipError_t sp_run_block(const void *u, const float *A, const float *Bm, const float *C,
+                               const float *dt, const float *D, const float *x_in, float *x_out, void *y,
+                               int B, int H, int64_t N, int S, int T, void *ws, hipStream_t s) {
+    using T_ = typename io_elem<IO>::T;
+    const SpLayout L = sp_layout(B, H, N, S, T, false);
+    char *w = (char *)ws;
+    hipError_t e = launch(k_spb_params, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, (float *)(w + L.fb),
+                          (uint16_t *)(w + L.Eb), (uint16_t *)(w + L.Rb), (cf *)(w + L.ab), (cf *)(w + L.ak),
+                          (float *)(w + L.sb), S);
+    if (e != hipSuccess) return e;
+    return launch(k_sp_block<IO>, dim3(H, B), dim3(256), 0, s, (const T_ *)u, (T_ *)y, (const float *)(w + L.fb),
+                  (const uint16_t *)(w + L.Eb), (const uint16_t *)(w + L.Rb), (const cf *)(w + L.ab),
+                  (const cf *)(w + L.ak), (const float *)(w + L.sb), x_in, x_out, H, N, S);
 }
 
 hipError_t launch_state_pass(const void *u, const float *A, const float *Bm, const float *C,
@@ -980,9 +889,9 @@ hipError_t launch_state_pass(const void *u, const float *A, const float *Bm, con
                              void *y, int B, int H, int64_t N, int S, int T, int io, void *ws,
                              hipStream_t s) {
     switch (io) {
-        case IO_F32: return sp_run<IO_F32>(u, A, Bm, C, dt, D, x_in, x_out, y, B, H, N, S, T, ws, s);
-        case IO_F16: return sp_run<IO_F16>(u, A, Bm, C, dt, D, x_in, x_out, y, B, H, N, S, T, ws, s);
-        case IO_BF16: return sp_run<IO_BF16>(u, A, Bm, C, dt, D, x_in, x_out, y, B, H, N, S, T, ws, s);
+        case IO_F32: return sp_run_f32(u, A, Bm, C, dt, D, x_in, x_out, y, B, H, N, S, T, ws, s);
+        case IO_F16: return sp_run_block<IO_F16>(u, A, Bm, C, dt, D, x_in, x_out, y, B, H, N, S, T, ws, s);
+        case IO_BF16: return sp_run_block<IO_BF16>(u, A, Bm, C, dt, D, x_in, x_out, y, B, H, N, S, T, ws, s);
         default: return hipErrorInvalidValue;
     }
 }

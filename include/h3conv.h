@@ -160,10 +160,15 @@ h3conv_status h3conv_ssm_filter(const float *A, const float *Bm, const float *C,
  * The output equals the full-length diagonal SSM
  *     x_t = Abar x_{t-1} + Bbar u_t,   y_t = 2 Re(C . x_t) + D u_t
  * with Abar = exp(dt A), Bbar = dt B and x_{-1} = x_in (zero if NULL).
- * Each chunk of T samples is convolved with the length-T SSM filter by FFT;
- * between chunks the state is carried as
+ * Between chunks of T samples the state is carried as
  *     x_c = Abar^T x_{c-1} + sum_k Abar^{T-1-k} Bbar u_{c,k}
- * and chunk c adds 2 Re(sum_j C_j Abar_j^{t+1} x_{c-1,j}) at offset t.
+ * and chunk c adds 2 Re(sum_j C_j Abar_j^{t+1} x_{c-1,j}) at offset t to its
+ * own convolution with the length-T filter.  fp32 activations convolve each
+ * chunk by FFT.  16-bit activations pass the state at every block of 64
+ * samples, a refinement of any chunk grid T (so the result is the same for
+ * every valid T): each block's own convolution (a 64 x 64 Toeplitz product),
+ * its contribution and its correction are matrix-core products, and y is
+ * written once.
  *
  *   u      [B,H,N]  io dtype      input
  *   A,Bm,C [H,S]    complex fp32  SSM parameters

@@ -266,3 +266,20 @@ def test_h3_mix_mh_validation(lib):
     assert call(out=0x100000) == pkg.ERR_INVALID_ARG    # out aliases q
     assert call(B=0) == pkg.OK
     assert pkg.workspace_size(pkg.OP_H3_MIX_MH, 2, 8, 64, 2) == 2 * (2 * 64 * 8 * 2 * 2)
+
+
+def test_noalloc_refuses_sizes_past_the_array(lib):
+    """The entry point without a workspace refuses, before any HIP call,
+    sizes whose workspace exceeds its static array, for every activation
+    type (the pointers are fake and never touched)."""
+    B, H, N, S, T = 2, 8192, 65536, 64, 8192
+    # lower bounds of each type's workspace past the array: the 16-bit
+    # projection tables alone (32 KiB per channel) and the fp32 chunk filter
+    # alone (H * T * 4 bytes)
+    assert H * 32768 > pkg.NOALLOC_WORKSPACE_BYTES
+    assert H * T * 4 > pkg.NOALLOC_WORKSPACE_BYTES
+    A = 1 << 36
+    for io in (pkg.F16, pkg.BF16, pkg.F32):
+        r = lib.h3conv_state_pass_noalloc(A, A + (1 << 30), A + (2 << 30), A + (3 << 30), A + (4 << 30),
+                                          A + (5 << 30), None, None, A + (8 << 30), B, H, N, S, T, io, None)
+        assert r == pkg.ERR_WORKSPACE
