@@ -466,46 +466,52 @@ __device__ __forceinline__ uint16_t f16bits(double x) {
 //   sb  [H, 2]        sB, sC: powers of two with |Bbar_j| < sB and 2 |C_j| < sC fp32
 // (modes j >= S are zero in every table).
 
-// The tables of one channel per workgroup of 8 waves.
-__global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A, const float *__restrict__ Bm,
+// The tables of one channel per workgroup of four waves: the fp64 powers
+// Abar^1, ^16, ^64, ^1024 (ssm_powers), then runs of 16 consecutive powers
+// per (mode, quarter) give every table entry, the filter's 64 taps as sums
+// over the modes (in mode order, so the result does not depend on the
+// schedule), and the scales.
+constexpr int SPB_EH = 66;  // Eb rows in this kernel's LDS (16-bit units; lanes = modes write 2 rows apart)
+__global__ __launch_bounds__(256) void k_spb_params(const float *__restrict__ A, const float *__restrict__ Bm,
                                                    const float *__restrict__ Cc, const float *__restrict__ dt,
                                                    const float *__restrict__ D, float *__restrict__ fb,
                                                    uint16_t *__restrict__ Eb, uint16_t *__restrict__ Rb,
                                                    cf *__restrict__ ab, cf *__restrict__ ak, float *__restrict__ sb,
                                                    int S) {
-    static_assert(2 * 128 * 64 * 2 <= FILT_LDS * 4, "the tables fit the filter's LDS");
-    __shared__ __attribute__((aligned(16))) float lds[FILT_LDS];
+    __shared__ __attribute__((aligned(16))) uint16_t Eh[128 * SPB_EH];
+    __shared__ __attribute__((aligned(16))) uint16_t Rh[64 * 128];
+    __shared__ float Ft[64][65];  // Ft[k][j] = 2 Re(C_j Bbar_j Abar_j^k)
     __shared__ double2 pw[4][64];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const double dth = (double)dt[h];
     ssm_powers(A, dth, S, h, pw);
-    __syncthreads();
-    ssm_filter_body(Bm, Cc, dth, D, fb, S, 64, 64, h, pw, lds);
-    __syncthreads();  // (the filter's operands have been read)
-    // scales, the same in every thread
-    double mb = 0.0, mc = 0.0;
-    for (int j = 0; j < S; ++j) {
-        const float *bj = Bm + ((size_t)h * S + j) * 2, *cj = Cc + ((size_t)h * S + j) * 2;
-        mb = fmax(mb, fabs(dth) * sqrt((double)bj[0] * bj[0] + (double)bj[1] * bj[1]));
-        mc = fmax(mc, 2.0 * sqrt((double)cj[0] * cj[0] + (double)cj[1] * cj[1]));
+    // scales (every wave: lane = mode, then the largest over the modes)
+    float mb = 0.f, mc = 0.f;
+    if (lane < S) {
+        const float *bj = Bm + ((size_t)h * S + lane) * 2, *cj = Cc + ((size_t)h * S + lane) * 2;
+        mb = (float)(fabs(dth) * sqrt((double)bj[0] * bj[0] + (double)bj[1] * bj[1]));
+        mc = (float)(2.0 * sqrt((double)cj[0] * cj[0] + (double)cj[1] * cj[1]));
     }
+    mb = mf::wave_max(mb);
+    mc = mf::wave_max(mc);
     int eb = 0, ec = 0;
-    if (mb > 0.0) (void)frexp(mb, &eb);
-    if (mc > 0.0) (void)frexp(mc, &ec);
-    const double sB = ldexp(1.0, eb), sC = ldexp(1.0, ec);
-    uint16_t *const Eh = (uint16_t *)lds, *const Rh = Eh + 128 * 64;
-    // runs of 16 powers per (mode, quarter): Abar^(16 q + k); q = 4 is Abar^64
-    for (int e = tid; e < 64 * 5; e += 512) {
+    if (mb > 0.f) (void)frexpf(mb, &eb);
+    if (mc > 0.f) (void)frexpf(mc, &ec);
+    const double sB = ldexp(1.0, eb), sC = ldexp(1.0, ec);  // |Bbar_j| < sB, 2 |C_j| < sC
+    const double rB = ldexp(1.0, -eb), rC2 = ldexp(2.0, -ec);  // 1 / sB, 2 / sC (exact)
+    __syncthreads();  // pw
+    for (int e = tid; e < 64 * 5; e += 256) {
         const int j = e & 63, q = e >> 6;
         const bool on = j < S;
         double br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
         if (on) {
             const size_t o = ((size_t)h * S + j) * 2;
-            br = dth * (double)Bm[o] / sB;
-            bi = dth * (double)Bm[o + 1] / sB;
-            cr = (double)Cc[o] / sC;
-            ci = (double)Cc[o + 1] / sC;
+            br = dth * (double)Bm[o];
+            bi = dth * (double)Bm[o + 1];
+            cr = (double)Cc[o];
+            ci = (double)Cc[o + 1];
         }
+        const double wr = cr * br - ci * bi, wi = cr * bi + ci * br;  // C_j Bbar_j
         double2 p = double2{1.0, 0.0};
         for (int r = 0; r < q; ++r) p = dmul(p, pw[1][j]);
         const int cnt = q < 4 ? 16 : 1;
@@ -513,14 +519,14 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
             const int pp = 16 * q + k;
             const double pr = on ? p.x : 0.0, pi = on ? p.y : 0.0;
             if (pp <= 63) {
-                const double zr = pr * br - pi * bi, zi = pr * bi + pi * br;
-                Eh[(2 * j) * 64 + 63 - pp] = f16bits(zr);
-                Eh[(2 * j + 1) * 64 + 63 - pp] = f16bits(zi);
+                Eh[(2 * j) * SPB_EH + 63 - pp] = f16bits((pr * br - pi * bi) * rB);
+                Eh[(2 * j + 1) * SPB_EH + 63 - pp] = f16bits((pr * bi + pi * br) * rB);
+                Ft[pp][j] = (float)(2.0 * (wr * pr - wi * pi));
             }
             if (pp >= 1) {
                 const double zr = cr * pr - ci * pi, zi = cr * pi + ci * pr;
-                Rh[(pp - 1) * 128 + 2 * j] = f16bits(2.0 * zr);
-                Rh[(pp - 1) * 128 + 2 * j + 1] = f16bits(-2.0 * zi);
+                Rh[(pp - 1) * 128 + 2 * j] = f16bits(zr * rC2);
+                Rh[(pp - 1) * 128 + 2 * j + 1] = f16bits(-zi * rC2);
             }
             if (pp == 64) ab[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
             p = dmul(p, pw[0][j]);
@@ -532,14 +538,22 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
         sb[2 * h + 1] = (float)sC;
     }
     __syncthreads();
-    using u32x4 = mf::u32x4;
-    u32x4 *eo = (u32x4 *)(Eb + (size_t)h * 8192), *ro = (u32x4 *)(Rb + (size_t)h * 8192);
-    for (int e = tid; e < 1024; e += 512) {
-        eo[e] = ((const u32x4 *)Eh)[e];
-        ro[e] = ((const u32x4 *)Rh)[e];
+    if (tid < 64) {
+        double acc = tid == 0 ? (double)D[h] : 0.0;
+        for (int j = 0; j < 64; ++j) acc += (double)Ft[tid][j];
+        fb[(size_t)h * 64 + tid] = (float)acc;
     }
+    uint32_t *eo = (uint32_t *)(Eb + (size_t)h * 8192);
+    for (int e = tid; e < 4096; e += 256) eo[e] = *(const uint32_t *)(Eh + (e >> 5) * SPB_EH + 2 * (e & 31));
+    using u32x4 = mf::u32x4;
+    u32x4 *ro = (u32x4 *)(Rb + (size_t)h * 8192);
+    for (int e = tid; e < 1024; e += 256) ro[e] = ((const u32x4 *)Rh)[e];
 }
 
+// x * a + s on complex values, as four fused multiply-adds
+__device__ __forceinline__ cf cfma(cf a, cf x, cf s) {
+    return mk(fmaf(a.x, x.x, fmaf(-a.y, x.y, s.x)), fmaf(a.x, x.y, fmaf(a.y, x.x, s.y)));
+}
 __device__ __forceinline__ mf::f4 mfma16(mf::half8 a, mf::half8 b, mf::f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -561,9 +575,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-constexpr int SPB_ES = 72;   // Eb rows in LDS (16-bit units; 144 bytes apart spreads a tile's 16 rows over the banks)
-constexpr int SPB_SS = 66;   // contributions of one block in LDS (complex; 64 modes + pad)
-constexpr int SPB_XS = 136;  // states entering one block in LDS (fp16; 128 + pad)
+// LDS of the block kernel, sized for three workgroups per compute unit:
+//   Es  the contribution operands in the order the lanes read them: for row
+//       tile rt and k step ks, lane l's 16 bytes at [(2 rt + ks) 64 + l]
+//   Ss  per wave, one row per block (66 complex: 64 modes and a pad): first
+//       the block's contributions, then the fp16 states entering the blocks
+//       (136 halves per row)
+constexpr int SPB_SS = 66;
+constexpr int SPB_XS = 136;
 
 // One workgroup of four waves per (batch row b, channel h).  A step takes 64
 // blocks (4096 samples); wave w holds blocks 16 w .. 16 w + 15 of it, the
@@ -582,7 +601,7 @@ constexpr int SPB_XS = 136;  // states entering one block in LDS (fp16; 128 + pa
 //      B-operand layout), and Y += Rb . X (the correction);
 //   5. y stored once, rounded once.
 template <int IO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_sp_block(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_sp_block(
     const typename io_elem<IO>::T *__restrict__ u, typename io_elem<IO>::T *__restrict__ y,
     const float *__restrict__ fb, const uint16_t *__restrict__ Eb, const uint16_t *__restrict__ Rb,
     const cf *__restrict__ ab, const cf *__restrict__ ak, const float *__restrict__ sb,
@@ -590,15 +609,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     using namespace mf;
     using T_ = typename io_elem<IO>::T;
     const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
-    __shared__ __attribute__((aligned(16))) uint16_t Es[128 * SPB_ES];
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __shared__ __attribute__((aligned(16))) u32x4 Es[16 * 64];
     __shared__ __attribute__((aligned(16))) cf Ss[4][16 * SPB_SS];
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[4][16 * SPB_XS];
-    __shared__ cf Lsh[2][4][64], Psh[2][4][64];
+    __shared__ cf Lsh[2][4][64];
     const size_t row = (size_t)b * H + h;
     {
         const u32x4 *eh = (const u32x4 *)(Eb + (size_t)h * 8192);
-        for (int e = tid; e < 1024; e += 256) *(u32x4 *)(Es + (e >> 3) * SPB_ES + 8 * (e & 7)) = eh[e];
+        // operand (rt, ks) of lane l: row 16 rt + l % 16, pieces 4 ks + l / 16
+        for (int e = tid; e < 1024; e += 256) {
+            const int l = e & 63, rt = e >> 7, ks = (e >> 6) & 1;
+            Es[e] = eh[(16 * rt + (l & 15)) * 8 + 4 * ks + (l >> 4)];
+        }
     }
     // correction operands (A): rows t = 16 rt + col, columns 32 ks + 8 g ..
     half8 Ra[4][4];
@@ -652,9 +675,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __syncthreads();  // Es
     u32x4 cur[2], nxt[2];
     load(0, cur);
+    asm volatile("" : "+v"(cur[0]), "+v"(cur[1]));  // (complete before the loop: see below)
     cf *const Sw = Ss[w];
-    uint16_t *const Xw = Xs[w];
+    uint16_t *const Xw = (uint16_t *)Sw;
     const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // a step's packed outputs, kept live into the next step: a store's data
+    // registers may not be reused before the store completes, so reusing
+    // them at the top of the next step would wait for every store of this one
+    u32x2 opk[4] = {};
     for (int st = 0; st < nst; ++st) {
         load(st + 1, nxt);
         // B operands in fp16: bf16 activations are scaled by a power of two
@@ -696,47 +724,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // 1. contributions: rows 16 rt + 4 g + v of tile rt are (mode 8 rt + 2 g + v / 2, part v % 2)
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
-            const half8 e0 = __builtin_bit_cast(half8, *(const u32x4 *)(Es + (16 * rt + col) * SPB_ES + 8 * g));
-            const half8 e1 = __builtin_bit_cast(half8, *(const u32x4 *)(Es + (16 * rt + col) * SPB_ES + 32 + 8 * g));
+            const half8 e0 = __builtin_bit_cast(half8, Es[(2 * rt) * 64 + lane]);
+            const half8 e1 = __builtin_bit_cast(half8, Es[(2 * rt + 1) * 64 + lane]);
             f4 s = mfma16(e0, U0, z4);
             s = mfma16(e1, U1, s);
             *(f4 *)(Sw + col * SPB_SS + 8 * rt + 2 * g) = s;
         }
-        //    and the blocks' own convolutions (tiles on and below the diagonal)
-        f4 Y[4];
-        Y[0] = mfma16(La[0], U0, z4);
-        Y[1] = mfma16(La[1], U0, z4);
-        Y[2] = mfma16(La[0], U1, mfma16(La[2], U0, z4));
-        Y[3] = mfma16(La[1], U1, mfma16(La[3], U0, z4));
         wave_lds_sync();
-        // 2. lane = mode j: this wave's blocks from a zero state
+        // 2. lane = mode j: this wave's blocks from a zero state (the
+        //    contributions are read again in 4 rather than kept in registers)
+        auto contrib = [&](int c) -> cf { return cscale(Sw[c * SPB_SS + lane], isu); };
         cf s[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) s[c] = cscale(Sw[c * SPB_SS + lane], isu);
+        for (int c = 0; c < 16; ++c) s[c] = contrib(c);
         const int64_t cb = (int64_t)st * 64 + 16 * w;
         const int nv = (int)(nch - cb >= 16 ? 16 : (nch - cb > 0 ? nch - cb : 0));
-        cf L = mk(0.f, 0.f), P = a16;
+        cf L = mk(0.f, 0.f);
         if (nv == 16) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) L = cadd(cmul(a, L), s[c]);
+            for (int c = 0; c < 16; ++c) L = cfma(a, L, s[c]);
         } else {
-            P = mk(1.f, 0.f);
 #pragma unroll
             for (int c = 0; c < 16; ++c)
-                if (c < nv) {
-                    L = cadd(cmul(a, L), s[c]);
-                    P = cmul(a, P);
-                }
+                if (c < nv) L = cfma(a, L, s[c]);
         }
         Lsh[par][w][lane] = L;
-        Psh[par][w][lane] = P;
         __syncthreads();
+        asm volatile("" : "+v"(opk[0]), "+v"(opk[1]), "+v"(opk[2]), "+v"(opk[3]));
         // 3. the carried state through the four waves' blocks
+        //    (wave v's blocks advance the state by Abar^(64 n_v); n_v = 16
+        //    but in a row's last step)
         cf X0 = X;
+        if ((int64_t)st * 64 + 64 <= nch) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            if (v == w) X0 = X;
-            X = cadd(cmul(Psh[par][v][lane], X), Lsh[par][v][lane]);
+            for (int v = 0; v < 4; ++v) {
+                if (v == w) X0 = X;
+                X = cfma(a16, X, Lsh[par][v][lane]);
+            }
+        } else {
+            for (int v = 0; v < 4; ++v) {
+                const int64_t rv = nch - ((int64_t)st * 64 + 16 * v);
+                const int nvv = rv >= 16 ? 16 : (rv > 0 ? (int)rv : 0);
+                cf P = mk(1.f, 0.f);
+                for (int c = 0; c < nvv; ++c) P = cmul(a, P);
+                if (v == w) X0 = X;
+                X = cfma(P, X, Lsh[par][v][lane]);
+            }
         }
         // 4. states entering the wave's blocks
         cf xin[16];
@@ -747,7 +780,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int c = 0; c < 16; ++c) {
                 xin[c] = x;
                 m = fmaxf(m, fmaxf(fabsf(x.x), fabsf(x.y)));
-                x = cadd(cmul(a, x), s[c]);
+                x = cfma(a, x, contrib(c));
             }
         }
         m = wave_max(m);
@@ -756,13 +789,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         ex = ex < -100 ? -100 : ex;
         const float sx = ldexpf(1.f, 14 - ex);  // |x sx| < 2^14
 #pragma unroll
-        for (int c = 0; c < 16; ++c) *(uint32_t *)(Xw + c * SPB_XS + 2 * lane) = pk(xin[c].x * sx, xin[c].y * sx);
+        for (int c = 0; c < 16; ++c)
+            *(uint32_t *)(Xw + c * SPB_XS + 2 * lane) = pk(xin[c].x * sx, xin[c].y * sx);
         wave_lds_sync();
         half8 Xo[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) Xo[ks] = __builtin_bit_cast(half8, *(const u32x4 *)(Xw + col * SPB_XS + 32 * ks + 8 * g));
-        const float inv = sB * sC / sx;
+        const float inv = ldexpf(sB * sC, ex - 14);  // sB sC / sx
+        // The next step's activations are taken here, before this step's
+        // stores: loads and stores share one counter whose events can
+        // complete out of order, so a wait for loads issued before stores
+        // would also wait for the stores.
+        asm volatile("" : "+v"(nxt[0]), "+v"(nxt[1]));
         const __amdgpu_buffer_rsrc_t yrs = window(yrow, st);
+        // the blocks' own convolutions (Toeplitz tiles on and below the diagonal)
+        f4 Y[4];
+        Y[0] = mfma16(La[0], U0, z4);
+        Y[1] = mfma16(La[1], U0, z4);
+        Y[2] = mfma16(La[0], U1, mfma16(La[2], U0, z4));
+        Y[3] = mfma16(La[1], U1, mfma16(La[3], U0, z4));
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             f4 cc = z4;
@@ -770,8 +815,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int ks = 0; ks < 4; ++ks) cc = mfma16(Ra[rt][ks], Xo[ks], cc);
             const f4 o = Y[rt] * isu + cc * inv;
             // 5. rows t = 16 rt + 4 g .. + 3 of block 16 w + col
-            const u32x2 v2 = {spb_pk<IO>(o[0], o[1]), spb_pk<IO>(o[2], o[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v2), yrs, (16 * w + col) * 128 + 2 * (16 * rt + 4 * g), 0, 0);
+            opk[rt] = u32x2{spb_pk<IO>(o[0], o[1]), spb_pk<IO>(o[2], o[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(opk[rt], yrs, (16 * w + col) * 128 + 2 * (16 * rt + 4 * g), 0, 0);
         }
         cur[0] = nxt[0];
         cur[1] = nxt[1];
@@ -875,7 +920,7 @@ static hipError_t sp_run_block(const void *u, const float *A, const float *Bm, c
     using T_ = typename io_elem<IO>::T;
     const SpLayout L = sp_layout(B, H, N, S, T, false);
     char *w = (char *)ws;
-    hipError_t e = launch(k_spb_params, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, (float *)(w + L.fb),
+    hipError_t e = launch(k_spb_params, dim3(H), dim3(256), 0, s, A, Bm, C, dt, D, (float *)(w + L.fb),
                           (uint16_t *)(w + L.Eb), (uint16_t *)(w + L.Rb), (cf *)(w + L.ab), (cf *)(w + L.ak),
                           (float *)(w + L.sb), S);
     if (e != hipSuccess) return e;
