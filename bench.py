@@ -61,7 +61,7 @@ KERNEL_SRC_DIR = "fft_long_convolution_flashconv_amd/csrc"
 # counter summary of the dominant kernel of each workload
 PROFILES = {"conv_1k": "profiles/k_fft_conv_mfma_conv_1k.md",
             "conv_8k": "profiles/k_fft_conv_mfma_conv_8k.md",
-            "state_64k": "profiles/k_sp_chunk_conv_mfma_state_64k.md",
+            "state_64k": "profiles/k_sp_block_state_64k.md",
             "h3_mix_2k": "profiles/k_fft_conv_mfma_h3_mix_2k.md",
             "conv_1k_bwd": "profiles/k_fft_bwd_mfma_conv_1k_bwd.md",
             "decode_125m": "profiles/k_ssm_step_decode_125m.md",

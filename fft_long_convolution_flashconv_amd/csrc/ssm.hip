@@ -13,8 +13,10 @@
 // update matrix M_ux = [Abar^{T-1} B, ..., Abar B, B]).  Per chunk c:
 //   y_c = (f[:T] * u_c) + D u_c + 2 Re(sum_j C_j Abar_j^{t+1} x_{c-1,j})
 //   x_c = Abar^T x_{c-1} + sum_k Abar^{T-1-k} Bbar u_{c,k}
-// The chunk convolutions run on the fused FFT engine; the two projections use
-// the same factored power tables.
+// fp32 activations: the chunk convolutions run on the fp32 FFT engine, the
+// two projections on the vector ALUs.  16-bit activations: the same update
+// with chunks of 64 samples in one pass over the row (k_sp_block below),
+// every product on the matrix cores.
 #include <algorithm>
 #include <atomic>
 
@@ -453,9 +455,12 @@ __device__ __forceinline__ uint16_t f16bits(double x) {
 // convolution is a 64 x 64 lower-triangular Toeplitz product (f_0 .. f_63,
 // D folded into f_0), the contribution is M_ux u_c and the correction the
 // projection of the carried state; the three are dense products on the
-// matrix cores (16x16x32, fp32 accumulate) over the 16 blocks a wave holds at
-// once, and only the state recurrence itself, x_c = Abar^64 x_{c-1} + s_c,
-// runs on the vector ALUs in fp32.
+// matrix cores (16x16x32, fp16 operands, fp32 accumulate) over the 16 blocks
+// a wave holds at once, and only the state recurrence itself,
+// x_c = Abar^64 x_{c-1} + s_c, runs on the vector ALUs in fp32.  Against a
+// 2T-point FFT per chunk this costs 64 multiply-adds per sample for the
+// block's own convolution and 2 x 2S for the projections, all of it dense
+// matrix-core work, and it reads u and writes y exactly once.
 //
 // Workspace of 16-bit activations (per channel h):
 //   fb  [H, 64]       taps f_0 .. f_63, D folded into f_0                       fp32
@@ -466,13 +471,14 @@ __device__ __forceinline__ uint16_t f16bits(double x) {
 //   sb  [H, 2]        sB, sC: powers of two with |Bbar_j| < sB and 2 |C_j| < sC fp32
 // (modes j >= S are zero in every table).
 
-// The tables of one channel per workgroup of four waves: the fp64 powers
-// Abar^1, ^16, ^64, ^1024 (ssm_powers), then runs of 16 consecutive powers
-// per (mode, quarter) give every table entry, the filter's 64 taps as sums
-// over the modes (in mode order, so the result does not depend on the
-// schedule), and the scales.
+// The tables of one channel per workgroup of eight waves.  Each thread takes
+// a run of 8 consecutive powers of one mode, Abar^(8 r) .. Abar^(8 r + 7)
+// (run 8: Abar^64 alone), starting from an exact fp64 exponential and
+// stepping by Abar, and writes every table entry of those powers; the
+// filter's 64 taps are then sums over the modes in mode order (so the result
+// does not depend on the schedule).
 constexpr int SPB_EH = 66;  // Eb rows in this kernel's LDS (16-bit units; lanes = modes write 2 rows apart)
-__global__ __launch_bounds__(256) void k_spb_params(const float *__restrict__ A, const float *__restrict__ Bm,
+__global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A, const float *__restrict__ Bm,
                                                    const float *__restrict__ Cc, const float *__restrict__ dt,
                                                    const float *__restrict__ D, float *__restrict__ fb,
                                                    uint16_t *__restrict__ Eb, uint16_t *__restrict__ Rb,
@@ -481,10 +487,8 @@ __global__ __launch_bounds__(256) void k_spb_params(const float *__restrict__ A,
     __shared__ __attribute__((aligned(16))) uint16_t Eh[128 * SPB_EH];
     __shared__ __attribute__((aligned(16))) uint16_t Rh[64 * 128];
     __shared__ float Ft[64][65];  // Ft[k][j] = 2 Re(C_j Bbar_j Abar_j^k)
-    __shared__ double2 pw[4][64];
     const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const double dth = (double)dt[h];
-    ssm_powers(A, dth, S, h, pw);
     // scales (every wave: lane = mode, then the largest over the modes)
     float mb = 0.f, mc = 0.f;
     if (lane < S) {
@@ -499,24 +503,26 @@ __global__ __launch_bounds__(256) void k_spb_params(const float *__restrict__ A,
     if (mc > 0.f) (void)frexpf(mc, &ec);
     const double sB = ldexp(1.0, eb), sC = ldexp(1.0, ec);  // |Bbar_j| < sB, 2 |C_j| < sC
     const double rB = ldexp(1.0, -eb), rC2 = ldexp(2.0, -ec);  // 1 / sB, 2 / sC (exact)
-    __syncthreads();  // pw
-    for (int e = tid; e < 64 * 5; e += 256) {
-        const int j = e & 63, q = e >> 6;
+    for (int e = tid; e < 64 * 9; e += 512) {
+        const int j = e & 63, r = e >> 6;
         const bool on = j < S;
-        double br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0;
+        double br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0, are = 0.0, aim = 0.0;
         if (on) {
             const size_t o = ((size_t)h * S + j) * 2;
             br = dth * (double)Bm[o];
             bi = dth * (double)Bm[o + 1];
             cr = (double)Cc[o];
             ci = (double)Cc[o + 1];
+            are = dth * (double)A[o];
+            aim = dth * (double)A[o + 1];
         }
         const double wr = cr * br - ci * bi, wi = cr * bi + ci * br;  // C_j Bbar_j
-        double2 p = double2{1.0, 0.0};
-        for (int r = 0; r < q; ++r) p = dmul(p, pw[1][j]);
-        const int cnt = q < 4 ? 16 : 1;
+        double2 p, st;
+        apow64(are, aim, 8.0 * r, p.x, p.y);
+        apow64(are, aim, 1.0, st.x, st.y);
+        const int cnt = r < 8 ? 8 : 1;
         for (int k = 0; k < cnt; ++k) {
-            const int pp = 16 * q + k;
+            const int pp = 8 * r + k;
             const double pr = on ? p.x : 0.0, pi = on ? p.y : 0.0;
             if (pp <= 63) {
                 Eh[(2 * j) * SPB_EH + 63 - pp] = f16bits((pr * br - pi * bi) * rB);
@@ -528,11 +534,15 @@ __global__ __launch_bounds__(256) void k_spb_params(const float *__restrict__ A,
                 Rh[(pp - 1) * 128 + 2 * j] = f16bits(zr * rC2);
                 Rh[(pp - 1) * 128 + 2 * j + 1] = f16bits(-zi * rC2);
             }
-            if (pp == 64) ab[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
-            p = dmul(p, pw[0][j]);
+            if (pp == 64) {
+                ab[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
+                double qr, qi;
+                apow64(are, aim, 1024.0, qr, qi);
+                ak[(size_t)h * 64 + j] = on ? mk((float)qr, (float)qi) : mk(0.f, 0.f);
+            }
+            p = dmul(p, st);
         }
     }
-    if (tid < 64) ak[(size_t)h * 64 + tid] = tid < S ? mk((float)pw[3][tid].x, (float)pw[3][tid].y) : mk(0.f, 0.f);
     if (tid == 0) {
         sb[2 * h] = (float)sB;
         sb[2 * h + 1] = (float)sC;
@@ -544,10 +554,10 @@ __global__ __launch_bounds__(256) void k_spb_params(const float *__restrict__ A,
         fb[(size_t)h * 64 + tid] = (float)acc;
     }
     uint32_t *eo = (uint32_t *)(Eb + (size_t)h * 8192);
-    for (int e = tid; e < 4096; e += 256) eo[e] = *(const uint32_t *)(Eh + (e >> 5) * SPB_EH + 2 * (e & 31));
+    for (int e = tid; e < 4096; e += 512) eo[e] = *(const uint32_t *)(Eh + (e >> 5) * SPB_EH + 2 * (e & 31));
     using u32x4 = mf::u32x4;
     u32x4 *ro = (u32x4 *)(Rb + (size_t)h * 8192);
-    for (int e = tid; e < 1024; e += 256) ro[e] = ((const u32x4 *)Rh)[e];
+    for (int e = tid; e < 1024; e += 512) ro[e] = ((const u32x4 *)Rh)[e];
 }
 
 // x * a + s on complex values, as four fused multiply-adds
@@ -731,12 +741,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             *(f4 *)(Sw + col * SPB_SS + 8 * rt + 2 * g) = s;
         }
         wave_lds_sync();
-        // 2. lane = mode j: this wave's blocks from a zero state (the
-        //    contributions are read again in 4 rather than kept in registers)
-        auto contrib = [&](int c) -> cf { return cscale(Sw[c * SPB_SS + lane], isu); };
+        // 2. lane = mode j: this wave's blocks from a zero state
         cf s[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) s[c] = contrib(c);
+        for (int c = 0; c < 16; ++c) s[c] = cscale(Sw[c * SPB_SS + lane], isu);
         const int64_t cb = (int64_t)st * 64 + 16 * w;
         const int nv = (int)(nch - cb >= 16 ? 16 : (nch - cb > 0 ? nch - cb : 0));
         cf L = mk(0.f, 0.f);
@@ -780,7 +788,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             for (int c = 0; c < 16; ++c) {
                 xin[c] = x;
                 m = fmaxf(m, fmaxf(fabsf(x.x), fabsf(x.y)));
-                x = cfma(a, x, contrib(c));
+                x = cfma(a, x, s[c]);
             }
         }
         m = wave_max(m);
@@ -920,7 +928,7 @@ static hipError_t sp_run_block(const void *u, const float *A, const float *Bm, c
     using T_ = typename io_elem<IO>::T;
     const SpLayout L = sp_layout(B, H, N, S, T, false);
     char *w = (char *)ws;
-    hipError_t e = launch(k_spb_params, dim3(H), dim3(256), 0, s, A, Bm, C, dt, D, (float *)(w + L.fb),
+    hipError_t e = launch(k_spb_params, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, (float *)(w + L.fb),
                           (uint16_t *)(w + L.Eb), (uint16_t *)(w + L.Rb), (cf *)(w + L.ab), (cf *)(w + L.ak),
                           (float *)(w + L.sb), S);
     if (e != hipSuccess) return e;
