@@ -11,8 +11,9 @@ Operations (after "Hungry Hungry Hippos: Towards Language Modeling with State
 Space Models"):
   fft_conv    y = (f * u)[:N] + D u, fused FFT convolution per channel
   ssm_filter  f_k = 2 Re(sum_j C_j exp(dt A_j k) dt B_j)
-  state_pass  chunked FFT convolution with the diagonal-SSM state carried
-              between chunks (exactly the full-length SSM)
+  state_pass  chunked convolution with the diagonal-SSM state carried
+              between chunks (exactly the full-length SSM; 16-bit activations
+              pass the state every 64 samples, fp32 convolve chunks of T by FFT)
   h3_mix      out = q * (f * (shift(k) * v) + D * shift(k) * v)
 """
 from __future__ import annotations
