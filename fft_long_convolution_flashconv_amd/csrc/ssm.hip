@@ -474,9 +474,9 @@ __device__ __forceinline__ uint16_t f16bits(double x) {
 // The tables of one channel per workgroup of eight waves.  Each thread takes
 // a run of 8 consecutive powers of one mode, Abar^(8 r) .. Abar^(8 r + 7)
 // (run 8: Abar^64 alone), starting from an exact fp64 exponential and
-// stepping by Abar, and writes every table entry of those powers; the
-// filter's 64 taps are then sums over the modes in mode order (so the result
-// does not depend on the schedule).
+// stepping by Abar in fp32, and writes every table entry of those powers;
+// the filter's 64 taps are then sums over the modes in mode order, in fp64
+// (so the result does not depend on the schedule).
 constexpr int SPB_EH = 66;  // Eb rows in this kernel's LDS (16-bit units; lanes = modes write 2 rows apart)
 __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A, const float *__restrict__ Bm,
                                                    const float *__restrict__ Cc, const float *__restrict__ dt,
@@ -516,31 +516,36 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
             are = dth * (double)A[o];
             aim = dth * (double)A[o + 1];
         }
-        const double wr = cr * br - ci * bi, wi = cr * bi + ci * br;  // C_j Bbar_j
-        double2 p, st;
-        apow64(are, aim, 8.0 * r, p.x, p.y);
-        apow64(are, aim, 1.0, st.x, st.y);
+        // the run in fp32 from exact fp64 exponentials (8 steps: relative
+        // error ~1e-6, far below the fp16 tables' 2^-11; the taps' terms are
+        // fp32 as well and summed in fp64 below)
+        const float fbr = (float)(br * rB), fbi = (float)(bi * rB);  // Bbar_j / sB
+        const float fcr = (float)(cr * rC2), fci = (float)(ci * rC2);  // 2 C_j / sC
+        const float fwr = (float)(2.0 * (cr * br - ci * bi)), fwi = (float)(2.0 * (cr * bi + ci * br));  // 2 C_j Bbar_j
+        double2 p0, s0;
+        apow64(are, aim, 8.0 * r, p0.x, p0.y);
+        apow64(are, aim, 1.0, s0.x, s0.y);
+        cf p = on ? mk((float)p0.x, (float)p0.y) : mk(0.f, 0.f);
+        const cf st = mk((float)s0.x, (float)s0.y);
         const int cnt = r < 8 ? 8 : 1;
         for (int k = 0; k < cnt; ++k) {
             const int pp = 8 * r + k;
-            const double pr = on ? p.x : 0.0, pi = on ? p.y : 0.0;
             if (pp <= 63) {
-                Eh[(2 * j) * SPB_EH + 63 - pp] = f16bits((pr * br - pi * bi) * rB);
-                Eh[(2 * j + 1) * SPB_EH + 63 - pp] = f16bits((pr * bi + pi * br) * rB);
-                Ft[pp][j] = (float)(2.0 * (wr * pr - wi * pi));
+                Eh[(2 * j) * SPB_EH + 63 - pp] = __builtin_bit_cast(uint16_t, (_Float16)(p.x * fbr - p.y * fbi));
+                Eh[(2 * j + 1) * SPB_EH + 63 - pp] = __builtin_bit_cast(uint16_t, (_Float16)(p.x * fbi + p.y * fbr));
+                Ft[pp][j] = p.x * fwr - p.y * fwi;
             }
             if (pp >= 1) {
-                const double zr = cr * pr - ci * pi, zi = cr * pi + ci * pr;
-                Rh[(pp - 1) * 128 + 2 * j] = f16bits(zr * rC2);
-                Rh[(pp - 1) * 128 + 2 * j + 1] = f16bits(-zi * rC2);
+                Rh[(pp - 1) * 128 + 2 * j] = __builtin_bit_cast(uint16_t, (_Float16)(fcr * p.x - fci * p.y));
+                Rh[(pp - 1) * 128 + 2 * j + 1] = __builtin_bit_cast(uint16_t, (_Float16)(-(fcr * p.y + fci * p.x)));
             }
             if (pp == 64) {
-                ab[(size_t)h * 64 + j] = mk((float)pr, (float)pi);
+                ab[(size_t)h * 64 + j] = p;
                 double qr, qi;
                 apow64(are, aim, 1024.0, qr, qi);
                 ak[(size_t)h * 64 + j] = on ? mk((float)qr, (float)qi) : mk(0.f, 0.f);
             }
-            p = dmul(p, st);
+            p = cmul(p, st);
         }
     }
     if (tid == 0) {

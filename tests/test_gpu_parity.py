@@ -264,6 +264,31 @@ def test_state_pass_16bit_chunks_and_split(io, T, S):
 
 
 @pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("N,T,S", [(4416, 64, 64), (6144, 2048, 20), (64, 64, 1)])
+def test_state_pass_16bit_ragged_steps(io, N, T, S):
+    """16-bit state passing over lengths that end inside a step of 64 blocks
+    (a wave with only part of its 16 blocks, waves with none), from a given
+    state: every row against the recurrence, and the final state."""
+    dev = device()
+    B, H = 3, 2
+    say("state_pass ragged io=%s B=%d H=%d N=%d S=%d T=%d" % (io, B, H, N, S, T))
+    u, p, D = _sp_inputs(B, H, N, S, io, seed=N + S)
+    d = {k: v.to(dev) for k, v in p.items()}
+    g = wl.gen(N + S + 1)
+    xi = (torch.randn(B, H, S, dtype=torch.float64, generator=g)
+          + 1j * torch.randn(B, H, S, dtype=torch.float64, generator=g)).to(torch.complex64)
+    y, x = pkg.state_pass(u.to(dev), d["A"], d["Bm"], d["C"], d["dt"], D.to(dev), T, x_in=xi.to(dev),
+                          return_state=True)
+    torch.cuda.synchronize()
+    ref, xr = _sp_ref(u, p, D, x_in=xi.numpy().astype(np.complex128))
+    got = to_np(y)
+    err, errx = rel_l2(got, ref), rel_l2(x.cpu().numpy().astype(np.complex128), xr)
+    rows = row_rel_l2(got.reshape(B * H, N), ref.reshape(B * H, N))
+    say("  rel_l2=%.3e max_row=%.3e state=%.3e" % (err, rows.max(), errx))
+    assert err <= TOL[io] and rows.max() <= TOL[io] and errx <= 1e-3
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
 def test_state_pass_zero_state_equals_none(io):
     """An all-zero x_in gives exactly the result of no x_in (the carried
     state starts at zero either way)."""
