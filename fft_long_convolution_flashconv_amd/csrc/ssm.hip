@@ -590,33 +590,34 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// LDS of the block kernel, sized for three workgroups per compute unit:
-//   Es  the contribution operands in the order the lanes read them: for row
-//       tile rt and k step ks, lane l's 16 bytes at [(2 rt + ks) 64 + l]
-//   Ss  per wave, one row per block (66 complex: 64 modes and a pad): first
-//       the block's contributions, then the fp16 states entering the blocks
-//       (136 halves per row)
+// LDS of the block kernel (37 KiB), per wave one row per block (66 complex:
+// 64 modes and a pad): first the block's contributions, then the fp16 states
+// entering the blocks (136 halves per row); and the waves' end states.
 constexpr int SPB_SS = 66;
 constexpr int SPB_XS = 136;
 
-// One workgroup of four waves per (batch row b, channel h).  A step takes 64
-// blocks (4096 samples); wave w holds blocks 16 w .. 16 w + 15 of it, the
+// One workgroup of four waves per (batch row b, channel h), two waves per
+// SIMD (232 registers: the contribution and correction operands, 32 KiB of
+// the channel's tables, stay in registers for the whole row).  A step takes
+// 64 blocks (4096 samples); wave w holds blocks 16 w .. 16 w + 15 of it, the
 // 16 columns of its matrix-core products (the B operand, read straight from
-// HBM: lane (n, g) loads samples 32 ks + 8 g .. + 7 of block n).  Per step:
-//   1. contributions S[(j, part)][n] = Eb . U (8 row tiles) -> LDS, and the
-//      blocks' own convolutions Y = L . U (the Toeplitz tiles depend only on
-//      the tile's distance from the diagonal: 4 distinct tiles, 6 products);
+// HBM one step ahead: lane (n, g) loads samples 32 ks + 8 g .. + 7 of block
+// n).  Per step:
+//   1. contributions S[(j, part)][n] = Eb . U (8 row tiles) -> LDS;
 //   2. lane = mode: the wave's blocks scanned from a zero state (end state
-//      L_w, and P_w = Abar^(64 n_w) for its n_w valid blocks) -> LDS;
-//   3. one barrier; every wave folds the four (P_w, L_w) in order into the
-//      state carried between steps (the same in every wave), and takes the
-//      state entering its own first block;
+//      L_w; a wave with n_w < 16 valid blocks advances the state by
+//      Abar^(64 n_w)) -> LDS;
+//   3. one barrier; every wave folds the four waves' end states in order into
+//      the state carried between steps (the same in every wave), and takes
+//      the state entering its own first block;
 //   4. the scan again from that state gives the state entering each block,
 //      scaled by a power of two into fp16 range -> LDS (transposed to the
-//      B-operand layout), and Y += Rb . X (the correction);
+//      B-operand layout); the blocks' own convolutions Y = L . U (the
+//      Toeplitz tiles depend only on their distance from the diagonal: 4
+//      distinct tiles, 6 products) and Y += Rb . X (the correction);
 //   5. y stored once, rounded once.
 template <int IO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_sp_block(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_sp_block(
     const typename io_elem<IO>::T *__restrict__ u, typename io_elem<IO>::T *__restrict__ y,
     const float *__restrict__ fb, const uint16_t *__restrict__ Eb, const uint16_t *__restrict__ Rb,
     const cf *__restrict__ ab, const cf *__restrict__ ak, const float *__restrict__ sb,
@@ -626,17 +627,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __shared__ __attribute__((aligned(16))) u32x4 Es[16 * 64];
     __shared__ __attribute__((aligned(16))) cf Ss[4][16 * SPB_SS];
     __shared__ cf Lsh[2][4][64];
     const size_t row = (size_t)b * H + h;
+    // contribution operands (A): rows 16 rt + col (mode 8 rt + col / 2, part
+    // col % 2), columns 32 ks + 8 g ..
+    half8 Ea[8][2];
     {
-        const u32x4 *eh = (const u32x4 *)(Eb + (size_t)h * 8192);
-        // operand (rt, ks) of lane l: row 16 rt + l % 16, pieces 4 ks + l / 16
-        for (int e = tid; e < 1024; e += 256) {
-            const int l = e & 63, rt = e >> 7, ks = (e >> 6) & 1;
-            Es[e] = eh[(16 * rt + (l & 15)) * 8 + 4 * ks + (l >> 4)];
-        }
+        const uint16_t *eh = Eb + (size_t)h * 8192;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                Ea[rt][ks] = __builtin_bit_cast(half8, *(const u32x4 *)(eh + (16 * rt + col) * 64 + 32 * ks + 8 * g));
     }
     // correction operands (A): rows t = 16 rt + col, columns 32 ks + 8 g ..
     half8 Ra[4][4];
@@ -687,7 +690,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         for (int ks = 0; ks < 2; ++ks)
             v[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, uoff + 64 * ks, 0, 0));
     };
-    __syncthreads();  // Es
     u32x4 cur[2], nxt[2];
     load(0, cur);
     asm volatile("" : "+v"(cur[0]), "+v"(cur[1]));  // (complete before the loop: see below)
@@ -739,10 +741,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         // 1. contributions: rows 16 rt + 4 g + v of tile rt are (mode 8 rt + 2 g + v / 2, part v % 2)
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
-            const half8 e0 = __builtin_bit_cast(half8, Es[(2 * rt) * 64 + lane]);
-            const half8 e1 = __builtin_bit_cast(half8, Es[(2 * rt + 1) * 64 + lane]);
-            f4 s = mfma16(e0, U0, z4);
-            s = mfma16(e1, U1, s);
+            f4 s = mfma16(Ea[rt][0], U0, z4);
+            s = mfma16(Ea[rt][1], U1, s);
             *(f4 *)(Sw + col * SPB_SS + 8 * rt + 2 * g) = s;
         }
         wave_lds_sync();
