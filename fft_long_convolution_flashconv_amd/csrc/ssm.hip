@@ -471,98 +471,95 @@ __device__ __forceinline__ uint16_t f16bits(double x) {
 //   sb  [H, 2]        sB, sC: powers of two with |Bbar_j| < sB and 2 |C_j| < sC fp32
 // (modes j >= S are zero in every table).
 
-// The tables of one channel per workgroup of eight waves.  Each thread takes
-// a run of 8 consecutive powers of one mode, Abar^(8 r) .. Abar^(8 r + 7)
-// (run 8: Abar^64 alone), starting from an exact fp64 exponential and
-// stepping by Abar in fp32, and writes every table entry of those powers;
-// the filter's 64 taps are then sums over the modes in mode order, in fp64
-// (so the result does not depend on the schedule).
-constexpr int SPB_EH = 66;  // Eb rows in this kernel's LDS (16-bit units; lanes = modes write 2 rows apart)
+// The tables of one channel per workgroup of eight waves: wave r, lane j
+// takes the powers Abar_j^(8 r) .. Abar_j^(8 r + 7), the first an exact fp64
+// exponential and the rest stepped by Abar in fp32 (7 steps: relative error
+// ~1e-6, far below the fp16 tables' 2^-11), and writes their table entries
+// straight to memory: two 16-byte pieces of Eb (one per part) and, per
+// power, 4 bytes of a row of Rb (the wave's lanes fill the row).  The
+// filter's 64 taps are sums over the modes in fp64, in mode order (so the
+// result does not depend on the schedule), of fp32 terms staged in LDS.
 __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A, const float *__restrict__ Bm,
                                                    const float *__restrict__ Cc, const float *__restrict__ dt,
                                                    const float *__restrict__ D, float *__restrict__ fb,
                                                    uint16_t *__restrict__ Eb, uint16_t *__restrict__ Rb,
                                                    cf *__restrict__ ab, cf *__restrict__ ak, float *__restrict__ sb,
                                                    int S) {
-    __shared__ __attribute__((aligned(16))) uint16_t Eh[128 * SPB_EH];
-    __shared__ __attribute__((aligned(16))) uint16_t Rh[64 * 128];
     __shared__ float Ft[64][65];  // Ft[k][j] = 2 Re(C_j Bbar_j Abar_j^k)
-    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int h = blockIdx.x, tid = threadIdx.x, j = tid & 63, r = tid >> 6;
     const double dth = (double)dt[h];
-    // scales (every wave: lane = mode, then the largest over the modes)
-    float mb = 0.f, mc = 0.f;
-    if (lane < S) {
-        const float *bj = Bm + ((size_t)h * S + lane) * 2, *cj = Cc + ((size_t)h * S + lane) * 2;
-        mb = (float)(fabs(dth) * sqrt((double)bj[0] * bj[0] + (double)bj[1] * bj[1]));
-        mc = (float)(2.0 * sqrt((double)cj[0] * cj[0] + (double)cj[1] * cj[1]));
+    const bool on = j < S;
+    double br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0, are = 0.0, aim = 0.0;
+    if (on) {
+        const size_t o = ((size_t)h * S + j) * 2;
+        br = dth * (double)Bm[o];
+        bi = dth * (double)Bm[o + 1];
+        cr = (double)Cc[o];
+        ci = (double)Cc[o + 1];
+        are = dth * (double)A[o];
+        aim = dth * (double)A[o + 1];
     }
-    mb = mf::wave_max(mb);
-    mc = mf::wave_max(mc);
+    // scales: the largest |Bbar_j| and 2 |C_j| over the modes (lane = mode)
+    const float mb = mf::wave_max((float)sqrt(br * br + bi * bi));
+    const float mc = mf::wave_max((float)(2.0 * sqrt(cr * cr + ci * ci)));
     int eb = 0, ec = 0;
     if (mb > 0.f) (void)frexpf(mb, &eb);
     if (mc > 0.f) (void)frexpf(mc, &ec);
-    const double sB = ldexp(1.0, eb), sC = ldexp(1.0, ec);  // |Bbar_j| < sB, 2 |C_j| < sC
-    const double rB = ldexp(1.0, -eb), rC2 = ldexp(2.0, -ec);  // 1 / sB, 2 / sC (exact)
-    for (int e = tid; e < 64 * 9; e += 512) {
-        const int j = e & 63, r = e >> 6;
-        const bool on = j < S;
-        double br = 0.0, bi = 0.0, cr = 0.0, ci = 0.0, are = 0.0, aim = 0.0;
-        if (on) {
-            const size_t o = ((size_t)h * S + j) * 2;
-            br = dth * (double)Bm[o];
-            bi = dth * (double)Bm[o + 1];
-            cr = (double)Cc[o];
-            ci = (double)Cc[o + 1];
-            are = dth * (double)A[o];
-            aim = dth * (double)A[o + 1];
+    const double rB = ldexp(1.0, -eb), rC2 = ldexp(2.0, -ec);  // 1 / sB, 2 / sC (exact powers of two)
+    const float fbr = (float)(br * rB), fbi = (float)(bi * rB);  // Bbar_j / sB
+    const float fcr = (float)(cr * rC2), fci = (float)(ci * rC2);  // 2 C_j / sC
+    const float fwr = (float)(2.0 * (cr * br - ci * bi)), fwi = (float)(2.0 * (cr * bi + ci * br));  // 2 C_j Bbar_j
+    double2 p0, s0;
+    apow64(are, aim, 8.0 * r, p0.x, p0.y);
+    apow64(are, aim, 1.0, s0.x, s0.y);
+    cf p = on ? mk((float)p0.x, (float)p0.y) : mk(0.f, 0.f);
+    const cf st = mk((float)s0.x, (float)s0.y);
+    uint16_t er[8], ei[8];
+    uint16_t *const rh = Rb + (size_t)h * 8192;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int pp = 8 * r + k;
+        er[7 - k] = __builtin_bit_cast(uint16_t, (_Float16)(p.x * fbr - p.y * fbi));
+        ei[7 - k] = __builtin_bit_cast(uint16_t, (_Float16)(p.x * fbi + p.y * fbr));
+        Ft[pp][j] = p.x * fwr - p.y * fwi;
+        if (pp >= 1) {
+            const uint16_t zr = __builtin_bit_cast(uint16_t, (_Float16)(fcr * p.x - fci * p.y));
+            const uint16_t zi = __builtin_bit_cast(uint16_t, (_Float16)(-(fcr * p.y + fci * p.x)));
+            *(uint32_t *)(rh + (pp - 1) * 128 + 2 * j) = (uint32_t)zr | ((uint32_t)zi << 16);
         }
-        // the run in fp32 from exact fp64 exponentials (8 steps: relative
-        // error ~1e-6, far below the fp16 tables' 2^-11; the taps' terms are
-        // fp32 as well and summed in fp64 below)
-        const float fbr = (float)(br * rB), fbi = (float)(bi * rB);  // Bbar_j / sB
-        const float fcr = (float)(cr * rC2), fci = (float)(ci * rC2);  // 2 C_j / sC
-        const float fwr = (float)(2.0 * (cr * br - ci * bi)), fwi = (float)(2.0 * (cr * bi + ci * br));  // 2 C_j Bbar_j
-        double2 p0, s0;
-        apow64(are, aim, 8.0 * r, p0.x, p0.y);
-        apow64(are, aim, 1.0, s0.x, s0.y);
-        cf p = on ? mk((float)p0.x, (float)p0.y) : mk(0.f, 0.f);
-        const cf st = mk((float)s0.x, (float)s0.y);
-        const int cnt = r < 8 ? 8 : 1;
-        for (int k = 0; k < cnt; ++k) {
-            const int pp = 8 * r + k;
-            if (pp <= 63) {
-                Eh[(2 * j) * SPB_EH + 63 - pp] = __builtin_bit_cast(uint16_t, (_Float16)(p.x * fbr - p.y * fbi));
-                Eh[(2 * j + 1) * SPB_EH + 63 - pp] = __builtin_bit_cast(uint16_t, (_Float16)(p.x * fbi + p.y * fbr));
-                Ft[pp][j] = p.x * fwr - p.y * fwi;
-            }
-            if (pp >= 1) {
-                Rh[(pp - 1) * 128 + 2 * j] = __builtin_bit_cast(uint16_t, (_Float16)(fcr * p.x - fci * p.y));
-                Rh[(pp - 1) * 128 + 2 * j + 1] = __builtin_bit_cast(uint16_t, (_Float16)(-(fcr * p.y + fci * p.x)));
-            }
-            if (pp == 64) {
-                ab[(size_t)h * 64 + j] = p;
-                double qr, qi;
-                apow64(are, aim, 1024.0, qr, qi);
-                ak[(size_t)h * 64 + j] = on ? mk((float)qr, (float)qi) : mk(0.f, 0.f);
-            }
-            p = cmul(p, st);
-        }
+        p = cmul(p, st);
     }
-    if (tid == 0) {
-        sb[2 * h] = (float)sB;
-        sb[2 * h + 1] = (float)sC;
+    // Eb row 2j (+1), columns 56 - 8 r .. 63 - 8 r hold Abar^(8 r + 7) .. Abar^(8 r)
+    using u32x4 = mf::u32x4;
+    auto pack = [](const uint16_t (&v)[8]) -> u32x4 {
+        return u32x4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+                     (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+    };
+    uint16_t *const eh = Eb + (size_t)h * 8192;
+    *(u32x4 *)(eh + (2 * j) * 64 + 56 - 8 * r) = pack(er);
+    *(u32x4 *)(eh + (2 * j + 1) * 64 + 56 - 8 * r) = pack(ei);
+    if (r == 0) {
+        // Abar^64 (the block step), its correction row t = 63, and Abar^1024
+        double qr, qi;
+        apow64(are, aim, 64.0, qr, qi);
+        const cf q = on ? mk((float)qr, (float)qi) : mk(0.f, 0.f);
+        ab[(size_t)h * 64 + j] = q;
+        const uint16_t zr = __builtin_bit_cast(uint16_t, (_Float16)(fcr * q.x - fci * q.y));
+        const uint16_t zi = __builtin_bit_cast(uint16_t, (_Float16)(-(fcr * q.y + fci * q.x)));
+        *(uint32_t *)(rh + 63 * 128 + 2 * j) = (uint32_t)zr | ((uint32_t)zi << 16);
+        apow64(are, aim, 1024.0, qr, qi);
+        ak[(size_t)h * 64 + j] = on ? mk((float)qr, (float)qi) : mk(0.f, 0.f);
+        if (j == 0) {
+            sb[2 * h] = ldexpf(1.f, eb);
+            sb[2 * h + 1] = ldexpf(1.f, ec);
+        }
     }
     __syncthreads();
     if (tid < 64) {
         double acc = tid == 0 ? (double)D[h] : 0.0;
-        for (int j = 0; j < 64; ++j) acc += (double)Ft[tid][j];
+        for (int jj = 0; jj < 64; ++jj) acc += (double)Ft[tid][jj];
         fb[(size_t)h * 64 + tid] = (float)acc;
     }
-    uint32_t *eo = (uint32_t *)(Eb + (size_t)h * 8192);
-    for (int e = tid; e < 4096; e += 512) eo[e] = *(const uint32_t *)(Eh + (e >> 5) * SPB_EH + 2 * (e & 31));
-    using u32x4 = mf::u32x4;
-    u32x4 *ro = (u32x4 *)(Rb + (size_t)h * 8192);
-    for (int e = tid; e < 1024; e += 512) ro[e] = ((const u32x4 *)Rh)[e];
 }
 
 // x * a + s on complex values, as four fused multiply-adds
