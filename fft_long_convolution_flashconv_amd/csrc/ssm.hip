@@ -220,7 +220,7 @@ hipError_t launch_ssm_filter(const float *A, const float *Bm, const float *C, co
 // described above k_spb_params.  The workspace size the API reports is the
 // larger of the two.
 struct SpLayout {
-    size_t fT, E, G, sc, fb, Eb, Rb, ab, ak, sb, total;
+    size_t fT, E, G, sc, fb, Eb, Rb, ab, sb, total;
 };
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -239,7 +239,6 @@ static SpLayout sp_layout(int64_t B, int64_t H, int64_t N, int64_t S, int64_t T,
         L.Eb = o; o += al256((size_t)H * 128 * 64 * 2);
         L.Rb = o; o += al256((size_t)H * 64 * 128 * 2);
         L.ab = o; o += al256((size_t)H * 64 * 8);
-        L.ak = o; o += al256((size_t)H * 64 * 8);
         L.sb = o; o += al256((size_t)H * 2 * 4);
     }
     L.total = o;
@@ -275,7 +274,6 @@ template <int LOG2M, int IO>
 __global__ __launch_bounds__(Plan<LOG2M>::NT) void k_sp_chunk_conv(
     const typename io_elem<IO>::T *__restrict__ u, const float *__restrict__ fT,
     typename io_elem<IO>::T *__restrict__ y, int B, int H, int64_t N, int T) {
-    using T_ = typename io_elem<IO>::T;
     __shared__ cf lds[Plan<LOG2M>::LDS_ELEMS];
     const int tid = threadIdx.x;
     const int h = blockIdx.x;
@@ -467,7 +465,6 @@ __device__ __forceinline__ uint16_t f16bits(double x) {
 //   Eb  [H, 128, 64]  row 2j+p, column k: part p of Abar_j^(63-k) Bbar_j / sB  fp16
 //   Rb  [H, 64, 128]  row t, columns 2j, 2j+1: 2 Re, -2 Im of C_j Abar_j^(t+1) / sC   fp16
 //   ab  [H, 64]       Abar_j^64                                                 complex
-//   ak  [H, 64]       Abar_j^1024                                               complex
 //   sb  [H, 2]        sB, sC: powers of two with |Bbar_j| < sB and 2 |C_j| < sC fp32
 // (modes j >= S are zero in every table).
 
@@ -483,8 +480,7 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
                                                    const float *__restrict__ Cc, const float *__restrict__ dt,
                                                    const float *__restrict__ D, float *__restrict__ fb,
                                                    uint16_t *__restrict__ Eb, uint16_t *__restrict__ Rb,
-                                                   cf *__restrict__ ab, cf *__restrict__ ak, float *__restrict__ sb,
-                                                   int S) {
+                                                   cf *__restrict__ ab, float *__restrict__ sb, int S) {
     __shared__ float Ft[64][65];  // Ft[k][j] = 2 Re(C_j Bbar_j Abar_j^k)
     const int h = blockIdx.x, tid = threadIdx.x, j = tid & 63, r = tid >> 6;
     const double dth = (double)dt[h];
@@ -539,7 +535,7 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
     *(u32x4 *)(eh + (2 * j) * 64 + 56 - 8 * r) = pack(er);
     *(u32x4 *)(eh + (2 * j + 1) * 64 + 56 - 8 * r) = pack(ei);
     if (r == 0) {
-        // Abar^64 (the block step), its correction row t = 63, and Abar^1024
+        // Abar^64 (the block step) and its correction row t = 63
         double qr, qi;
         apow64(are, aim, 64.0, qr, qi);
         const cf q = on ? mk((float)qr, (float)qi) : mk(0.f, 0.f);
@@ -547,8 +543,6 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
         const uint16_t zr = __builtin_bit_cast(uint16_t, (_Float16)(fcr * q.x - fci * q.y));
         const uint16_t zi = __builtin_bit_cast(uint16_t, (_Float16)(-(fcr * q.y + fci * q.x)));
         *(uint32_t *)(rh + 63 * 128 + 2 * j) = (uint32_t)zr | ((uint32_t)zi << 16);
-        apow64(are, aim, 1024.0, qr, qi);
-        ak[(size_t)h * 64 + j] = on ? mk((float)qr, (float)qi) : mk(0.f, 0.f);
         if (j == 0) {
             sb[2 * h] = ldexpf(1.f, eb);
             sb[2 * h + 1] = ldexpf(1.f, ec);
@@ -587,45 +581,39 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// LDS of the block kernel (37 KiB), per wave one row per block (66 complex:
-// 64 modes and a pad): first the block's contributions, then the fp16 states
-// entering the blocks (136 halves per row); and the waves' end states.
-constexpr int SPB_SS = 66;
-constexpr int SPB_XS = 136;
+constexpr int SPB_SS = 66;   // LDS row of one block: 64 modes (complex) and a pad
+constexpr int SPB_XS = 136;  // the same row read as the fp16 states entering the block
 
-// One workgroup of four waves per (batch row b, channel h), two waves per
-// SIMD (232 registers: the contribution and correction operands, 32 KiB of
-// the channel's tables, stay in registers for the whole row).  A step takes
-// 64 blocks (4096 samples); wave w holds blocks 16 w .. 16 w + 15 of it, the
-// 16 columns of its matrix-core products (the B operand, read straight from
-// HBM one step ahead: lane (n, g) loads samples 32 ks + 8 g .. + 7 of block
-// n).  Per step:
-//   1. contributions S[(j, part)][n] = Eb . U (8 row tiles) -> LDS;
-//   2. lane = mode: the wave's blocks scanned from a zero state (end state
-//      L_w; a wave with n_w < 16 valid blocks advances the state by
-//      Abar^(64 n_w)) -> LDS;
-//   3. one barrier; every wave folds the four waves' end states in order into
-//      the state carried between steps (the same in every wave), and takes
-//      the state entering its own first block;
-//   4. the scan again from that state gives the state entering each block,
-//      scaled by a power of two into fp16 range -> LDS (transposed to the
-//      B-operand layout); the blocks' own convolutions Y = L . U (the
-//      Toeplitz tiles depend only on their distance from the diagonal: 4
-//      distinct tiles, 6 products) and Y += Rb . X (the correction);
-//   5. y stored once, rounded once.
+// One wave per (batch row b, channel h), two waves per SIMD (232 registers:
+// the contribution and correction operands, 32 KiB of the channel's tables,
+// stay in registers for the whole row), walking the row in steps of 16
+// blocks (1024 samples).  The blocks are the 16 columns of its matrix-core
+// products (the B operand, read straight from HBM one step ahead: lane
+// (n, g) loads samples 32 ks + 8 g .. + 7 of block n).  Per step:
+//   1. contributions S[(j, part)][n] = Eb . U (8 row tiles) -> LDS (one row
+//      per block), read back with lane = mode j;
+//   2. from the state carried into the step, the state entering each block
+//      (x <- Abar^64 x + s, fp32), and the state carried out of the step;
+//      the entering states are scaled by a power of two into fp16 range and
+//      written back to LDS in the B-operand layout (over the contributions);
+//   3. the blocks' own convolutions Y = L . U (the Toeplitz tiles depend only
+//      on their distance from the diagonal: 4 distinct tiles, 6 products)
+//      and Y += Rb . X (the correction), in fp32;
+//   4. y rounded once and stored once.
+// A row's steps are sequential; the rows (2048 at B = 2, H = 1024) fill the
+// GPU at two waves per SIMD, with no barrier and no exchange between waves.
 template <int IO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_sp_block(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_sp_block(
     const typename io_elem<IO>::T *__restrict__ u, typename io_elem<IO>::T *__restrict__ y,
     const float *__restrict__ fb, const uint16_t *__restrict__ Eb, const uint16_t *__restrict__ Rb,
-    const cf *__restrict__ ab, const cf *__restrict__ ak, const float *__restrict__ sb,
-    const float *__restrict__ x_in, float *__restrict__ x_out, int H, int64_t N, int S) {
+    const cf *__restrict__ ab, const float *__restrict__ sb, const float *__restrict__ x_in,
+    float *__restrict__ x_out, int H, int64_t N, int S) {
     using namespace mf;
     using T_ = typename io_elem<IO>::T;
     const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __shared__ __attribute__((aligned(16))) cf Ss[4][16 * SPB_SS];
-    __shared__ cf Lsh[2][4][64];
+    const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
+    __shared__ __attribute__((aligned(16))) cf Sw[16 * SPB_SS];
+    uint16_t *const Xw = (uint16_t *)Sw;
     const size_t row = (size_t)b * H + h;
     // contribution operands (A): rows 16 rt + col (mode 8 rt + col / 2, part
     // col % 2), columns 32 ks + 8 g ..
@@ -661,7 +649,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 La[d][e] = (_Float16)(i < 0 ? 0.f : v);
             }
     }
-    const cf a = ab[(size_t)h * 64 + lane], a16 = ak[(size_t)h * 64 + lane];
+    const cf a = ab[(size_t)h * 64 + lane];
     const float sB = sb[2 * h], sC = sb[2 * h + 1];
     // state carried into the step (lane = mode), in units of sB
     cf X = mk(0.f, 0.f);
@@ -670,17 +658,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         X = mk(x_in[(row * S + lane) * 2] * r, x_in[(row * S + lane) * 2 + 1] * r);
     }
     const int64_t nch = N / 64;
-    const int nst = (int)((nch + 63) / 64);
+    const int nst = (int)((nch + 15) / 16);
     const T_ *urow = u + row * N;
     T_ *yrow = y + row * N;
     // the step's window of the row as a buffer resource (empty past the end:
     // its loads return zeros and its stores are dropped)
     auto window = [&](const void *base, int st) -> __amdgpu_buffer_rsrc_t {
-        const int64_t s0 = (int64_t)st * 4096, rem = N - s0;
-        const int bytes = rem <= 0 ? 0 : (int)(2 * (rem < 4096 ? rem : 4096));
+        const int64_t s0 = (int64_t)st * 1024, rem = N - s0;
+        const int bytes = rem <= 0 ? 0 : (int)(2 * (rem < 1024 ? rem : 1024));
         return row_rsrc((const char *)base + 2 * (rem > 0 ? s0 : 0), bytes);
     };
-    const int uoff = (16 * w + col) * 128 + 16 * g;
+    const int uoff = col * 128 + 16 * g;
     auto load = [&](int st, u32x4 (&v)[2]) {
         const __amdgpu_buffer_rsrc_t rs = window(urow, st);
 #pragma unroll
@@ -690,8 +678,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     u32x4 cur[2], nxt[2];
     load(0, cur);
     asm volatile("" : "+v"(cur[0]), "+v"(cur[1]));  // (complete before the loop: see below)
-    cf *const Sw = Ss[w];
-    uint16_t *const Xw = (uint16_t *)Sw;
     const f4 z4 = {0.f, 0.f, 0.f, 0.f};
     // a step's packed outputs, kept live into the next step: a store's data
     // registers may not be reused before the store completes, so reusing
@@ -700,7 +686,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int st = 0; st < nst; ++st) {
         load(st + 1, nxt);
         // B operands in fp16: bf16 activations are scaled by a power of two
-        // into fp16 range (largest magnitude of the wave's 1024 samples
+        // into fp16 range (largest magnitude of the step's 1024 samples
         // below 2^14), then converted exactly but for fp16's subnormals
         half8 U0, U1;
         float isu = 1.f;
@@ -734,7 +720,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             U0 = __builtin_bit_cast(half8, cur[0]);
             U1 = __builtin_bit_cast(half8, cur[1]);
         }
-        const int par = st & 1;
         // 1. contributions: rows 16 rt + 4 g + v of tile rt are (mode 8 rt + 2 g + v / 2, part v % 2)
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
@@ -743,64 +728,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             *(f4 *)(Sw + col * SPB_SS + 8 * rt + 2 * g) = s;
         }
         wave_lds_sync();
-        // 2. lane = mode j: this wave's blocks from a zero state
-        cf s[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) s[c] = cscale(Sw[c * SPB_SS + lane], isu);
-        const int64_t cb = (int64_t)st * 64 + 16 * w;
-        const int nv = (int)(nch - cb >= 16 ? 16 : (nch - cb > 0 ? nch - cb : 0));
-        cf L = mk(0.f, 0.f);
-        if (nv == 16) {
-#pragma unroll
-            for (int c = 0; c < 16; ++c) L = cfma(a, L, s[c]);
-        } else {
-#pragma unroll
-            for (int c = 0; c < 16; ++c)
-                if (c < nv) L = cfma(a, L, s[c]);
-        }
-        Lsh[par][w][lane] = L;
-        __syncthreads();
-        asm volatile("" : "+v"(opk[0]), "+v"(opk[1]), "+v"(opk[2]), "+v"(opk[3]));
-        // 3. the carried state through the four waves' blocks
-        //    (wave v's blocks advance the state by Abar^(64 n_v); n_v = 16
-        //    but in a row's last step)
-        cf X0 = X;
-        if ((int64_t)st * 64 + 64 <= nch) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                if (v == w) X0 = X;
-                X = cfma(a16, X, Lsh[par][v][lane]);
-            }
-        } else {
-            for (int v = 0; v < 4; ++v) {
-                const int64_t rv = nch - ((int64_t)st * 64 + 16 * v);
-                const int nvv = rv >= 16 ? 16 : (rv > 0 ? (int)rv : 0);
-                cf P = mk(1.f, 0.f);
-                for (int c = 0; c < nvv; ++c) P = cmul(a, P);
-                if (v == w) X0 = X;
-                X = cfma(P, X, Lsh[par][v][lane]);
-            }
-        }
-        // 4. states entering the wave's blocks
+        // 2. lane = mode j: the states entering the blocks, and the largest
+        //    of their parts (a step that ends the row early holds the state
+        //    after its last block)
+        const int64_t rem = nch - (int64_t)st * 16;
+        const int nv = rem >= 16 ? 16 : (int)rem;
         cf xin[16];
         float m = 0.f;
         {
-            cf x = X0;
+            cf x = X;
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
                 xin[c] = x;
                 m = fmaxf(m, fmaxf(fabsf(x.x), fabsf(x.y)));
-                x = cfma(a, x, s[c]);
+                const cf sc = cscale(Sw[c * SPB_SS + lane], isu);
+                if (nv == 16 || c < nv) x = cfma(a, x, sc);
             }
+            X = x;
         }
+        asm volatile("" : "+v"(opk[0]), "+v"(opk[1]), "+v"(opk[2]), "+v"(opk[3]));
         m = wave_max(m);
         int ex = 0;
         if (m > 0.f) (void)frexpf(m, &ex);
         ex = ex < -100 ? -100 : ex;
         const float sx = ldexpf(1.f, 14 - ex);  // |x sx| < 2^14
+        wave_lds_sync();  // (the contributions have been read)
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-            *(uint32_t *)(Xw + c * SPB_XS + 2 * lane) = pk(xin[c].x * sx, xin[c].y * sx);
+        for (int c = 0; c < 16; ++c) *(uint32_t *)(Xw + c * SPB_XS + 2 * lane) = pk(xin[c].x * sx, xin[c].y * sx);
         wave_lds_sync();
         half8 Xo[4];
 #pragma unroll
@@ -812,7 +766,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // would also wait for the stores.
         asm volatile("" : "+v"(nxt[0]), "+v"(nxt[1]));
         const __amdgpu_buffer_rsrc_t yrs = window(yrow, st);
-        // the blocks' own convolutions (Toeplitz tiles on and below the diagonal)
+        // 3. the blocks' own convolutions (Toeplitz tiles on and below the diagonal)
         f4 Y[4];
         Y[0] = mfma16(La[0], U0, z4);
         Y[1] = mfma16(La[1], U0, z4);
@@ -824,14 +778,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) cc = mfma16(Ra[rt][ks], Xo[ks], cc);
             const f4 o = Y[rt] * isu + cc * inv;
-            // 5. rows t = 16 rt + 4 g .. + 3 of block 16 w + col
+            // 4. rows t = 16 rt + 4 g .. + 3 of block col
             opk[rt] = u32x2{spb_pk<IO>(o[0], o[1]), spb_pk<IO>(o[2], o[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(opk[rt], yrs, (16 * w + col) * 128 + 2 * (16 * rt + 4 * g), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(opk[rt], yrs, col * 128 + 2 * (16 * rt + 4 * g), 0, 0);
         }
         cur[0] = nxt[0];
         cur[1] = nxt[1];
     }
-    if (x_out && w == 0 && lane < S) {
+    if (x_out && lane < S) {
         x_out[(row * S + lane) * 2] = X.x * sB;
         x_out[(row * S + lane) * 2 + 1] = X.y * sB;
     }
@@ -931,12 +885,12 @@ static hipError_t sp_run_block(const void *u, const float *A, const float *Bm, c
     const SpLayout L = sp_layout(B, H, N, S, T, false);
     char *w = (char *)ws;
     hipError_t e = launch(k_spb_params, dim3(H), dim3(512), 0, s, A, Bm, C, dt, D, (float *)(w + L.fb),
-                          (uint16_t *)(w + L.Eb), (uint16_t *)(w + L.Rb), (cf *)(w + L.ab), (cf *)(w + L.ak),
+                          (uint16_t *)(w + L.Eb), (uint16_t *)(w + L.Rb), (cf *)(w + L.ab),
                           (float *)(w + L.sb), S);
     if (e != hipSuccess) return e;
-    return launch(k_sp_block<IO>, dim3(H, B), dim3(256), 0, s, (const T_ *)u, (T_ *)y, (const float *)(w + L.fb),
+    return launch(k_sp_block<IO>, dim3(H, B), dim3(64), 0, s, (const T_ *)u, (T_ *)y, (const float *)(w + L.fb),
                   (const uint16_t *)(w + L.Eb), (const uint16_t *)(w + L.Rb), (const cf *)(w + L.ab),
-                  (const cf *)(w + L.ak), (const float *)(w + L.sb), x_in, x_out, H, N, S);
+                  (const float *)(w + L.sb), x_in, x_out, H, N, S);
 }
 
 hipError_t launch_state_pass(const void *u, const float *A, const float *Bm, const float *C,
