@@ -340,15 +340,17 @@ def torch_fftconv_bwd(u, f, D, dy):
 
 def sweep(dev, steps: int, warmup: int) -> list:
     """Sequence-length sweep at the H3-125M width (B=8, H=768, fp16, 64
-    modes): fused fft_conv for N <= 16384, state passing (T = 8192) at 16384
-    and above, and the backward pass (fft_conv_bwd) for N <= 8192, each
-    timed beside its unfused torch.fft counterpart on the same inputs."""
+    modes): fused fft_conv for N <= 16384 (the filter given), state passing
+    (T = min(N, 8192); the call builds its channel tables from the SSM
+    parameters) for N = 1024 ... 32768, and the backward pass (fft_conv_bwd)
+    for N <= 8192, each timed beside its unfused torch.fft counterpart on the
+    same inputs."""
     out = []
     pts = [(N, "fft_conv") for N in (256, 512, 1024, 2048, 4096, 8192, 16384)] + \
-          [(16384, "state_pass"), (32768, "state_pass")] + \
+          [(N, "state_pass") for N in (1024, 4096, 8192, 16384, 32768)] + \
           [(N, "fft_conv_bwd") for N in (256, 512, 1024, 2048, 4096, 8192)]
     for i, (N, kind) in enumerate(pts):
-        w = wl.Workload("sweep_%d" % N, kind, "f16", B=8, H=768, N=N, T=8192 if kind == "state_pass" else 0,
+        w = wl.Workload("sweep_%d" % N, kind, "f16", B=8, H=768, N=N, T=min(N, 8192) if kind == "state_pass" else 0,
                         seed=100 + i)
         c = Case(w, dev)
         _, m_ms = time_case(c, steps, warmup)
