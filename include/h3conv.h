@@ -201,8 +201,10 @@ h3conv_status h3conv_state_pass(const void *u, const float *A, const float *Bm, 
  * allocates or frees anything.
  * Sizes whose workspace, h3conv_workspace_size(H3CONV_OP_STATE_PASS, ...) for
  * this activation type, exceeds the array return H3CONV_ERR_WORKSPACE before
- * any HIP call (16-bit activations: about 90 KiB per channel at T = 8192,
- * so up to about 1450 channels of chunk 8192).
+ * any HIP call (16-bit activations: about 33 KiB of channel tables per
+ * channel whatever B, N and T, so up to about 3900 channels; fp32
+ * activations: the chunk filter, power tables and per-chunk contributions,
+ * which grow with T and with B * N / T).
  * All calls on one device share that device's array: calls that overlap in
  * time on one device (several streams, or several host threads) race and
  * must be serialised by the caller, e.g. by issuing them on one stream.
