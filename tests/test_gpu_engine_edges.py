@@ -143,3 +143,47 @@ def test_state_pass_rows_of_different_magnitude(io):
             assert np.count_nonzero(y[b]) == 0, (label, b)
         else:
             assert rows[b].max() <= TOL[io], (label, b, s, float(rows[b].max()))
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_state_pass_extreme_scales(io):
+    """16-bit state passing with inputs, initial states and SSM parameters far
+    from unit scale: rows whose magnitudes need the per-step power-of-two
+    input scale (bf16 beyond fp16's range), an initial state much larger than
+    the inputs (the carried state's fp16 scale), small B and large C (the
+    channel tables' scales); every row and the final state against the
+    recurrence."""
+    from parity_util import cplx, row_rel_l2
+    big, small, xs = (1e12, 1e-12, 1e10) if io == "bf16" else (1e2, 1e-2, 10.0)
+    sc = [big, small, 1.0]
+    B, H, S, T = len(sc), 3, 16, 512
+    N = 4 * T
+    label = "state_pass extreme scales io=%s B=%d H=%d N=%d T=%d" % (io, B, H, N, T)
+    say(label)
+    g = wl.gen(5151)
+    u = (torch.randn(B, H, N, generator=g, dtype=torch.float64) *
+         torch.tensor(sc, dtype=torch.float64)[:, None, None]).to(DT[io])
+    p = wl.diag_ssm_params(H, S, g)
+    p["Bm"] = p["Bm"] * 1e-3
+    p["C"] = p["C"] * 20.0
+    p["A"][1, :4, 0] = 0.0  # a few neutral modes in one channel
+    D = wl.normal((H,), g)
+    xi = (torch.randn(B, H, S, dtype=torch.float64, generator=g)
+          + 1j * torch.randn(B, H, S, dtype=torch.float64, generator=g)) * xs
+    xi = xi.to(torch.complex64)
+    dev = device()
+    d = {k: v.to(dev) for k, v in p.items()}
+    y, x = pkg.state_pass(u.to(dev), d["A"], d["Bm"], d["C"], d["dt"], D.to(dev), T, x_in=xi.to(dev),
+                          return_state=True)
+    torch.cuda.synchronize()
+    y = to_np(y)
+    ref, xr = oracle.ssm_recurrence(u, cplx(p["A"]), cplx(p["Bm"]), cplx(p["C"]), to_np(p["dt"]), to_np(D),
+                                    x_in=xi.numpy().astype(np.complex128), return_state=True)
+    assert np.isfinite(y).all(), label
+    rows = row_rel_l2(y.reshape(B * H, N), ref.reshape(B * H, N)).reshape(B, H)
+    gx = x.cpu().numpy().astype(np.complex128)
+    errx = float(np.linalg.norm(gx - xr) / np.linalg.norm(xr))
+    say("  per-row rel_l2 max by batch row: " + " ".join("%.1e" % r for r in rows.max(axis=1))
+        + "  state %.1e" % errx)
+    assert rows.max() <= TOL[io], (label, float(rows.max()))
+    assert errx <= 1e-3, (label, errx)
