@@ -43,6 +43,18 @@ __device__ __forceinline__ void apow64(double are, double aim, double n, double 
     re = m * cs;
     im = m * sn;
 }
+// Abar^n for the fp16 tables: the phase n dt Im A is formed and reduced by
+// whole turns in fp64, then the fp32 sine, cosine and exponential of the
+// reduced values (about one ulp of fp32 each)
+__device__ __forceinline__ cf apow_f32(double are, double aim, double n) {
+    constexpr double kTwoPi = 6.283185307179586232;
+    const double ph = aim * n;
+    const float phr = (float)fma(-rint(ph * (1.0 / kTwoPi)), kTwoPi, ph);
+    float sn, cs;
+    sincosf(phr, &sn, &cs);
+    const float m = expf((float)(are * n));
+    return mk(m * cs, m * sn);
+}
 __device__ __forceinline__ cf abar_pow(double are, double aim, double n) {
     double re, im;
     apow64(are, aim, n, re, im);
@@ -469,9 +481,11 @@ __device__ __forceinline__ uint16_t f16bits(double x) {
 // (modes j >= S are zero in every table).
 
 // The tables of one channel per workgroup of eight waves: wave r, lane j
-// takes the powers Abar_j^(8 r) .. Abar_j^(8 r + 7), the first an exact fp64
-// exponential and the rest stepped by Abar in fp32 (7 steps: relative error
-// ~1e-6, far below the fp16 tables' 2^-11), and writes their table entries
+// takes the powers Abar_j^(8 r) .. Abar_j^(8 r + 7), the first from an exact
+// fp64 phase reduction and fp32 sine, cosine and exponential, the rest
+// stepped by Abar in fp32 (7 steps: relative error ~1e-6, far below the fp16
+// tables' 2^-11; Abar^64 itself, which the scan applies once per block, is
+// an fp64 exponential), and writes their table entries
 // straight to memory: two 16-byte pieces of Eb (one per part) and, per
 // power, 4 bytes of a row of Rb (the wave's lanes fill the row).  The
 // filter's 64 taps are sums over the modes in fp64, in mode order (so the
@@ -481,7 +495,7 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
                                                    const float *__restrict__ D, float *__restrict__ fb,
                                                    uint16_t *__restrict__ Eb, uint16_t *__restrict__ Rb,
                                                    cf *__restrict__ ab, float *__restrict__ sb, int S) {
-    __shared__ float Ft[64][65];  // Ft[k][j] = 2 Re(C_j Bbar_j Abar_j^k)
+    __shared__ __attribute__((aligned(16))) float Ft[64][65];  // Ft[k][j] = 2 Re(C_j Bbar_j Abar_j^k)
     const int h = blockIdx.x, tid = threadIdx.x, j = tid & 63, r = tid >> 6;
     const double dth = (double)dt[h];
     const bool on = j < S;
@@ -505,11 +519,8 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
     const float fbr = (float)(br * rB), fbi = (float)(bi * rB);  // Bbar_j / sB
     const float fcr = (float)(cr * rC2), fci = (float)(ci * rC2);  // 2 C_j / sC
     const float fwr = (float)(2.0 * (cr * br - ci * bi)), fwi = (float)(2.0 * (cr * bi + ci * br));  // 2 C_j Bbar_j
-    double2 p0, s0;
-    apow64(are, aim, 8.0 * r, p0.x, p0.y);
-    apow64(are, aim, 1.0, s0.x, s0.y);
-    cf p = on ? mk((float)p0.x, (float)p0.y) : mk(0.f, 0.f);
-    const cf st = mk((float)s0.x, (float)s0.y);
+    cf p = on ? apow_f32(are, aim, 8.0 * r) : mk(0.f, 0.f);
+    const cf st = apow_f32(are, aim, 1.0);
     uint16_t er[8], ei[8];
     uint16_t *const rh = Rb + (size_t)h * 8192;
 #pragma unroll
@@ -549,10 +560,21 @@ __global__ __launch_bounds__(512) void k_spb_params(const float *__restrict__ A,
         }
     }
     __syncthreads();
-    if (tid < 64) {
-        double acc = tid == 0 ? (double)D[h] : 0.0;
-        for (int jj = 0; jj < 64; ++jj) acc += (double)Ft[tid][jj];
-        fb[(size_t)h * 64 + tid] = (float)acc;
+    // taps: wave r sums modes 8 r .. 8 r + 7 of tap k = lane, then tap k sums
+    // the eight partial sums (fixed order throughout)
+    {
+        double part = 0.0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) part += (double)Ft[j][8 * r + q];
+        __syncthreads();  // (every term has been read)
+        ((double *)&Ft[0][0])[r * 64 + j] = part;
+        __syncthreads();
+        if (tid < 64) {
+            double acc = tid == 0 ? (double)D[h] : 0.0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc += ((const double *)&Ft[0][0])[q * 64 + tid];
+            fb[(size_t)h * 64 + tid] = (float)acc;
+        }
     }
 }
 
