@@ -10,6 +10,7 @@ row, each within the bar (1e-5 fp32, 2e-2 fp16/bf16 with fp32 accumulation);
 and a second run of the same call bitwise equal to the first (no atomics, no
 order-dependent reductions).  Every step prints its wall time.
 """
+import dataclasses
 import time
 
 import numpy as np
@@ -89,8 +90,11 @@ def test_fft_conv_workload_every_row(name):
     clk.lap("done")
 
 
-def test_state_64k_workload_every_row():
-    w = wl.WORKLOADS["state_64k"]
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_state_64k_workload_every_row(io):
+    """The state_64k workload (fp16, as the bench times it) and the same
+    shape with bf16 activations (the per-step power-of-two input scale)."""
+    w = dataclasses.replace(wl.WORKLOADS["state_64k"], dtype=io)
     dev = device()
     say("workload %s B=%d H=%d N=%d T=%d %s: full size, every row against the full-length recurrence"
         % (w.name, w.B, w.H, w.N, w.T, w.dtype))
