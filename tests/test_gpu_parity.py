@@ -289,6 +289,24 @@ def test_state_pass_16bit_ragged_steps(io, N, T, S):
 
 
 @pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_state_pass_16bit_same_for_every_chunk_length(io):
+    """16-bit state passing carries the state at every 64-sample block, a
+    refinement of every chunk grid T: outputs and final states are bitwise
+    the same for every valid T."""
+    dev = device()
+    B, H, N, S = 2, 3, 8192, 64
+    say("state_pass T-independence io=%s B=%d H=%d N=%d S=%d" % (io, B, H, N, S))
+    u, p, D = _sp_inputs(B, H, N, S, io, seed=808)
+    d = {k: v.to(dev) for k, v in p.items()}
+    ud, Dd = u.to(dev), D.to(dev)
+    y0, x0 = pkg.state_pass(ud, d["A"], d["Bm"], d["C"], d["dt"], Dd, 64, return_state=True)
+    for T in (128, 1024, 8192):
+        y, x = pkg.state_pass(ud, d["A"], d["Bm"], d["C"], d["dt"], Dd, T, return_state=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0) and torch.equal(x, x0), T
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
 def test_state_pass_zero_state_equals_none(io):
     """An all-zero x_in gives exactly the result of no x_in (the carried
     state starts at zero either way)."""
